@@ -1,0 +1,221 @@
+"""Plain, slow, float64 oracle of chunk-wise recurrent hybrid attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the library
+path may import or call this module.
+
+Sources (page title, then the part of the page):
+
+* "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers",
+  abstract: attention that mixes exact softmax attention with linear
+  attention, evaluated chunk by chunk as a recurrence with a memory footprint
+  that does not grow with the sequence.
+* "Long-Horizon Streaming Video Generation via Hybrid Attention with Decoupled
+  Distillation" (explainer page), section 2.A "Hybrid Attention": recent
+  frames inside a sliding window get softmax attention, organised in blocks as
+  in FlashAttention; the key/value content of frames that leave the window is
+  accumulated online into a fixed-size linear-attention state.  Section 1
+  "Background and problem": the sliding window keeps only recent frames in a
+  KV cache of an autoregressive (streaming) generator.
+* "Transformers are RNNs: Fast Autoregressive Transformers with Linear
+  Attention" (listed among the works ReHyAt builds on): the feature map
+  phi(x) = elu(x) + 1 and the recurrent form S = sum phi(k) v^T,
+  z = sum phi(k).
+
+The pages print no equation for the hybrid.  This oracle uses the shared
+normaliser form: for query i in chunk c = floor(i / C) with window w chunks
+(the query's own chunk included),
+
+    W(i) = { j : max(0, c - w + 1) <= floor(j / C) <= c }   softmax window
+    H(i) = { j : floor(j / C) <= c - w }                      folded history
+    a_ij = exp(q_i . k_j / sqrt(d))   for j in W(i)
+         = phi(q_i) . phi(k_j)         for j in H(i)
+         = 0                           otherwise
+    out_i = sum_j a_ij v_j / sum_j a_ij
+
+Splitting the sums over H(i) gives S_c = sum_{H} phi(k_j) v_j^T and
+z_c = sum_{H} phi(k_j), the state the recurrence carries.  Readings taken where
+the pages are silent: chunk-causal (no future chunk is visible, no token mask
+inside the window); w counts the query's own chunk; w = 0 means the own chunk
+is already folded into the state (pure linear attention); phi acts on the raw
+q and k, feature size d; softmax scale 1/sqrt(d) with the natural exponential.
+
+Every function here is pinned by tests against something other than itself
+(brute force, torch's SDPA in the w >= N limit, a token-by-token linear RNN
+in the w = 0 limit, hand-derived closed forms, and algebraic invariants).
+
+Arrays are numpy float64.  Per-head functions take [L, d] arrays; the
+``*_batched`` helpers loop over [B, H, L, d].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# exp of a score is taken literally (no max subtraction); scores this large
+# would overflow float64, so the oracle refuses them rather than return inf.
+_MAX_ABS_SCORE = 700.0
+
+
+def phi(x):
+    """Feature map elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (always > 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def window_range(c: int, w: int):
+    """Chunks [lo, hi] of the softmax window of query chunk c (empty if w == 0)."""
+    if w <= 0:
+        return c + 1, c  # empty
+    return max(0, c - w + 1), c
+
+
+def _scores(q, k):
+    d = q.shape[-1]
+    s = (q @ k.T) / math.sqrt(d)
+    if s.size and np.abs(s).max() >= _MAX_ABS_SCORE:
+        raise OverflowError("score magnitude too large for the literal exponential")
+    return s
+
+
+def brute_masked(q, k, v, C: int, w: int, return_den: bool = False):
+    """The definition written out as one L x L weight matrix (tiny inputs only).
+
+    a_ij as in the module docstring, out = (A V) / (A 1).
+    """
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L = q.shape[0]
+    cid = np.arange(L) // C
+    cq, ck = cid[:, None], cid[None, :]
+    in_window = (ck <= cq) & (ck >= cq - w + 1) if w > 0 else np.zeros((L, L), bool)
+    in_history = ck <= cq - w
+    a = np.zeros((L, L))
+    s = _scores(q, k)
+    a[in_window] = np.exp(s[in_window])
+    lin = phi(q) @ phi(k).T
+    a[in_history] = lin[in_history]
+    den = a.sum(axis=1)
+    out = (a @ v) / den[:, None]
+    return (out, den) if return_den else out
+
+
+def chunk_states(k, v, C: int):
+    """Per-chunk contributions U_c = phi(K_c)^T V_c (d x d) and u_c = sum phi(k_t)."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    L, d = k.shape
+    N = L // C
+    fk = phi(k)
+    U = np.zeros((N, d, v.shape[1]))
+    u = np.zeros((N, d))
+    for c in range(N):
+        sl = slice(c * C, (c + 1) * C)
+        U[c] = fk[sl].T @ v[sl]
+        u[c] = fk[sl].sum(axis=0)
+    return U, u
+
+
+def state_scan(k, v, C: int, w: int):
+    """State seen by each query chunk: S_c = sum_{j <= c-w} U_j, z_c likewise.
+
+    Zero for c < w.  With w = 0 the own chunk is included.
+    """
+    U, u = chunk_states(k, v, C)
+    N = U.shape[0]
+    S = np.zeros_like(U)
+    z = np.zeros_like(u)
+    for c in range(N):
+        last = c - w  # last folded chunk
+        if last >= 0:
+            S[c] = U[: last + 1].sum(axis=0)
+            z[c] = u[: last + 1].sum(axis=0)
+    return S, z
+
+
+def state_after(k, v, C: int, w: int, T: int):
+    """State after T committed streaming steps: every chunk j <= T - w folded.
+
+    This is the state the next chunk (index T) attends to.
+    """
+    U, u = chunk_states(k[: T * C], v[: T * C], C)
+    last = T - w
+    if last < 0:
+        return np.zeros(U.shape[1:]), np.zeros(u.shape[1:])
+    return U[: last + 1].sum(axis=0), u[: last + 1].sum(axis=0)
+
+
+def hybrid(q, k, v, C: int, w: int, return_den: bool = False):
+    """Chunked evaluation of the definition: per query chunk, the window block
+    of exponentials plus the history folded into (S_c, z_c)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L, d = q.shape
+    N = L // C
+    S, z = state_scan(k, v, C, w)
+    fq = phi(q)
+    out = np.empty((L, v.shape[1]))
+    den_all = np.empty(L)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        num = fq[rows] @ S[c]
+        den = fq[rows] @ z[c]
+        lo, hi = window_range(c, w)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            e = np.exp(_scores(q[rows], k[keys]))
+            num = num + e @ v[keys]
+            den = den + e.sum(axis=1)
+        out[rows] = num / den[:, None]
+        den_all[rows] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_rows(q, k, v, C: int, w: int, rows, S=None, z=None, return_den=False):
+    """The definition evaluated for selected query rows only.
+
+    For full-size workloads: the per-chunk states (S, z from ``state_scan``)
+    cost O(L d^2); each row then costs O(w C d).  Pass S, z to reuse them.
+    """
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    if S is None:
+        S, z = state_scan(k, v, C, w)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]))
+    den_all = np.empty(rows.size)
+    for n, i in enumerate(rows):
+        c = int(i) // C
+        fq = phi(q[i])
+        num = fq @ S[c]
+        den = fq @ z[c]
+        lo, hi = window_range(c, w)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            e = np.exp(_scores(q[i : i + 1], k[keys]))[0]
+            num = num + e @ v[keys]
+            den = den + e.sum()
+        out[n] = num / den
+        den_all[n] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_batched(q, k, v, C: int, w: int, return_den: bool = False):
+    """``hybrid`` over [B, H, L, d] arrays (any float dtype; computed in float64)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    den = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], den[b, h] = hybrid(q[b, h], k[b, h], v[b, h], C, w, return_den=True)
+    return (out, den) if return_den else out
+
+
+def state_scan_batched(k, v, C: int, w: int):
+    """``state_scan`` over [B, H, L, d]: S [B, H, N, d, d], z [B, H, N, d]."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    B, H, L, d = k.shape
+    N = L // C
+    S = np.empty((B, H, N, d, v.shape[-1]))
+    z = np.empty((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            S[b, h], z[b, h] = state_scan(k[b, h], v[b, h], C, w)
+    return S, z

@@ -1,0 +1,332 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* phi: closed-form values and torch's elu + 1.
+* hand-derived closed forms for a six-token case (tests/golden/hand_worked_d1.json).
+* brute-force masked quadratic form vs the chunked oracle over many shapes.
+* w >= N limit: torch's scaled_dot_product_attention with a block-causal mask;
+  C = 1: its is_causal mode; N = 1: plain full attention.
+* w = 0 limit: a token-by-token linear-attention recurrence written here.
+* invariants: constant V, linearity and translation in V, permutation of a
+  chunk's tokens, convex hull.
+* the state scan: summed chunk contributions equal one matmul; lag relations.
+* planted mistakes in the oracle are caught by at least one of the pins.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rha_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_d1.json")
+_NS = {"e": math.e, "ln2": math.log(2.0), "ln3": math.log(3.0)}
+
+
+def _ev(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, dict(_NS)))
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _qkv(L, d, seed, qs=1.0, ks=1.0):
+    return _rand((L, d), seed, qs), _rand((L, d), seed + 1, ks), _rand((L, d), seed + 2)
+
+
+# ---------------------------------------------------------------- phi
+
+def test_phi_closed_form():
+    assert O.phi(0.0) == 1.0
+    assert O.phi(2.0) == 3.0
+    assert O.phi(-1.0) == pytest.approx(1.0 / math.e, rel=1e-15)
+    assert O.phi(-50.0) == pytest.approx(math.exp(-50.0), rel=1e-15)
+    x = np.linspace(-30, 30, 10001)
+    assert (O.phi(x) > 0).all()
+    # continuous at 0 from both sides
+    assert O.phi(-1e-12) == pytest.approx(1.0, abs=1e-11)
+    assert O.phi(1e-12) == pytest.approx(1.0, abs=1e-11)
+
+
+def test_phi_matches_torch_elu_plus_one():
+    x = _rand((4096,), 7, 3.0)
+    ref = torch.nn.functional.elu(torch.from_numpy(x), alpha=1.0) + 1.0
+    # torch forms elu + 1 as expm1(x) + 1, which loses absolute precision 1e-16
+    np.testing.assert_allclose(O.phi(x), ref.numpy(), rtol=1e-15, atol=2e-16)
+
+
+# ---------------------------------------------------------------- golden
+
+def _golden_check(case, data):
+    q = np.array([[_ev(s)] for s in data["q"]])
+    k = np.array([[_ev(s)] for s in data["k"]])
+    v = np.array([[_ev(s)] for s in data["v"]])
+    C, w = data["C"], case["w"]
+    want = np.array([_ev(s) for s in case["out"]])
+    errs = []
+    for fn in (O.brute_masked, O.hybrid):
+        got, den = fn(q, k, v, C, w, return_den=True)
+        errs.append(np.max(np.abs(got[:, 0] - want) / np.maximum(1.0, np.abs(want))))
+        if "den" in case:
+            wd = np.array([_ev(s) for s in case["den"]])
+            errs.append(np.max(np.abs(den - wd) / wd))
+    S, z = O.state_scan(k, v, C, w)
+    errs.append(np.max(np.abs(S[:, 0, 0] - [_ev(s) for s in case["S"]])))
+    errs.append(np.max(np.abs(z[:, 0] - [_ev(s) for s in case["z"]])))
+    return max(errs)
+
+
+def _golden_max_err():
+    data = json.load(open(GOLDEN))
+    return max(_golden_check(case, data) for case in data["cases"])
+
+
+@pytest.mark.parametrize("case_idx", [0, 1, 2])
+def test_hand_worked_closed_forms(case_idx):
+    data = json.load(open(GOLDEN))
+    assert _golden_check(data["cases"][case_idx], data) < 1e-14
+
+
+# ---------------------------------------------------------------- brute vs chunked
+
+SWEEP = [
+    (C, N, w, d)
+    for C in (1, 3, 64)
+    for N in (1, 2, 4, 6)
+    for w in sorted({0, 1, 2, N, N + 3})
+    for d in (4, 64)
+    if C * N <= 512
+]
+
+
+def _brute_vs_chunked(C, N, w, d, seed=3):
+    q, k, v = _qkv(C * N, d, seed + 10 * C + N, qs=1.5)
+    a, da = O.brute_masked(q, k, v, C, w, return_den=True)
+    b, db = O.hybrid(q, k, v, C, w, return_den=True)
+    return max(np.max(np.abs(a - b)) / np.max(np.abs(a)), np.max(np.abs(da - db) / da))
+
+
+@pytest.mark.parametrize("C,N,w,d", SWEEP)
+def test_brute_equals_chunked(C, N, w, d):
+    assert _brute_vs_chunked(C, N, w, d) < 1e-12
+
+
+def test_hybrid_rows_equals_hybrid():
+    q, k, v = _qkv(6 * 37, 16, 91)
+    full, den = O.hybrid(q, k, v, 37, 2, return_den=True)
+    rows = np.array([0, 36, 37, 73, 74, 111, 150, 221])
+    got, gden = O.hybrid_rows(q, k, v, 37, 2, rows, return_den=True)
+    np.testing.assert_allclose(got, full[rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gden, den[rows], rtol=1e-13)
+
+
+# ---------------------------------------------------------------- w >= N limit: SDPA
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    t = lambda x: torch.from_numpy(x)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask,
+                                                         is_causal=causal)
+    return o[0, 0].numpy()
+
+
+def _block_causal(L, C):
+    c = torch.arange(L) // C
+    return (c[None, :] <= c[:, None])[None, None]
+
+
+def _sdpa_limit_err(C=48, N=5, d=64, seed=21):
+    q, k, v = _qkv(C * N, d, seed, qs=2.0)
+    errs = []
+    for w in (N, N + 1, 10 * N):
+        errs.append(np.max(np.abs(O.hybrid(q, k, v, C, w) - _sdpa(q, k, v, _block_causal(C * N, C)))))
+        errs.append(np.max(np.abs(O.brute_masked(q, k, v, C, w) - _sdpa(q, k, v, _block_causal(C * N, C)))))
+    # the last chunk sees every key: plain unmasked attention for its rows
+    last = slice((N - 1) * C, N * C)
+    errs.append(np.max(np.abs(O.hybrid(q, k, v, C, N)[last] - _sdpa(q, k, v)[last])))
+    return max(errs)
+
+
+def test_window_all_equals_block_causal_sdpa():
+    assert _sdpa_limit_err() < 1e-12
+
+
+def test_chunk1_window_all_equals_causal_sdpa():
+    q, k, v = _qkv(97, 32, 5, qs=2.0)
+    np.testing.assert_allclose(O.hybrid(q, k, v, 1, 97), _sdpa(q, k, v, causal=True), atol=1e-12)
+
+
+def test_one_chunk_equals_full_attention():
+    q, k, v = _qkv(130, 64, 9, qs=2.0)
+    for w in (1, 2, 7):
+        np.testing.assert_allclose(O.hybrid(q, k, v, 130, w), _sdpa(q, k, v), atol=1e-12)
+
+
+# ---------------------------------------------------------------- w = 0 limit: linear RNN
+
+def _torch_phi(x):
+    return (torch.nn.functional.elu(torch.from_numpy(x)) + 1.0).numpy()
+
+
+def _linear_rnn(q, k, v, C):
+    """Causal linear attention token by token: the state absorbs every token of
+    a chunk before any query of that chunk reads it (C = 1: plain RNN form)."""
+    L, d = q.shape
+    fq, fk = _torch_phi(q), _torch_phi(k)
+    s = np.zeros((d, v.shape[1]))
+    z = np.zeros(d)
+    out = np.empty_like(v)
+    for c0 in range(0, L, C):
+        for t in range(c0, c0 + C):
+            s += np.outer(fk[t], v[t])
+            z += fk[t]
+        for t in range(c0, c0 + C):
+            out[t] = fq[t] @ s / (fq[t] @ z)
+    return out
+
+
+def _rnn_limit_err():
+    errs = []
+    for C, N in ((1, 83), (7, 9), (32, 4)):
+        q, k, v = _qkv(C * N, 16, 40 + C)
+        ref = _linear_rnn(q, k, v, C)
+        errs.append(np.max(np.abs(O.hybrid(q, k, v, C, 0) - ref)))
+        errs.append(np.max(np.abs(O.brute_masked(q, k, v, C, 0) - ref)))
+    return max(errs)
+
+
+def test_window0_equals_linear_rnn():
+    assert _rnn_limit_err() < 1e-12
+
+
+# ---------------------------------------------------------------- invariants
+
+MIXED = [(20, 6, 2, 16), (33, 5, 3, 32), (16, 8, 1, 8)]
+
+
+@pytest.mark.parametrize("C,N,w,d", MIXED)
+def test_constant_values_reproduce(C, N, w, d):
+    q, k, _ = _qkv(C * N, d, 61, qs=3.0)
+    v = np.tile(_rand((1, d), 62), (C * N, 1))
+    np.testing.assert_allclose(O.hybrid(q, k, v, C, w), v, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("C,N,w,d", MIXED)
+def test_linear_and_translation_in_values(C, N, w, d):
+    q, k, v1 = _qkv(C * N, d, 71, qs=2.0)
+    v2 = _rand(v1.shape, 72)
+    f = lambda v: O.hybrid(q, k, v, C, w)
+    np.testing.assert_allclose(f(2.5 * v1 - 0.75 * v2), 2.5 * f(v1) - 0.75 * f(v2), atol=1e-12)
+    shift = _rand((1, d), 73)
+    np.testing.assert_allclose(f(v1 + shift), f(v1) + shift, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w,d", MIXED)
+def test_permuting_a_chunk_permutes_only_its_rows(C, N, w, d):
+    q, k, v = _qkv(C * N, d, 81, qs=2.0)
+    base = O.hybrid(q, k, v, C, w)
+    c = N // 2
+    perm = np.arange(C * N)
+    perm[c * C:(c + 1) * C] = c * C + np.random.default_rng(82).permutation(C)
+    got = O.hybrid(q[perm], k[perm], v[perm], C, w)
+    np.testing.assert_allclose(got, base[perm], atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w,d", MIXED)
+def test_convex_hull(C, N, w, d):
+    q, k, v = _qkv(C * N, d, 91, qs=3.0)
+    out = O.hybrid(q, k, v, C, w)
+    for i in range(0, C * N, 7):
+        c = i // C
+        reach = (c + 1) * C  # chunk-causal: every key up to the own chunk has a_ij > 0
+        assert (out[i] <= v[:reach].max(axis=0) + 1e-12).all()
+        assert (out[i] >= v[:reach].min(axis=0) - 1e-12).all()
+
+
+def test_future_chunks_do_not_matter():
+    C, N, w, d = 24, 5, 2, 16
+    q, k, v = _qkv(C * N, d, 101)
+    base = O.hybrid(q, k, v, C, w)
+    k2, v2 = k.copy(), v.copy()
+    k2[3 * C:] += 5.0
+    v2[3 * C:] -= 7.0
+    np.testing.assert_allclose(O.hybrid(q, k2, v2, C, w)[: 3 * C], base[: 3 * C], atol=0)
+
+
+# ---------------------------------------------------------------- state scan
+
+def _scan_identity_err(C=40, N=7, d=24, w=2):
+    _, k, v = _qkv(C * N, d, 111)
+    U, u = O.chunk_states(k, v, C)
+    fk = _torch_phi(k)
+    errs = [np.max(np.abs(U.sum(axis=0) - fk.T @ v)), np.max(np.abs(u.sum(axis=0) - fk.sum(axis=0)))]
+    S, z = O.state_scan(k, v, C, w)
+    errs.append(np.max(np.abs(S[:w])))
+    errs.append(np.max(np.abs(z[:w])))
+    for c in range(w, N):
+        lastc = c - w
+        ref = fk[: (lastc + 1) * C].T @ v[: (lastc + 1) * C]
+        errs.append(np.max(np.abs(S[c] - ref)))
+        errs.append(np.max(np.abs(z[c] - fk[: (lastc + 1) * C].sum(axis=0))))
+    for c in range(w + 1, N):
+        errs.append(np.max(np.abs(S[c] - S[c - 1] - U[c - w])))
+    return max(errs)
+
+
+def test_state_scan_identities():
+    assert _scan_identity_err() < 1e-11
+
+
+def test_state_after_matches_scan():
+    C, N, d = 16, 9, 8
+    _, k, v = _qkv(C * N, d, 121)
+    for w in (1, 3, 9):
+        S, z = O.state_scan(k, v, C, w)
+        for T in range(1, N):
+            sT, zT = O.state_after(k, v, C, w, T)
+            np.testing.assert_allclose(sT, S[T], atol=1e-12)
+            np.testing.assert_allclose(zT, z[T], atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _all_pins_err():
+    return {
+        "golden": _golden_max_err(),
+        "brute": max(_brute_vs_chunked(C, N, w, d) for (C, N, w, d) in [(3, 6, 2, 4), (64, 4, 1, 64)]),
+        "sdpa": _sdpa_limit_err(),
+        "rnn": _rnn_limit_err(),
+        "scan": _scan_identity_err(),
+    }
+
+
+MUTANTS = {
+    "phi_without_plus_one": ("phi", lambda orig: (lambda x: orig(x) - 1.0)),
+    "phi_linear_for_negatives": ("phi", lambda orig: (lambda x: np.asarray(x, np.float64) + 1.0)),
+    "missing_score_scale": ("_scores", lambda orig: (lambda q, k: q @ k.T)),
+    "score_sign_flip": ("_scores", lambda orig: (lambda q, k: -orig(q, k))),
+    "window_one_chunk_short": ("window_range",
+                               lambda orig: (lambda c, w: (max(0, c - w + 2), c) if w > 0 else (c + 1, c))),
+    "transposed_chunk_state": ("chunk_states",
+                               lambda orig: (lambda k, v, C: (np.swapaxes(orig(k, v, C)[0], 1, 2),
+                                                              orig(k, v, C)[1]))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    try:
+        errs = _all_pins_err()
+    except (OverflowError, FloatingPointError, ValueError):
+        return  # the oracle refuses the mutated arithmetic outright: caught
+    # NaN (a zero or negative normaliser) counts as caught
+    assert any(not (e < 1e-6) for e in errs.values()), errs
+
+
+def test_unmutated_pins_pass():
+    errs = _all_pins_err()
+    assert max(errs.values()) < 1e-11, errs
