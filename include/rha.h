@@ -1,0 +1,179 @@
+/*
+ * librha: chunk-wise recurrent hybrid attention for video diffusion
+ * transformers, for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Sources: "ReHyAt: Recurrent Hybrid Attention for Video
+ * Diffusion Transformers" (abstract: softmax attention combined with linear
+ * attention, evaluated chunk by chunk as a recurrence with constant memory);
+ * "Long-Horizon Streaming Video Generation via Hybrid Attention with
+ * Decoupled Distillation" (explainer page, section 2.A "Hybrid Attention":
+ * softmax attention over a sliding window of recent frames computed in
+ * FlashAttention-style blocks; frames leaving the window are folded online
+ * into a fixed-size linear-attention state); "Transformers are RNNs" (listed
+ * by the ReHyAt page among its foundations) for phi(x) = elu(x) + 1.
+ *
+ * Per (batch b, head h) with q, k, v in R^{L x d}, chunk length C (one latent
+ * frame), N = L / C chunks, window w chunks counting the query's own chunk:
+ *
+ *   query i in chunk c = floor(i / C)
+ *   window  W(i) = keys of chunks max(0, c-w+1) .. c      (empty if w == 0)
+ *   history H(i) = keys of chunks 0 .. c-w                (empty if c < w)
+ *   S_c = sum_{j in H} phi(k_j) v_j^T   (d x d),   z_c = sum_{j in H} phi(k_j)
+ *   out_i = ( sum_{j in W} exp(q_i.k_j/sqrt d) v_j + phi(q_i)^T S_c )
+ *         / ( sum_{j in W} exp(q_i.k_j/sqrt d)     + phi(q_i)^T z_c )
+ *
+ * Readings where the pages are silent: attention is chunk-causal (no chunk
+ * after the query's own is visible; no token mask inside the window); w >= N
+ * gives block-causal softmax attention; w == 0 is linear attention whose
+ * state already holds the own chunk; phi acts on the raw q and k.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory, keeps no pointer after a call returns and has
+ *    no global mutable state except a thread-local error message.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; results are ready when the stream is.
+ *  - Every argument is validated before anything is enqueued: a call that
+ *    returns an error has had no side effect.  rha_last_error() then gives a
+ *    human-readable reason.  NaN/Inf in the data are not detected; they
+ *    propagate into the outputs.
+ *  - Element layout of q, k, v and out: element (b, h, t, f) of a tensor with
+ *    base pointer P is at P[b*stride_b + h*stride_h + t*stride_t + f] (feature
+ *    stride 1).  For bf16 every base pointer and every stride*2 must be a
+ *    multiple of 16 bytes; for f32 every base pointer and stride*4 likewise.
+ *  - State tensors are always contiguous float32.
+ */
+#ifndef RHA_H
+#define RHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RHA_OK = 0,
+  RHA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad stride or alignment */
+  RHA_ERR_UNSUPPORTED = 2, /* valid but not implemented (head_dim, dtype) */
+  RHA_ERR_CURSOR = 3,      /* streaming cursor out of range */
+  RHA_ERR_HIP = 4          /* HIP runtime error: no device, launch failure */
+} rha_status;
+
+typedef enum {
+  RHA_F32 = 0, /* IEEE float32 storage; all arithmetic in float32 */
+  RHA_BF16 = 1 /* bfloat16 storage; bf16 matrix-core products, float32 accumulation */
+} rha_dtype;
+
+typedef struct {
+  int32_t batch;     /* B >= 0 */
+  int32_t heads;     /* H >= 0 */
+  int32_t head_dim;  /* d: 64 or 128 */
+  int32_t chunk_len; /* C >= 1 tokens per chunk */
+  int32_t n_chunks;  /* N >= 0 chunks per sequence, L = N*C (ignored by rha_stream_step) */
+  int32_t window;    /* w >= 0 softmax window in chunks, the query's own chunk included */
+  int32_t dtype;     /* rha_dtype of q, k, v, out and the KV cache */
+  int32_t reserved;  /* must be 0 */
+  int64_t stride_b;  /* element strides of q, k, v and out (see above) */
+  int64_t stride_h;
+  int64_t stride_t;  /* >= head_dim */
+} rha_problem;
+
+/*
+ * rha_state_scan -- the folded history each query chunk reads.
+ *
+ * ReHyAt abstract (chunk-wise recurrent form); Hybrid Forcing explainer
+ * section 2.A (frames leaving the window are accumulated into the state).
+ * For every (b, h) and chunk c in [0, N):
+ *   S[b,h,c] = sum over chunks j <= c - w of phi(K_j)^T V_j      (d x d)
+ *   z[b,h,c] = sum over chunks j <= c - w of sum_t phi(k_t)       (d)
+ * and zero where c < w.  Per chunk the contribution is one bf16 (f32 for
+ * RHA_F32) matrix-core product with float32 accumulation; the prefix over
+ * chunks is summed in float32 in chunk order, so results are bitwise
+ * reproducible.
+ *
+ *   k, v : [B, H, L, d] with the problem's strides, dtype p->dtype (read)
+ *   S    : [B, H, N, d, d] float32 contiguous (written)
+ *   z    : [B, H, N, d]    float32 contiguous (written)
+ *
+ * rha_hybrid_fwd must be given the S, z produced with the same window.
+ */
+rha_status rha_state_scan(const rha_problem* p, const void* k, const void* v, float* S, float* z,
+                          void* stream);
+
+/*
+ * rha_hybrid_fwd -- the hybrid attention output for a whole sequence.
+ *
+ * Hybrid Forcing explainer section 2.A (window attention in FlashAttention
+ * blocks plus the linear state) with the shared normaliser written at the top
+ * of this header.  One fused pass per query tile: the linear term
+ * phi(Q)^T S_c, phi(Q).z_c seeds the running numerator and denominator at
+ * reference maximum 0, then the window keys are streamed with an online
+ * maximum.
+ *
+ *   q, k, v : [B, H, L, d] with the problem's strides, dtype p->dtype (read)
+ *   S, z    : the output of rha_state_scan for the same problem (read)
+ *   out     : [B, H, L, d] with the problem's strides, dtype p->dtype (written)
+ *   lse     : NULL, or [B, H, L] float32 contiguous: ln of the denominator
+ *
+ * out must not overlap q, k, v, S or z.
+ */
+rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, const void* v,
+                          const float* S, const float* z, void* out, float* lse, void* stream);
+
+/*
+ * Streaming cursor: the number of chunks committed so far, which is the
+ * index of the chunk the next call processes.  Start at 0 with S, z zeroed.
+ */
+typedef struct {
+  int64_t t;
+} rha_stream_cursor;
+
+/*
+ * rha_stream_step -- one new chunk of an autoregressive (streaming) generator.
+ *
+ * Hybrid Forcing explainer section 1 (a sliding-window KV cache of recent
+ * frames) and section 2.A (frames evicted from the window are folded online
+ * into the linear state; the local window can then shrink, e.g. from 21 to 9
+ * frames).  With t = cursor->t and window w >= 1:
+ *   1. the new chunk's k, v are copied into cache slot t % w;
+ *   2. the new chunk's queries attend, with exact softmax, to the cached
+ *      chunks max(0, t-w+1) .. t (all in the cache now) plus the state S, z
+ *      (chunks 0 .. t-w), with the shared normaliser;
+ *   3. if commit != 0 and t >= w-1: chunk t-w+1 (slot (t+1) % w) leaves the
+ *      window, so phi(K)^T V and sum phi(k) of that slot are added into S, z;
+ *      then cursor->t is incremented.
+ * With commit == 0 nothing but the cache slot of chunk t changes, so the same
+ * chunk can be re-run (e.g. once per denoising step) before committing it.
+ * Outputs equal those of rha_hybrid_fwd over the concatenated sequence, and
+ * S, z after each commit equal rha_state_scan's entry for chunk t+1 bitwise.
+ *
+ *   p->n_chunks is ignored; p's strides describe q_new, k_new, v_new, out
+ *   q_new, k_new, v_new : [B, H, C, d] (read)
+ *   k_cache, v_cache    : [B, H, w, C, d] contiguous, dtype p->dtype (read/written)
+ *   S : [B, H, d, d] float32, z : [B, H, d] float32 (read; written on commit)
+ *   out : [B, H, C, d] (written);  lse : NULL or [B, H, C] float32
+ *   cursor : host memory, read and (on commit) updated at enqueue time
+ *
+ * Errors: RHA_ERR_CURSOR if cursor is NULL or cursor->t < 0.
+ */
+rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache, float* S, float* z,
+                           rha_stream_cursor* cursor, int32_t commit, void* out, float* lse,
+                           void* stream);
+
+/* Static name of a status code. */
+const char* rha_status_string(rha_status s);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* rha_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t rha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RHA_H */

@@ -1,0 +1,36 @@
+"""Python binding of librha (chunk-wise recurrent hybrid attention, MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``librha.so`` (built from ``csrc/`` by ``build.py``).  PyTorch
+supplies device memory and the current HIP stream.  If the library has not
+been built, every call raises ``LibraryNotBuilt``; there is no fallback.
+
+Functions mirror the C ABI in ``include/rha.h``:
+
+* ``state_scan(k, v, C, w)``                     -> S [B,H,N,d,d], z [B,H,N,d]
+* ``hybrid_fwd(q, k, v, S, z, C, w)``            -> out [B,H,L,d] (and lse)
+* ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
+"""
+from ._rha import (
+    LibraryNotBuilt,
+    RhaError,
+    StreamState,
+    hybrid_fwd,
+    lib,
+    lib_path,
+    state_scan,
+    stream_step,
+    version,
+)
+
+__all__ = [
+    "LibraryNotBuilt",
+    "RhaError",
+    "StreamState",
+    "hybrid_fwd",
+    "lib",
+    "lib_path",
+    "state_scan",
+    "stream_step",
+    "version",
+]

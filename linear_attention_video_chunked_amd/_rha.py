@@ -1,0 +1,211 @@
+"""ctypes marshalling for librha.so.  See ``include/rha.h`` for the contract."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librha.so")
+
+RHA_F32, RHA_BF16 = 0, 1
+_STATUS = {0: "RHA_OK", 1: "RHA_ERR_INVALID_ARG", 2: "RHA_ERR_UNSUPPORTED", 3: "RHA_ERR_CURSOR", 4: "RHA_ERR_HIP"}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class RhaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
+        ("n_chunks", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+    ]
+
+
+class Cursor(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int64)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load librha.so (once).  Raises LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{_LIB_PATH} is missing: build it with `python -m linear_attention_video_chunked_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    L.rha_state_scan.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
+    L.rha_hybrid_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
+                                  ctypes.c_int32, _vp, _vp, _vp]
+    for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_stream_step"):
+        getattr(L, name).restype = ctypes.c_int
+    L.rha_status_string.argtypes = [ctypes.c_int]
+    L.rha_status_string.restype = ctypes.c_char_p
+    L.rha_last_error.argtypes = []
+    L.rha_last_error.restype = ctypes.c_char_p
+    L.rha_version.argtypes = []
+    L.rha_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def version() -> int:
+    return int(lib().rha_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise RhaError(status, lib().rha_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RHA_BF16
+    if t.dtype == torch.float32:
+        return RHA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _problem(x: torch.Tensor, C: int, w: int, n_chunks: int) -> Problem:
+    if x.dim() != 4:
+        raise ValueError("tensors are [B, H, T, d]")
+    if x.stride(3) != 1:
+        raise ValueError("feature dimension must be contiguous")
+    B, H, _, d = x.shape
+    return Problem(B, H, d, C, n_chunks, w, _dtype_code(x), 0, x.stride(0), x.stride(1), x.stride(2))
+
+
+def _same_layout(ref: torch.Tensor, *others: torch.Tensor):
+    for o in others:
+        if o.shape != ref.shape or o.stride() != ref.stride() or o.dtype != ref.dtype:
+            raise ValueError("q, k, v and out must share shape, strides and dtype")
+        if o.device != ref.device:
+            raise ValueError("all tensors must be on the same device")
+
+
+def state_scan(k: torch.Tensor, v: torch.Tensor, C: int, w: int,
+               S: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rha_state_scan: S[b,h,c] = sum_{chunks j <= c-w} phi(K_j)^T V_j, z likewise."""
+    _same_layout(k, v)
+    B, H, L, d = k.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    if S is None:
+        S = torch.empty((B, H, N, d, d), dtype=torch.float32, device=k.device)
+    if z is None:
+        z = torch.empty((B, H, N, d), dtype=torch.float32, device=k.device)
+    prob = _problem(k, C, w, N)
+    _check(lib().rha_state_scan(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _stream(stream)))
+    return S, z
+
+
+def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
+               C: int, w: int, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               return_lse: bool = False, stream=None):
+    """rha_hybrid_fwd: the fused window + linear-state attention pass."""
+    if out is None:
+        out = torch.empty_like(q)
+    _same_layout(q, k, v, out)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S, z must be float32 [B,H,N,d,d] and [B,H,N,d]")
+    if not (S.is_contiguous() and z.is_contiguous()):
+        raise ValueError("S and z must be contiguous")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    prob = _problem(q, C, w, N)
+    _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
+                                _ptr(lse), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+class StreamState:
+    """Caller-owned streaming state: KV cache ring of w chunks, S, z, cursor."""
+
+    def __init__(self, B: int, H: int, d: int, C: int, w: int, dtype=torch.bfloat16, device="cuda"):
+        self.B, self.H, self.d, self.C, self.w = B, H, d, C, w
+        self.k_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
+        self.v_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
+        self.S = torch.zeros((B, H, d, d), dtype=torch.float32, device=device)
+        self.z = torch.zeros((B, H, d), dtype=torch.float32, device=device)
+        self.cursor = Cursor(0)
+
+    @property
+    def t(self) -> int:
+        return int(self.cursor.t)
+
+    def clone(self) -> "StreamState":
+        n = StreamState.__new__(StreamState)
+        n.B, n.H, n.d, n.C, n.w = self.B, self.H, self.d, self.C, self.w
+        n.k_cache, n.v_cache = self.k_cache.clone(), self.v_cache.clone()
+        n.S, n.z = self.S.clone(), self.z.clone()
+        n.cursor = Cursor(self.cursor.t)
+        return n
+
+
+def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                commit: bool = True, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """rha_stream_step: attend one new chunk to the cache + state; on commit fold
+    the chunk that leaves the window and advance the cursor."""
+    if out is None:
+        out = torch.empty_like(q_new)
+    _same_layout(q_new, k_new, v_new, out)
+    B, H, C, d = q_new.shape
+    if (B, H, C, d) != (st.B, st.H, st.C, st.d):
+        raise ValueError("chunk shape does not match the stream state")
+    if q_new.dtype != st.k_cache.dtype:
+        raise ValueError("chunk dtype does not match the cache")
+    if lse is not None and (lse.shape != (B, H, C) or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 contiguous [B,H,C]")
+    prob = _problem(q_new, C, st.w, 1)
+    _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
+                                 _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
+                                 ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _stream(stream)))
+    return out

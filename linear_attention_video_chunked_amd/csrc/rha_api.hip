@@ -1,0 +1,296 @@
+// C ABI of librha (declared in include/rha.h): argument validation, then
+// kernel launches on the caller's stream.  Every check runs before anything
+// is enqueued, so a call that fails has no side effect.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "rha.h"
+#include "rha_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rha_status fail(rha_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+rha_status ok() {
+  g_last_error.clear();
+  return RHA_OK;
+}
+
+rha_status hip_fail(hipError_t e, const char* what) {
+  return fail(RHA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+
+int elem_bytes(const rha_problem* p) { return p->dtype == RHA_BF16 ? 2 : 4; }
+
+// Checks shared by all calls.  `stream` selects the streaming rules
+// (n_chunks ignored, window >= 1).
+rha_status check_problem(const rha_problem* p, bool stream) {
+  if (p == nullptr) return fail(RHA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 0 || p->heads < 0)
+    return fail(RHA_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 0", p->batch, p->heads);
+  if (p->dtype != RHA_F32 && p->dtype != RHA_BF16)
+    return fail(RHA_ERR_INVALID_ARG, "dtype %d is not RHA_F32 or RHA_BF16", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if (p->chunk_len < 1) return fail(RHA_ERR_INVALID_ARG, "chunk_len %d must be >= 1", p->chunk_len);
+  if (!stream && p->n_chunks < 0) return fail(RHA_ERR_INVALID_ARG, "n_chunks %d must be >= 0", p->n_chunks);
+  if (p->window < 0) return fail(RHA_ERR_INVALID_ARG, "window %d must be >= 0", p->window);
+  if (stream && p->window < 1) return fail(RHA_ERR_INVALID_ARG, "streaming needs window >= 1 (got %d)", p->window);
+  if (p->reserved != 0) return fail(RHA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (p->stride_t < p->head_dim)
+    return fail(RHA_ERR_INVALID_ARG, "stride_t %lld < head_dim %d", (long long)p->stride_t, p->head_dim);
+  if (p->stride_h < 0 || p->stride_b < 0) return fail(RHA_ERR_INVALID_ARG, "strides must be >= 0");
+  const int64_t eb = elem_bytes(p);
+  if ((p->stride_t * eb) % 16 || (p->stride_h * eb) % 16 || (p->stride_b * eb) % 16)
+    return fail(RHA_ERR_INVALID_ARG, "strides must be multiples of 16 bytes");
+  // index arithmetic in the kernels keeps token and tile counts in 32 bits
+  const int64_t nc = stream ? 1 : p->n_chunks;
+  const int64_t L = nc * (int64_t)p->chunk_len;
+  const int64_t bhn = (int64_t)p->batch * p->heads * nc;
+  const int64_t win_keys = (int64_t)(p->window < 1 ? 1 : p->window) * p->chunk_len;
+  if (L > INT32_MAX / 2 || bhn * p->chunk_len > INT32_MAX || (int64_t)p->batch * p->heads > INT32_MAX / 2 ||
+      (stream && win_keys > INT32_MAX / 2))
+    return fail(RHA_ERR_INVALID_ARG, "problem too large for 32-bit tile indexing");
+  return RHA_OK;
+}
+
+bool empty(const rha_problem* p, bool stream) {
+  return p->batch == 0 || p->heads == 0 || (!stream && p->n_chunks == 0);
+}
+
+rha_status need(const void* ptr, const char* name, bool data = true, int elem_align = 16) {
+  if (ptr == nullptr) return fail(RHA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (data && (reinterpret_cast<uintptr_t>(ptr) % elem_align) != 0)
+    return fail(RHA_ERR_INVALID_ARG, "%s is not %d-byte aligned", name, elem_align);
+  return RHA_OK;
+}
+
+#define RHA_TRY(expr)             \
+  do {                            \
+    rha_status _s = (expr);       \
+    if (_s != RHA_OK) return _s;  \
+  } while (0)
+
+rha::ChunkStateParams state_params(const rha_problem* p, const void* k, const void* v, float* S, float* z) {
+  rha::ChunkStateParams c{};
+  c.k = k;
+  c.v = v;
+  c.S = S;
+  c.z = z;
+  c.kv_sb = p->stride_b;
+  c.kv_sh = p->stride_h;
+  c.kv_st = p->stride_t;
+  c.B = p->batch;
+  c.H = p->heads;
+  c.C = p->chunk_len;
+  return c;
+}
+
+hipError_t launch_chunk_state(const rha_problem* p, const rha::ChunkStateParams& c, hipStream_t s) {
+  return p->dtype == RHA_BF16 ? rha::launch_chunk_state_bf16(c, p->head_dim, s)
+                              : rha::launch_chunk_state_f32(c, p->head_dim, s);
+}
+
+hipError_t launch_fwd(const rha_problem* p, rha::FwdParams& f, hipStream_t s) {
+  return p->dtype == RHA_BF16 ? rha::launch_fwd_bf16(f, p->head_dim, s) : rha::launch_fwd_f32(f, p->head_dim, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+rha_status rha_state_scan(const rha_problem* p, const void* k, const void* v, float* S, float* z, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S, "S"));
+  RHA_TRY(need(z, "z"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int N = p->n_chunks, w = p->window, d = p->head_dim;
+  const int nproc = N - w;  // chunks 0 .. N-1-w are folded into some later chunk's state
+  if (nproc > 0) {
+    rha::ChunkStateParams c = state_params(p, k, v, S, z);
+    c.chunk0 = 0;
+    c.n_chunks = nproc;
+    c.slot_offset = w;
+    c.accumulate = 0;
+    c.s_bh = (int64_t)N * d * d;
+    c.z_bh = (int64_t)N * d;
+    hipError_t e = launch_chunk_state(p, c, s);
+    if (e != hipSuccess) return hip_fail(e, "chunk state launch");
+  }
+  rha::PrefixParams pp{S, z, p->batch * p->heads, N, w, d};
+  hipError_t e = rha::launch_prefix(pp, s);
+  if (e != hipSuccess) return hip_fail(e, "prefix launch");
+  return ok();
+}
+
+rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                          const float* z, void* out, float* lse, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(q, "q"));
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S, "S"));
+  RHA_TRY(need(z, "z"));
+  RHA_TRY(need(out, "out"));
+  if (lse != nullptr) RHA_TRY(need(lse, "lse", true, 4));
+  rha::FwdParams f{};
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.out = out;
+  f.lse = lse;
+  f.S = S;
+  f.z = z;
+  f.q_sb = f.kv_sb = p->stride_b;
+  f.q_sh = f.kv_sh = p->stride_h;
+  f.q_st = f.kv_st = p->stride_t;
+  f.B = p->batch;
+  f.H = p->heads;
+  f.C = p->chunk_len;
+  f.w = p->window;
+  f.n_qchunks = p->n_chunks;
+  f.stream_mode = 0;
+  f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  hipError_t e = launch_fwd(p, f, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
+rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
+                           int32_t commit, void* out, float* lse, void* stream) {
+  RHA_TRY(check_problem(p, true));
+  if (cursor == nullptr) return fail(RHA_ERR_CURSOR, "cursor is NULL");
+  if (cursor->t < 0) return fail(RHA_ERR_CURSOR, "cursor->t = %lld < 0", (long long)cursor->t);
+  if (empty(p, true)) {
+    if (commit) cursor->t += 1;
+    return ok();
+  }
+  RHA_TRY(need(q_new, "q_new"));
+  RHA_TRY(need(k_new, "k_new"));
+  RHA_TRY(need(v_new, "v_new"));
+  RHA_TRY(need(k_cache, "k_cache"));
+  RHA_TRY(need(v_cache, "v_cache"));
+  RHA_TRY(need(S, "S"));
+  RHA_TRY(need(z, "z"));
+  RHA_TRY(need(out, "out"));
+  if (lse != nullptr) RHA_TRY(need(lse, "lse", true, 4));
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t t = cursor->t;
+  const int w = p->window, C = p->chunk_len, d = p->head_dim;
+  const int slot = (int)(t % w);
+
+  // 1. the new chunk's keys and values into its cache slot
+  rha::CopyParams cp{};
+  cp.sb = p->stride_b;
+  cp.sh = p->stride_h;
+  cp.st = p->stride_t;
+  cp.B = p->batch;
+  cp.H = p->heads;
+  cp.C = C;
+  cp.d = d;
+  cp.w = w;
+  cp.slot = slot;
+  cp.elem_bytes = elem_bytes(p);
+  cp.src = k_new;
+  cp.dst = k_cache;
+  hipError_t e = rha::launch_copy_chunk(cp, s);
+  if (e != hipSuccess) return hip_fail(e, "cache copy launch");
+  cp.src = v_new;
+  cp.dst = v_cache;
+  e = rha::launch_copy_chunk(cp, s);
+  if (e != hipSuccess) return hip_fail(e, "cache copy launch");
+
+  // 2. attention of the new chunk: cached window (chunks max(0,t-w+1)..t) + state
+  const int64_t in_window = t + 1 < w ? t + 1 : w;
+  rha::FwdParams f{};
+  f.q = q_new;
+  f.k = k_cache;
+  f.v = v_cache;
+  f.out = out;
+  f.lse = lse;
+  f.S = S;
+  f.z = z;
+  f.q_sb = p->stride_b;
+  f.q_sh = p->stride_h;
+  f.q_st = p->stride_t;
+  f.kv_sb = (int64_t)p->heads * w * C * d;
+  f.kv_sh = (int64_t)w * C * d;
+  f.kv_st = d;
+  f.B = p->batch;
+  f.H = p->heads;
+  f.C = C;
+  f.w = w;
+  f.n_qchunks = 1;
+  f.stream_mode = 1;
+  f.n_keys = (int)(in_window * C);
+  f.has_state = t >= w ? 1 : 0;
+  f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  e = launch_fwd(p, f, s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+
+  // 3. commit: fold the chunk that leaves the window, advance the cursor
+  if (commit) {
+    if (t >= w - 1) {
+      rha::ChunkStateParams c{};
+      c.k = k_cache;
+      c.v = v_cache;
+      c.S = S;
+      c.z = z;
+      c.kv_sb = f.kv_sb;
+      c.kv_sh = f.kv_sh;
+      c.kv_st = d;
+      c.B = p->batch;
+      c.H = p->heads;
+      c.C = C;
+      c.chunk0 = (int)((t + 1) % w);
+      c.n_chunks = 1;
+      c.slot_offset = 0;
+      c.accumulate = 1;
+      c.s_bh = (int64_t)d * d;
+      c.z_bh = d;
+      e = launch_chunk_state(p, c, s);
+      if (e != hipSuccess) return hip_fail(e, "fold launch");
+    }
+    cursor->t = t + 1;
+  }
+  return ok();
+}
+
+const char* rha_status_string(rha_status st) {
+  switch (st) {
+    case RHA_OK: return "RHA_OK";
+    case RHA_ERR_INVALID_ARG: return "RHA_ERR_INVALID_ARG";
+    case RHA_ERR_UNSUPPORTED: return "RHA_ERR_UNSUPPORTED";
+    case RHA_ERR_CURSOR: return "RHA_ERR_CURSOR";
+    case RHA_ERR_HIP: return "RHA_ERR_HIP";
+  }
+  return "RHA_ERR_UNKNOWN";
+}
+
+const char* rha_last_error(void) { return g_last_error.c_str(); }
+
+int32_t rha_version(void) { return 100; }  // 0.1.0
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Small memory-bound kernels: the lagged prefix over chunk states and the
+// copy of a new chunk into the streaming KV cache.
+#include "rha_device.hpp"
+#include "rha_launch.hpp"
+
+namespace rha {
+namespace {
+
+// ReHyAt (abstract): the chunk-wise recurrence carries one state from chunk to
+// chunk.  Slots c >= w hold per-chunk contributions on entry; on exit slot c
+// holds their running sum over slots w..c, i.e. the state of every chunk up to
+// c - w.  Slots c < w see no folded history and are zeroed.  Sequential float32
+// sum in chunk order, the same order the streaming fold uses.
+__global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
+  const int64_t per = (int64_t)p.d * p.d + p.d;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)p.BH * per) return;
+  const int64_t bh = idx / per, e = idx % per;
+  float* base;
+  int64_t stride;
+  if (e < (int64_t)p.d * p.d) {
+    stride = (int64_t)p.d * p.d;
+    base = p.S + bh * p.N * stride + e;
+  } else {
+    stride = p.d;
+    base = p.z + bh * p.N * stride + (e - (int64_t)p.d * p.d);
+  }
+  float acc = 0.f;
+  for (int c = 0; c < p.N; ++c) {
+    float* ptr = base + c * stride;
+    if (c < p.w) {
+      *ptr = 0.f;
+    } else {
+      acc = (c == p.w) ? *ptr : acc + *ptr;
+      *ptr = acc;
+    }
+  }
+}
+
+// 16-byte copy of one [B,H,C,d] chunk (strided rows) into slot `slot` of a
+// contiguous [B,H,w,C,d] cache.
+__global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p) {
+  const int row_vecs = p.d * p.elem_bytes / 16;
+  const int64_t total = (int64_t)p.B * p.H * p.C * row_vecs;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int vcol = (int)(idx % row_vecs);
+  const int64_t r = idx / row_vecs;
+  const int t = (int)(r % p.C);
+  const int64_t bh = r / p.C;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const unsigned char* src = (const unsigned char*)p.src +
+                             ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
+                             vcol * 16;
+  unsigned char* dst = (unsigned char*)p.dst +
+                       (((bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
+  st16(dst, ld16(src));
+}
+
+}  // namespace
+
+hipError_t launch_prefix(const PrefixParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefix_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.H * p.C * (p.d * p.elem_bytes / 16);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace rha

@@ -1,0 +1,84 @@
+// Kernel parameter blocks and launchers (host side), shared by the C ABI
+// (rha_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rha {
+
+// One fused hybrid-attention pass over query tiles.  Two key sources:
+//   seq mode    (stream_mode == 0): keys are the query sequence itself; query
+//               chunk c reads keys [max(0,c-w+1)*C, (c+1)*C) and state slot
+//               S[bh, c] (present when w == 0 or c >= w).
+//   stream mode (stream_mode == 1): one query chunk (n_qchunks == 1); keys are
+//               rows [0, n_keys) of a contiguous cache [bh][w*C][d]; state
+//               S[bh] present when has_state != 0.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const float* S;
+  const float* z;
+  int64_t q_sb, q_sh, q_st;   // q and out strides (elements)
+  int64_t kv_sb, kv_sh, kv_st;  // k and v strides (elements)
+  int B, H, C, w;
+  int n_qchunks;      // query chunks per (b, h)
+  int tiles_per_chunk;  // set by the launcher
+  int total_tiles;      // set by the launcher
+  int stream_mode;
+  int n_keys;         // stream mode
+  int has_state;      // stream mode
+  float scale_log2;   // log2(e) / sqrt(d)
+};
+
+// Per-chunk state contribution phi(K_c)^T V_c, sum_t phi(k_t) for a list of
+// chunks, written to (or, with accumulate, added into) float32 state slots.
+//   chunk index j in [0, n_chunks) of head bh reads tokens
+//   [ (chunk0 + j) * C, +C ) of k, v; it writes slot (j + slot_offset) of
+//   S[bh] (slot stride d*d, head stride s_bh) and z[bh] (slot stride d, head
+//   stride z_bh).
+struct ChunkStateParams {
+  const void* k;
+  const void* v;
+  float* S;
+  float* z;
+  int64_t kv_sb, kv_sh, kv_st;
+  int64_t s_bh, z_bh;
+  int B, H, C;
+  int chunk0;
+  int n_chunks;
+  int slot_offset;
+  int accumulate;
+};
+
+// In-place inclusive prefix over the state slots of every head:
+//   slot c < w        -> 0
+//   slot c >= w       -> sum of the per-chunk contributions stored in slots w..c
+struct PrefixParams {
+  float* S;
+  float* z;
+  int BH, N, w, d;
+};
+
+// Copy one chunk [B,H,C,d] (strided) into cache slot `slot` of [B,H,w,C,d].
+struct CopyParams {
+  const void* src;
+  void* dst;
+  int64_t sb, sh, st;
+  int B, H, C, d, w, slot;
+  int elem_bytes;
+};
+
+// The forward launchers fill in tiles_per_chunk and total_tiles (they depend
+// on the kernel's tile height) before launching.
+hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
+hipError_t launch_fwd_f32(FwdParams& p, int d, hipStream_t s);
+hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s);
+hipError_t launch_chunk_state_f32(const ChunkStateParams& p, int d, hipStream_t s);
+hipError_t launch_prefix(const PrefixParams& p, hipStream_t s);
+hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s);
+
+}  // namespace rha

@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rha.h declares, and rejects bad arguments before enqueuing anything.
+
+Only argument errors are exercised here: each call below fails validation, so
+no HIP runtime call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_video_chunked_amd import _rha
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rha.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_rha.lib_path()):
+        from linear_attention_video_chunked_amd import build
+        build.build(verbose=False)
+    return _rha.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rha_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("rha_state_scan", "rha_hybrid_fwd", "rha_stream_step", "rha_status_string",
+              "rha_last_error", "rha_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in _rha._STATUS.items():
+        assert L.rha_status_string(code).decode() == name
+    assert L.rha_version() >= 100
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, head_dim=128, chunk_len=64, n_chunks=4, window=2, dtype=_rha.RHA_BF16,
+                reserved=0, stride_b=2 * 256 * 128, stride_h=256 * 128, stride_t=128)
+    base.update(kw)
+    return _rha.Problem(**base)
+
+
+# fake, 256-byte aligned addresses: never dereferenced because validation fails first
+P = ctypes.c_void_p(0x100000)
+BAD = ctypes.c_void_p(0x100008)
+
+
+def _scan(L, prob, k=P, v=P, S=P, z=P):
+    return L.rha_state_scan(ctypes.byref(prob) if prob is not None else None, k, v, S, z, None)
+
+
+def _fwd(L, prob, q=P, k=P, v=P, S=P, z=P, out=P, lse=None):
+    return L.rha_hybrid_fwd(ctypes.byref(prob) if prob is not None else None, q, k, v, S, z, out, lse, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, 1), ("heads", -3, 1), ("head_dim", 96, 2), ("head_dim", 256, 2),
+    ("chunk_len", 0, 1), ("n_chunks", -1, 1), ("window", -1, 1), ("dtype", 7, 1),
+    ("reserved", 1, 1), ("stride_t", 64, 1), ("stride_t", 132, 1), ("stride_h", -128, 1),
+])
+def test_invalid_problem_fields(L, field, value, code):
+    prob = _prob(**{field: value})
+    assert _scan(L, prob) == code
+    assert L.rha_last_error().decode() != ""
+    assert _fwd(L, prob) == code
+
+
+def test_null_problem(L):
+    assert _scan(L, None) == 1
+    assert _fwd(L, None) == 1
+
+
+@pytest.mark.parametrize("which", ["k", "v", "S", "z"])
+def test_scan_null_and_misaligned_pointers(L, which):
+    prob = _prob()
+    assert _scan(L, prob, **{which: None}) == 1
+    assert "NULL" in L.rha_last_error().decode()
+    assert _scan(L, prob, **{which: BAD}) == 1
+    assert "aligned" in L.rha_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "S", "z", "out"])
+def test_fwd_null_and_misaligned_pointers(L, which):
+    prob = _prob()
+    assert _fwd(L, prob, **{which: None}) == 1
+    assert _fwd(L, prob, **{which: BAD}) == 1
+
+
+def test_fwd_misaligned_lse(L):
+    assert _fwd(L, _prob(), lse=ctypes.c_void_p(0x100002)) == 1
+
+
+def test_empty_problems_are_no_ops(L):
+    # nothing to compute: OK without touching any pointer
+    for kw in (dict(batch=0), dict(heads=0), dict(n_chunks=0)):
+        prob = _prob(**kw)
+        assert _scan(L, prob, k=None, v=None, S=None, z=None) == 0
+        assert _fwd(L, prob, q=None, k=None, v=None, S=None, z=None, out=None) == 0
+
+
+def test_f32_strides_must_be_16_byte_multiples(L):
+    assert _scan(L, _prob(dtype=_rha.RHA_F32, stride_t=130)) == 1
+    # 132 float32 = 528 bytes is a multiple of 16
+    prob = _prob(dtype=_rha.RHA_F32, stride_t=132, head_dim=128)
+    assert _scan(L, prob, k=None) == 1  # still fails, but on the pointer, not the stride
+    assert "NULL" in L.rha_last_error().decode()
+
+
+def _step(L, prob, cursor, commit=1, **ptrs):
+    a = dict(q=P, k=P, v=P, kc=P, vc=P, S=P, z=P, out=P)
+    a.update(ptrs)
+    return L.rha_stream_step(ctypes.byref(prob), a["q"], a["k"], a["v"], a["kc"], a["vc"], a["S"], a["z"],
+                             cursor, commit, a["out"], None, None)
+
+
+def test_stream_validation(L):
+    prob = _prob(window=0)
+    cur = _rha.Cursor(0)
+    assert _step(L, prob, ctypes.byref(cur)) == 1  # streaming needs w >= 1
+    prob = _prob(window=3)
+    assert _step(L, prob, None) == 3
+    cur = _rha.Cursor(-1)
+    assert _step(L, prob, ctypes.byref(cur)) == 3
+    cur = _rha.Cursor(5)
+    assert _step(L, prob, ctypes.byref(cur), kc=None) == 1
+    assert cur.t == 5  # nothing happened
+    assert _step(L, prob, ctypes.byref(cur), out=BAD) == 1
+    assert cur.t == 5
+
+
+def test_stream_empty_problem_advances_cursor(L):
+    prob = _prob(batch=0, window=3)
+    cur = _rha.Cursor(4)
+    assert _step(L, prob, ctypes.byref(cur), commit=1, q=None) == 0
+    assert cur.t == 5
+    assert _step(L, prob, ctypes.byref(cur), commit=0, q=None) == 0
+    assert cur.t == 5
+
+
+def test_too_large_problem_rejected(L):
+    prob = _prob(chunk_len=1 << 20, n_chunks=1 << 12)
+    assert _scan(L, prob) == 1
+    assert "too large" in L.rha_last_error().decode()
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_rha, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_rha, "_lib", None)
+    with pytest.raises(_rha.LibraryNotBuilt):
+        _rha.lib()

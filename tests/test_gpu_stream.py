@@ -1,0 +1,144 @@
+"""GPU parity of rha_stream_step: a stream of chunks equals the hybrid over
+the concatenated sequence (oracle), the folded state equals the oracle's
+prefix, and equals rha_state_scan bitwise; resuming from copied buffers and
+re-running an uncommitted chunk change nothing."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, Workload, gen_qkv
+import linear_attention_video_chunked_amd as rha
+from parity_utils import TOL, rel_l2, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rha.lib()
+
+
+def chunk(x, t, C):
+    return x[:, :, t * C:(t + 1) * C].to(DEV)
+
+
+def run_stream(wl, q, k, v, T, lse=False):
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w,
+                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device=DEV)
+    outs, lses = [], []
+    for t in range(T):
+        l = torch.empty((wl.B, wl.H, wl.C), dtype=torch.float32, device=DEV) if lse else None
+        outs.append(rha.stream_step(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C), lse=l))
+        lses.append(l)
+    torch.cuda.synchronize()
+    return st, outs, lses
+
+
+SMALL = {
+    "bf16_d128_C100_w3": Workload("s1", 300, B=1, H=2, d=128, C=100, N=12, w=3, dtype="bf16"),
+    "bf16_d128_C100_w3_q4": Workload("s2", 301, B=2, H=2, d=128, C=100, N=10, w=3, dtype="bf16", qscale=4.0),
+    "bf16_d128_C57_w1": Workload("s3", 302, B=1, H=2, d=128, C=57, N=8, w=1, dtype="bf16"),
+    "bf16_d64_C64_w2": Workload("s4", 303, B=1, H=3, d=64, C=64, N=9, w=2, dtype="bf16"),
+    "f32_d64_C48_w2": Workload("s5", 304, B=1, H=2, d=64, C=48, N=7, w=2, dtype="f32"),
+    "f32_d128_C20_w4": Workload("s6", 305, B=1, H=1, d=128, C=20, N=9, w=4, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_stream_matches_oracle_on_concatenation(name):
+    wl = SMALL[name]
+    q, k, v = gen_qkv(wl)
+    st, outs, lses = run_stream(wl, q, k, v, wl.N, lse=True)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    ref, den = oracle.hybrid_batched(q64, k64, v64, wl.C, wl.w, return_den=True)
+    tol = TOL[wl.dtype]
+    for t, o in enumerate(outs):
+        sl = slice(t * wl.C, (t + 1) * wl.C)
+        e = rel_l2(to64(o), ref[:, :, sl])
+        assert e <= tol, f"step {t}: rel-L2 {e:.3e}"
+        assert np.abs(to64(lses[t]) - np.log(den[:, :, sl])).max() <= (1e-2 if wl.dtype == "bf16" else 1e-4)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            Sref, zref = oracle.state_after(k64[b, h], v64[b, h], wl.C, wl.w, wl.N)
+            assert rel_l2(to64(st.S[b, h]), Sref) <= tol
+            assert rel_l2(to64(st.z[b, h]), zref) <= tol
+    assert st.t == wl.N
+
+
+def test_stream_state_equals_state_scan_bitwise():
+    wl = SMALL["bf16_d128_C100_w3"]
+    q, k, v = gen_qkv(wl)
+    S_scan, z_scan = rha.state_scan(k.to(DEV), v.to(DEV), wl.C, wl.w)
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+    for t in range(wl.N - 1):
+        rha.stream_step(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C))
+        torch.cuda.synchronize()
+        assert torch.equal(st.S, S_scan[:, :, t + 1]), f"S after commit {t}"
+        assert torch.equal(st.z, z_scan[:, :, t + 1]), f"z after commit {t}"
+
+
+def test_uncommitted_rerun_and_resume_are_exact():
+    wl = SMALL["bf16_d128_C100_w3_q4"]
+    q, k, v = gen_qkv(wl)
+    st_a, outs_a, _ = run_stream(wl, q, k, v, wl.N)
+    st_b = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+    outs_b = []
+    half = wl.N // 2
+    for t in range(wl.N):
+        if t == half:
+            # checkpoint: host copies of the whole constant-size state, restored into fresh buffers
+            saved = [x.cpu() for x in (st_b.k_cache, st_b.v_cache, st_b.S, st_b.z)]
+            cur = st_b.t
+            st_b = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+            for dst, src in zip((st_b.k_cache, st_b.v_cache, st_b.S, st_b.z), saved):
+                dst.copy_(src)
+            st_b.cursor.t = cur
+        # an uncommitted pass with other data first (as a denoising step would)
+        noise = torch.randn_like(chunk(q, t, wl.C))
+        rha.stream_step(st_b, noise, noise, noise, commit=False)
+        assert st_b.t == t
+        outs_b.append(rha.stream_step(st_b, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C)))
+    torch.cuda.synchronize()
+    for a, b in zip(outs_a, outs_b):
+        assert torch.equal(a, b)
+    assert torch.equal(st_a.S, st_b.S) and torch.equal(st_a.z, st_b.z)
+
+
+@pytest.mark.timeout(900)
+def test_stream_workload_full_size():
+    """9-frame window, 21-chunk prefill then 60 committed steps (81 chunks)."""
+    wl = CONFIGS["stream"]
+    print(f"[parity] stream: H{wl.H} C{wl.C} w{wl.w} chunks {wl.N}", flush=True)
+    q, k, v = gen_qkv(wl)
+    S_scan, z_scan = rha.state_scan(k.to(DEV), v.to(DEV), wl.C, wl.w)
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+    rng = np.random.default_rng(7)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    Sref, zref = oracle.state_scan_batched(k64, v64, wl.C, wl.w)
+    got_all, ref_all = [], []
+    for t in range(wl.N):
+        o = rha.stream_step(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C))
+        if t + 1 < wl.N and (t + 1) % 20 == 0:
+            torch.cuda.synchronize()
+            assert torch.equal(st.S, S_scan[:, :, t + 1]) and torch.equal(st.z, z_scan[:, :, t + 1])
+        rows = np.unique(np.concatenate([[0, 127, 128, wl.C - 1], rng.integers(0, wl.C, 8)]))
+        og = o.cpu()
+        for b in range(wl.B):
+            for h in range(wl.H):
+                ref = oracle.hybrid_rows(q64[b, h], k64[b, h], v64[b, h], wl.C, wl.w, t * wl.C + rows,
+                                         S=Sref[b, h], z=zref[b, h])
+                got_all.append(og[b, h, rows].double().numpy())
+                ref_all.append(ref)
+    torch.cuda.synchronize()
+    g = rel_l2(np.concatenate(got_all), np.concatenate(ref_all))
+    print(f"[parity] stream: sampled rel-L2 {g:.3e}", flush=True)
+    assert g <= TOL["bf16"]
+    for b in range(wl.B):
+        for h in range(wl.H):
+            Sf, zf = oracle.state_after(k64[b, h], v64[b, h], wl.C, wl.w, wl.N)
+            assert rel_l2(to64(st.S[b, h]), Sf) <= TOL["bf16"]
+            assert rel_l2(to64(st.z[b, h]), zf) <= TOL["bf16"]
