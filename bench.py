@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of librha's hot path on one MI355X.
+
+A step is one pass of the whole path over the Wan 2.1 1.3B 480p workload
+(B=1, H=12, d=128, 21 latent frames x 1560 tokens, 3-frame window, bf16):
+rha_state_scan followed by rha_hybrid_fwd.  Inputs are seeded synthetic
+Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Extra modes used for profiling (not part of the contract):
+    --only fwd|scan|stream   run just that call --steps times (for rocprofv3)
+    --copy-calib             run a plain device copy of a known size (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn query tokens/s + % MFMA bf16 peak, Wan-1.3B shape (H12 d128 32760 tok)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (vendor figure)
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_wan13b_traffic.md")
+FWD_SOURCE = os.path.join(ROOT, "linear_attention_video_chunked_amd", "csrc", "rha_fwd_bf16.hip")
+
+
+def fwd_flops(C, N, w, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_fwd call: 4d per (query, window key)
+    pair (QK^T and PV) plus 2d^2 + 2d per query whose state is non-empty."""
+    f = 0
+    for c in range(N):
+        nwin = min(c + 1, w) * C if w > 0 else 0
+        f += C * (4 * d * nwin + ((2 * d * d + 2 * d) if (w == 0 or c >= w) else 0))
+    return f * BH
+
+
+def fwd_bytes(C, N, w, d, BH, elem=2):
+    """Algorithmic HBM bytes of one rha_hybrid_fwd call: q, k, v read once, the
+    state slots of chunks with history read once, out written once."""
+    L = N * C
+    n_state = sum(1 for c in range(N) if (w == 0 or c >= w))
+    return BH * (4 * L * d * elem + n_state * (d * d + d) * 4)
+
+
+def scan_bytes(C, N, w, d, BH, elem=2):
+    """Algorithmic HBM bytes of rha_state_scan: k, v of the folded chunks read
+    once, every state slot written once."""
+    return BH * (2 * max(0, N - w) * C * d * elem + N * (d * d + d) * 4)
+
+
+def stream_step_flops(C, w, d, BH):
+    return BH * C * (4 * d * w * C + 2 * d * d + 2 * d)
+
+
+def read_traffic():
+    """HBM traffic per fwd launch from the committed rocprofv3 counter summary,
+    valid only while the kernel source is the one that was measured."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*[-*]?\s*`?([a-z_0-9]+)`?\s*:\s*`?([0-9a-fA-F.eE+-]+)`?\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle on the host: whole heads of the same workload, run until
+    the time budget is spent (at least one head)."""
+    import numpy as np
+    import oracle
+    from synth import gen_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    heads, elapsed = 0, 0.0
+    while True:
+        q = gen_head(wl, "q", 0, heads).double().numpy()
+        k = gen_head(wl, "k", 0, heads).double().numpy()
+        v = gen_head(wl, "v", 0, heads).double().numpy()
+        ts = time.perf_counter()
+        oracle.hybrid(q, k, v, wl.C, wl.w)
+        elapsed += time.perf_counter() - ts  # input generation stays off the clock
+        heads += 1
+        if elapsed > budget_s or heads >= wl.H:
+            break
+    # query tokens/s in the metric's unit: one query token = one row across all H heads
+    value = wl.B * wl.L * heads / wl.H / elapsed
+    return {"value": value, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 chunked oracle on {heads} of {wl.H} heads (b=0) of the full "
+                      f"{wl.N}x{wl.C}-token sequence, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream"], default=None)
+    ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is "
+              f"single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_video_chunked_amd as rha
+    from synth import CONFIGS, gen_qkv
+
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calib:
+        n = 256 << 20  # 256 MiB
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
+
+    wl = CONFIGS["wan13b"]
+    BH = wl.B * wl.H
+    q, k, v = (t.to(dev) for t in gen_qkv(wl))
+    S = torch.empty((wl.B, wl.H, wl.N, wl.d, wl.d), dtype=torch.float32, device=dev)
+    z = torch.empty((wl.B, wl.H, wl.N, wl.d), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+        rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n  # seconds per call
+
+    if args.only == "fwd":
+        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+        for _ in range(args.steps):
+            rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
+        torch.cuda.synchronize()
+        return
+    if args.only == "scan":
+        for _ in range(args.steps):
+            rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+        torch.cuda.synchronize()
+        return
+
+    # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
+    sw = CONFIGS["stream"]
+    sq, sk, sv = (t.to(dev) for t in gen_qkv(sw))
+    sout = torch.empty_like(sq)  # step outputs land in place, with the inputs' strides
+    st = rha.StreamState(sw.B, sw.H, sw.d, sw.C, sw.w, device=dev)
+
+    def push(t):
+        sl = slice(t * sw.C, (t + 1) * sw.C)
+        rha.stream_step(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], out=sout[:, :, sl], stream=stream)
+
+    for t in range(sw.prefill):
+        push(t)
+    torch.cuda.synchronize()
+    if args.only == "stream":
+        for t in range(sw.prefill, sw.prefill + sw.steps):
+            push(t)
+        torch.cuda.synchronize()
+        return
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(sw.prefill, sw.prefill + sw.steps):
+        push(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_stream = e0.elapsed_time(e1) / 1e3 / sw.steps
+
+    # ---- the contract: W warmup steps, then exactly K timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) / 1e3 / args.steps
+
+    # ---- per-kernel averages over timed regions (same stream)
+    n_k = max(args.steps, 10)
+    t_fwd = timed(lambda: rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream), n_k)
+    t_scan = timed(lambda: rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream), n_k)
+
+    F = fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
+    achieved = F / t_fwd / 1e12
+    traffic = read_traffic()
+    tokens = wl.B * wl.L
+    sF = stream_step_flops(sw.C, sw.w, sw.d, sw.B * sw.H)
+    result = {
+        "metric": METRIC,
+        "value": tokens / t_step,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan2.1-1.3b-480p: B1 H12 d128, 21 chunks x 1560 tokens (L=32760), "
+                               "window 3 chunks, bf16 q/v~N(0,1), k~0.5*N(0,1); step = state_scan + hybrid_fwd",
+                   "global_batch": wl.B, "seq_len": wl.L, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "fwd_bf16_kernel (rha_hybrid_fwd)", "flops_per_launch": F,
+                     "algorithmic_bytes_per_launch": fwd_bytes(wl.C, wl.N, wl.w, wl.d, BH),
+                     "avg_launch_us": t_fwd * 1e6},
+        "detail": {
+            "fwd_query_tokens_per_s": tokens / t_fwd,
+            "fwd_us": t_fwd * 1e6,
+            "scan_us": t_scan * 1e6,
+            "scan_GBps": scan_bytes(wl.C, wl.N, wl.w, wl.d, BH) / t_scan / 1e9,
+            "scan_hbm_frac": scan_bytes(wl.C, wl.N, wl.w, wl.d, BH) / t_scan / 1e9 / PEAK_HBM_GBS,
+            "stream_step_us": t_stream * 1e6,
+            "stream_chunks_per_s": 1.0 / t_stream,
+            "stream_step_TFLOPs": sF / t_stream / 1e12,
+            "stream_step_mfma_frac": sF / t_stream / 1e12 / PEAK_BF16_TFLOPS,
+            "timed_wall_s": wall,
+        },
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
