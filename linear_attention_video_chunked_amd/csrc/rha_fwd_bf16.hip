@@ -9,10 +9,9 @@
 // in FlashAttention-style blocks, folded linear state for evicted frames).
 //
 // Design (gfx950, wave64, 32x32x16 bf16 MFMA):
-//  * one workgroup = 4 waves = one query tile of 128 rows inside one chunk;
-//    each wave owns 32 query rows, kept in registers as MFMA B operands.
-//    Two workgroups share a CU (<= 256 registers per wave, 64 KB LDS each),
-//    so one wave's softmax overlaps another's matrix products.
+//  * one workgroup = NW waves = one query tile of 32*NW rows inside one
+//    chunk; each wave owns 32 query rows, kept in registers as MFMA B
+//    operands.  Two waves share each SIMD (<= 256 registers per wave).
 //  * scores are produced transposed, S^T = K Q^T (M = keys, N = queries), so
 //    every lane holds one query's scores: the row max and row sum need one
 //    lane-pair exchange (v_permlane32_swap) instead of a 32-lane reduction,
@@ -21,17 +20,21 @@
 //    lane, so rescaling and normalisation are lane-local.
 //  * the linear term seeds the accumulators: O^T = S_c^T phi(Q)^T and
 //    l = phi(Q).z_c at reference maximum 0 (the same as multiplying it by
-//    exp(-m) at the end), then the window keys are streamed in tiles of 64
-//    with an online maximum.  Rescaling is lazy: the reference maximum only
-//    moves when a new score exceeds it by more than 2^8, which keeps every
-//    probability <= 256 and leaves the result unchanged.
-//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4:
-//    no registers, no VALU), row-major with an XOR swizzle of the 16-byte
-//    granules.  K fragments are read with ds_read_b128; V fragments are read
-//    transposed with ds_read_b64_tr_b16, which hands each lane 4 keys of one
-//    feature column.  Tiles are double-buffered: the loads of tile j+1 are in
-//    flight while tile j is multiplied.  Keys past the window end are loaded
-//    from the last valid row (finite values) and masked to -inf.
+//    exp(-m) at the end), then the window keys are streamed with an online
+//    maximum.  Rescaling is lazy: the reference maximum only moves when a new
+//    score exceeds it by more than 2^8, which keeps every probability <= 256
+//    and leaves the result unchanged.
+//  * software pipeline over 32-key blocks b: step s issues the QK^T products
+//    of block s+1, the softmax of block s and the PV products of block s-1,
+//    so the exponentials of one block run on the VALU while the matrix cores
+//    work on its neighbours.  Two blocks form one 64-key LDS tile; each
+//    "period" of two steps reads one K tile and the previous V tile.
+//  * K and V tiles are loaded from HBM into registers one period ahead and
+//    written to LDS row-major with an XOR swizzle of the 16-byte granules.
+//    K fragments are read with ds_read_b128; V fragments are read transposed
+//    with ds_read_b64_tr_b16, which hands each lane 4 keys of one feature
+//    column.  Keys past the window end are loaded from the last valid row
+//    (finite values) and masked to -inf.
 //  * workgroup ids are remapped so that each of the 8 XCDs gets a contiguous
 //    range of tiles; neighbouring tiles share their window keys in that XCD's
 //    L2.
@@ -41,16 +44,12 @@
 namespace rha {
 namespace {
 
-constexpr int NW = 4;
-constexpr int THREADS = NW * kWave;
-constexpr int BM = NW * 32;       // query rows per workgroup
-constexpr int BN = 64;            // keys per tile
+constexpr int BN = 64;                 // keys per LDS tile (two 32-key blocks)
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
   const int per = total >> 3, rem = total & 7;
@@ -67,16 +66,18 @@ __device__ __forceinline__ bf16x8 phi8(const bf16x8& x) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int D>
+template <int D, int NW>
 struct FwdCfg {
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BM = NW * 32;              // query rows per workgroup
   static constexpr int DS = D / 16;               // MFMA k-steps over features
   static constexpr int DB = D / 32;               // 32-wide feature blocks
   static constexpr int GR = D / 8;                // 16-byte granules per row
   static constexpr int TILE = BN * D * 2;         // bytes of one K or V tile
-  static constexpr int LPW = BN * GR / (NW * 64); // direct loads per wave per tile
-  static_assert(LPW * NW * 64 == BN * GR, "tile must split into whole wave loads");
+  static constexpr int LPT = BN * GR / THREADS;   // granules per thread per tile
+  static_assert(LPT * THREADS == BN * GR, "tile must split evenly over the threads");
   static_assert(TILE >= D * D, "half of the state staging must fit one V buffer");
-  static_assert(TILE >= 2 * 32 * D * 2, "two waves' output rows must fit one K buffer");
+  static_assert(4 * TILE >= NW * 32 * D * 2, "output staging must fit the tile buffers");
 };
 
 // Granule swizzles (16-byte granule g of row r is stored at slot g ^ sw(r)).
@@ -89,16 +90,20 @@ template <int D> __device__ __forceinline__ int vsw(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// s_waitcnt immediates (gfx9 encoding): wait for all vector-memory loads,
-// or for all LDS operations, leaving the other counters alone.
-constexpr int kWaitVm0 = 0x0F70;
+// s_waitcnt immediate (gfx9 encoding) for "at most n vector-memory loads
+// outstanding", leaving the other counters alone.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkm0 = 0xC07F;
+// Fourth word of a raw buffer descriptor on gfx9-class GPUs (32-bit format,
+// no swizzle); out-of-range reads return zero.
+constexpr int kBufWord3 = 0x00020000;
 
-template <int D>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const FwdParams p) {
-  using Cfg = FwdCfg<D>;
-  constexpr int DS = Cfg::DS, DB = Cfg::DB, GR = Cfg::GR;
+  using Cfg = FwdCfg<D, NW>;
+  constexpr int DS = Cfg::DS, DB = Cfg::DB, GR = Cfg::GR, BM = Cfg::BM, THREADS = Cfg::THREADS;
+  constexpr int LPT = Cfg::LPT;
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[Cfg::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[Cfg::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[Cfg::TILE];
@@ -144,6 +149,43 @@ void fwd_bf16_kernel(const FwdParams p) {
     Sp = p.S + (int64_t)bh * D * D;
     zp = p.z + (int64_t)bh * D;
   }
+  const int T = (int)((kend - kbeg + BN - 1) / BN);  // LDS tiles in the window
+
+  // ---- tile loads: granule f = i*THREADS + tid of a tile (row f / GR,
+  // granule f % GR) goes through registers into LDS slot g ^ sw(row).
+  // Buffer loads: a scalar descriptor per tensor whose extent ends at the
+  // window end, a fixed per-lane byte offset, and the tile base as a scalar
+  // offset.  Rows at or past the window end read as zero (out-of-range buffer
+  // reads return 0), so the last partial tile needs no clamping.
+  int goff[LPT], kls[LPT], vls[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int f = i * THREADS + tid;
+    const int row = f / GR, g = f % GR;
+    goff[i] = (row * (int)p.kv_st + g * 8) * 2;
+    kls[i] = row * D * 2 + (g ^ ksw<D>(row)) * 16;
+    vls[i] = row * D * 2 + (g ^ vsw<D>(row)) * 16;
+  }
+  const int win_bytes = (int)(kend * p.kv_st * 2);  // bytes of rows [0, kend) from the head base
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
+  auto gload = [&](const __amdgpu_buffer_rsrc_t& rs, int t, u32x4 (&dst)[LPT]) {
+    const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff[i], tile_off, 0));
+  };
+  auto lstore = [&](unsigned char* dstbuf, const int (&ls)[LPT], const u32x4 (&src)[LPT]) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(dstbuf + ls[i]) = src[i];
+  };
+
+  // Issue the first window loads before the Q and state loads so they overlap.
+  u32x4 kst[LPT], vst[LPT];
+  if (T > 0) {
+    gload(krsrc, 0, kst);
+    gload(vrsrc, 0, vst);
+  }
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[row l32][16s + 8hh .. +7].
   // Rows past the chunk re-read the last valid row; their results are not stored.
@@ -153,6 +195,10 @@ void fwd_bf16_kernel(const FwdParams p) {
     const bf16_t* qr = qbase + (int64_t)row * p.q_st + hh * 8;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ld16(qr + s * 16));
+    // Mark the fragments as produced here (the load wait lands on this empty
+    // statement), so the loop below is not made to wait for them again.
+#pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[s]));
   }
 
   f32x16 o[DB];
@@ -206,124 +252,181 @@ void fwd_bf16_kernel(const FwdParams p) {
     mrun = -INFINITY;
   }
 
-  // ---- window keys
-  const int ntiles = (int)((kend - kbeg + BN - 1) / BN);
-
-  // Direct loads: load i of wave `wave` writes physical granules
-  // (wave*LPW + i)*64 + lane of the tile; granule slot ps of row r holds
-  // logical granule ps ^ sw(r).
-  int krow[Cfg::LPW], kgo[Cfg::LPW], vgo[Cfg::LPW];
+  if (T > 0) {
+    // ---- pipeline pieces on one 32-key block (half hb of an LDS tile)
+    const int kswz = ksw<D>(l32);
+    // K fragment (A of S^T): row 32*hb + l32, granule 2s + hh.
+    auto qk = [&](const unsigned char* kt, int hb, f32x16& acc) {
+      acc = f32x16{};
+      const unsigned char* rowp = kt + (32 * hb + l32) * D * 2;
 #pragma unroll
-  for (int i = 0; i < Cfg::LPW; ++i) {
-    const int pg = (wave * Cfg::LPW + i) * 64 + lane;
-    krow[i] = pg / GR;
-    const int ps = pg % GR;
-    kgo[i] = (ps ^ ksw<D>(krow[i])) * 8;
-    vgo[i] = (ps ^ vsw<D>(krow[i])) * 8;
-  }
-  auto issue = [&](int j, unsigned char* kdst, unsigned char* vdst) {
-    const int64_t k0 = kbeg + (int64_t)j * BN;
-#pragma unroll
-    for (int i = 0; i < Cfg::LPW; ++i) {
-      const int64_t key = min(k0 + krow[i], kend - 1);
-      const int64_t off = key * p.kv_st;
-      const int dst = (wave * Cfg::LPW + i) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + off + kgo[i]), (lds_void*)(kdst + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + off + vgo[i]), (lds_void*)(vdst + dst), 16, 0, 0);
-    }
-  };
-
-  // K fragment (A of S^T): row kb*32 + l32, granule 2s + hh.
-  const int kswz = ksw<D>(l32);  // same for rows l32 and 32 + l32
-  // V fragment (A of O^T, transposed read): in each 16-lane group, source
-  // lane 4e + r supplies row 16ks + 8t + 4hh + e, columns nb*32 + 16*(group&1) + 4r;
-  // lane j of the group then holds column nb*32 + 16*(group&1) + j, rows e = 0..3.
-  const int vj = lane & 15;
-  const int ve = vj >> 2, vr = vj & 3;
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * vr;  // + nb*32
-  const int vrow0 = 4 * hh + ve;                      // + 16ks + 8t
-
-  if (ntiles > 0) issue(0, kb0, vb0);
-
-  for (int j = 0; j < ntiles; ++j) {
-    unsigned char* kcur = (j & 1) ? kb1 : kb0;
-    unsigned char* vcur = (j & 1) ? vb1 : vb0;
-    // tile j has landed (own loads), and every wave's loads are visible after the barrier
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1, (j & 1) ? kb0 : kb1, (j & 1) ? vb0 : vb1);
-    const int valid = (int)min((int64_t)BN, kend - (kbeg + (int64_t)j * BN));
-
-    // S^T = K Q^T : sacc[kb] reg 4r+i <-> key kb*32 + 8r + 4hh + i, query l32
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const int slot = ((2 * s + hh) ^ kswz) * 16;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kcur + (kb2 * 32 + l32) * D * 2 + slot));
-        sacc[kb2] = mfma32(a, qf[s], sacc[kb2]);
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + ((2 * s + hh) ^ kswz) * 16));
+        acc = mfma32(a, qf[s], acc);
       }
-    }
-
-    // online softmax (log2 domain), probabilities packed to bf16 pairs
-    if (valid < BN) {
+    };
+    // Online softmax of a block: acc reg 4r+i <-> key 8r + 4hh + i of the block.
+    // Returns the rescale factor for everything accumulated before this block
+    // (1 unless the reference maximum moved).
+    auto softmax = [&](f32x16& acc, int valid, bf16x2 (&pk)[8]) -> float {
+      if (__builtin_expect(valid < 32, 0)) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * hh + (i & 3) >= valid) acc[i] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb2 * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= valid) sacc[kb2][i] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-    mx = half_max(mx) * p.scale_log2;
-    const float mnew = fmaxf(mrun, mx);
-    if (__any(mnew > mrun + kRescaleSlack)) {
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      mrun = mnew;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+      mx = half_max(mx) * p.scale_log2;
+      // move the reference only when some lane's maximum outgrew it by the
+      // slack (wave-uniform decision, no branch); alpha is 1 otherwise
+      const float mnew = fmaxf(mrun, mx);
+      const bool move = __any(mnew > mrun + kRescaleSlack);
+      const float mref = move ? mnew : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mref);
+      mrun = mref;
       lsum *= alpha;
-#pragma unroll
-      for (int nb = 0; nb < DB; ++nb) o[nb] *= alpha;
-    }
-    const float mneg = -mrun;
-    uint32_t pk[2][8];
-    float ps = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      const float mneg = -mrun;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][2 * i], p.scale_log2, mneg));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][2 * i + 1], p.scale_log2, mneg));
-        ps += p0 + p1;
-        pk[kb2][i] = pack_bf16(p0, p1);
+        pk[i][0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[2 * i], p.scale_log2, mneg));
+        pk[i][1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[2 * i + 1], p.scale_log2, mneg));
       }
-    lsum += ps;
+      // row sum of the rounded probabilities (the values the P V product uses)
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ps = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, ps, false);
+      lsum += ps;
+      return alpha;
+    };
+    // V fragment (A of O^T, transposed read): in each 16-lane group, source
+    // lane 4e + r supplies row 16ks + 8t + 4hh + e, columns nb*32 + 16*(group&1) + 4r;
+    // lane j of the group then holds column nb*32 + 16*(group&1) + j, rows e = 0..3.
+    const int vj = lane & 15;
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (vj & 3);  // + nb*32
+    const int vrow0 = 4 * hh + (vj >> 2);                    // + 32hb + 16ks + 8t
+    auto pv = [&](const unsigned char* vt, int hb, const bf16x2 (&pk)[8]) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 w4 = {__builtin_bit_cast(uint32_t, pk[4 * ks]), __builtin_bit_cast(uint32_t, pk[4 * ks + 1]),
+                          __builtin_bit_cast(uint32_t, pk[4 * ks + 2]), __builtin_bit_cast(uint32_t, pk[4 * ks + 3])};
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, w4);
+        const int r_a = 32 * hb + 16 * ks + vrow0, r_b = r_a + 8;
+#pragma unroll
+        for (int nb = 0; nb < DB; ++nb) {
+          const int col = nb * 32 + vcol;
+          const int ga = col >> 3, cb = (col & 7) * 2;
+          const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vt + r_a * D * 2 + ((ga ^ vsw<D>(r_a)) * 16) + cb));
+          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vt + r_b * D * 2 + ((ga ^ vsw<D>(r_b)) * 16) + cb));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
+          const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
+          o[nb] = mfma32(__builtin_bit_cast(bf16x8, av), pf, o[nb]);
+        }
+      }
+    };
+    auto rescale = [&](float alpha) {
+      if (__builtin_expect(__any(alpha != 1.0f), 0)) {
+#pragma unroll
+        for (int nb = 0; nb < DB; ++nb) o[nb] *= alpha;
+      }
+    };
+    // Interleave one pipeline step: LDS fragment reads run ahead, then each
+    // matrix-core product is followed by a slice of the softmax VALU work.
+    auto interleave = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+      }
+    };
+    // keys of block blk that lie inside the window
+    auto block_valid = [&](int blk) { return (int)min((int64_t)32, kend - (kbeg + (int64_t)blk * 32)); };
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const int kb2 = ks >> 1, r0 = (ks & 1) * 2;
-      const u32x4 w4 = {pk[kb2][r0 * 2], pk[kb2][r0 * 2 + 1], pk[kb2][r0 * 2 + 2], pk[kb2][r0 * 2 + 3]};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, w4);
-      const int r_a = 16 * ks + vrow0, r_b = r_a + 8;
-#pragma unroll
-      for (int nb = 0; nb < DB; ++nb) {
-        const int col = nb * 32 + vcol;
-        const int ga = col >> 3, cb = (col & 7) * 2;
-        const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vcur + r_a * D * 2 + ((ga ^ vsw<D>(r_a)) * 16) + cb));
-        const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vcur + r_b * D * 2 + ((ga ^ vsw<D>(r_b)) * 16) + cb));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
-        const u32x4 av = {w0[0], w0[1], w1[0], w1[1]};
-        o[nb] = mfma32(__builtin_bit_cast(bf16x8, av), pf, o[nb]);
+    // ---- prologue: K tile 0 into LDS, K tile 1 and V tile 0 in flight
+    lstore(kb0, kls, kst);
+    if (T > 1) gload(krsrc, 1, kst);
+    // every load issued so far except the K tile 1 in flight is complete (Q, state)
+    constexpr int kWaitAllButKTile = wait_vm(LPT), kWaitAll = wait_vm(0);
+    if (T > 1)
+      __builtin_amdgcn_s_waitcnt(kWaitAllButKTile);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();
+
+    // Period t = steps 2t-1 and 2t: reads K tile t (QK of blocks 2t, 2t+1) and
+    // V tile t-1 (PV of blocks 2t-2, 2t-1); writes K tile t+1 and V tile t
+    // from registers and starts the loads of K tile t+2 and V tile t+1.
+    f32x16 sacc[2];
+    bf16x2 pk[2][8];
+    auto kbuf = [&](int t) { return (t & 1) ? kb1 : kb0; };
+    auto vbuf = [&](int t) { return (t & 1) ? vb1 : vb0; };
+
+    qk(kb0, 0, sacc[0]);  // block 0
+    // period 0: step 0 only (QK block 1, softmax block 0)
+    {
+      if (T > 1) lstore(kb1, kls, kst);
+      lstore(vb0, vls, vst);
+      if (T > 2) gload(krsrc, 2, kst);
+      if (T > 1) gload(vrsrc, 1, vst);
+      qk(kb0, 1, sacc[1]);
+      const float alpha = softmax(sacc[0], T > 1 ? 32 : block_valid(0), pk[0]);
+      rescale(alpha);
+      __syncthreads();
+    }
+    // steady state: every block of K tile t and V tile t-1 is full
+    for (int t = 1; t + 1 < T; ++t) {
+      const unsigned char* kt = kbuf(t);
+      const unsigned char* vprev = vbuf(t - 1);
+      lstore(kbuf(t + 1), kls, kst);
+      lstore(vbuf(t), vls, vst);
+      if (t + 2 < T) gload(krsrc, t + 2, kst);
+      gload(vrsrc, t + 1, vst);
+      {  // step 2t-1: QK block 2t, softmax block 2t-1, PV block 2t-2
+        qk(kt, 0, sacc[0]);
+        const float alpha = softmax(sacc[1], 32, pk[1]);
+        pv(vprev, 0, pk[0]);
+        interleave();
+        rescale(alpha);
       }
+      {  // step 2t: QK block 2t+1, softmax block 2t, PV block 2t-1
+        qk(kt, 1, sacc[1]);
+        const float alpha = softmax(sacc[0], 32, pk[0]);
+        pv(vprev, 1, pk[1]);
+        interleave();
+        rescale(alpha);
+      }
+      __syncthreads();
+    }
+    if (T > 1) {  // period T-1: the last K tile (may be partial)
+      const int t = T - 1;
+      const unsigned char* kt = kbuf(t);
+      const unsigned char* vprev = vbuf(t - 1);
+      lstore(vbuf(t), vls, vst);
+      {
+        qk(kt, 0, sacc[0]);
+        const float alpha = softmax(sacc[1], 32, pk[1]);
+        pv(vprev, 0, pk[0]);
+        rescale(alpha);
+      }
+      {
+        qk(kt, 1, sacc[1]);
+        const float alpha = softmax(sacc[0], block_valid(2 * t), pk[0]);
+        pv(vprev, 1, pk[1]);
+        rescale(alpha);
+      }
+      __syncthreads();
+    }
+    {  // period T: softmax of the last block, PV of the last V tile
+      const unsigned char* vprev = vbuf(T - 1);
+      const float alpha = softmax(sacc[1], block_valid(2 * T - 1), pk[1]);
+      pv(vprev, 0, pk[0]);
+      rescale(alpha);
+      pv(vprev, 1, pk[1]);
     }
   }
 
@@ -331,7 +434,9 @@ void fwd_bf16_kernel(const FwdParams p) {
   __syncthreads();
   const float ltot = half_sum(lsum);
   const float inv = 1.0f / ltot;
-  unsigned char* stage = ((wave < 2) ? kb0 : kb1) + (wave & 1) * 32 * D * 2;
+  constexpr int WAVE_BYTES = 32 * D * 2;
+  const int wbuf = (wave * WAVE_BYTES) / Cfg::TILE;
+  unsigned char* stage = (wbuf == 0 ? kb0 : wbuf == 1 ? kb1 : wbuf == 2 ? vb0 : vb1) + (wave * WAVE_BYTES) % Cfg::TILE;
 #pragma unroll
   for (int nb = 0; nb < DB; ++nb)
 #pragma unroll
@@ -359,20 +464,21 @@ void fwd_bf16_kernel(const FwdParams p) {
   }
 }
 
-template <int D>
+template <int D, int NW>
 hipError_t launch(FwdParams& p, hipStream_t s) {
+  constexpr int BM = FwdCfg<D, NW>::BM;
   p.tiles_per_chunk = (p.C + BM - 1) / BM;
   p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk;
   if (p.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(p.total_tiles), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s) {
-  if (d == 128) return launch<128>(p, s);
-  return launch<64>(p, s);
+  if (d == 128) return launch<128, 8>(p, s);
+  return launch<64, 4>(p, s);
 }
 
 }  // namespace rha
