@@ -67,6 +67,11 @@ rha_status check_problem(const rha_problem* p, bool stream) {
   if (L > INT32_MAX / 2 || bhn * p->chunk_len > INT32_MAX || (int64_t)p->batch * p->heads > INT32_MAX / 2 ||
       (stream && win_keys > INT32_MAX / 2))
     return fail(RHA_ERR_INVALID_ARG, "problem too large for 32-bit tile indexing");
+  // the forward kernels address one head's keys with 32-bit byte offsets
+  // (buffer loads), reaching up to two 64-key tiles past the last key
+  const int64_t head_keys = stream ? win_keys : L;
+  if ((head_keys + 128) * p->stride_t * eb > INT32_MAX)
+    return fail(RHA_ERR_INVALID_ARG, "one head's keys span more than 2 GiB (stride_t %lld)", (long long)p->stride_t);
   return RHA_OK;
 }
 

@@ -39,32 +39,13 @@
 //    range of tiles; neighbouring tiles share their window keys in that XCD's
 //    L2.
 #include "rha_device.hpp"
+#include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
 
 namespace rha {
 namespace {
 
-constexpr int BN = 64;                 // keys per LDS tile (two 32-key blocks)
-constexpr float kRescaleSlack = 8.0f;  // log2 units
-constexpr float kLn2 = 0.6931471805599453f;
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = bid & 7, local = bid >> 3;
-  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
-}
-
-// phi of 8 bf16 values, rounded back to bf16.
-__device__ __forceinline__ bf16x8 phi8(const bf16x8& x) {
-  const u32x4 w = __builtin_bit_cast(u32x4, x);
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_bf16(phi(bf16_lo(w[i])), phi(bf16_hi(w[i])));
-  return __builtin_bit_cast(bf16x8, r);
-}
+using namespace fwd;
 
 template <int D, int NW>
 struct FwdCfg {
@@ -80,23 +61,7 @@ struct FwdCfg {
   static_assert(4 * TILE >= NW * 32 * D * 2, "output staging must fit the tile buffers");
 };
 
-// Granule swizzles (16-byte granule g of row r is stored at slot g ^ sw(r)).
-// K: ds_read_b128 of 16 consecutive rows at one granule hits 16 distinct slots.
-template <int D> __device__ __forceinline__ int ksw(int r) { return r & (D / 8 - 1); }
-// V: a transpose read covers 4 consecutive rows x 4 granules (D = 128) or
-// 4 rows x 4 granules of a 128-byte row (D = 64); the swizzle puts them in
-// distinct bank ranges.
-template <int D> __device__ __forceinline__ int vsw(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
 
-// s_waitcnt immediate (gfx9 encoding) for "at most n vector-memory loads
-// outstanding", leaving the other counters alone.
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-constexpr int kWaitLgkm0 = 0xC07F;
-// Fourth word of a raw buffer descriptor on gfx9-class GPUs (32-bit format,
-// no swizzle); out-of-range reads return zero.
-constexpr int kBufWord3 = 0x00020000;
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -154,9 +119,10 @@ void fwd_bf16_kernel(const FwdParams p) {
   // ---- tile loads: granule f = i*THREADS + tid of a tile (row f / GR,
   // granule f % GR) goes through registers into LDS slot g ^ sw(row).
   // Buffer loads: a scalar descriptor per tensor whose extent ends at the
-  // window end, a fixed per-lane byte offset, and the tile base as a scalar
-  // offset.  Rows at or past the window end read as zero (out-of-range buffer
-  // reads return 0), so the last partial tile needs no clamping.
+  // window end; the per-lane byte offset (tile base + row + granule) is the
+  // vector offset, which the hardware range-checks against that extent.  Rows
+  // at or past the window end read as zero, so the last partial tile needs no
+  // clamping.  The host guarantees every such offset fits in 31 bits.
   int goff[LPT], kls[LPT], vls[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
@@ -173,7 +139,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
 #pragma unroll
     for (int i = 0; i < LPT; ++i)
-      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff[i], tile_off, 0));
+      dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff[i] + tile_off, 0, 0));
   };
   auto lstore = [&](unsigned char* dstbuf, const int (&ls)[LPT], const u32x4 (&src)[LPT]) {
 #pragma unroll
@@ -477,7 +443,7 @@ hipError_t launch(FwdParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s) {
-  if (d == 128) return launch<128, 8>(p, s);
+  if (d == 128) return launch_fwd_bf16_qb2(p, s);
   return launch<64, 4>(p, s);
 }
 

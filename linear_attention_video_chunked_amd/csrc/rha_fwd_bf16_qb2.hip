@@ -1,0 +1,629 @@
+// Fused hybrid-attention forward, bf16, head dimension 128: 64 query rows
+// per wave, one wave per SIMD.
+//
+// Computes ("Long-Horizon Streaming Video Generation via Hybrid Attention with
+// Decoupled Distillation", explainer section 2.A: FlashAttention-style window
+// blocks plus the folded linear state, one shared normaliser)
+//   out_i = (sum_{j in window} exp(s_ij) v_j + phi(q_i)^T S_c)
+//         / (sum_{j in window} exp(s_ij)     + phi(q_i)^T z_c)
+//
+// Design (gfx950):
+// * Each wave owns two 32-row query blocks, so every K or V fragment read
+//   from LDS feeds two 32x32x16 products.  Scores are computed transposed
+//   (S^T = K Q^T, one query per lane) and the output as O^T = V^T P^T, so the
+//   probabilities of a lane feed the product without any exchange.
+// * Registers: O^T accumulators (128) in AGPRs, Q fragments, score
+//   accumulators and probabilities in VGPRs; one wave per SIMD.
+// * Software pipeline over 32-key blocks; step s computes QK^T of block s+1,
+//   the softmax of block s and P V of block s-1.  Every step is hand-ordered:
+//   8 rounds of 4 groups, each group one matrix product followed by a short
+//   slice of independent VALU work, closed by a scheduling fence.
+// * The softmax keeps a stale reference maximum: exponentials are taken
+//   against the current reference without a per-block maximum, and the block
+//   is accepted while its row sum stays below 2^64 (which bounds every term).
+//   A block that fails (first block without linear state, or a score that
+//   grew by 2^64) is redone against its true maximum; if the reference of a
+//   query moved after something was accumulated, the whole tile is computed
+//   again with the final references, which nothing exceeds by the bound.
+// * K/V tiles of 64 keys are staged one period ahead through registers with
+//   buffer loads (zero past the window end) into XOR-swizzled LDS; V is read
+//   transposed with ds_read_b64_tr_b16; tiles are visited in an XCD-aware
+//   order, longest windows first.
+#include <type_traits>
+
+#include "rha_device.hpp"
+#include "rha_fwd_common.hpp"
+#include "rha_launch.hpp"
+
+namespace rha {
+namespace {
+
+using namespace fwd;
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+// Empty asm that claims to modify x: the value is produced before this point
+// and cannot be moved past it (keeps hand-ordered work in its slot).
+template <typename T> __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+template <typename T> __device__ __forceinline__ void pin_acc(T& x) { asm volatile("" : "+a"(x)); }
+
+// S^T += K Q^T block product in the VGPR-accumulator form of the
+// instruction (the softmax VALU reads these accumulators; in AGPRs every read
+// would cost a copy).  Written as asm because the compiler picks the AGPR
+// form for every product of a kernel that keeps accumulators in AGPRs.  The
+// leading s_nop covers the wait states a VALU write of an operand needs before
+// a matrix-core read; the results are first read by VALU code one pipeline
+// step (32 further products) later, far past the result latency, and the
+// accumulation chain has three other products between dependent ones.
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+constexpr int Q2_NW = 4;
+constexpr int Q2_THREADS = Q2_NW * 64;
+constexpr int Q2_QB = 2;                   // 32-row query blocks per wave
+constexpr int Q2_BM = Q2_NW * 32 * Q2_QB;  // query rows per workgroup
+// Probabilities up to 2^kQ2Slack are accepted against a stale reference
+// (far inside the bf16 and f32 ranges).
+constexpr float kQ2Slack = 64.0f;
+
+// LDS tile buffers (head dimension 128): K and V, double buffered.  At
+// namespace scope so that the rare second pass, a separate function, shares
+// them with the kernel.
+constexpr int Q2_D = 128;
+constexpr int Q2_TILE = BN * Q2_D * 2;
+__shared__ __attribute__((aligned(1024))) unsigned char q2_kb0[Q2_TILE];
+__shared__ __attribute__((aligned(1024))) unsigned char q2_kb1[Q2_TILE];
+__shared__ __attribute__((aligned(1024))) unsigned char q2_vb0[Q2_TILE];
+__shared__ __attribute__((aligned(1024))) unsigned char q2_vb1[Q2_TILE];
+
+// One pass over a tile, output included.  FIRST: references start at 0 (with
+// linear state) or -inf and blocks are checked against the bound; returns
+// nonzero where a reference moved after accumulation.  Otherwise references
+// start at mio and no block is checked.  mio receives the final references.
+template <int D, bool FIRST>
+__device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]) {
+  static_assert(D == Q2_D, "tile buffers are sized for head dimension 128");
+  constexpr int NW = Q2_NW, THREADS = Q2_THREADS, QB = Q2_QB, BM = Q2_BM;
+  constexpr int DS = D / 16, DB = D / 32, GR = D / 8;
+  constexpr int TILE = BN * D * 2;
+  constexpr int LPT = BN * GR / THREADS;
+  static_assert(LPT * THREADS == BN * GR, "tile must split evenly over the threads");
+  static_assert(TILE >= D * D, "half of the state staging must fit one V buffer");
+  static_assert(TILE >= 32 * QB * D * 2, "one wave's output rows must fit one tile buffer");
+  static_assert(NW == 4, "the epilogue stages one wave per tile buffer");
+  static_assert(LPT == 4, "stage ops assume four loads per tensor and thread");
+  static_assert(TILE == Q2_TILE, "tile buffer size");
+  unsigned char* const kb0 = q2_kb0;
+  unsigned char* const kb1 = q2_kb1;
+  unsigned char* const vb0 = q2_vb0;
+  unsigned char* const vb1 = q2_vb1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // ---- which tile
+  const int logical = xcd_remap(blockIdx.x, p.total_tiles);
+  const int tile = logical % p.tiles_per_chunk;
+  const int rest = logical / p.tiles_per_chunk;
+  const int c = p.n_qchunks - 1 - rest % p.n_qchunks;  // later chunks (longer windows) first
+  const int bh = rest / p.n_qchunks;
+  const int b = bh / p.H, h = bh % p.H;
+  const int qrow0 = tile * BM;
+  const int nrows = min(BM, p.C - qrow0);
+  const int64_t qtok0 = (int64_t)c * p.C + qrow0;
+
+  const bf16_t* qbase = (const bf16_t*)p.q + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
+  const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh;
+  const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh;
+
+  int64_t kbeg, kend;
+  bool has_state;
+  const float* Sp;
+  const float* zp;
+  if (!p.stream_mode) {
+    if (p.w > 0) {
+      kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
+      kend = (int64_t)(c + 1) * p.C;
+    } else {
+      kbeg = kend = 0;
+    }
+    has_state = (p.w == 0) || (c >= p.w);
+    Sp = p.S + ((int64_t)bh * p.n_qchunks + c) * D * D;
+    zp = p.z + ((int64_t)bh * p.n_qchunks + c) * D;
+  } else {
+    kbeg = 0;
+    kend = p.n_keys;
+    has_state = p.has_state != 0;
+    Sp = p.S + (int64_t)bh * D * D;
+    zp = p.z + (int64_t)bh * D;
+  }
+  const int T = (int)((kend - kbeg + BN - 1) / BN);  // LDS tiles in the window
+
+  // ---- tile loads: granule f = i*THREADS + tid of a tile (row f / GR,
+  // granule f % GR) goes through registers into LDS slot g ^ sw(row).  Buffer
+  // loads: a descriptor per tensor whose extent ends at the window end, the
+  // per-lane byte offset as the (range-checked) vector offset, so rows at or
+  // past the window end read as zero.  Load i of a thread is row
+  // i*THREADS/GR further than load 0, and both swizzles repeat within those
+  // rows, so one per-lane offset serves all i.
+  static_assert(THREADS % GR == 0 && (THREADS / GR) % 16 == 0, "swizzle period must divide the row step");
+  constexpr int ROWS_PER_LOAD = THREADS / GR;
+  const int row0 = tid / GR, g0 = tid % GR;
+  const int goff0 = (row0 * (int)p.kv_st + g0 * 8) * 2;
+  const int gstep = ROWS_PER_LOAD * (int)p.kv_st * 2;
+  const int kls0 = row0 * D * 2 + (g0 ^ ksw<D>(row0)) * 16;
+  const int vls0 = row0 * D * 2 + (g0 ^ vsw<D>(row0)) * 16;
+  constexpr int LSTEP = ROWS_PER_LOAD * D * 2;
+  const int win_bytes = (int)(kend * p.kv_st * 2);
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
+  auto gload1 = [&](const __amdgpu_buffer_rsrc_t& rs, int t, int i) __attribute__((always_inline)) -> u32x4 {
+    const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff0 + tile_off + i * gstep, 0, 0));
+  };
+  auto gload = [&](const __amdgpu_buffer_rsrc_t& rs, int t, u32x4 (&dst)[LPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) dst[i] = gload1(rs, t, i);
+  };
+  u32x4 kst[LPT], vst[LPT];
+  if (T > 0) {  // tile 0, in flight while Q loads
+    gload(krsrc, 0, kst);
+    gload(vrsrc, 0, vst);
+  }
+
+  // ---- Q fragments of both query blocks (rows past the chunk re-read the last valid row)
+  bf16x8 qf[QB][DS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = min(wave * 32 * QB + qb * 32 + l32, nrows - 1);
+    const bf16_t* qr = qbase + (int64_t)row * p.q_st + hh * 8;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[qb][s] = __builtin_bit_cast(bf16x8, ld16(qr + s * 16));
+  }
+  // Mark the fragments as produced here (the load wait lands on this empty
+  // statement), so the loop below is not made to wait for them again.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[qb][s]));
+
+  f32x16 o[QB][DB];
+  float lsum[QB], mrun[QB];
+  // Reference maximum (log2 units; an integer, or -inf before the first
+  // block): 0 where the linear term seeds the accumulators.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mrun[qb] = FIRST ? (has_state ? 0.f : -INFINITY) : mio[qb];
+
+  // ---- accumulators at the start of a pass: the linear term at the
+  // reference, O^T = 2^-m S^T phi(Q)^T and l = 2^-m phi(Q).z (m is an integer,
+  // so scaling phi(Q) by 2^-m before rounding it to bf16 is exact)
+  auto init_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      lsum[qb] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < DB; ++nb) o[qb][nb] = f32x16{};
+    }
+    if (!has_state) return;
+    constexpr int SUNITS = (D / 8) * (D / 4);
+    for (int u = tid; u < SUNITS; u += THREADS) {
+      const int eg = u / (D / 4), ng = u % (D / 4);
+      f32x4 rows[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rows[i] = *reinterpret_cast<const f32x4*>(Sp + (int64_t)(eg * 8 + i) * D + ng * 4);
+      unsigned char* dst = eg < DS ? vb0 + (size_t)eg * D * 16 : vb1 + (size_t)(eg - DS) * D * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16(rows[2 * i][j], rows[2 * i + 1][j]);
+        *reinterpret_cast<u32x4*>(dst + (size_t)(ng * 4 + j) * 16) = w;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float sc = ldexpf(1.0f, -(int)mrun[qb]);
+      float lz = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, qf[qb][s]);
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = phi(bf16_lo(qw[i]));
+          f[2 * i + 1] = phi(bf16_hi(qw[i]));
+        }
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8 + 4);
+        lz += f[0] * z0[0] + f[1] * z0[1] + f[2] * z0[2] + f[3] * z0[3] + f[4] * z1[0] + f[5] * z1[1] +
+              f[6] * z1[2] + f[7] * z1[3];
+        const u32x4 pw = {pack_bf16(f[0] * sc, f[1] * sc), pack_bf16(f[2] * sc, f[3] * sc),
+                          pack_bf16(f[4] * sc, f[5] * sc), pack_bf16(f[6] * sc, f[7] * sc)};
+        const int eg = s * 2 + hh;
+        const unsigned char* src = eg < DS ? vb0 + (size_t)eg * D * 16 : vb1 + (size_t)(eg - DS) * D * 16;
+#pragma unroll
+        for (int nb = 0; nb < DB; ++nb) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + (nb * 32 + l32) * 16));
+          o[qb][nb] = mfma32(a, __builtin_bit_cast(bf16x8, pw), o[qb][nb]);
+        }
+      }
+      lsum[qb] = lz * sc;  // this lane's half of the features; the halves are summed at the end
+    }
+    __syncthreads();
+  };
+
+  // ---- pipeline machinery
+  const int kswz = ksw<D>(l32);
+  // V fragment layout of the transposed read: in each 16-lane group, source
+  // lane 4e + r supplies row 16ks + 8t + 4hh + e, columns nb*32 + 16*(group&1)
+  // + 4r; lane j of the group then holds column nb*32 + 16*(group&1) + j.
+  const int vj = lane & 15;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (vj & 3);
+  const int vrow0 = 4 * hh + (vj >> 2);
+  // keys of block blk inside the window (<= 0 for the second block of a last
+  // tile that holds at most 32 keys)
+  auto block_valid = [&](int blk) __attribute__((always_inline)) {
+    return (int)min((int64_t)32, kend - (kbeg + (int64_t)blk * 32));
+  };
+  // Tile buffers by tile index t + AHEAD.  PAR is the parity of t when known
+  // at compile time (0 or 1; -1 if not); then every LDS address folds into a
+  // constant offset from a per-lane register.
+  auto kbuf = [&](auto par_c, int t, auto ahead_c) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int par = decltype(par_c)::value, ahead = decltype(ahead_c)::value;
+    if constexpr (par < 0) return ((t + ahead) & 1) ? kb1 : kb0;
+    else return ((par + ahead) & 1) ? kb1 : kb0;
+  };
+  auto vbuf = [&](auto par_c, int t, auto ahead_c) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int par = decltype(par_c)::value, ahead = decltype(ahead_c)::value;
+    if constexpr (par < 0) return ((t + ahead) & 1) ? vb1 : vb0;
+    else return ((par + ahead + 2) & 1) ? vb1 : vb0;
+  };
+  using A0 = std::integral_constant<int, 0>;
+  using A1 = std::integral_constant<int, 1>;
+  using Am1 = std::integral_constant<int, -1>;
+
+  f32x16 sacc[2][QB];
+  bf16x2 pk[2][QB][8];
+  bf16x8 kf[3], vf[3];  // fragment ring
+  // Per-lane LDS byte offsets of the fragments within a tile; everything else
+  // (tile buffer, 32-key half, 16-key step, the second 8 rows of a V read) is
+  // a constant added to them.  K fragment s: row l32, granule (2s + hh) ^
+  // ksw(l32).  V fragment (ks, nb): rows 16ks + vrow0 (+8), column nb*32 +
+  // vcol; the swizzle vsw(row) depends on vrow0 only.
+  int kofs[DS], vofs[DB];
+#pragma unroll
+  for (int sidx = 0; sidx < DS; ++sidx) kofs[sidx] = l32 * D * 2 + ((2 * sidx + hh) ^ kswz) * 16;
+#pragma unroll
+  for (int nb = 0; nb < DB; ++nb) {
+    const int col = nb * 32 + vcol;
+    vofs[nb] = vrow0 * D * 2 + (((col >> 3) ^ vsw<D>(vrow0)) * 16) + (col & 7) * 2;
+  }
+  auto read_k = [&](const unsigned char* kt, int qh, int sidx) __attribute__((always_inline)) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + kofs[sidx] + 32 * qh * D * 2));
+  };
+  auto read_v = [&](const unsigned char* vt, int vh, int r) __attribute__((always_inline)) -> bf16x8 {
+    const int ks = r >> 2, nb = r & 3;
+    const unsigned char* pa = vt + vofs[nb] + (32 * vh + 16 * ks) * D * 2;
+    const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * D * 2));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
+    return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+  };
+
+  // Softmax of one 32-key block for both query blocks, 16 slices per block
+  // (slice u of block x runs in group 2u + x of the step).  Per block x,
+  // elements 2j and 2j+1 (acc reg 4r+i holds key 8r + 4hh + i):
+  //   slice 2j:   argument fma of the pair; rounding and summing of pair j-1
+  //   slice 2j+1: exponentials of the pair
+  // so no slice waits on its own results; pair 7 is finished after the rounds.
+  float sm_f[QB][2], sm_e[QB][2], sm_ps[QB][2], sm_lold[QB];
+  bool sm_bad[QB];
+  int dirty = 0;
+  const float ps_max = __builtin_amdgcn_exp2f(kQ2Slack);
+  auto sm_slice = [&](auto u_c, auto x_c, const f32x16 (&acc)[QB], bf16x2 (&pkc)[QB][8]) __attribute__((always_inline)) {
+    constexpr int u = decltype(u_c)::value, x = decltype(x_c)::value, j = u >> 1;
+    if constexpr ((u & 1) == 0) {
+      sm_f[x][0] = fmaf(acc[x][2 * j], p.scale_log2, -mrun[x]);
+      sm_f[x][1] = fmaf(acc[x][2 * j + 1], p.scale_log2, -mrun[x]);
+      pin(sm_f[x][0]);
+      pin(sm_f[x][1]);
+      if constexpr (j >= 1) {
+        bf16x2 pr;
+        pr[0] = (__bf16)sm_e[x][0];
+        pr[1] = (__bf16)sm_e[x][1];
+        pkc[x][j - 1] = pr;
+        pin(pkc[x][j - 1]);
+        if constexpr (j == 1) {
+          sm_ps[x][0] = sm_e[x][0];
+          sm_ps[x][1] = sm_e[x][1];
+        } else {
+          sm_ps[x][0] += sm_e[x][0];
+          sm_ps[x][1] += sm_e[x][1];
+        }
+        pin(sm_ps[x][0]);
+        pin(sm_ps[x][1]);
+      }
+    } else {
+      sm_e[x][0] = __builtin_amdgcn_exp2f(sm_f[x][0]);
+      sm_e[x][1] = __builtin_amdgcn_exp2f(sm_f[x][1]);
+      pin(sm_e[x][0]);
+      pin(sm_e[x][1]);
+    }
+  };
+  // Pair 7 and the block's row sum; CHECK: test the bound.
+  auto sm_finish = [&](auto x_c, auto check_c, bf16x2 (&pkc)[QB][8]) __attribute__((always_inline)) {
+    constexpr int x = decltype(x_c)::value;
+    bf16x2 pr;
+    pr[0] = (__bf16)sm_e[x][0];
+    pr[1] = (__bf16)sm_e[x][1];
+    pkc[x][7] = pr;
+    const float ps = (sm_ps[x][0] + sm_e[x][0]) + (sm_ps[x][1] + sm_e[x][1]);
+    if constexpr (decltype(check_c)::value) sm_bad[x] = __any(!(ps <= ps_max));
+    sm_lold[x] = lsum[x];
+    lsum[x] += ps;
+  };
+  // The rare path: redo block x against its true maximum (merged over the two
+  // lanes that hold a query's keys), rounded up to an integer.  Before the
+  // first accepted block nothing has been accumulated; after it, the
+  // accumulators no longer match the new reference and the tile is marked
+  // for a second pass.
+  auto sm_redo = [&](auto x_c, const f32x16 (&acc)[QB], bf16x2 (&pkc)[QB][8]) __attribute__((always_inline)) {
+    constexpr int x = decltype(x_c)::value;
+    const f32x16& a = acc[x];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, a[i]);
+    const float mold = mrun[x];
+    const float mnew = fmaxf(mold, ceilf(half_max(mx) * p.scale_log2));
+    dirty |= (int)(mold != -INFINITY && mnew != mold);
+    mrun[x] = mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(a[2 * i], p.scale_log2, -mnew));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(a[2 * i + 1], p.scale_log2, -mnew));
+      pkc[x][i][0] = (__bf16)e0;
+      pkc[x][i][1] = (__bf16)e1;
+      ps += e0 + e1;
+    }
+    lsum[x] = mold == -INFINITY ? ps : fmaf(sm_lold[x], __builtin_amdgcn_exp2f(mold - mnew), ps);
+  };
+  // keys at or past `valid` get score -inf
+  auto sm_mask = [&](f32x16 (&acc)[QB], int valid) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < QB; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * hh + (i & 3) >= valid) acc[x][i] = -INFINITY;
+  };
+  // Staged-tile work of a period's first step: op j of 16, two per round.
+  auto stage_op = [&](auto j_c, auto par_c, int t) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_c)::value;
+    if constexpr (j < 4) {
+      *reinterpret_cast<u32x4*>(kbuf(par_c, t, A1{}) + kls0 + j * LSTEP) = kst[j];
+    } else if constexpr (j < 8) {
+      kst[j - 4] = gload1(krsrc, t + 2, j - 4);
+    } else if constexpr (j < 12) {
+      *reinterpret_cast<u32x4*>(vbuf(par_c, t, A0{}) + vls0 + (j - 8) * LSTEP) = vst[j - 8];
+    } else {
+      vst[j - 12] = gload1(vrsrc, t + 1, j - 12);
+    }
+  };
+
+  // One step.  F: flags; BASE: ring slot of round 0; CHECK: test the softmax
+  // bound (first pass).  PRE_K / PRE_V: the period's second step needs K / V
+  // fragments, prefetched in rounds 6 and 7.
+  enum : int { kQK = 1, kSM = 2, kPV = 4, kMASK = 8, kSTAGE = 16, kPRE_K = 32, kPRE_V = 64 };
+  auto step = [&](auto f_c, auto base_c, auto par_c, auto check_c, int t, const unsigned char* kt, int qh,
+                  f32x16 (&acc_next)[QB], f32x16 (&acc_cur)[QB], bf16x2 (&pk_cur)[QB][8], int valid,
+                  const unsigned char* vt, int vh, const bf16x2 (&pk_prev)[QB][8]) __attribute__((always_inline)) {
+    constexpr int F = decltype(f_c)::value, base = decltype(base_c)::value;
+    constexpr bool QK = F & kQK, SM = F & kSM, PV = F & kPV, CHECK = decltype(check_c)::value;
+    if constexpr (SM && (F & kMASK)) {
+      if (valid < 32) sm_mask(acc_cur, valid);
+    }
+    static_for<0, 8>([&](auto r_c) __attribute__((always_inline)) {
+      constexpr int r = decltype(r_c)::value;
+      constexpr int slot = (base + r) % 3, pre = (base + r + 2) % 3;
+      constexpr int ks = r >> 2, nb = r & 3;
+      // group 0: LDS reads two rounds ahead, QK^T for query block 0
+      if constexpr (r + 2 < 8) {
+        if constexpr (QK) kf[pre] = read_k(kt, qh, r + 2);
+        if constexpr (PV) vf[pre] = read_v(vt, vh, r + 2);
+      } else {
+        if constexpr ((F & kPRE_K) != 0) kf[pre] = read_k(kt, qh + 1, r - 6);
+        if constexpr ((F & kPRE_V) != 0) vf[pre] = read_v(vt, vh + 1, r - 6);
+      }
+      if constexpr (QK) {
+        if constexpr (r == 0) mfma_qk_first(acc_next[0], kf[slot], qf[0][r]);
+        else mfma_qk(acc_next[0], kf[slot], qf[0][r]);
+      }
+      if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r>{}, A0{}, acc_cur, pk_cur);
+      __builtin_amdgcn_sched_barrier(0);
+      // group 1: QK^T for query block 1
+      if constexpr (QK) {
+        if constexpr (r == 0) mfma_qk_first(acc_next[1], kf[slot], qf[1][r]);
+        else mfma_qk(acc_next[1], kf[slot], qf[1][r]);
+      }
+      if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r>{}, A1{}, acc_cur, pk_cur);
+      __builtin_amdgcn_sched_barrier(0);
+      // group 2: P V for query block 0 (+ staged-tile work)
+      if constexpr (PV) {
+        const u32x4 w4 = {__builtin_bit_cast(uint32_t, pk_prev[0][4 * ks]), __builtin_bit_cast(uint32_t, pk_prev[0][4 * ks + 1]),
+                          __builtin_bit_cast(uint32_t, pk_prev[0][4 * ks + 2]), __builtin_bit_cast(uint32_t, pk_prev[0][4 * ks + 3])};
+        o[0][nb] = mfma32(vf[slot], __builtin_bit_cast(bf16x8, w4), o[0][nb]);
+        pin_acc(o[0][nb]);
+      }
+      if constexpr ((F & kSTAGE) != 0) {
+        stage_op(std::integral_constant<int, 2 * r>{}, par_c, t);
+        stage_op(std::integral_constant<int, 2 * r + 1>{}, par_c, t);
+      }
+      if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r + 1>{}, A0{}, acc_cur, pk_cur);
+      __builtin_amdgcn_sched_barrier(0);
+      // group 3: P V for query block 1
+      if constexpr (PV) {
+        const u32x4 w4 = {__builtin_bit_cast(uint32_t, pk_prev[1][4 * ks]), __builtin_bit_cast(uint32_t, pk_prev[1][4 * ks + 1]),
+                          __builtin_bit_cast(uint32_t, pk_prev[1][4 * ks + 2]), __builtin_bit_cast(uint32_t, pk_prev[1][4 * ks + 3])};
+        o[1][nb] = mfma32(vf[slot], __builtin_bit_cast(bf16x8, w4), o[1][nb]);
+        pin_acc(o[1][nb]);
+      }
+      if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r + 1>{}, A1{}, acc_cur, pk_cur);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (SM) {
+      sm_finish(A0{}, check_c, pk_cur);
+      sm_finish(A1{}, check_c, pk_cur);
+      if constexpr (CHECK) {
+        if (__builtin_expect(sm_bad[0] | sm_bad[1], 0)) {
+          if (sm_bad[0]) sm_redo(A0{}, acc_cur, pk_cur);
+          if (sm_bad[1]) sm_redo(A1{}, acc_cur, pk_cur);
+        }
+      }
+    }
+  };
+  // Period t: steps A and B with flags FA, FB (prefetch flags derived here).
+  auto period = [&](int t, auto par_c, auto check_c, auto fa_c, auto fb_c, int valid_a, int valid_b) __attribute__((always_inline)) {
+    constexpr int FA0 = decltype(fa_c)::value, FB = decltype(fb_c)::value;
+    constexpr int FA = FA0 | ((FB & kQK) ? kPRE_K : 0) | ((FB & kPV) ? kPRE_V : 0);
+    const unsigned char* kt = kbuf(par_c, t, A0{});
+    const unsigned char* vprev = vbuf(par_c, t, Am1{});
+    if constexpr ((FA & kQK) != 0) {
+      kf[0] = read_k(kt, 0, 0);
+      kf[1] = read_k(kt, 0, 1);
+    }
+    if constexpr ((FA & kPV) != 0) {
+      vf[0] = read_v(vprev, 0, 0);
+      vf[1] = read_v(vprev, 0, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    step(std::integral_constant<int, FA>{}, A0{}, par_c, check_c, t, kt, 0, sacc[0], sacc[1], pk[1], valid_a, vprev, 0, pk[0]);
+    step(std::integral_constant<int, FB>{}, std::integral_constant<int, 2>{}, par_c, check_c, t, kt, 1, sacc[1], sacc[0], pk[0],
+         valid_b, vprev, 1, pk[1]);
+  };
+  using C0 = std::integral_constant<int, kQK | kSTAGE>;
+  using C1 = std::integral_constant<int, kQK | kSM | kMASK>;
+  using CA = std::integral_constant<int, kQK | kSM | kPV | kSTAGE>;
+  using CB = std::integral_constant<int, kQK | kSM | kPV>;
+  using CBm = std::integral_constant<int, kQK | kSM | kPV | kMASK>;
+  using CTa = std::integral_constant<int, kSM | kPV | kMASK>;
+  using CTb = std::integral_constant<int, kPV>;
+
+  // The whole window: period t (0 <= t <= T) covers K tile t and V tile t-1.
+  // Its first step also moves the staged tiles: LDS stores of K tile t+1 and
+  // V tile t from registers, buffer loads of K tile t+2 and V tile t+1
+  // (tiles past the window read as zeros and are never used).
+  auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
+    // prologue: K tile 0 into LDS, K tile 1 and V tile 0 in flight
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(kb0 + kls0 + i * LSTEP) = kst[i];
+    gload(krsrc, 1, kst);
+    constexpr int kWaitAllButKTile = wait_vm(LPT);
+    __builtin_amdgcn_s_waitcnt(kWaitAllButKTile);
+    __syncthreads();
+    period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
+    __syncthreads();
+    // steady state: every block of K tile t and V tile t-1 is full; two
+    // periods per iteration so the buffer parity is known
+    int t = 1;
+    for (; t + 2 < T; t += 2) {
+      period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
+      __syncthreads();
+      period(t + 1, A0{}, check_c, CA{}, CB{}, 32, 32);
+      __syncthreads();
+    }
+    if (t + 1 < T) {
+      period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
+      __syncthreads();
+    }
+    if (T > 1) {  // period T-1: the last K tile (may be partial)
+      period(T - 1, Am1{}, check_c, CA{}, CBm{}, 32, block_valid(2 * T - 2));
+      __syncthreads();
+    }
+    // period T: softmax of the last block, P V of the last V tile
+    period(T, Am1{}, check_c, CTa{}, CTb{}, block_valid(2 * T - 1), 32);
+  };
+
+  init_acc();
+  if (T > 0) pipeline(std::integral_constant<bool, FIRST>{});
+
+  // ---- epilogue: normalise, stage bf16 rows in LDS (per wave), write coalesced
+  __syncthreads();
+  unsigned char* stage = wave == 0 ? kb0 : wave == 1 ? kb1 : wave == 2 ? vb0 : vb1;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = half_sum(lsum[qb]);
+    const float inv = 1.0f / ltot;
+    const int r = qb * 32 + l32;  // row within the wave's 64
+#pragma unroll
+    for (int nb = 0; nb < DB; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int col = nb * 32 + 8 * rr + 4 * hh;
+        const int g = col >> 3;
+        u32x2 pr = {pack_bf16(o[qb][nb][4 * rr] * inv, o[qb][nb][4 * rr + 1] * inv),
+                    pack_bf16(o[qb][nb][4 * rr + 2] * inv, o[qb][nb][4 * rr + 3] * inv)};
+        *reinterpret_cast<u32x2*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16) + (col & 7) * 2) = pr;
+      }
+    const int myrow = wave * 32 * QB + r;
+    if (p.lse != nullptr && hh == 0 && myrow < nrows) {
+      const int64_t L = (int64_t)p.n_qchunks * p.C;
+      p.lse[(int64_t)bh * L + qtok0 + myrow] = (mrun[qb] + __log2f(ltot)) * kLn2;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging writes are complete
+  __builtin_amdgcn_wave_barrier();
+  bf16_t* obase = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
+  for (int idx = lane; idx < 32 * QB * GR; idx += 64) {
+    const int r = idx / GR, g = idx % GR;
+    const int row = wave * 32 * QB + r;
+    if (row < nrows)
+      st16(obase + (int64_t)row * p.q_st + g * 8,
+           *reinterpret_cast<const u32x4*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16)));
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mio[qb] = mrun[qb];
+  return dirty;
+}
+
+// The rare second pass, kept out of line so that its registers do not add to
+// the first pass's.
+template <int D>
+__device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float m1) {
+  float m[Q2_QB] = {m0, m1};
+  tile_pass<D, false>(p, m);
+}
+
+template <int D>
+__global__ __launch_bounds__(Q2_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_qb2_kernel(const FwdParams p) {
+  float m[Q2_QB];
+  const int dirty = tile_pass<D, true>(p, m);
+  // Every wave reaches this barrier.  Where some query's reference moved after
+  // accumulation, the whole tile is computed again with the final references
+  // (which no score exceeds by the bound); its output replaces the first.
+  if (__syncthreads_or(dirty)) tile_second_pass<D>(p, m[0], m[1]);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s) {
+  p.tiles_per_chunk = (p.C + Q2_BM - 1) / Q2_BM;
+  p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk;
+  if (p.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128>), dim3(p.total_tiles), dim3(Q2_THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace rha

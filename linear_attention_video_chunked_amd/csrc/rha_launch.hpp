@@ -75,6 +75,8 @@ struct CopyParams {
 // The forward launchers fill in tiles_per_chunk and total_tiles (they depend
 // on the kernel's tile height) before launching.
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
+// head_dim 128 with 64 query rows per wave (the default for d = 128)
+hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(FwdParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_f32(const ChunkStateParams& p, int d, hipStream_t s);

@@ -158,6 +158,14 @@ def test_too_large_problem_rejected(L):
     assert "too large" in L.rha_last_error().decode()
 
 
+def test_head_byte_span_limit(L):
+    # 32-bit buffer offsets: one head's keys (plus two tiles of slack) must
+    # span less than 2 GiB; token-major strides make that the binding limit
+    prob = _prob(chunk_len=4096, n_chunks=16, stride_t=16384)
+    assert _scan(L, prob) == 1
+    assert "2 GiB" in L.rha_last_error().decode()
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_rha, "_LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_rha, "_lib", None)

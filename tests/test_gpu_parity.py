@@ -157,6 +157,25 @@ def test_empty_problems():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("alpha", [40.0, 170.0, -170.0])
+def test_score_growth_within_window(alpha):
+    # Every query shares a component along feature 0; the last key of every
+    # chunk is alpha along that feature, so windows see ordinary scores first
+    # and then one key scoring about 0.35 * alpha (natural log units) above
+    # them.  alpha = 40 stays inside the kernels' tolerance for a stale
+    # reference maximum; alpha = 170 (a ~60-nat jump, 2^86) forces reference
+    # moves after accumulation, both where the linear state seeds the
+    # accumulators and where it does not; -170 makes those keys vanish.
+    wl = Workload("growth", 950, B=1, H=2, d=128, C=100, N=4, w=2, dtype="bf16", qscale=1.0, kscale=0.5)
+    q, k, v = gen_qkv(wl)
+    q = q.clone()
+    k = k.clone()
+    q[..., 0] += 4.0
+    k[:, :, wl.C - 1:: wl.C, 0] = alpha
+    out, lse, S, z = run_lib(q, k, v, wl.C, wl.w)
+    check_full(wl, out, lse, S, z, to64(q), to64(k), to64(v))
+
+
 def test_bitwise_deterministic():
     wl = mid_workload("bf16_d128_C200_N5_w2_q4")
     q, k, v = gen_qkv(wl)
