@@ -7,15 +7,18 @@
 // (explainer, section 2.A) folds each frame that leaves the sliding window into
 // this state; "ReHyAt" (abstract) evaluates the same quantity chunk by chunk.
 //
-// One workgroup per (head, chunk): 4 waves, each owning a 32-row block of the
-// feature axis e of U (all of n for d = 128).  Tokens stream through LDS in
-// tiles of 64; both operands are contracted over tokens, so both phi(K) and V
-// are stored transposed (8 consecutive tokens per 16-byte MFMA fragment) by an
-// in-register 4x8 transpose of the 16-byte global loads.  phi is evaluated in
-// float32 and rounded to bf16 for the product; u is summed from the float32
+// One workgroup per (head, chunk, 64-row slice of the feature axis e of U):
+// 4 waves, each owning 32x32 output blocks of the slice.  Tokens stream
+// through LDS in tiles of 64, stored as loaded (token-major rows, 16-byte
+// granules XOR-swizzled); both operands are contracted over tokens, so both
+// are read with the LDS transpose read ds_read_b64_tr_b16, which hands each
+// lane 8 tokens of one feature column.  Two tiles are in flight from HBM while
+// one is multiplied (the kernel is bound by HBM, not by the products).  phi is evaluated
+// in float32 and rounded to bf16 for the product; u is summed from the float32
 // phi values in a fixed order.  With `accumulate` the result is added into
 // the destination (the streaming fold), otherwise it is stored.
 #include "rha_device.hpp"
+#include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
 
 namespace rha {
@@ -23,65 +26,78 @@ namespace {
 
 constexpr int NW = 4;
 constexpr int THREADS = NW * kWave;
-constexpr int BT = 64;  // tokens per tile
+constexpr int BT = 64;      // tokens per tile
+constexpr int ESLICE = 64;  // rows e of U per workgroup
 
 template <int D>
 struct StateCfg {
-  static constexpr int TBYTES = BT * D * 2;        // one transposed tile
-  static constexpr int UNITS = (BT / 4) * (D / 8);  // 4-token x 8-feature load units
-  static constexpr int EB = D / 32;
-  static constexpr int NBW = EB * EB / NW;          // output 32x32 blocks per wave
-  static_assert(UNITS <= THREADS, "one unit per thread at most");
-  static_assert(NBW >= 1, "at least one block per wave");
+  static constexpr int ES = D / ESLICE;                   // slices per chunk
+  static constexpr int KBYTES = BT * ESLICE * 2;          // one phi(K) slice tile
+  static constexpr int VBYTES = BT * D * 2;               // one V tile
+  static constexpr int KUNITS = (BT / 4) * (ESLICE / 8);  // 4-token x 8-feature load units
+  static constexpr int VUNITS = (BT / 4) * (D / 8);
+  static constexpr int NBW = (ESLICE / 32) * (D / 32) / NW;  // output 32x32 blocks per wave
+  static_assert(KUNITS <= THREADS && VUNITS <= THREADS, "one unit per thread at most");
+  static_assert(NBW >= 1 && (ESLICE / 32) * (D / 32) % NW == 0, "whole blocks per wave");
 };
 
-// Store a 4-token x 8-feature unit transposed: tokens 4*tq .. +3 of the tile.
-// Layout: element (token t, feature f) of the tile at ((ks*2 + g)*D + f)*8 + i
-// where ks = t/16 and (g, i) follow the MFMA k-order used for both operands.
-template <int D>
-__device__ __forceinline__ void store_unit_t(unsigned char* tbuf, int tq, int fo, const uint32_t (&w)[4][4]) {
-  const int ks = tq >> 2, m = tq & 3;
-  const int g = m & 1, e0 = (m >> 1) * 4;
-#pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    const int wd = f >> 1, sh = (f & 1) * 16;
-    const uint32_t x0 = (w[0][wd] >> sh) & 0xffffu, x1 = (w[1][wd] >> sh) & 0xffffu;
-    const uint32_t x2 = (w[2][wd] >> sh) & 0xffffu, x3 = (w[3][wd] >> sh) & 0xffffu;
-    u32x2 pr = {x0 | (x1 << 16), x2 | (x3 << 16)};
-    *reinterpret_cast<u32x2*>(tbuf + (((size_t)(ks * 2 + g) * D + fo * 8 + f) * 8 + e0) * 2) = pr;
-  }
+// Row-major tile of W features: granule g (8 features) of token row r sits at
+// slot g ^ sw(r); the swizzle spreads the rows a transpose read covers over
+// distinct banks (as for the attention kernels' V tiles).
+template <int W> __device__ __forceinline__ int tsw(int r) { return fwd::vsw<W>(r); }
+
+// One 16-byte granule: token row r, granule g.
+template <int W>
+__device__ __forceinline__ void store_granule(unsigned char* tile, int r, int g, const u32x4& x) {
+  *reinterpret_cast<u32x4*>(tile + r * W * 2 + ((g ^ tsw<W>(r)) * 16)) = x;
+}
+
+// MFMA operand fragment over tokens 16ks .. 16ks+15 for feature columns
+// cb*32 .. cb*32+31 of a W-wide tile: lane l gets column cb*32 + l%32 and 8
+// tokens, in the same k-order for every operand read this way.
+template <int W>
+__device__ __forceinline__ bf16x8 read_frag_t(const unsigned char* tile, int ks, int cb, int lane) {
+  const int hh = lane >> 5, vj = lane & 15;
+  const int col = cb * 32 + 16 * ((lane >> 4) & 1) + 4 * (vj & 3);
+  const int ra = 16 * ks + 4 * hh + (vj >> 2), rb = ra + 8;
+  const int ga = col >> 3, cbyte = (col & 7) * 2;
+  const fwd::i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (fwd::lds_i16x4*)(tile + ra * W * 2 + ((ga ^ tsw<W>(ra)) * 16) + cbyte));
+  const fwd::i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (fwd::lds_i16x4*)(tile + rb * W * 2 + ((ga ^ tsw<W>(rb)) * 16) + cbyte));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
+  return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 }
 
 template <int D>
 __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkStateParams p) {
   using Cfg = StateCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * Cfg::TBYTES];
-  __shared__ float zred[BT / 4][D];
-  unsigned char* const kt0 = smem;                      // phi(K)^T, 2 buffers
-  unsigned char* const vt0 = smem + 2 * Cfg::TBYTES;    // V^T, 2 buffers
+  __shared__ __attribute__((aligned(1024))) unsigned char kt_s[2][Cfg::KBYTES];  // phi(K) slice, 2 buffers
+  __shared__ __attribute__((aligned(1024))) unsigned char vt_s[2][Cfg::VBYTES];  // V, 2 buffers
+  __shared__ float zred[BT / 4][ESLICE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  const int jc = blockIdx.x % p.n_chunks;
-  const int bh = blockIdx.x / p.n_chunks;
+  // slices of one chunk are adjacent in the logical order, which keeps them
+  // on one XCD (one L2) so V is fetched from HBM once
+  const int total = p.B * p.H * p.n_chunks * Cfg::ES;
+  const int logical = fwd::xcd_remap(blockIdx.x, total);
+  const int es = logical % Cfg::ES;
+  const int jc = (logical / Cfg::ES) % p.n_chunks;
+  const int bh = logical / Cfg::ES / p.n_chunks;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t t0 = (int64_t)(p.chunk0 + jc) * p.C;
-  const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
+  const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st + es * ESLICE;
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
 
-  const bool active = Cfg::UNITS == THREADS || tid < Cfg::UNITS;
-  const int fo = tid % (D / 8), tq = tid / (D / 8);
+  const bool kact = tid < Cfg::KUNITS, vact = tid < Cfg::VUNITS;
+  const int kfo = tid % (ESLICE / 8), ktq = tid / (ESLICE / 8);
+  const int vfo = tid % (D / 8), vtq = tid / (D / 8);
 
-  int eb, nb0;
-  if (Cfg::EB == 4) {
-    eb = wave;
-    nb0 = 0;
-  } else {
-    eb = wave >> 1;
-    nb0 = wave & 1;
-  }
+  const int eb = wave / (NW * Cfg::NBW / (D / 32));
+  const int nb0 = (wave * Cfg::NBW) % (D / 32);
 
   f32x16 acc[Cfg::NBW];
 #pragma unroll
@@ -91,76 +107,92 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
   const int ntiles = (p.C + BT - 1) / BT;
-  uint32_t kw[4][4], vw[4][4];
+  u32x4 kw[2][4], vw[2][4];  // two tiles in flight: 4 token rows x 16 bytes each
 
-  auto gload = [&](int j) {
-    if (!active) return;
+  // Buffer loads whose descriptors end at the chunk's last token: rows past
+  // it (and the lanes without a unit) read zeros, so loads and stores need no
+  // branches and the load waits stay exact.
+  const int chunk_bytes = p.C * (int)p.kv_st * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, chunk_bytes, fwd::kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, chunk_bytes, fwd::kBufWord3);
+  const int kofs0 = kact ? (ktq * 4 * (int)p.kv_st + kfo * 8) * 2 : chunk_bytes;
+  const int vofs0 = vact ? (vtq * 4 * (int)p.kv_st + vfo * 8) * 2 : chunk_bytes;
+  const int row_bytes = (int)p.kv_st * 2;
+  auto gload = [&](int j, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    const int tile_off = j * BT * row_bytes;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = j * BT + tq * 4 + r;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (t < p.C) {
-        xk = ld16(kbase + (int64_t)t * p.kv_st + fo * 8);
-        xv = ld16(vbase + (int64_t)t * p.kv_st + fo * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kw[r][i] = xk[i];
-        vw[r][i] = xv[i];
-      }
+      const int ko = kact ? kofs0 + tile_off + r * row_bytes : chunk_bytes;
+      const int vo = vact ? vofs0 + tile_off + r * row_bytes : chunk_bytes;
+      kw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ko, 0, 0));
+      vw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
     }
   };
-  auto lstore = [&](int j, int buf) {
-    if (!active) return;
-    uint32_t fw[4][4];
+  auto lstore = [&](int j, int buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    if (kact) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = j * BT + tq * 4 + r < p.C;
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = j * BT + ktq * 4 + r < p.C;  // rows past the chunk: phi(0) would be 1
+        u32x4 fw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = ok ? phi(bf16_lo(kw[r][i])) : 0.f;
-        const float c = ok ? phi(bf16_hi(kw[r][i])) : 0.f;
-        zacc[2 * i] += a;
-        zacc[2 * i + 1] += c;
-        fw[r][i] = pack_bf16(a, c);
+        for (int i = 0; i < 4; ++i) {
+          const float a = ok ? phi(bf16_lo(kw[sl][r][i])) : 0.f;
+          const float c = ok ? phi(bf16_hi(kw[sl][r][i])) : 0.f;
+          zacc[2 * i] += a;
+          zacc[2 * i + 1] += c;
+          fw[i] = pack_bf16(a, c);
+        }
+        store_granule<ESLICE>(kt_s[buf], ktq * 4 + r, kfo, fw);
       }
     }
-    store_unit_t<D>(kt0 + buf * Cfg::TBYTES, tq, fo, fw);
-    store_unit_t<D>(vt0 + buf * Cfg::TBYTES, tq, fo, vw);
+    if (vact) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_granule<D>(vt_s[buf], vtq * 4 + r, vfo, vw[sl][r]);
+    }
   };
-
-  gload(0);
-  lstore(0, 0);
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
-    const unsigned char* kt = kt0 + buf * Cfg::TBYTES;
-    const unsigned char* vt = vt0 + buf * Cfg::TBYTES;
+  auto mma = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < BT / 16; ++ks) {
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(kt + ((size_t)(ks * 2 + hh) * D + eb * 32 + l32) * 16));
+      const bf16x8 a = read_frag_t<ESLICE>(kt_s[buf], ks, eb, lane);
 #pragma unroll
-      for (int i = 0; i < Cfg::NBW; ++i) {
-        const int nb = nb0 + i;
-        const bf16x8 bb = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(vt + ((size_t)(ks * 2 + hh) * D + nb * 32 + l32) * 16));
-        acc[i] = mfma32(a, bb, acc[i]);
-      }
+      for (int i = 0; i < Cfg::NBW; ++i) acc[i] = mfma32(a, read_frag_t<D>(vt_s[buf], ks, nb0 + i, lane), acc[i]);
     }
-    if (j + 1 < ntiles) lstore(j + 1, buf ^ 1);
-    __syncthreads();
-  }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
-  // U: acc[i] reg 4r+q <-> e = eb*32 + 8r + 4hh + q, n = (nb0+i)*32 + l32
+  // tile j lives in register slot j & 1 and LDS buffer j & 1
+  // (tiles past the chunk load as zeros and store harmlessly: phi is masked
+  // by token index, and the buffer they land in is not read again)
+  gload(0, S0{});
+  gload(1, S1{});
+  lstore(0, 0, S0{});
+  __syncthreads();
+  auto iter = [&](int j, auto slot_c) {  // slot_c = j & 1
+    constexpr int sl = decltype(slot_c)::value;
+    using Next = std::integral_constant<int, sl ^ 1>;
+    gload(j + 2, slot_c);  // slot of tile j, already in LDS
+    mma(sl);
+    lstore(j + 1, sl ^ 1, Next{});
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    iter(j, S0{});
+    iter(j + 1, S1{});
+  }
+  if (j < ntiles) iter(j, S0{});
+
+  // U: acc[i] reg 4r+q <-> e = es*64 + eb*32 + 8r + 4hh + q, n = (nb0+i)*32 + l32
   float* Sdst = p.S + (int64_t)bh * p.s_bh + (int64_t)(jc + p.slot_offset) * D * D;
 #pragma unroll
   for (int i = 0; i < Cfg::NBW; ++i) {
     const int n = (nb0 + i) * 32 + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int e = eb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int e = es * ESLICE + eb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
       float* dst = Sdst + (int64_t)e * D + n;
       const float val = acc[i][r];
       *dst = p.accumulate ? *dst + val : val;
@@ -168,16 +200,16 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   }
 
   // u: fixed-order reduction of the per-thread partial sums
-  if (active) {
+  if (kact) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zred[tq][fo * 8 + i] = zacc[i];
+    for (int i = 0; i < 8; ++i) zred[ktq][kfo * 8 + i] = zacc[i];
   }
   __syncthreads();
-  if (tid < D) {
+  if (tid < ESLICE) {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < BT / 4; ++r) s += zred[r][tid];
-    float* zd = p.z + (int64_t)bh * p.z_bh + (int64_t)(jc + p.slot_offset) * D + tid;
+    float* zd = p.z + (int64_t)bh * p.z_bh + (int64_t)(jc + p.slot_offset) * D + es * ESLICE + tid;
     *zd = p.accumulate ? *zd + s : s;
   }
 }
@@ -185,11 +217,11 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
 }  // namespace
 
 hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.H * p.n_chunks));
+  const int64_t heads_chunks = (int64_t)p.B * p.H * p.n_chunks;
   if (d == 128)
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<128>, grid, dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL(chunk_state_bf16_kernel<128>, dim3((unsigned)(heads_chunks * StateCfg<128>::ES)), dim3(THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<64>, grid, dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL(chunk_state_bf16_kernel<64>, dim3((unsigned)(heads_chunks * StateCfg<64>::ES)), dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 
