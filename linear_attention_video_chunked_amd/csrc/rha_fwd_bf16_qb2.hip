@@ -101,7 +101,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   static_assert(TILE >= D * D, "half of the state staging must fit one V buffer");
   static_assert(TILE >= 32 * QB * D * 2, "one wave's output rows must fit one tile buffer");
   static_assert(NW == 4, "the epilogue stages one wave per tile buffer");
-  static_assert(LPT == 4, "stage ops assume four loads per tensor and thread");
+
   static_assert(TILE == Q2_TILE, "tile buffer size");
   unsigned char* const kb0 = q2_kb0;
   unsigned char* const kb1 = q2_kb1;
@@ -150,37 +150,34 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   }
   const int T = (int)((kend - kbeg + BN - 1) / BN);  // LDS tiles in the window
 
-  // ---- tile loads: granule f = i*THREADS + tid of a tile (row f / GR,
-  // granule f % GR) goes through registers into LDS slot g ^ sw(row).  Buffer
-  // loads: a descriptor per tensor whose extent ends at the window end, the
-  // per-lane byte offset as the (range-checked) vector offset, so rows at or
-  // past the window end read as zero.  Load i of a thread is row
-  // i*THREADS/GR further than load 0, and both swizzles repeat within those
-  // rows, so one per-lane offset serves all i.
-  static_assert(THREADS % GR == 0 && (THREADS / GR) % 16 == 0, "swizzle period must divide the row step");
-  constexpr int ROWS_PER_LOAD = THREADS / GR;
-  const int row0 = tid / GR, g0 = tid % GR;
-  const int goff0 = (row0 * (int)p.kv_st + g0 * 8) * 2;
-  const int gstep = ROWS_PER_LOAD * (int)p.kv_st * 2;
-  const int kls0 = row0 * D * 2 + (g0 ^ ksw<D>(row0)) * 16;
-  const int vls0 = row0 * D * 2 + (g0 ^ vsw<D>(row0)) * 16;
-  constexpr int LSTEP = ROWS_PER_LOAD * D * 2;
+  // ---- tile loads: direct HBM -> LDS (buffer loads with the LDS flag).  One
+  // such load moves 64 lanes x 16 bytes into 1 KiB of consecutive LDS (lane L
+  // at byte 16L): 4 rows of a tile.  Wave w issues loads i = 0..3 of a tile,
+  // rows 4(4w+i) .. +3; lane L fills row 4(4w+i) + L/16, slot L%16, with the
+  // global granule that the swizzle puts there (g = slot ^ sw(row)).  The
+  // descriptor ends at the window end, so rows past it read as zero.
+  static_assert(NW * 4 * 4 == BN && GR == 16, "four 4-row loads per wave cover a 64-row tile");
+  const int lrow = lane >> 4, lslot = lane & 15;
+  int kdma[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (4 * wave + i) + lrow;
+    kdma[i] = (row * (int)p.kv_st + (lslot ^ ksw<D>(row)) * 8) * 2;
+  }
+  const int vdma0 = ((16 * wave + lrow) * (int)p.kv_st + (lslot ^ vsw<D>(lrow)) * 8) * 2;  // vsw(row) = vsw(lrow)
+  const int vdma_step = 4 * (int)p.kv_st * 2;
   const int win_bytes = (int)(kend * p.kv_st * 2);
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
-  auto gload1 = [&](const __amdgpu_buffer_rsrc_t& rs, int t, int i) __attribute__((always_inline)) -> u32x4 {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dma_k = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
     const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff0 + tile_off + i * gstep, 0, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(dst + (4 * wave + i) * 1024), 16, kdma[i] + tile_off, 0, 0, 0);
   };
-  auto gload = [&](const __amdgpu_buffer_rsrc_t& rs, int t, u32x4 (&dst)[LPT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) dst[i] = gload1(rs, t, i);
+  auto dma_v = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
+    const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(dst + (4 * wave + i) * 1024), 16, vdma0 + i * vdma_step + tile_off, 0, 0, 0);
   };
-  u32x4 kst[LPT], vst[LPT];
-  if (T > 0) {  // tile 0, in flight while Q loads
-    gload(krsrc, 0, kst);
-    gload(vrsrc, 0, vst);
-  }
 
   // ---- Q fragments of both query blocks (rows past the chunk re-read the last valid row)
   bf16x8 qf[QB][DS];
@@ -408,18 +405,12 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + 4 * hh + (i & 3) >= valid) acc[x][i] = -INFINITY;
   };
-  // Staged-tile work of a period's first step: op j of 16, two per round.
+  // Tile loads of a period's first step, one per round: K tile t+1 and V
+  // tile t (their buffers were last read in period t-1).
   auto stage_op = [&](auto j_c, auto par_c, int t) __attribute__((always_inline)) {
     constexpr int j = decltype(j_c)::value;
-    if constexpr (j < 4) {
-      *reinterpret_cast<u32x4*>(kbuf(par_c, t, A1{}) + kls0 + j * LSTEP) = kst[j];
-    } else if constexpr (j < 8) {
-      kst[j - 4] = gload1(krsrc, t + 2, j - 4);
-    } else if constexpr (j < 12) {
-      *reinterpret_cast<u32x4*>(vbuf(par_c, t, A0{}) + vls0 + (j - 8) * LSTEP) = vst[j - 8];
-    } else {
-      vst[j - 12] = gload1(vrsrc, t + 1, j - 12);
-    }
+    if constexpr (j < 4) dma_k(kbuf(par_c, t, A1{}), t + 1, j);
+    else dma_v(vbuf(par_c, t, A0{}), t, j - 4);
   };
 
   // One step.  F: flags; BASE: ring slot of round 0; CHECK: test the softmax
@@ -467,8 +458,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
         pin_acc(o[0][nb]);
       }
       if constexpr ((F & kSTAGE) != 0) {
-        stage_op(std::integral_constant<int, 2 * r>{}, par_c, t);
-        stage_op(std::integral_constant<int, 2 * r + 1>{}, par_c, t);
+        stage_op(std::integral_constant<int, r>{}, par_c, t);
       }
       if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r + 1>{}, A0{}, acc_cur, pk_cur);
       __builtin_amdgcn_sched_barrier(0);
@@ -525,12 +515,10 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // V tile t from registers, buffer loads of K tile t+2 and V tile t+1
   // (tiles past the window read as zeros and are never used).
   auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
-    // prologue: K tile 0 into LDS, K tile 1 and V tile 0 in flight
+    // prologue: K tile 0 into LDS
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(kb0 + kls0 + i * LSTEP) = kst[i];
-    gload(krsrc, 1, kst);
-    constexpr int kWaitAllButKTile = wait_vm(LPT);
-    __builtin_amdgcn_s_waitcnt(kWaitAllButKTile);
+    for (int i = 0; i < 4; ++i) dma_k(kb0, 0, i);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
     __syncthreads();
