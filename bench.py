@@ -29,7 +29,8 @@ METRIC = "hybrid-attn query tokens/s + % MFMA bf16 peak, Wan-1.3B shape (H12 d12
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (vendor figure)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_wan13b_traffic.md")
-FWD_SOURCE = os.path.join(ROOT, "linear_attention_video_chunked_amd", "csrc", "rha_fwd_bf16.hip")
+# the dominant kernel at this shape (head_dim 128, bf16)
+FWD_SOURCE = os.path.join(ROOT, "linear_attention_video_chunked_amd", "csrc", "rha_fwd_bf16_qb2.hip")
 
 
 def fwd_flops(C, N, w, d, BH):
@@ -57,7 +58,20 @@ def scan_bytes(C, N, w, d, BH, elem=2):
 
 
 def stream_step_flops(C, w, d, BH):
-    return BH * C * (4 * d * w * C + 2 * d * d + 2 * d)
+    """Algorithmic FLOPs of one rha_stream_step with a full window: the new
+    chunk's queries against w cached chunks (4d per pair) and the state (2d^2
+    + 2d per query), plus the fold of the evicted chunk (2d^2 + 2d per key)."""
+    return BH * C * (4 * d * w * C + 2 * d * d + 2 * d) + BH * C * (2 * d * d + 2 * d)
+
+
+def stream_step_bytes(C, w, d, BH, elem=2):
+    """Algorithmic HBM bytes of one rha_stream_step with a full window: new
+    q, k, v read and out written; k, v copied into the cache (read + write);
+    the w cached chunks' k, v read; S, z read; the evicted chunk's k, v read
+    and S, z read and written back by the fold."""
+    chunk = C * d * elem
+    state = (d * d + d) * 4
+    return BH * (3 * chunk + chunk + 2 * chunk + 2 * w * chunk + state + 2 * chunk + 2 * state)
 
 
 def read_traffic():
@@ -108,8 +122,9 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # ~0.2 s of work before the timed region, so the GPU clocks have settled
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["fwd", "scan", "stream"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -172,33 +187,35 @@ def main():
         return
 
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
-    sw = CONFIGS["stream"]
-    sq, sk, sv = (t.to(dev) for t in gen_qkv(sw))
-    sout = torch.empty_like(sq)  # step outputs land in place, with the inputs' strides
-    st = rha.StreamState(sw.B, sw.H, sw.d, sw.C, sw.w, device=dev)
+    def stream_run(timed_run):
+        sw = CONFIGS["stream"]
+        sq, sk, sv = (t.to(dev) for t in gen_qkv(sw))
+        sout = torch.empty_like(sq)  # step outputs land in place, with the inputs' strides
+        st = rha.StreamState(sw.B, sw.H, sw.d, sw.C, sw.w, device=dev)
 
-    def push(t):
-        sl = slice(t * sw.C, (t + 1) * sw.C)
-        rha.stream_step(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], out=sout[:, :, sl], stream=stream)
+        def push(t):
+            sl = slice(t * sw.C, (t + 1) * sw.C)
+            rha.stream_step(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], out=sout[:, :, sl], stream=stream)
 
-    for t in range(sw.prefill):
-        push(t)
-    torch.cuda.synchronize()
-    if args.only == "stream":
-        for t in range(sw.prefill, sw.prefill + sw.steps):
+        for t in range(sw.prefill):
             push(t)
         torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        z1 = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for t in range(sw.prefill, sw.prefill + sw.steps):
+            push(t)
+        z1.record(stream)
+        torch.cuda.synchronize()
+        return sw, a.elapsed_time(z1) / 1e3 / sw.steps
+
+    if args.only == "stream":
+        stream_run(False)
         return
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for t in range(sw.prefill, sw.prefill + sw.steps):
-        push(t)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_stream = e0.elapsed_time(e1) / 1e3 / sw.steps
 
     # ---- the contract: W warmup steps, then exactly K timed steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -216,11 +233,13 @@ def main():
     t_fwd = timed(lambda: rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream), n_k)
     t_scan = timed(lambda: rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream), n_k)
 
+    sw, t_stream = stream_run(True)
     F = fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     achieved = F / t_fwd / 1e12
     traffic = read_traffic()
     tokens = wl.B * wl.L
     sF = stream_step_flops(sw.C, sw.w, sw.d, sw.B * sw.H)
+    sB = stream_step_bytes(sw.C, sw.w, sw.d, sw.B * sw.H)
     result = {
         "metric": METRIC,
         "value": tokens / t_step,
@@ -239,7 +258,7 @@ def main():
                    "global_batch": wl.B, "seq_len": wl.L, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "fwd_bf16_kernel (rha_hybrid_fwd)", "flops_per_launch": F,
+                     "kernel": "fwd_bf16_qb2_kernel (rha_hybrid_fwd)", "flops_per_launch": F,
                      "algorithmic_bytes_per_launch": fwd_bytes(wl.C, wl.N, wl.w, wl.d, BH),
                      "avg_launch_us": t_fwd * 1e6},
         "detail": {
@@ -252,6 +271,8 @@ def main():
             "stream_chunks_per_s": 1.0 / t_stream,
             "stream_step_TFLOPs": sF / t_stream / 1e12,
             "stream_step_mfma_frac": sF / t_stream / 1e12 / PEAK_BF16_TFLOPS,
+            "stream_step_GBps": sB / t_stream / 1e9,
+            "stream_step_hbm_frac": sB / t_stream / 1e9 / PEAK_HBM_GBS,
             "timed_wall_s": wall,
         },
     }

@@ -397,13 +397,16 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     }
     lsum[x] = mold == -INFINITY ? ps : fmaf(sm_lold[x], __builtin_amdgcn_exp2f(mold - mnew), ps);
   };
-  // keys at or past `valid` get score -inf
+  // keys at or past `valid` get score -inf (acc reg i holds key
+  // 8(i/4) + 4hh + i%4; compared as constant >= valid - 4hh, so no per-key
+  // lane values are kept live)
   auto sm_mask = [&](f32x16 (&acc)[QB], int valid) __attribute__((always_inline)) {
+    const int vrel = valid - 4 * hh;
 #pragma unroll
     for (int x = 0; x < QB; ++x)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (8 * (i >> 2) + 4 * hh + (i & 3) >= valid) acc[x][i] = -INFINITY;
+        if (8 * (i >> 2) + (i & 3) >= vrel) acc[x][i] = -INFINITY;
   };
   // Tile loads of a period's first step, one per round: K tile t+1 and V
   // tile t (their buffers were last read in period t-1).
