@@ -11,29 +11,39 @@ namespace {
 // holds their running sum over slots w..c, i.e. the state of every chunk up to
 // c - w.  Slots c < w see no folded history and are zeroed.  Sequential float32
 // sum in chunk order, the same order the streaming fold uses.
+// Each thread owns 4 consecutive floats of one head's S (or z) and walks the
+// slots in groups of 8: all loads of a group are issued before the running
+// sum touches them, so the HBM latency is paid once per group, not per slot.
 __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
-  const int64_t per = (int64_t)p.d * p.d + p.d;
+  const int64_t per4 = ((int64_t)p.d * p.d + p.d) / 4;  // float4 units per head (d is a multiple of 4)
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)p.BH * per) return;
-  const int64_t bh = idx / per, e = idx % per;
-  float* base;
-  int64_t stride;
-  if (e < (int64_t)p.d * p.d) {
-    stride = (int64_t)p.d * p.d;
-    base = p.S + bh * p.N * stride + e;
+  if (idx >= (int64_t)p.BH * per4) return;
+  const int64_t bh = idx / per4, e4 = idx % per4;
+  const int64_t dd4 = (int64_t)p.d * p.d / 4;
+  f32x4* base;
+  int64_t stride;  // in float4 units
+  if (e4 < dd4) {
+    stride = dd4;
+    base = reinterpret_cast<f32x4*>(p.S) + bh * p.N * stride + e4;
   } else {
-    stride = p.d;
-    base = p.z + bh * p.N * stride + (e - (int64_t)p.d * p.d);
+    stride = p.d / 4;
+    base = reinterpret_cast<f32x4*>(p.z) + bh * p.N * stride + (e4 - dd4);
   }
-  float acc = 0.f;
-  for (int c = 0; c < p.N; ++c) {
-    float* ptr = base + c * stride;
-    if (c < p.w) {
-      *ptr = 0.f;
-    } else {
-      acc = (c == p.w) ? *ptr : acc + *ptr;
-      *ptr = acc;
-    }
+  const int w = min(p.w, p.N);
+  for (int c = 0; c < w; ++c) base[c * stride] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int G = 8;
+  for (int c0 = w; c0 < p.N; c0 += G) {
+    f32x4 v[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (c0 + g < p.N) v[g] = base[(c0 + g) * stride];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (c0 + g < p.N) {
+        acc = (c0 + g == w) ? v[g] : acc + v[g];
+        base[(c0 + g) * stride] = acc;
+      }
   }
 }
 
@@ -60,7 +70,7 @@ __global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p) {
 }  // namespace
 
 hipError_t launch_prefix(const PrefixParams& p, hipStream_t s) {
-  const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d);
+  const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d) / 4;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(prefix_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();

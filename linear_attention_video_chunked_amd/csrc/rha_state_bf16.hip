@@ -34,10 +34,11 @@ struct StateCfg {
   static constexpr int ES = D / ESLICE;                   // slices per chunk
   static constexpr int KBYTES = BT * ESLICE * 2;          // one phi(K) slice tile
   static constexpr int VBYTES = BT * D * 2;               // one V tile
-  static constexpr int KUNITS = (BT / 4) * (ESLICE / 8);  // 4-token x 8-feature load units
+  static constexpr int KG = BT * (ESLICE / 8) / THREADS;  // phi(K) granules per thread (every thread)
+  static constexpr int KROWSTEP = THREADS / (ESLICE / 8);  // token rows between a thread's granules
   static constexpr int VUNITS = (BT / 4) * (D / 8);
   static constexpr int NBW = (ESLICE / 32) * (D / 32) / NW;  // output 32x32 blocks per wave
-  static_assert(KUNITS <= THREADS && VUNITS <= THREADS, "one unit per thread at most");
+  static_assert(KG * THREADS == BT * (ESLICE / 8) && VUNITS <= THREADS, "even phi(K) split, one V unit per thread at most");
   static_assert(NBW >= 1 && (ESLICE / 32) * (D / 32) % NW == 0, "whole blocks per wave");
 };
 
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   using Cfg = StateCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char kt_s[2][Cfg::KBYTES];  // phi(K) slice, 2 buffers
   __shared__ __attribute__((aligned(1024))) unsigned char vt_s[2][Cfg::VBYTES];  // V, 2 buffers
-  __shared__ float zred[BT / 4][ESLICE];
+  __shared__ float zred[THREADS / (ESLICE / 8)][ESLICE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st + es * ESLICE;
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
 
-  const bool kact = tid < Cfg::KUNITS, vact = tid < Cfg::VUNITS;
-  const int kfo = tid % (ESLICE / 8), ktq = tid / (ESLICE / 8);
+  const bool vact = tid < Cfg::VUNITS;
+  const int kfo = tid % (ESLICE / 8), krow0 = tid / (ESLICE / 8);  // phi(K): every thread, KG rows
   const int vfo = tid % (D / 8), vtq = tid / (D / 8);
 
   const int eb = wave / (NW * Cfg::NBW / (D / 32));
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
   const int ntiles = (p.C + BT - 1) / BT;
-  u32x4 kw[2][4], vw[2][4];  // two tiles in flight: 4 token rows x 16 bytes each
+  u32x4 kw[2][Cfg::KG], vw[2][4];  // two tiles in flight
 
   // Buffer loads whose descriptors end at the chunk's last token: rows past
   // it (and the lanes without a unit) read zeros, so loads and stores need no
@@ -115,37 +116,38 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   const int chunk_bytes = p.C * (int)p.kv_st * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, chunk_bytes, fwd::kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, chunk_bytes, fwd::kBufWord3);
-  const int kofs0 = kact ? (ktq * 4 * (int)p.kv_st + kfo * 8) * 2 : chunk_bytes;
+  const int kofs0 = (krow0 * (int)p.kv_st + kfo * 8) * 2;
   const int vofs0 = vact ? (vtq * 4 * (int)p.kv_st + vfo * 8) * 2 : chunk_bytes;
   const int row_bytes = (int)p.kv_st * 2;
   auto gload = [&](int j, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
     const int tile_off = j * BT * row_bytes;
 #pragma unroll
+    for (int r = 0; r < Cfg::KG; ++r)
+      kw[sl][r] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kofs0 + tile_off + r * Cfg::KROWSTEP * row_bytes, 0, 0));
+#pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int ko = kact ? kofs0 + tile_off + r * row_bytes : chunk_bytes;
       const int vo = vact ? vofs0 + tile_off + r * row_bytes : chunk_bytes;
-      kw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ko, 0, 0));
       vw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
     }
   };
   auto lstore = [&](int j, int buf, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
-    if (kact) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = j * BT + ktq * 4 + r < p.C;  // rows past the chunk: phi(0) would be 1
-        u32x4 fw;
+    for (int r = 0; r < Cfg::KG; ++r) {
+      const int row = krow0 + r * Cfg::KROWSTEP;
+      const bool ok = j * BT + row < p.C;  // rows past the chunk: phi(0) would be 1
+      u32x4 fw;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = ok ? phi(bf16_lo(kw[sl][r][i])) : 0.f;
-          const float c = ok ? phi(bf16_hi(kw[sl][r][i])) : 0.f;
-          zacc[2 * i] += a;
-          zacc[2 * i + 1] += c;
-          fw[i] = pack_bf16(a, c);
-        }
-        store_granule<ESLICE>(kt_s[buf], ktq * 4 + r, kfo, fw);
+      for (int i = 0; i < 4; ++i) {
+        const float a = ok ? phi(bf16_lo(kw[sl][r][i])) : 0.f;
+        const float c = ok ? phi(bf16_hi(kw[sl][r][i])) : 0.f;
+        zacc[2 * i] += a;
+        zacc[2 * i + 1] += c;
+        fw[i] = pack_bf16(a, c);
       }
+      store_granule<ESLICE>(kt_s[buf], row, kfo, fw);
     }
     if (vact) {
 #pragma unroll
@@ -200,15 +202,13 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   }
 
   // u: fixed-order reduction of the per-thread partial sums
-  if (kact) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zred[ktq][kfo * 8 + i] = zacc[i];
-  }
+  for (int i = 0; i < 8; ++i) zred[krow0][kfo * 8 + i] = zacc[i];
   __syncthreads();
   if (tid < ESLICE) {
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < BT / 4; ++r) s += zred[r][tid];
+    for (int r = 0; r < THREADS / (ESLICE / 8); ++r) s += zred[r][tid];
     float* zd = p.z + (int64_t)bh * p.z_bh + (int64_t)(jc + p.slot_offset) * D + es * ESLICE + tid;
     *zd = p.accumulate ? *zd + s : s;
   }
