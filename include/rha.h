@@ -146,8 +146,9 @@ typedef struct {
  *      then cursor->t is incremented.
  * With commit == 0 nothing but the cache slot of chunk t changes, so the same
  * chunk can be re-run (e.g. once per denoising step) before committing it.
- * Outputs equal those of rha_hybrid_fwd over the concatenated sequence, and
- * S, z after each commit equal rha_state_scan's entry for chunk t+1 bitwise.
+ * Outputs equal those of rha_hybrid_fwd over the concatenated sequence up to
+ * float rounding (the key window is visited in another order), and S, z
+ * after each commit equal rha_state_scan's entry for chunk t+1 bitwise.
  *
  *   p->n_chunks is ignored; p's strides describe q_new, k_new, v_new, out
  *   q_new, k_new, v_new : [B, H, C, d] (read)
@@ -155,13 +156,31 @@ typedef struct {
  *   S : [B, H, d, d] float32, z : [B, H, d] float32 (read; written on commit)
  *   out : [B, H, C, d] (written);  lse : NULL or [B, H, C] float32
  *   cursor : host memory, read and (on commit) updated at enqueue time
+ *   workspace, workspace_bytes : NULL/0 or device scratch, see below
  *
  * Errors: RHA_ERR_CURSOR if cursor is NULL or cursor->t < 0.
  */
 rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new,
                            const void* v_new, void* k_cache, void* v_cache, float* S, float* z,
                            rha_stream_cursor* cursor, int32_t commit, void* out, float* lse,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rha_stream_workspace_size -- bytes of device workspace with which
+ * rha_stream_step spreads one step over more of the GPU.
+ *
+ * One chunk has few query tiles, so the step splits the key window across
+ * several workgroups per tile and merges their partial results (numerators,
+ * denominators and reference maxima, in float32) in a second small kernel.
+ * The size depends on p (batch, heads, chunk_len, head_dim, window) and on
+ * the number of compute units of the current device; it is 0 when p would not
+ * be split (problems other than bf16 with head_dim 128, or enough tiles).
+ * Pass workspace = NULL, or workspace_bytes below this size, to run without
+ * the split; results agree to rounding either way.  The workspace must be
+ * 16-byte aligned device memory owned by the caller, not used by anything else
+ * while the step runs; its contents need no initialisation.
+ */
+size_t rha_stream_workspace_size(const rha_problem* p);
 
 /* Static name of a status code. */
 const char* rha_status_string(rha_status s);

@@ -65,7 +65,9 @@ def lib():
     L.rha_state_scan.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
-                                  ctypes.c_int32, _vp, _vp, _vp]
+                                  ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.rha_stream_workspace_size.argtypes = [P]
+    L.rha_stream_workspace_size.restype = ctypes.c_size_t
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_stream_step"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
@@ -166,15 +168,26 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
 
 
 class StreamState:
-    """Caller-owned streaming state: KV cache ring of w chunks, S, z, cursor."""
+    """Caller-owned streaming state: KV cache ring of w chunks, S, z, cursor,
+    and the step's scratch workspace (rha_stream_workspace_size bytes; none if
+    split=False or the library would not split this problem)."""
 
-    def __init__(self, B: int, H: int, d: int, C: int, w: int, dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, B: int, H: int, d: int, C: int, w: int, dtype=torch.bfloat16, device="cuda",
+                 split: bool = True):
         self.B, self.H, self.d, self.C, self.w = B, H, d, C, w
         self.k_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
         self.v_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
         self.S = torch.zeros((B, H, d, d), dtype=torch.float32, device=device)
         self.z = torch.zeros((B, H, d), dtype=torch.float32, device=device)
         self.cursor = Cursor(0)
+        self.workspace = None
+        if split:
+            prob = Problem(batch=B, heads=H, head_dim=d, chunk_len=C, n_chunks=1, window=w,
+                           dtype=RHA_BF16 if dtype == torch.bfloat16 else RHA_F32, reserved=0,
+                           stride_b=H * C * d, stride_h=C * d, stride_t=d)
+            nbytes = int(lib().rha_stream_workspace_size(ctypes.byref(prob)))
+            if nbytes > 0:
+                self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     @property
     def t(self) -> int:
@@ -186,6 +199,7 @@ class StreamState:
         n.k_cache, n.v_cache = self.k_cache.clone(), self.v_cache.clone()
         n.S, n.z = self.S.clone(), self.z.clone()
         n.cursor = Cursor(self.cursor.t)
+        n.workspace = None if self.workspace is None else torch.empty_like(self.workspace)
         return n
 
 
@@ -207,5 +221,7 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
     prob = _problem(q_new, C, st.w, 1)
     _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
                                  _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
-                                 ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _stream(stream)))
+                                 ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _ptr(st.workspace),
+                                 ctypes.c_size_t(0 if st.workspace is None else st.workspace.numel()),
+                                 _stream(stream)))
     return out

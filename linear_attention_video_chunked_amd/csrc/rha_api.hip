@@ -116,6 +116,22 @@ hipError_t launch_fwd(const rha_problem* p, rha::FwdParams& f, hipStream_t s) {
   return p->dtype == RHA_BF16 ? rha::launch_fwd_bf16(f, p->head_dim, s) : rha::launch_fwd_f32(f, p->head_dim, s);
 }
 
+// Split of a stream step's key window: enough workgroups per query tile to
+// give every compute unit one, at most 8, and at least 4 key tiles each.
+int stream_splits(const rha_problem* p, int64_t n_keys) {
+  if (p->dtype != RHA_BF16 || p->head_dim != 128) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 1;
+  const int64_t tiles = (int64_t)p->batch * p->heads * ((p->chunk_len + rha::kQb2RowsPerTile - 1) / rha::kQb2RowsPerTile);
+  int64_t splits = cus / (tiles > 0 ? tiles : 1);
+  const int64_t key_tiles = (n_keys + 63) / 64;
+  if (splits > key_tiles / 4) splits = key_tiles / 4;
+  if (splits > 8) splits = 8;
+  return splits < 2 ? 1 : (int)splits;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,9 +197,17 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
   return ok();
 }
 
+size_t rha_stream_workspace_size(const rha_problem* p) {
+  if (p == nullptr || check_problem(p, true) != RHA_OK || empty(p, true)) return 0;
+  const int splits = stream_splits(p, (int64_t)p->window * p->chunk_len);
+  if (splits < 2) return 0;
+  return rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits);
+}
+
 rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
                            void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
-                           int32_t commit, void* out, float* lse, void* stream) {
+                           int32_t commit, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   RHA_TRY(check_problem(p, true));
   if (cursor == nullptr) return fail(RHA_ERR_CURSOR, "cursor is NULL");
   if (cursor->t < 0) return fail(RHA_ERR_CURSOR, "cursor->t = %lld < 0", (long long)cursor->t);
@@ -200,6 +224,7 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   RHA_TRY(need(z, "z"));
   RHA_TRY(need(out, "out"));
   if (lse != nullptr) RHA_TRY(need(lse, "lse", true, 4));
+  if (workspace != nullptr) RHA_TRY(need(workspace, "workspace"));
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t t = cursor->t;
@@ -252,8 +277,20 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.n_keys = (int)(in_window * C);
   f.has_state = t >= w ? 1 : 0;
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-  e = launch_fwd(p, f, s);
-  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  const int splits = workspace != nullptr ? stream_splits(p, f.n_keys) : 1;
+  if (splits > 1 && workspace_bytes >= rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) {
+    // the key window split over several workgroups per query tile, then merged
+    f.n_splits = splits;
+    f.part = static_cast<float*>(workspace);
+    e = launch_fwd(p, f, s);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    e = rha::launch_fwd_combine(f, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  } else {
+    f.n_splits = 1;
+    e = launch_fwd(p, f, s);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
 
   // 3. commit: fold the chunk that leaves the window, advance the cursor
   if (commit) {

@@ -68,10 +68,10 @@ __device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
+constexpr int Q2_QB = 2;  // 32-row query blocks per wave
+// waves per workgroup: 4 (256 query rows); 2 (128 rows, less padding of
+// 1560-row chunks) measured 5% slower on the Wan 1.3B shape
 constexpr int Q2_NW = 4;
-constexpr int Q2_THREADS = Q2_NW * 64;
-constexpr int Q2_QB = 2;                   // 32-row query blocks per wave
-constexpr int Q2_BM = Q2_NW * 32 * Q2_QB;  // query rows per workgroup
 // Probabilities up to 2^kQ2Slack are accepted against a stale reference
 // (far inside the bf16 and f32 ranges).
 constexpr float kQ2Slack = 64.0f;
@@ -90,17 +90,17 @@ __shared__ __attribute__((aligned(1024))) unsigned char q2_vb1[Q2_TILE];
 // linear state) or -inf and blocks are checked against the bound; returns
 // nonzero where a reference moved after accumulation.  Otherwise references
 // start at mio and no block is checked.  mio receives the final references.
-template <int D, bool FIRST>
+template <int D, int NW, bool FIRST, bool PARTIAL>
 __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]) {
   static_assert(D == Q2_D, "tile buffers are sized for head dimension 128");
-  constexpr int NW = Q2_NW, THREADS = Q2_THREADS, QB = Q2_QB, BM = Q2_BM;
+  constexpr int THREADS = NW * 64, QB = Q2_QB, BM = NW * 32 * Q2_QB;
   constexpr int DS = D / 16, DB = D / 32, GR = D / 8;
   constexpr int TILE = BN * D * 2;
   constexpr int LPT = BN * GR / THREADS;
   static_assert(LPT * THREADS == BN * GR, "tile must split evenly over the threads");
   static_assert(TILE >= D * D, "half of the state staging must fit one V buffer");
   static_assert(TILE >= 32 * QB * D * 2, "one wave's output rows must fit one tile buffer");
-  static_assert(NW == 4, "the epilogue stages one wave per tile buffer");
+  static_assert(NW == 2 || NW == 4, "the epilogue stages one wave per tile buffer; loads split evenly");
 
   static_assert(TILE == Q2_TILE, "tile buffer size");
   unsigned char* const kb0 = q2_kb0;
@@ -113,7 +113,9 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- which tile
-  const int logical = xcd_remap(blockIdx.x, p.total_tiles);
+  const int logical0 = xcd_remap(blockIdx.x, p.total_tiles);
+  const int split = PARTIAL ? logical0 % p.n_splits : 0;  // splits of a tile adjacent (one XCD)
+  const int logical = PARTIAL ? logical0 / p.n_splits : logical0;
   const int tile = logical % p.tiles_per_chunk;
   const int rest = logical / p.tiles_per_chunk;
   const int c = p.n_qchunks - 1 - rest % p.n_qchunks;  // later chunks (longer windows) first
@@ -145,6 +147,14 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     kbeg = 0;
     kend = p.n_keys;
     has_state = p.has_state != 0;
+    if (PARTIAL) {  // this split's share of the key tiles; the first split takes the state
+      const int tiles_all = (p.n_keys + BN - 1) / BN;
+      const int t_lo = (int)((int64_t)split * tiles_all / p.n_splits);
+      const int t_hi = (int)((int64_t)(split + 1) * tiles_all / p.n_splits);
+      kbeg = (int64_t)t_lo * BN;
+      kend = min((int64_t)t_hi * BN, (int64_t)p.n_keys);
+      has_state = has_state && split == 0;
+    }
     Sp = p.S + (int64_t)bh * D * D;
     zp = p.z + (int64_t)bh * D;
   }
@@ -152,19 +162,20 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 
   // ---- tile loads: direct HBM -> LDS (buffer loads with the LDS flag).  One
   // such load moves 64 lanes x 16 bytes into 1 KiB of consecutive LDS (lane L
-  // at byte 16L): 4 rows of a tile.  Wave w issues loads i = 0..3 of a tile,
-  // rows 4(4w+i) .. +3; lane L fills row 4(4w+i) + L/16, slot L%16, with the
-  // global granule that the swizzle puts there (g = slot ^ sw(row)).  The
-  // descriptor ends at the window end, so rows past it read as zero.
-  static_assert(NW * 4 * 4 == BN && GR == 16, "four 4-row loads per wave cover a 64-row tile");
+  // at byte 16L): 4 rows of a tile.  Wave w issues loads i = 0..LPW-1 of a
+  // tile, rows 4(LPW*w+i) .. +3; lane L fills row 4(LPW*w+i) + L/16, slot L%16,
+  // with the global granule that the swizzle puts there (g = slot ^ sw(row)).
+  // The descriptor ends at the window end, so rows past it read as zero.
+  constexpr int LPW = BN / 4 / NW;  // 4-row loads per wave and tile
+  static_assert(LPW * 4 * NW == BN && LPW % 4 == 0 && GR == 16, "whole 4-row loads per wave");
   const int lrow = lane >> 4, lslot = lane & 15;
-  int kdma[4];
+  int kdma[4];  // the K swizzle repeats every 16 rows: load i uses kdma[i % 4] + (i / 4) 16-row steps
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (4 * wave + i) + lrow;
+    const int row = 4 * (LPW * wave + i) + lrow;
     kdma[i] = (row * (int)p.kv_st + (lslot ^ ksw<D>(row)) * 8) * 2;
   }
-  const int vdma0 = ((16 * wave + lrow) * (int)p.kv_st + (lslot ^ vsw<D>(lrow)) * 8) * 2;  // vsw(row) = vsw(lrow)
+  const int vdma0 = ((4 * LPW * wave + lrow) * (int)p.kv_st + (lslot ^ vsw<D>(lrow)) * 8) * 2;  // vsw(row) = vsw(lrow)
   const int vdma_step = 4 * (int)p.kv_st * 2;
   const int win_bytes = (int)(kend * p.kv_st * 2);
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
@@ -172,11 +183,13 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   typedef __attribute__((address_space(3))) void lds_void;
   auto dma_k = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
     const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(dst + (4 * wave + i) * 1024), 16, kdma[i] + tile_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
+                                             kdma[i % 4] + (i / 4) * 4 * vdma_step + tile_off, 0, 0, 0);
   };
   auto dma_v = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
     const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(dst + (4 * wave + i) * 1024), 16, vdma0 + i * vdma_step + tile_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
+                                             vdma0 + i * vdma_step + tile_off, 0, 0, 0);
   };
 
   // ---- Q fragments of both query blocks (rows past the chunk re-read the last valid row)
@@ -412,8 +425,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // tile t (their buffers were last read in period t-1).
   auto stage_op = [&](auto j_c, auto par_c, int t) __attribute__((always_inline)) {
     constexpr int j = decltype(j_c)::value;
-    if constexpr (j < 4) dma_k(kbuf(par_c, t, A1{}), t + 1, j);
-    else dma_v(vbuf(par_c, t, A0{}), t, j - 4);
+    if constexpr (j < LPW) dma_k(kbuf(par_c, t, A1{}), t + 1, j);
+    else dma_v(vbuf(par_c, t, A0{}), t, j - LPW);
   };
 
   // One step.  F: flags; BASE: ring slot of round 0; CHECK: test the softmax
@@ -461,7 +474,9 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
         pin_acc(o[0][nb]);
       }
       if constexpr ((F & kSTAGE) != 0) {
-        stage_op(std::integral_constant<int, r>{}, par_c, t);
+        static_for<0, LPW / 4>([&](auto o_c) __attribute__((always_inline)) {
+          stage_op(std::integral_constant<int, r * (LPW / 4) + decltype(o_c)::value>{}, par_c, t);
+        });
       }
       if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r + 1>{}, A0{}, acc_cur, pk_cur);
       __builtin_amdgcn_sched_barrier(0);
@@ -520,7 +535,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
     // prologue: K tile 0 into LDS
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_k(kb0, 0, i);
+    for (int i = 0; i < LPW; ++i) dma_k(kb0, 0, i);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
@@ -549,39 +564,65 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   init_acc();
   if (T > 0) pipeline(std::integral_constant<bool, FIRST>{});
 
-  // ---- epilogue: normalise, stage bf16 rows in LDS (per wave), write coalesced
-  __syncthreads();
-  unsigned char* stage = wave == 0 ? kb0 : wave == 1 ? kb1 : wave == 2 ? vb0 : vb1;
+  if constexpr (PARTIAL) {
+    // ---- partial results: unnormalised numerator rows, denominator, reference
+    const int64_t pidx = ((int64_t)bh * p.tiles_per_chunk + tile) * p.n_splits + split;
+    const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
+    float* po = p.part + pidx * BM * D;
+    float* plm = p.part + n_part * BM * D + pidx * BM * 2;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = half_sum(lsum[qb]);
-    const float inv = 1.0f / ltot;
-    const int r = qb * 32 + l32;  // row within the wave's 64
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ltot = half_sum(lsum[qb]);
+      const int row = wave * 32 * QB + qb * 32 + l32;
+      if (row < nrows) {
 #pragma unroll
-    for (int nb = 0; nb < DB; ++nb)
+        for (int nb = 0; nb < DB; ++nb)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int col = nb * 32 + 8 * rr + 4 * hh;
-        const int g = col >> 3;
-        u32x2 pr = {pack_bf16(o[qb][nb][4 * rr] * inv, o[qb][nb][4 * rr + 1] * inv),
-                    pack_bf16(o[qb][nb][4 * rr + 2] * inv, o[qb][nb][4 * rr + 3] * inv)};
-        *reinterpret_cast<u32x2*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16) + (col & 7) * 2) = pr;
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 v4 = {o[qb][nb][4 * rr], o[qb][nb][4 * rr + 1], o[qb][nb][4 * rr + 2], o[qb][nb][4 * rr + 3]};
+            *reinterpret_cast<f32x4*>(po + (int64_t)row * D + nb * 32 + 8 * rr + 4 * hh) = v4;
+          }
+        if (hh == 0) {
+          plm[row * 2] = ltot;
+          plm[row * 2 + 1] = mrun[qb];
+        }
       }
-    const int myrow = wave * 32 * QB + r;
-    if (p.lse != nullptr && hh == 0 && myrow < nrows) {
-      const int64_t L = (int64_t)p.n_qchunks * p.C;
-      p.lse[(int64_t)bh * L + qtok0 + myrow] = (mrun[qb] + __log2f(ltot)) * kLn2;
     }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging writes are complete
-  __builtin_amdgcn_wave_barrier();
-  bf16_t* obase = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
-  for (int idx = lane; idx < 32 * QB * GR; idx += 64) {
-    const int r = idx / GR, g = idx % GR;
-    const int row = wave * 32 * QB + r;
-    if (row < nrows)
-      st16(obase + (int64_t)row * p.q_st + g * 8,
-           *reinterpret_cast<const u32x4*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16)));
+  } else {
+    // ---- epilogue: normalise, stage bf16 rows in LDS (per wave), write coalesced
+    __syncthreads();
+    unsigned char* stage = wave == 0 ? kb0 : wave == 1 ? kb1 : wave == 2 ? vb0 : vb1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ltot = half_sum(lsum[qb]);
+      const float inv = 1.0f / ltot;
+      const int r = qb * 32 + l32;  // row within the wave's 64
+#pragma unroll
+      for (int nb = 0; nb < DB; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int col = nb * 32 + 8 * rr + 4 * hh;
+          const int g = col >> 3;
+          u32x2 pr = {pack_bf16(o[qb][nb][4 * rr] * inv, o[qb][nb][4 * rr + 1] * inv),
+                      pack_bf16(o[qb][nb][4 * rr + 2] * inv, o[qb][nb][4 * rr + 3] * inv)};
+          *reinterpret_cast<u32x2*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16) + (col & 7) * 2) = pr;
+        }
+      const int myrow = wave * 32 * QB + r;
+      if (p.lse != nullptr && hh == 0 && myrow < nrows) {
+        const int64_t L = (int64_t)p.n_qchunks * p.C;
+        p.lse[(int64_t)bh * L + qtok0 + myrow] = (mrun[qb] + __log2f(ltot)) * kLn2;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging writes are complete
+    __builtin_amdgcn_wave_barrier();
+    bf16_t* obase = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
+    for (int idx = lane; idx < 32 * QB * GR; idx += 64) {
+      const int r = idx / GR, g = idx % GR;
+      const int row = wave * 32 * QB + r;
+      if (row < nrows)
+        st16(obase + (int64_t)row * p.q_st + g * 8,
+             *reinterpret_cast<const u32x4*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16)));
+    }
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mio[qb] = mrun[qb];
@@ -590,30 +631,88 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 
 // The rare second pass, kept out of line so that its registers do not add to
 // the first pass's.
-template <int D>
+template <int D, int NW, bool PARTIAL>
 __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float m1) {
   float m[Q2_QB] = {m0, m1};
-  tile_pass<D, false>(p, m);
+  tile_pass<D, NW, false, PARTIAL>(p, m);
 }
 
-template <int D>
-__global__ __launch_bounds__(Q2_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int NW, bool PARTIAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
   float m[Q2_QB];
-  const int dirty = tile_pass<D, true>(p, m);
+  const int dirty = tile_pass<D, NW, true, PARTIAL>(p, m);
   // Every wave reaches this barrier.  Where some query's reference moved after
   // accumulation, the whole tile is computed again with the final references
   // (which no score exceeds by the bound); its output replaces the first.
-  if (__syncthreads_or(dirty)) tile_second_pass<D>(p, m[0], m[1]);
+  if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL>(p, m[0], m[1]);
+}
+
+// Merge of a split pass: per query row, the partial numerators and
+// denominators are brought to the largest reference and summed in split
+// order; one thread per 4 output columns.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p) {
+  constexpr int BM = Q2_NW * 32 * Q2_QB;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.H * p.C * (D / 4);
+  if (idx >= total) return;
+  const int col = (int)(idx % (D / 4)) * 4;
+  const int64_t r = idx / (D / 4);
+  const int row = (int)(r % p.C);
+  const int bh = (int)(r / p.C);
+  const int b = bh / p.H, h = bh % p.H;
+  const int tile = row / BM, trow = row % BM;
+  const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
+  const int64_t pidx0 = ((int64_t)bh * p.tiles_per_chunk + tile) * p.n_splits;
+  const float* plm = p.part + n_part * BM * D;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < p.n_splits; ++sp) mmax = fmaxf(mmax, plm[((pidx0 + sp) * BM + trow) * 2 + 1]);
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int sp = 0; sp < p.n_splits; ++sp) {
+    const float* lm = plm + ((pidx0 + sp) * BM + trow) * 2;
+    const float sc = lm[1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lm[1] - mmax);
+    den = fmaf(lm[0], sc, den);
+    num += sc * *reinterpret_cast<const f32x4*>(p.part + ((pidx0 + sp) * BM + trow) * D + col);
+  }
+  const float inv = 1.0f / den;
+  bf16_t* dst = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + (int64_t)row * p.q_st + col;
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv)};
+  if (p.lse != nullptr && col == 0) p.lse[(int64_t)bh * p.C + row] = (mmax + __log2f(den)) * kLn2;
+}
+
+template <int NW>
+hipError_t launch_nw(FwdParams& p, hipStream_t s) {
+  constexpr int BM = NW * 32 * Q2_QB;
+  static_assert(BM == kQb2RowsPerTile, "partial-result tile size");
+  p.tiles_per_chunk = (p.C + BM - 1) / BM;
+  const int splits = p.n_splits > 1 ? p.n_splits : 1;
+  p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk * splits;
+  if (p.total_tiles == 0) return hipSuccess;
+  if (splits > 1)
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s) {
-  p.tiles_per_chunk = (p.C + Q2_BM - 1) / Q2_BM;
-  p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk;
-  if (p.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128>), dim3(p.total_tiles), dim3(Q2_THREADS), 0, s, p);
+  return launch_nw<Q2_NW>(p, s);
+}
+
+size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits) {
+  const int64_t tiles = (C + kQb2RowsPerTile - 1) / kQb2RowsPerTile;
+  const int64_t n_part = (int64_t)B * H * tiles * n_splits;
+  return (size_t)(n_part * kQb2RowsPerTile * (d + 2) * sizeof(float));
+}
+
+hipError_t launch_fwd_combine(const FwdParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.H * p.C * (128 / 4);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

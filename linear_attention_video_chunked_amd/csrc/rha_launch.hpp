@@ -32,6 +32,16 @@ struct FwdParams {
   int n_keys;         // stream mode
   int has_state;      // stream mode
   float scale_log2;   // log2(e) / sqrt(d)
+  // Split of the key range (stream mode, head_dim 128 bf16 only): with
+  // n_splits > 1 every query tile is processed by n_splits workgroups, each
+  // over its share of the key tiles (the first one also takes the state), and
+  // the unnormalised partial results go to `part` instead of out:
+  //   part[(pidx * BM + row) * d + col]            numerator (float32)
+  //   part[n_part * BM * d + (pidx * BM + row) * 2] {denominator, reference}
+  // with pidx = (bh * tiles_per_chunk + tile) * n_splits + split and n_part the
+  // number of pidx values.  launch_fwd_combine merges them into out and lse.
+  int n_splits;
+  float* part;
 };
 
 // Per-chunk state contribution phi(K_c)^T V_c, sum_t phi(k_t) for a list of
@@ -77,6 +87,12 @@ struct CopyParams {
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
 // head_dim 128 with 64 query rows per wave (the default for d = 128)
 hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s);
+// Query rows per workgroup of the d = 128 bf16 kernel (the partial-result tile).
+constexpr int kQb2RowsPerTile = 256;
+// Bytes of partial results for a split stream pass (see FwdParams::part).
+size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits);
+// Merge the partial results of a split pass into out (and lse).
+hipError_t launch_fwd_combine(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(FwdParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_f32(const ChunkStateParams& p, int d, hipStream_t s);

@@ -125,7 +125,7 @@ def _step(L, prob, cursor, commit=1, **ptrs):
     a = dict(q=P, k=P, v=P, kc=P, vc=P, S=P, z=P, out=P)
     a.update(ptrs)
     return L.rha_stream_step(ctypes.byref(prob), a["q"], a["k"], a["v"], a["kc"], a["vc"], a["S"], a["z"],
-                             cursor, commit, a["out"], None, None)
+                             cursor, commit, a["out"], None, a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 def test_stream_validation(L):
@@ -141,6 +141,19 @@ def test_stream_validation(L):
     assert cur.t == 5  # nothing happened
     assert _step(L, prob, ctypes.byref(cur), out=BAD) == 1
     assert cur.t == 5
+
+
+def test_stream_workspace_checks(L):
+    prob = _prob(window=3)
+    cur = _rha.Cursor(5)
+    assert _step(L, prob, ctypes.byref(cur), ws=BAD, ws_bytes=1 << 20) == 1
+    assert "workspace" in L.rha_last_error().decode()
+    assert cur.t == 5
+    # no split for float32 or head_dim 64 problems, nor for invalid ones
+    assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=3, dtype=_rha.RHA_F32, stride_t=128))) == 0
+    assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=3, head_dim=64, stride_t=64))) == 0
+    assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=0))) == 0
+    assert L.rha_stream_workspace_size(None) == 0
 
 
 def test_stream_empty_problem_advances_cursor(L):

@@ -26,9 +26,9 @@ def chunk(x, t, C):
     return x[:, :, t * C:(t + 1) * C].to(DEV)
 
 
-def run_stream(wl, q, k, v, T, lse=False):
+def run_stream(wl, q, k, v, T, lse=False, split=True):
     st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w,
-                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device=DEV)
+                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device=DEV, split=split)
     outs, lses = [], []
     for t in range(T):
         l = torch.empty((wl.B, wl.H, wl.C), dtype=torch.float32, device=DEV) if lse else None
@@ -45,6 +45,9 @@ SMALL = {
     "bf16_d64_C64_w2": Workload("s4", 303, B=1, H=3, d=64, C=64, N=9, w=2, dtype="bf16"),
     "f32_d64_C48_w2": Workload("s5", 304, B=1, H=2, d=64, C=48, N=7, w=2, dtype="f32"),
     "f32_d128_C20_w4": Workload("s6", 305, B=1, H=1, d=128, C=20, N=9, w=4, dtype="f32"),
+    # 256-row chunks and a 4-chunk window: enough key tiles for the split path
+    "bf16_d128_C256_w4": Workload("s7", 306, B=1, H=2, d=128, C=256, N=8, w=4, dtype="bf16"),
+    "bf16_d128_C300_w4_q4": Workload("s8", 307, B=1, H=1, d=128, C=300, N=7, w=4, dtype="bf16", qscale=4.0),
 }
 
 
@@ -67,6 +70,21 @@ def test_stream_matches_oracle_on_concatenation(name):
             assert rel_l2(to64(st.S[b, h]), Sref) <= tol
             assert rel_l2(to64(st.z[b, h]), zref) <= tol
     assert st.t == wl.N
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_C256_w4", "bf16_d128_C300_w4_q4"])
+def test_split_window_matches_unsplit(name):
+    # the key window spread over several workgroups per query tile (with the
+    # merge kernel) against one workgroup per tile: the same up to rounding
+    wl = SMALL[name]
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+    assert st.workspace is not None, "this problem should use the split path"
+    q, k, v = gen_qkv(wl)
+    _, outs_a, lses_a = run_stream(wl, q, k, v, wl.N, lse=True, split=True)
+    _, outs_b, lses_b = run_stream(wl, q, k, v, wl.N, lse=True, split=False)
+    for t, (a, b) in enumerate(zip(outs_a, outs_b)):
+        assert rel_l2(to64(a), to64(b)) <= 5e-3, f"step {t}"
+        assert (lses_a[t] - lses_b[t]).abs().max().item() <= 1e-3
 
 
 def test_stream_state_equals_state_scan_bitwise():
