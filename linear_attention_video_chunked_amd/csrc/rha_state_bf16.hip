@@ -12,7 +12,7 @@
 // through LDS in tiles of 64, stored as loaded (token-major rows, 16-byte
 // granules XOR-swizzled); both operands are contracted over tokens, so both
 // are read with the LDS transpose read ds_read_b64_tr_b16, which hands each
-// lane 8 tokens of one feature column.  Two tiles are in flight from HBM while
+// lane 8 tokens of one feature column.  Four tiles are in flight from HBM while
 // one is multiplied (the kernel is bound by HBM, not by the products).  phi is evaluated
 // in float32 and rounded to bf16 for the product; u is summed from the float32
 // phi values in a fixed order.  With `accumulate` the result is added into
@@ -108,7 +108,8 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
   const int ntiles = (p.C + BT - 1) / BT;
-  u32x4 kw[2][Cfg::KG], vw[2][4];  // two tiles in flight
+  constexpr int R = 4;                // tiles in flight from HBM (register ring)
+  u32x4 kw[R][Cfg::KG], vw[R][4];
 
   // Buffer loads whose descriptors end at the chunk's last token: rows past
   // it (and the lanes without a unit) read zeros, so loads and stores need no
@@ -164,28 +165,37 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  static_assert(R == 4, "the loop below is unrolled for a ring of four");
 
-  // tile j lives in register slot j & 1 and LDS buffer j & 1
-  // (tiles past the chunk load as zeros and store harmlessly: phi is masked
-  // by token index, and the buffer they land in is not read again)
+  // tile j lives in register slot j % R and LDS buffer j % 2 (tiles past the
+  // chunk load as zeros and store harmlessly: phi is masked by token index,
+  // and the buffer they land in is not read again)
   gload(0, S0{});
   gload(1, S1{});
+  gload(2, S2{});
+  gload(3, S3{});
   lstore(0, 0, S0{});
   __syncthreads();
-  auto iter = [&](int j, auto slot_c) {  // slot_c = j & 1
+  auto iter = [&](int j, auto slot_c) {  // slot_c = j % R
     constexpr int sl = decltype(slot_c)::value;
-    using Next = std::integral_constant<int, sl ^ 1>;
-    gload(j + 2, slot_c);  // slot of tile j, already in LDS
-    mma(sl);
-    lstore(j + 1, sl ^ 1, Next{});
+    using Next = std::integral_constant<int, (sl + 1) % R>;
+    gload(j + R, slot_c);  // slot of tile j, already in LDS
+    mma(sl & 1);
+    lstore(j + 1, (sl + 1) & 1, Next{});
     __syncthreads();
   };
   int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
+  for (; j + R - 1 < ntiles; j += R) {
     iter(j, S0{});
     iter(j + 1, S1{});
+    iter(j + 2, S2{});
+    iter(j + 3, S3{});
   }
   if (j < ntiles) iter(j, S0{});
+  if (j + 1 < ntiles) iter(j + 1, S1{});
+  if (j + 2 < ntiles) iter(j + 2, S2{});
 
   // U: acc[i] reg 4r+q <-> e = es*64 + eb*32 + 8r + 4hh + q, n = (nb0+i)*32 + l32
   float* Sdst = p.S + (int64_t)bh * p.s_bh + (int64_t)(jc + p.slot_offset) * D * D;
