@@ -245,11 +245,9 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   cp.elem_bytes = elem_bytes(p);
   cp.src = k_new;
   cp.dst = k_cache;
+  cp.src2 = v_new;
+  cp.dst2 = v_cache;
   hipError_t e = rha::launch_copy_chunk(cp, s);
-  if (e != hipSuccess) return hip_fail(e, "cache copy launch");
-  cp.src = v_new;
-  cp.dst = v_cache;
-  e = rha::launch_copy_chunk(cp, s);
   if (e != hipSuccess) return hip_fail(e, "cache copy launch");
 
   // 2. attention of the new chunk: cached window (chunks max(0,t-w+1)..t) + state

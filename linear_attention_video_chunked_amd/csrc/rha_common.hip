@@ -48,21 +48,29 @@ __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
 }
 
 // 16-byte copy of one [B,H,C,d] chunk (strided rows) into slot `slot` of a
-// contiguous [B,H,w,C,d] cache.
+// contiguous [B,H,w,C,d] cache; with src2 set, a second chunk into dst2 in
+// the same launch (the upper half of the grid).
 __global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p) {
   const int row_vecs = p.d * p.elem_bytes / 16;
   const int64_t total = (int64_t)p.B * p.H * p.C * row_vecs;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const void* srcp = p.src;
+  void* dstp = p.dst;
+  if (idx >= total) {
+    if (p.src2 == nullptr || idx >= 2 * total) return;
+    idx -= total;
+    srcp = p.src2;
+    dstp = p.dst2;
+  }
   const int vcol = (int)(idx % row_vecs);
   const int64_t r = idx / row_vecs;
   const int t = (int)(r % p.C);
   const int64_t bh = r / p.C;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const unsigned char* src = (const unsigned char*)p.src +
+  const unsigned char* src = (const unsigned char*)srcp +
                              ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
                              vcol * 16;
-  unsigned char* dst = (unsigned char*)p.dst +
+  unsigned char* dst = (unsigned char*)dstp +
                        (((bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
   st16(dst, ld16(src));
 }
@@ -77,7 +85,7 @@ hipError_t launch_prefix(const PrefixParams& p, hipStream_t s) {
 }
 
 hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s) {
-  const int64_t total = (int64_t)p.B * p.H * p.C * (p.d * p.elem_bytes / 16);
+  const int64_t total = (int64_t)p.B * p.H * p.C * (p.d * p.elem_bytes / 16) * (p.src2 != nullptr ? 2 : 1);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -77,6 +77,8 @@ struct PrefixParams {
 struct CopyParams {
   const void* src;
   void* dst;
+  const void* src2;  // optional second chunk (same shape and strides) into dst2
+  void* dst2;
   int64_t sb, sh, st;
   int B, H, C, d, w, slot;
   int elem_bytes;
