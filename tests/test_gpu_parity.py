@@ -43,6 +43,13 @@ MID = {
     "bf16_d128_C300_N4_w1": (1, 2, 128, 300, 4, 1, "bf16", 1.0, 1.0),
     "bf16_d128_C300_N4_w1_q4": (1, 2, 128, 300, 4, 1, "bf16", 4.0, 0.5),
     "bf16_d128_C130_N4_w0": (1, 2, 128, 130, 4, 0, "bf16", 1.0, 1.0),
+    # chunks of at least one 256-row tile: tiles run over the flat sequence and
+    # span chunk edges (aligned, ragged, pure linear, window past the start)
+    "bf16_d128_C256_N5_w2": (1, 2, 128, 256, 5, 2, "bf16", 1.0, 1.0),
+    "bf16_d128_C333_N6_w3": (2, 2, 128, 333, 6, 3, "bf16", 1.0, 0.5),
+    "bf16_d128_C333_N6_w3_q4": (1, 2, 128, 333, 6, 3, "bf16", 4.0, 0.5),
+    "bf16_d128_C300_N4_w0": (1, 2, 128, 300, 4, 0, "bf16", 1.0, 1.0),
+    "bf16_d128_C270_N5_w9": (1, 1, 128, 270, 5, 9, "bf16", 2.0, 1.0),
     "bf16_d128_C130_N4_w4": (1, 2, 128, 130, 4, 4, "bf16", 1.0, 1.0),
     "bf16_d128_C130_N4_w9": (1, 2, 128, 130, 4, 9, "bf16", 2.0, 1.0),
     "bf16_d128_C1_N300_w3": (1, 2, 128, 1, 300, 3, "bf16", 1.0, 1.0),
@@ -157,8 +164,9 @@ def test_empty_problems():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("C", [100, 300])
 @pytest.mark.parametrize("alpha", [40.0, 170.0, -170.0])
-def test_score_growth_within_window(alpha):
+def test_score_growth_within_window(alpha, C):
     # Every query shares a component along feature 0; the last key of every
     # chunk is alpha along that feature, so windows see ordinary scores first
     # and then one key scoring about 0.35 * alpha (natural log units) above
@@ -166,7 +174,8 @@ def test_score_growth_within_window(alpha):
     # reference maximum; alpha = 170 (a ~60-nat jump, 2^86) forces reference
     # moves after accumulation, both where the linear state seeds the
     # accumulators and where it does not; -170 makes those keys vanish.
-    wl = Workload("growth", 950, B=1, H=2, d=128, C=100, N=4, w=2, dtype="bf16", qscale=1.0, kscale=0.5)
+    # C = 300: query tiles that span two chunks.
+    wl = Workload("growth", 950, B=1, H=2, d=128, C=C, N=4, w=2, dtype="bf16", qscale=1.0, kscale=0.5)
     q, k, v = gen_qkv(wl)
     q = q.clone()
     k = k.clone()
