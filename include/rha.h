@@ -147,8 +147,10 @@ typedef struct {
  * With commit == 0 nothing but the cache slot of chunk t changes, so the same
  * chunk can be re-run (e.g. once per denoising step) before committing it.
  * Outputs equal those of rha_hybrid_fwd over the concatenated sequence up to
- * float rounding (the key window is visited in another order), and S, z
- * after each commit equal rha_state_scan's entry for chunk t+1 bitwise.
+ * float rounding (the key window is visited in another order).  Without a
+ * workspace, S, z after each commit equal rha_state_scan's entry for chunk
+ * t+1 bitwise; with one, up to float rounding (the fold sums token groups).
+ * Either way a step is deterministic.
  *
  *   p->n_chunks is ignored; p's strides describe q_new, k_new, v_new, out
  *   q_new, k_new, v_new : [B, H, C, d] (read)
@@ -172,9 +174,11 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
  * One chunk has few query tiles, so the step splits the key window across
  * several workgroups per tile and merges their partial results (numerators,
  * denominators and reference maxima, in float32) in a second small kernel.
- * The size depends on p (batch, heads, chunk_len, head_dim, window) and on
- * the number of compute units of the current device; it is 0 when p would not
- * be split (problems other than bf16 with head_dim 128, or enough tiles).
+ * Likewise the fold of a committed chunk splits the chunk's tokens into
+ * groups whose partial states are then added to S, z in group order.  The
+ * size depends on p (batch, heads, chunk_len, head_dim, window, dtype) and on
+ * the number of compute units of the current device; it is 0 when p would
+ * not be split (enough tiles and heads already, or float32 problems).
  * Pass workspace = NULL, or workspace_bytes below this size, to run without
  * the split; results agree to rounding either way.  The workspace must be
  * 16-byte aligned device memory owned by the caller, not used by anything else

@@ -132,6 +132,33 @@ int stream_splits(const rha_problem* p, int64_t n_keys) {
   return splits < 2 ? 1 : (int)splits;
 }
 
+// Split of the streaming fold (bf16): the folded chunk's tokens in groups of
+// whole 64-token tiles, enough groups for about one workgroup per compute
+// unit.  Returns the number of groups (1: no split) and their length.
+int fold_groups(const rha_problem* p, int* group_len) {
+  *group_len = p->chunk_len;
+  if (p->dtype != RHA_BF16) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 1;
+  const int64_t units = (int64_t)p->batch * p->heads * (p->head_dim / 64);  // workgroups per group
+  const int64_t ntiles = (p->chunk_len + 63) / 64;
+  int64_t g = (cus + units - 1) / units;
+  if (g > ntiles) g = ntiles;
+  if (g < 2) return 1;
+  const int64_t per = (ntiles + g - 1) / g;
+  g = (ntiles + per - 1) / per;
+  if (g < 2) return 1;
+  *group_len = (int)(per * 64);
+  return (int)g;
+}
+
+size_t fold_bytes(const rha_problem* p, int groups) {
+  const int64_t d = p->head_dim;
+  return (size_t)((int64_t)p->batch * p->heads * groups * (d * d + d) * (int64_t)sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +181,7 @@ rha_status rha_state_scan(const rha_problem* p, const void* k, const void* v, fl
     c.accumulate = 0;
     c.s_bh = (int64_t)N * d * d;
     c.z_bh = (int64_t)N * d;
+    c.tok_end = (int64_t)nproc * p->chunk_len;
     hipError_t e = launch_chunk_state(p, c, s);
     if (e != hipSuccess) return hip_fail(e, "chunk state launch");
   }
@@ -199,9 +227,14 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
 
 size_t rha_stream_workspace_size(const rha_problem* p) {
   if (p == nullptr || check_problem(p, true) != RHA_OK || empty(p, true)) return 0;
+  // the split window's partial results, and later in the step the split
+  // fold's partial states, share the workspace
   const int splits = stream_splits(p, (int64_t)p->window * p->chunk_len);
-  if (splits < 2) return 0;
-  return rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits);
+  int glen = 0;
+  const int groups = fold_groups(p, &glen);
+  size_t bytes = splits < 2 ? 0 : rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits);
+  if (groups > 1 && fold_bytes(p, groups) > bytes) bytes = fold_bytes(p, groups);
+  return bytes;
 }
 
 rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
@@ -293,25 +326,53 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   // 3. commit: fold the chunk that leaves the window, advance the cursor
   if (commit) {
     if (t >= w - 1) {
+      const int out_slot = (int)((t + 1) % w);
+      int glen = C;
+      const int groups = workspace != nullptr ? fold_groups(p, &glen) : 1;
       rha::ChunkStateParams c{};
-      c.k = k_cache;
-      c.v = v_cache;
-      c.S = S;
-      c.z = z;
       c.kv_sb = f.kv_sb;
       c.kv_sh = f.kv_sh;
       c.kv_st = d;
       c.B = p->batch;
       c.H = p->heads;
-      c.C = C;
-      c.chunk0 = (int)((t + 1) % w);
-      c.n_chunks = 1;
-      c.slot_offset = 0;
-      c.accumulate = 1;
-      c.s_bh = (int64_t)d * d;
-      c.z_bh = d;
-      e = launch_chunk_state(p, c, s);
-      if (e != hipSuccess) return hip_fail(e, "fold launch");
+      if (groups > 1 && workspace_bytes >= fold_bytes(p, groups)) {
+        // token groups of the chunk into partial states, then added in order
+        const int64_t slot_off = (int64_t)out_slot * C * d * elem_bytes(p);
+        float* part = static_cast<float*>(workspace);
+        const int64_t bh = (int64_t)p->batch * p->heads;
+        c.k = static_cast<const char*>(k_cache) + slot_off;
+        c.v = static_cast<const char*>(v_cache) + slot_off;
+        c.S = part;
+        c.z = part + bh * groups * d * d;
+        c.C = glen;
+        c.chunk0 = 0;
+        c.n_chunks = groups;
+        c.slot_offset = 0;
+        c.accumulate = 0;
+        c.s_bh = (int64_t)groups * d * d;
+        c.z_bh = (int64_t)groups * d;
+        c.tok_end = C;
+        e = launch_chunk_state(p, c, s);
+        if (e != hipSuccess) return hip_fail(e, "fold launch");
+        rha::StateCombineParams sc{S, z, part, (int)bh, groups, d};
+        e = rha::launch_state_combine(sc, s);
+        if (e != hipSuccess) return hip_fail(e, "fold merge launch");
+      } else {
+        c.k = k_cache;
+        c.v = v_cache;
+        c.S = S;
+        c.z = z;
+        c.C = C;
+        c.chunk0 = out_slot;
+        c.n_chunks = 1;
+        c.slot_offset = 0;
+        c.accumulate = 1;
+        c.s_bh = (int64_t)d * d;
+        c.z_bh = d;
+        c.tok_end = (int64_t)(out_slot + 1) * C;
+        e = launch_chunk_state(p, c, s);
+        if (e != hipSuccess) return hip_fail(e, "fold launch");
+      }
     }
     cursor->t = t + 1;
   }

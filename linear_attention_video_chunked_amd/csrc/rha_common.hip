@@ -48,31 +48,50 @@ __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
 }
 
 // 16-byte copy of one [B,H,C,d] chunk (strided rows) into slot `slot` of a
-// contiguous [B,H,w,C,d] cache; with src2 set, a second chunk into dst2 in
-// the same launch (the upper half of the grid).
-__global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p) {
+// contiguous [B,H,w,C,d] cache; with src2 set, a second chunk into dst2
+// (blockIdx.y = 1).  blockIdx.x = bh * blocks_per_bh + block within the head,
+// so every per-thread index is 32-bit.
+__global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p, int blocks_per_bh) {
   const int row_vecs = p.d * p.elem_bytes / 16;
-  const int64_t total = (int64_t)p.B * p.H * p.C * row_vecs;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const void* srcp = p.src;
-  void* dstp = p.dst;
-  if (idx >= total) {
-    if (p.src2 == nullptr || idx >= 2 * total) return;
-    idx -= total;
-    srcp = p.src2;
-    dstp = p.dst2;
-  }
-  const int vcol = (int)(idx % row_vecs);
-  const int64_t r = idx / row_vecs;
-  const int t = (int)(r % p.C);
-  const int64_t bh = r / p.C;
-  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const int bh = blockIdx.x / blocks_per_bh;
+  const int i = (blockIdx.x - bh * blocks_per_bh) * 256 + threadIdx.x;
+  if (i >= p.C * row_vecs) return;
+  const void* srcp = blockIdx.y ? p.src2 : p.src;
+  void* dstp = blockIdx.y ? p.dst2 : p.dst;
+  const int t = i / row_vecs, vcol = i - t * row_vecs;
+  const int b = bh / p.H, h = bh - b * p.H;
   const unsigned char* src = (const unsigned char*)srcp +
                              ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
                              vcol * 16;
   unsigned char* dst = (unsigned char*)dstp +
-                       (((bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
+                       ((((int64_t)bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
   st16(dst, ld16(src));
+}
+
+// S[bh] += sum_g part_S[bh][g] and z[bh] += sum_g part_z[bh][g], the partial
+// sums added in g order first (a fixed order, so the result is deterministic);
+// one thread per 4 floats.
+__global__ __launch_bounds__(256) void state_combine_kernel(const StateCombineParams p) {
+  const int per = (p.d * p.d + p.d) / 4;  // float4 units per head
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)p.BH * per) return;
+  const int bh = (int)(idx / per), r = (int)(idx - (int64_t)bh * per);
+  const int sq = p.d * p.d / 4;
+  const float* src;
+  int64_t gstride;
+  float* dst;
+  if (r < sq) {
+    src = p.part + ((int64_t)bh * p.G * p.d * p.d) + 4 * r;
+    gstride = (int64_t)p.d * p.d;
+    dst = p.S + (int64_t)bh * p.d * p.d + 4 * r;
+  } else {
+    src = p.part + (int64_t)p.BH * p.G * p.d * p.d + (int64_t)bh * p.G * p.d + 4 * (r - sq);
+    gstride = p.d;
+    dst = p.z + (int64_t)bh * p.d + 4 * (r - sq);
+  }
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int g = 1; g < p.G; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * gstride);
+  *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(dst) + acc;
 }
 
 }  // namespace
@@ -85,9 +104,19 @@ hipError_t launch_prefix(const PrefixParams& p, hipStream_t s) {
 }
 
 hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s) {
-  const int64_t total = (int64_t)p.B * p.H * p.C * (p.d * p.elem_bytes / 16) * (p.src2 != nullptr ? 2 : 1);
+  const int64_t per_bh = (int64_t)p.C * (p.d * p.elem_bytes / 16);
+  const int64_t BH = (int64_t)p.B * p.H;
+  if (per_bh == 0 || BH == 0) return hipSuccess;
+  const int blocks_per_bh = (int)((per_bh + 255) / 256);
+  hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)(BH * blocks_per_bh), p.src2 != nullptr ? 2u : 1u), dim3(256), 0, s,
+                     p, blocks_per_bh);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_combine(const StateCombineParams& p, hipStream_t s) {
+  const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d) / 4;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(state_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -144,6 +144,7 @@ __global__ __launch_bounds__(FST) void chunk_state_f32_kernel(const ChunkStatePa
   const int bh = blockIdx.x / p.n_chunks;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t t0 = (int64_t)(p.chunk0 + jc) * p.C;
+  const int len = (int)min((int64_t)p.C, p.tok_end - t0);  // tokens of this chunk
   const float* kbase = (const float*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
   const float* vbase = (const float*)p.v + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
 
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(FST) void chunk_state_f32_kernel(const ChunkStatePa
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
   }
 
-  for (int tb = 0; tb < p.C; tb += FBT) {
-    const int valid = min(FBT, p.C - tb);
+  for (int tb = 0; tb < len; tb += FBT) {
+    const int valid = min(FBT, len - tb);
     for (int i = tid; i < FBT * D; i += FST) {
       const int r = i / D, e = i % D;
       const bool in = r < valid;

@@ -47,9 +47,9 @@ struct FwdParams {
 // Per-chunk state contribution phi(K_c)^T V_c, sum_t phi(k_t) for a list of
 // chunks, written to (or, with accumulate, added into) float32 state slots.
 //   chunk index j in [0, n_chunks) of head bh reads tokens
-//   [ (chunk0 + j) * C, +C ) of k, v; it writes slot (j + slot_offset) of
-//   S[bh] (slot stride d*d, head stride s_bh) and z[bh] (slot stride d, head
-//   stride z_bh).
+//   [ (chunk0 + j) * C, +C ) of k, v, cut at token tok_end (tokens at or
+//   past it count as absent); it writes slot (j + slot_offset) of S[bh] (slot
+//   stride d*d, head stride s_bh) and z[bh] (slot stride d, head stride z_bh).
 struct ChunkStateParams {
   const void* k;
   const void* v;
@@ -62,6 +62,16 @@ struct ChunkStateParams {
   int n_chunks;
   int slot_offset;
   int accumulate;
+  int64_t tok_end;  // (chunk0 + n_chunks) * C for whole chunks
+};
+
+// S[bh] += sum over g of part[bh][g] (g = 0 .. G-1 in order), likewise z:
+// part holds B*H*G slots of d*d floats, then B*H*G slots of d floats.
+struct StateCombineParams {
+  float* S;
+  float* z;
+  const float* part;
+  int BH, G, d;
 };
 
 // In-place inclusive prefix over the state slots of every head:
@@ -100,5 +110,6 @@ hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t
 hipError_t launch_chunk_state_f32(const ChunkStateParams& p, int d, hipStream_t s);
 hipError_t launch_prefix(const PrefixParams& p, hipStream_t s);
 hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s);
+hipError_t launch_state_combine(const StateCombineParams& p, hipStream_t s);
 
 }  // namespace rha

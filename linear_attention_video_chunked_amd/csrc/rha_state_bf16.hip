@@ -16,7 +16,9 @@
 // one is multiplied (the kernel is bound by HBM, not by the products).  phi is evaluated
 // in float32 and rounded to bf16 for the product; u is summed from the float32
 // phi values in a fixed order.  With `accumulate` the result is added into
-// the destination (the streaming fold), otherwise it is stored.
+// the destination (the streaming fold), otherwise it is stored.  A "chunk" may
+// also be a token range of a real chunk (the split streaming fold): tok_end
+// cuts the last one short.
 #include "rha_device.hpp"
 #include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   const int bh = logical / Cfg::ES / p.n_chunks;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t t0 = (int64_t)(p.chunk0 + jc) * p.C;
+  const int len = (int)min((int64_t)p.C, p.tok_end - t0);  // tokens of this chunk
   const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st + es * ESLICE;
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
 
@@ -107,14 +110,14 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
 #pragma unroll
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
-  const int ntiles = (p.C + BT - 1) / BT;
+  const int ntiles = (len + BT - 1) / BT;
   constexpr int R = 4;                // tiles in flight from HBM (register ring)
   u32x4 kw[R][Cfg::KG], vw[R][4];
 
   // Buffer loads whose descriptors end at the chunk's last token: rows past
   // it (and the lanes without a unit) read zeros, so loads and stores need no
   // branches and the load waits stay exact.
-  const int chunk_bytes = p.C * (int)p.kv_st * 2;
+  const int chunk_bytes = len * (int)p.kv_st * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, chunk_bytes, fwd::kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, chunk_bytes, fwd::kBufWord3);
   const int kofs0 = (krow0 * (int)p.kv_st + kfo * 8) * 2;
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
 #pragma unroll
     for (int r = 0; r < Cfg::KG; ++r) {
       const int row = krow0 + r * Cfg::KROWSTEP;
-      const bool ok = j * BT + row < p.C;  // rows past the chunk: phi(0) would be 1
+      const bool ok = j * BT + row < len;  // rows past the chunk: phi(0) would be 1
       u32x4 fw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -149,9 +149,9 @@ def test_stream_workspace_checks(L):
     assert _step(L, prob, ctypes.byref(cur), ws=BAD, ws_bytes=1 << 20) == 1
     assert "workspace" in L.rha_last_error().decode()
     assert cur.t == 5
-    # no split for float32 or head_dim 64 problems, nor for invalid ones
+    # no split for float32 problems, nor for invalid ones
     assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=3, dtype=_rha.RHA_F32, stride_t=128))) == 0
-    assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=3, head_dim=64, stride_t=64))) == 0
+    assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=3, dtype=_rha.RHA_F32, head_dim=64, stride_t=64))) == 0
     assert L.rha_stream_workspace_size(ctypes.byref(_prob(window=0))) == 0
     assert L.rha_stream_workspace_size(None) == 0
 
