@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p, int
 // S[bh] += sum_g part_S[bh][g] and z[bh] += sum_g part_z[bh][g], the partial
 // sums added in g order first (a fixed order, so the result is deterministic);
 // one thread per 4 floats.
-__global__ __launch_bounds__(256) void state_combine_kernel(const StateCombineParams p) {
+__global__ __launch_bounds__(64) void state_combine_kernel(const StateCombineParams p) {
   const int per = (p.d * p.d + p.d) / 4;  // float4 units per head
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.BH * per) return;
@@ -89,8 +89,17 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const StateCombinePa
     gstride = p.d;
     dst = p.z + (int64_t)bh * p.d + 4 * (r - sq);
   }
-  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-  for (int g = 1; g < p.G; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * gstride);
+  // groups of eight loads in flight, added in g order
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int g = 0;
+  for (; g + 8 <= p.G; g += 8) {
+    f32x4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const f32x4*>(src + (g + i) * gstride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += x[i];
+  }
+  for (; g < p.G; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * gstride);
   *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(dst) + acc;
 }
 
@@ -116,7 +125,7 @@ hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s) {
 hipError_t launch_state_combine(const StateCombineParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d) / 4;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(state_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(state_combine_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
