@@ -18,6 +18,11 @@ from .rha_oracle import (
     hybrid_rows,
     hybrid_batched,
     state_scan_batched,
+    sparse_mask_shape,
+    brute_block_sparse,
+    hybrid_block_sparse,
+    hybrid_block_sparse_rows,
+    hybrid_block_sparse_batched,
 )
 
 __all__ = [
@@ -31,4 +36,9 @@ __all__ = [
     "hybrid_rows",
     "hybrid_batched",
     "state_scan_batched",
+    "sparse_mask_shape",
+    "brute_block_sparse",
+    "hybrid_block_sparse",
+    "hybrid_block_sparse_rows",
+    "hybrid_block_sparse_batched",
 ]

@@ -219,3 +219,130 @@ def state_scan_batched(k, v, C: int, w: int):
         for h in range(H):
             S[b, h], z[b, h] = state_scan(k[b, h], v[b, h], C, w)
     return S, z
+
+
+# ---------------------------------------------------------------- block-sparse window
+#
+# "Long-Horizon Streaming Video Generation via Hybrid Attention with Decoupled
+# Distillation" (explainer page), section 2.A, block-sparse sliding-window
+# attention: inside the local window, attention is evaluated in blocks as in
+# FlashAttention and the blocks judged unimportant are pruned.  The page gives
+# no importance criterion, so the kept blocks are an input: a 0/1 mask per
+# (query block, key block).  Blocks: query block i of chunk c holds rows
+# c*C + qtile*i .. (clipped to the chunk); key block j of that chunk's window
+# holds keys kbeg + ktile*j .. (clipped to the window), kbeg being the first
+# key of the window.  A pruned block contributes nothing (its a_ij are 0); the
+# folded history is not affected.  A query left with no weight at all (no
+# kept key and an empty history) gets output 0 and denominator 0.
+
+
+def sparse_mask_shape(C: int, N: int, w: int, qtile: int = 256, ktile: int = 64):
+    """Per-head mask shape (N, query blocks per chunk, key blocks per window)."""
+    nqt = -(-C // qtile)
+    wl = min(w, N) if w > 0 else 0
+    return N, nqt, -(-(wl * C) // ktile)
+
+
+def brute_block_sparse(q, k, v, C: int, w: int, mask, qtile: int = 256, ktile: int = 64,
+                       return_den: bool = False):
+    """The pruned definition as one L x L weight matrix (tiny inputs only)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    mask = np.asarray(mask)
+    L = q.shape[0]
+    s = _scores(q, k)
+    lin = phi(q) @ phi(k).T
+    a = np.zeros((L, L))
+    for i in range(L):
+        c = i // C
+        qi = (i - c * C) // qtile
+        lo, hi = window_range(c, w)
+        for j in range(L):
+            cj = j // C
+            if lo <= cj <= hi:
+                if mask[c, qi, (j - lo * C) // ktile]:
+                    a[i, j] = math.exp(s[i, j])
+            elif cj <= c - w:
+                a[i, j] = lin[i, j]
+    den = a.sum(axis=1)
+    num = a @ v
+    out = np.where(den[:, None] > 0, num / np.where(den > 0, den, 1.0)[:, None], 0.0)
+    return (out, den) if return_den else out
+
+
+def _window_keep(mask_row, n_keys: int, ktile: int):
+    """0/1 per key of a window of n_keys keys from one mask row."""
+    keep = np.repeat(np.asarray(mask_row, dtype=bool), ktile)[:n_keys]
+    if keep.size < n_keys:
+        raise ValueError("mask row too short for the window")
+    return keep
+
+
+def hybrid_block_sparse(q, k, v, C: int, w: int, mask, qtile: int = 256, ktile: int = 64,
+                        return_den: bool = False):
+    """Chunked evaluation of the pruned definition (one head; mask [N, nqt, nkt])."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    mask = np.asarray(mask)
+    L, d = q.shape
+    N = L // C
+    S, z = state_scan(k, v, C, w)
+    fq = phi(q)
+    out = np.empty((L, v.shape[1]))
+    den_all = np.empty(L)
+    for c in range(N):
+        lo, hi = window_range(c, w)
+        for i in range(-(-C // qtile)):
+            rows = slice(c * C + i * qtile, c * C + min(C, (i + 1) * qtile))
+            num = fq[rows] @ S[c]
+            den = fq[rows] @ z[c]
+            if lo <= hi:
+                keys = slice(lo * C, (hi + 1) * C)
+                keep = _window_keep(mask[c, i], (hi + 1 - lo) * C, ktile)
+                e = np.exp(_scores(q[rows], k[keys])) * keep[None, :]
+                num = num + e @ v[keys]
+                den = den + e.sum(axis=1)
+            safe = np.where(den > 0, den, 1.0)
+            out[rows] = np.where(den[:, None] > 0, num / safe[:, None], 0.0)
+            den_all[rows] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_block_sparse_rows(q, k, v, C: int, w: int, mask, rows, S=None, z=None, qtile: int = 256,
+                             ktile: int = 64, return_den: bool = False):
+    """The pruned definition for selected query rows (one head)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    mask = np.asarray(mask)
+    if S is None:
+        S, z = state_scan(k, v, C, w)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]))
+    den_all = np.empty(rows.size)
+    for n, r in enumerate(rows):
+        r = int(r)
+        c = r // C
+        fq = phi(q[r])
+        num = fq @ S[c]
+        den = fq @ z[c]
+        lo, hi = window_range(c, w)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            keep = _window_keep(mask[c, (r - c * C) // qtile], (hi + 1 - lo) * C, ktile)
+            e = np.exp(_scores(q[r : r + 1], k[keys]))[0] * keep
+            num = num + e @ v[keys]
+            den = den + e.sum()
+        out[n] = num / den if den > 0 else 0.0
+        den_all[n] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_block_sparse_batched(q, k, v, C: int, w: int, mask, return_den: bool = False, **tiles):
+    """``hybrid_block_sparse`` over [B, H, L, d] with mask [B, H, N, nqt, nkt]."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    mask = np.asarray(mask)
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    den = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], den[b, h] = hybrid_block_sparse(q[b, h], k[b, h], v[b, h], C, w, mask[b, h],
+                                                       return_den=True, **tiles)
+    return (out, den) if return_den else out

@@ -330,3 +330,85 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_pins_pass():
     errs = _all_pins_err()
     assert max(errs.values()) < 1e-11, errs
+
+
+# ---------------------------------------------------------------- block-sparse window
+# (explainer page of "Long-Horizon Streaming Video Generation via Hybrid
+# Attention with Decoupled Distillation", section 2.A: pruned blocks of the
+# local window).  The pruned definition is pinned to brute force and, through
+# the all-kept and all-pruned masks, to the dense oracle and a closed form.
+
+SPARSE_SWEEP = [
+    (C, N, w, qt, kt)
+    for C, N in ((3, 4), (5, 3), (6, 2), (4, 1))
+    for w in (1, 2, N + 1)
+    for qt, kt in ((2, 2), (3, 5), (C, 1))
+]
+
+
+def _mask(C, N, w, qt, kt, seed, density=0.5):
+    shape = O.sparse_mask_shape(C, N, w, qt, kt)
+    return (np.random.default_rng(seed).random(shape) < density).astype(np.uint8)
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", SPARSE_SWEEP)
+def test_block_sparse_brute_equals_chunked(C, N, w, qt, kt):
+    q, k, v = _qkv(C * N, 4, 700 + 10 * C + N, qs=1.5)
+    m = _mask(C, N, w, qt, kt, 7 * C + N + w)
+    a, da = O.brute_block_sparse(q, k, v, C, w, m, qt, kt, return_den=True)
+    b, db = O.hybrid_block_sparse(q, k, v, C, w, m, qt, kt, return_den=True)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(db, da, rtol=1e-12, atol=1e-300)
+    rows = np.arange(0, C * N, 2)
+    r, dr = O.hybrid_block_sparse_rows(q, k, v, C, w, m, rows, qtile=qt, ktile=kt, return_den=True)
+    np.testing.assert_allclose(r, a[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dr, da[rows], rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("C,N,w", [(3, 4, 2), (5, 3, 1), (4, 2, 3)])
+def test_block_sparse_all_kept_is_dense(C, N, w):
+    q, k, v = _qkv(C * N, 4, 800 + C, qs=1.5)
+    ones = np.ones(O.sparse_mask_shape(C, N, w, 2, 3), np.uint8)
+    np.testing.assert_allclose(O.brute_block_sparse(q, k, v, C, w, ones, 2, 3), O.brute_masked(q, k, v, C, w),
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(O.hybrid_block_sparse(q, k, v, C, w, ones, 2, 3), O.hybrid(q, k, v, C, w),
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_block_sparse_all_pruned_is_linear_only():
+    # no window key left: out = phi(q) S_c / phi(q) z_c where the history is
+    # non-empty (chunks c >= w), and 0 with denominator 0 where it is empty
+    C, N, w = 4, 5, 2
+    q, k, v = _qkv(C * N, 3, 850)
+    zeros = np.zeros(O.sparse_mask_shape(C, N, w, 2, 3), np.uint8)
+    out, den = O.brute_block_sparse(q, k, v, C, w, zeros, 2, 3, return_den=True)
+    fq, fk = O.phi(q), O.phi(k)
+    for i in range(C * N):
+        c = i // C
+        if c < w:
+            assert den[i] == 0 and np.all(out[i] == 0)
+        else:
+            hist = slice(0, (c - w + 1) * C)
+            wts = fk[hist] @ fq[i]
+            np.testing.assert_allclose(out[i], wts @ v[hist] / wts.sum(), rtol=1e-13)
+    np.testing.assert_allclose(O.hybrid_block_sparse(q, k, v, C, w, zeros, 2, 3), out, rtol=1e-13, atol=1e-13)
+
+
+def test_block_sparse_drops_exactly_the_block():
+    # pruning key block j of one query block equals giving those keys zero
+    # weight: the same query rows computed over the window with those keys
+    # deleted (the history untouched) -- checked on the definition directly
+    C, N, w, qt, kt = 6, 3, 2, 3, 4
+    q, k, v = _qkv(C * N, 5, 870, qs=1.2)
+    m = np.ones(O.sparse_mask_shape(C, N, w, qt, kt), np.uint8)
+    c, i, j = 2, 1, 1
+    m[c, i, j] = 0
+    out = O.hybrid_block_sparse(q, k, v, C, w, m, qt, kt)
+    lo = (c - w + 1) * C
+    keys = [t for t in range(lo, (c + 1) * C) if not (lo + j * kt <= t < lo + (j + 1) * kt)]
+    hist = list(range(0, lo))
+    for r in range(c * C + i * qt, c * C + (i + 1) * qt):
+        e = np.exp(q[r] @ k[keys].T / math.sqrt(5))
+        lin = O.phi(k[hist]) @ O.phi(q[r])
+        ref = (e @ v[keys] + lin @ v[hist]) / (e.sum() + lin.sum())
+        np.testing.assert_allclose(out[r], ref, rtol=1e-12)
