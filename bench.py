@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -55,6 +55,23 @@ def scan_bytes(C, N, w, d, BH, elem=2):
     """Algorithmic HBM bytes of rha_state_scan: k, v of the folded chunks read
     once, every state slot written once."""
     return BH * (2 * max(0, N - w) * C * d * elem + N * (d * d + d) * 4)
+
+
+def sparse_fwd_flops(C, N, w, d, mask, qtile=256, ktile=64):
+    """Algorithmic FLOPs of one rha_hybrid_fwd_sparse call: as fwd_flops, but
+    only the (query, key) pairs of kept blocks count.  mask: numpy [B,H,N,nqt,nkt]."""
+    B, H = mask.shape[:2]
+    f = 0
+    for c in range(N):
+        wk = min(c + 1, w) * C if w > 0 else 0  # keys in this chunk's window
+        keys = [max(0, min(ktile, wk - ktile * j)) for j in range(mask.shape[4])]
+        for i in range(mask.shape[3]):
+            rows = min(C, qtile * (i + 1)) - qtile * i
+            kept = (mask[:, :, c, i, :].astype(int) * keys).sum()  # over b, h
+            f += rows * 4 * d * kept
+            if w == 0 or c >= w:
+                f += rows * (2 * d * d + 2 * d) * B * H
+    return f
 
 
 def stream_step_flops(C, w, d, BH):
@@ -125,7 +142,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream"], default=None)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -136,7 +153,7 @@ def main():
 
     import torch
     import linear_attention_video_chunked_amd as rha
-    from synth import CONFIGS, gen_qkv
+    from synth import CONFIGS, gen_block_mask, gen_qkv
 
     dev = "cuda"
     torch.cuda.init()
@@ -186,6 +203,20 @@ def main():
         torch.cuda.synchronize()
         return
 
+    # ---- pruned window: half of the (query block, key block) pairs kept (seeded)
+    mask_cpu = gen_block_mask(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), 0.5, seed=31)
+    mask = mask_cpu.to(dev)
+
+    def sparse_call():
+        rha.hybrid_fwd_sparse(q, k, v, S, z, wl.C, wl.w, mask, out=out, stream=stream)
+
+    if args.only == "sparse":
+        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+        for _ in range(args.steps):
+            sparse_call()
+        torch.cuda.synchronize()
+        return
+
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
     def stream_run(timed_run):
         sw = CONFIGS["stream"]
@@ -232,6 +263,8 @@ def main():
     n_k = max(args.steps, 10)
     t_fwd = timed(lambda: rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream), n_k)
     t_scan = timed(lambda: rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream), n_k)
+    t_sparse = timed(sparse_call, n_k)
+    spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
 
     sw, t_stream = stream_run(True)
     F = fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
@@ -273,6 +306,10 @@ def main():
             "stream_step_mfma_frac": sF / t_stream / 1e12 / PEAK_BF16_TFLOPS,
             "stream_step_GBps": sB / t_stream / 1e9,
             "stream_step_hbm_frac": sB / t_stream / 1e9 / PEAK_HBM_GBS,
+            "sparse_half_fwd_us": t_sparse * 1e6,
+            "sparse_half_kept_frac": float(mask_cpu.float().mean()),
+            "sparse_half_TFLOPs": spF / t_sparse / 1e12,
+            "sparse_half_mfma_frac": spF / t_sparse / 1e12 / PEAK_BF16_TFLOPS,
             "timed_wall_s": wall,
         },
     }

@@ -123,6 +123,38 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
                           const float* S, const float* z, void* out, float* lse, void* stream);
 
 /*
+ * rha_hybrid_fwd_sparse -- rha_hybrid_fwd with pruned blocks of the window.
+ *
+ * Hybrid Forcing explainer section 2.A (block-sparse sliding-window
+ * attention: the window's attention is evaluated block by block and blocks
+ * judged unimportant are pruned).  The page gives no importance criterion, so
+ * the kept blocks are an input.  Blocks:
+ *   query block i of chunk c : rows c*C + RHA_SPARSE_QTILE*i ..  (clipped to the chunk)
+ *   key block j of its window: keys kbeg + RHA_SPARSE_KTILE*j .. (clipped to the window)
+ * with kbeg = max(0, c-w+1)*C the window's first key.  A pruned block adds
+ * nothing to the numerator or the denominator; the linear state is untouched.
+ * A query left with no weight at all (every block pruned and c < w) gets
+ * out = 0 and lse = -inf.
+ *
+ *   block_mask : uint8 [B, H, N, nqt, nkt] contiguous device memory (read);
+ *                nonzero keeps the block.  nqt = ceil(C / RHA_SPARSE_QTILE),
+ *                nkt = ceil(min(w, N) * C / RHA_SPARSE_KTILE); entries past a
+ *                shorter window (chunks c < w-1) are ignored.
+ *   other arguments as for rha_hybrid_fwd.
+ * With every entry nonzero the result equals rha_hybrid_fwd's bitwise.
+ *
+ * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16 and head_dim is 128,
+ * or when nkt exceeds RHA_SPARSE_MAX_KTILES.  With window 0 there is no
+ * window to prune and the call is rha_hybrid_fwd (block_mask may be NULL).
+ */
+#define RHA_SPARSE_QTILE 256
+#define RHA_SPARSE_KTILE 64
+#define RHA_SPARSE_MAX_KTILES 2048
+rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void* k, const void* v,
+                                 const float* S, const float* z, const uint8_t* block_mask, void* out,
+                                 float* lse, void* stream);
+
+/*
  * Streaming cursor: the number of chunks committed so far, which is the
  * index of the chunk the next call processes.  Start at 0 with S, z zeroed.
  */

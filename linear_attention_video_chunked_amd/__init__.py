@@ -9,6 +9,7 @@ Functions mirror the C ABI in ``include/rha.h``:
 
 * ``state_scan(k, v, C, w)``                     -> S [B,H,N,d,d], z [B,H,N,d]
 * ``hybrid_fwd(q, k, v, S, z, C, w)``            -> out [B,H,L,d] (and lse)
+* ``hybrid_fwd_sparse(q, k, v, S, z, C, w, m)``  the same with pruned window blocks
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
 """
 from ._rha import (
@@ -16,8 +17,10 @@ from ._rha import (
     RhaError,
     StreamState,
     hybrid_fwd,
+    hybrid_fwd_sparse,
     lib,
     lib_path,
+    sparse_mask_shape,
     state_scan,
     stream_step,
     version,
@@ -28,8 +31,10 @@ __all__ = [
     "RhaError",
     "StreamState",
     "hybrid_fwd",
+    "hybrid_fwd_sparse",
     "lib",
     "lib_path",
+    "sparse_mask_shape",
     "state_scan",
     "stream_step",
     "version",

@@ -64,11 +64,12 @@ def lib():
     P = ctypes.POINTER(Problem)
     L.rha_state_scan.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_hybrid_fwd_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
     L.rha_stream_workspace_size.restype = ctypes.c_size_t
-    for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_stream_step"):
+    for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_stream_step"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
     L.rha_status_string.restype = ctypes.c_char_p
@@ -164,6 +165,47 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     prob = _problem(q, C, w, N)
     _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
                                 _ptr(lse), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+# Block sizes of the pruned window (RHA_SPARSE_QTILE / RHA_SPARSE_KTILE).
+SPARSE_QTILE = 256
+SPARSE_KTILE = 64
+
+
+def sparse_mask_shape(B: int, H: int, C: int, N: int, w: int):
+    """Shape [B, H, N, nqt, nkt] of the block mask of hybrid_fwd_sparse."""
+    nqt = -(-C // SPARSE_QTILE)
+    wl = min(w, N) if w > 0 else 0
+    return (B, H, N, nqt, -(-(wl * C) // SPARSE_KTILE))
+
+
+def hybrid_fwd_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
+                      C: int, w: int, block_mask: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """rha_hybrid_fwd_sparse: hybrid_fwd with pruned (query block, key block)
+    pairs of the window; block_mask is uint8 [B,H,N,nqt,nkt] (sparse_mask_shape)."""
+    if out is None:
+        out = torch.empty_like(q)
+    _same_layout(q, k, v, out)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S, z must be float32 [B,H,N,d,d] and [B,H,N,d]")
+    if not (S.is_contiguous() and z.is_contiguous()):
+        raise ValueError("S and z must be contiguous")
+    if (tuple(block_mask.shape) != sparse_mask_shape(B, H, C, N, w) or block_mask.dtype != torch.uint8
+            or not block_mask.is_contiguous() or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be contiguous uint8 {sparse_mask_shape(B, H, C, N, w)} on q's device")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    prob = _problem(q, C, w, N)
+    _check(lib().rha_hybrid_fwd_sparse(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                                       _ptr(block_mask), _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -225,6 +225,54 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
   return ok();
 }
 
+static_assert(RHA_SPARSE_QTILE == rha::kQb2RowsPerTile && RHA_SPARSE_KTILE == 64 &&
+                  RHA_SPARSE_MAX_KTILES == rha::kSparseMaxKeyTiles,
+              "block sizes of the pruned window are the d = 128 kernel's tiles");
+
+rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                                 const float* z, const uint8_t* block_mask, void* out, float* lse, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (p->dtype != RHA_BF16 || p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "pruned windows need dtype RHA_BF16 and head_dim 128");
+  if (p->window == 0) return rha_hybrid_fwd(p, q, k, v, S, z, out, lse, stream);
+  const int64_t wl = p->window < p->n_chunks ? p->window : p->n_chunks;
+  const int64_t nkt = (wl * p->chunk_len + RHA_SPARSE_KTILE - 1) / RHA_SPARSE_KTILE;
+  if (nkt > RHA_SPARSE_MAX_KTILES)
+    return fail(RHA_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)nkt, RHA_SPARSE_MAX_KTILES);
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(q, "q"));
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S, "S"));
+  RHA_TRY(need(z, "z"));
+  RHA_TRY(need(block_mask, "block_mask", true, 1));
+  RHA_TRY(need(out, "out"));
+  if (lse != nullptr) RHA_TRY(need(lse, "lse", true, 4));
+  rha::FwdParams f{};
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.out = out;
+  f.lse = lse;
+  f.S = S;
+  f.z = z;
+  f.q_sb = f.kv_sb = p->stride_b;
+  f.q_sh = f.kv_sh = p->stride_h;
+  f.q_st = f.kv_st = p->stride_t;
+  f.B = p->batch;
+  f.H = p->heads;
+  f.C = p->chunk_len;
+  f.w = p->window;
+  f.n_qchunks = p->n_chunks;
+  f.stream_mode = 0;
+  f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  f.kmask = block_mask;
+  f.nkt = (int)nkt;
+  hipError_t e = launch_fwd(p, f, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
 size_t rha_stream_workspace_size(const rha_problem* p) {
   if (p == nullptr || check_problem(p, true) != RHA_OK || empty(p, true)) return 0;
   // the split window's partial results, and later in the step the split

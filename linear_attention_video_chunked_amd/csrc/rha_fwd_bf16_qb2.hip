@@ -85,14 +85,18 @@ __shared__ __attribute__((aligned(1024))) unsigned char q2_kb0[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_kb1[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_vb0[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_vb1[Q2_TILE];
+// kept key tiles of a pruned pass, in order, then one past the window
+__shared__ int q2_act[kSparseMaxKeyTiles + 1];
+__shared__ int q2_act_n;
 
 // One pass over a tile, output included.  FIRST: references start at 0 (with
 // linear state) or -inf and blocks are checked against the bound; returns
 // nonzero where a reference moved after accumulation.  Otherwise references
 // start at mio and no block is checked.  mio receives the final references.
-template <int D, int NW, bool FIRST, bool PARTIAL>
+template <int D, int NW, bool FIRST, bool PARTIAL, bool SPARSE>
 __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]) {
   static_assert(D == Q2_D, "tile buffers are sized for head dimension 128");
+  static_assert(!(PARTIAL && SPARSE), "pruned passes are not split");
   constexpr int THREADS = NW * 64, QB = Q2_QB, BM = NW * 32 * Q2_QB;
   constexpr int DS = D / 16, DB = D / 32, GR = D / 8;
   constexpr int TILE = BN * D * 2;
@@ -159,6 +163,35 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     zp = p.z + (int64_t)bh * D;
   }
   const int T = (int)((kend - kbeg + BN - 1) / BN);  // LDS tiles in the window
+
+  // Pruned pass: the kept key tiles of this query tile, listed in order by
+  // wave 0 (ballot + prefix count over the mask row), followed by T (one tile
+  // past the window, which loads as zeros).  The pipeline then visits Tp tiles;
+  // act(t) is the window tile that visit t loads.
+  int Tp = T;
+  if constexpr (SPARSE) {
+    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.tiles_per_chunk + tile) * p.nkt;
+    if (wave == 0) {
+      int base = 0;
+      for (int j0 = 0; j0 < T; j0 += 64) {
+        const int j = j0 + lane;
+        const bool keep = j < T && mrow[j] != 0;
+        const uint64_t bal = __ballot(keep);
+        if (keep) q2_act[base + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+        base += __popcll(bal);
+      }
+      if (lane == 0) {
+        q2_act[base] = T;
+        q2_act_n = base;
+      }
+    }
+    __syncthreads();
+    Tp = q2_act_n;
+  }
+  auto act = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return q2_act[t];
+    else return t;
+  };
 
   // ---- tile loads: direct HBM -> LDS (buffer loads with the LDS flag).  One
   // such load moves 64 lanes x 16 bytes into 1 KiB of consecutive LDS (lane L
@@ -285,7 +318,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // keys of block blk inside the window (<= 0 for the second block of a last
   // tile that holds at most 32 keys)
   auto block_valid = [&](int blk) __attribute__((always_inline)) {
-    return (int)min((int64_t)32, kend - (kbeg + (int64_t)blk * 32));
+    const int real = 2 * act(blk >> 1) + (blk & 1);  // block of the window
+    return (int)min((int64_t)32, kend - (kbeg + (int64_t)real * 32));
   };
   // Tile buffers by tile index t + AHEAD.  PAR is the parity of t when known
   // at compile time (0 or 1; -1 if not); then every LDS address folds into a
@@ -421,12 +455,13 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       for (int i = 0; i < 16; ++i)
         if (8 * (i >> 2) + (i & 3) >= vrel) acc[x][i] = -INFINITY;
   };
-  // Tile loads of a period's first step, one per round: K tile t+1 and V
-  // tile t (their buffers were last read in period t-1).
-  auto stage_op = [&](auto j_c, auto par_c, int t) __attribute__((always_inline)) {
+  // Tile loads of a period's first step, one per round: K of visit t+1 and
+  // V of visit t (their buffers were last read in period t-1); tk, tv are the
+  // window tiles of those visits.
+  auto stage_op = [&](auto j_c, auto par_c, int t, int tk, int tv) __attribute__((always_inline)) {
     constexpr int j = decltype(j_c)::value;
-    if constexpr (j < LPW) dma_k(kbuf(par_c, t, A1{}), t + 1, j);
-    else dma_v(vbuf(par_c, t, A0{}), t, j - LPW);
+    if constexpr (j < LPW) dma_k(kbuf(par_c, t, A1{}), tk, j);
+    else dma_v(vbuf(par_c, t, A0{}), tv, j - LPW);
   };
 
   // One step.  F: flags; BASE: ring slot of round 0; CHECK: test the softmax
@@ -435,7 +470,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   enum : int { kQK = 1, kSM = 2, kPV = 4, kMASK = 8, kSTAGE = 16, kPRE_K = 32, kPRE_V = 64 };
   auto step = [&](auto f_c, auto base_c, auto par_c, auto check_c, int t, const unsigned char* kt, int qh,
                   f32x16 (&acc_next)[QB], f32x16 (&acc_cur)[QB], bf16x2 (&pk_cur)[QB][8], int valid,
-                  const unsigned char* vt, int vh, const bf16x2 (&pk_prev)[QB][8]) __attribute__((always_inline)) {
+                  const unsigned char* vt, int vh, const bf16x2 (&pk_prev)[QB][8], int tk, int tv)
+                  __attribute__((always_inline)) {
     constexpr int F = decltype(f_c)::value, base = decltype(base_c)::value;
     constexpr bool QK = F & kQK, SM = F & kSM, PV = F & kPV, CHECK = decltype(check_c)::value;
     if constexpr (SM && (F & kMASK)) {
@@ -475,7 +511,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       }
       if constexpr ((F & kSTAGE) != 0) {
         static_for<0, LPW / 4>([&](auto o_c) __attribute__((always_inline)) {
-          stage_op(std::integral_constant<int, r * (LPW / 4) + decltype(o_c)::value>{}, par_c, t);
+          stage_op(std::integral_constant<int, r * (LPW / 4) + decltype(o_c)::value>{}, par_c, t, tk, tv);
         });
       }
       if constexpr (SM) sm_slice(std::integral_constant<int, 2 * r + 1>{}, A0{}, acc_cur, pk_cur);
@@ -507,6 +543,11 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     constexpr int FA = FA0 | ((FB & kQK) ? kPRE_K : 0) | ((FB & kPV) ? kPRE_V : 0);
     const unsigned char* kt = kbuf(par_c, t, A0{});
     const unsigned char* vprev = vbuf(par_c, t, Am1{});
+    int tk = t + 1, tv = t;  // window tiles staged in this period
+    if constexpr (SPARSE && ((FA0 & kSTAGE) != 0)) {
+      tk = act(t + 1);
+      tv = act(t);
+    }
     if constexpr ((FA & kQK) != 0) {
       kf[0] = read_k(kt, 0, 0);
       kf[1] = read_k(kt, 0, 1);
@@ -516,9 +557,10 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       vf[1] = read_v(vprev, 0, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    step(std::integral_constant<int, FA>{}, A0{}, par_c, check_c, t, kt, 0, sacc[0], sacc[1], pk[1], valid_a, vprev, 0, pk[0]);
+    step(std::integral_constant<int, FA>{}, A0{}, par_c, check_c, t, kt, 0, sacc[0], sacc[1], pk[1], valid_a, vprev, 0, pk[0],
+         tk, tv);
     step(std::integral_constant<int, FB>{}, std::integral_constant<int, 2>{}, par_c, check_c, t, kt, 1, sacc[1], sacc[0], pk[0],
-         valid_b, vprev, 1, pk[1]);
+         valid_b, vprev, 1, pk[1], tk, tv);
   };
   using C0 = std::integral_constant<int, kQK | kSTAGE>;
   using C1 = std::integral_constant<int, kQK | kSM | kMASK>;
@@ -535,7 +577,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
     // prologue: K tile 0 into LDS
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_k(kb0, 0, i);
+    for (int i = 0; i < LPW; ++i) dma_k(kb0, act(0), i);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
@@ -543,26 +585,26 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     // steady state: every block of K tile t and V tile t-1 is full; two
     // periods per iteration so the buffer parity is known
     int t = 1;
-    for (; t + 2 < T; t += 2) {
+    for (; t + 2 < Tp; t += 2) {
       period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
       __syncthreads();
       period(t + 1, A0{}, check_c, CA{}, CB{}, 32, 32);
       __syncthreads();
     }
-    if (t + 1 < T) {
+    if (t + 1 < Tp) {
       period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
       __syncthreads();
     }
-    if (T > 1) {  // period T-1: the last K tile (may be partial)
-      period(T - 1, Am1{}, check_c, CA{}, CBm{}, 32, block_valid(2 * T - 2));
+    if (Tp > 1) {  // period Tp-1: the last K tile (may be partial)
+      period(Tp - 1, Am1{}, check_c, CA{}, CBm{}, 32, block_valid(2 * Tp - 2));
       __syncthreads();
     }
-    // period T: softmax of the last block, P V of the last V tile
-    period(T, Am1{}, check_c, CTa{}, CTb{}, block_valid(2 * T - 1), 32);
+    // period Tp: softmax of the last block, P V of the last V tile
+    period(Tp, Am1{}, check_c, CTa{}, CTb{}, block_valid(2 * Tp - 1), 32);
   };
 
   init_acc();
-  if (T > 0) pipeline(std::integral_constant<bool, FIRST>{});
+  if (Tp > 0) pipeline(std::integral_constant<bool, FIRST>{});
 
   if constexpr (PARTIAL) {
     // ---- partial results: unnormalised numerator rows, denominator, reference
@@ -595,7 +637,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float ltot = half_sum(lsum[qb]);
-      const float inv = 1.0f / ltot;
+      // (a pruned pass can leave a row with no weight at all: output 0)
+      const float inv = SPARSE ? (ltot > 0.f ? 1.0f / ltot : 0.f) : 1.0f / ltot;
       const int r = qb * 32 + l32;  // row within the wave's 64
 #pragma unroll
       for (int nb = 0; nb < DB; ++nb)
@@ -631,21 +674,21 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 
 // The rare second pass, kept out of line so that its registers do not add to
 // the first pass's.
-template <int D, int NW, bool PARTIAL>
+template <int D, int NW, bool PARTIAL, bool SPARSE>
 __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float m1) {
   float m[Q2_QB] = {m0, m1};
-  tile_pass<D, NW, false, PARTIAL>(p, m);
+  tile_pass<D, NW, false, PARTIAL, SPARSE>(p, m);
 }
 
-template <int D, int NW, bool PARTIAL>
+template <int D, int NW, bool PARTIAL, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
   float m[Q2_QB];
-  const int dirty = tile_pass<D, NW, true, PARTIAL>(p, m);
+  const int dirty = tile_pass<D, NW, true, PARTIAL, SPARSE>(p, m);
   // Every wave reaches this barrier.  Where some query's reference moved after
   // accumulation, the whole tile is computed again with the final references
   // (which no score exceeds by the bound); its output replaces the first.
-  if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL>(p, m[0], m[1]);
+  if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL, SPARSE>(p, m[0], m[1]);
 }
 
 // Merge of a split pass: per query row, the partial numerators and
@@ -691,9 +734,11 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk * splits;
   if (p.total_tiles == 0) return hipSuccess;
   if (splits > 1)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+  else if (p.kmask != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, true>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -42,7 +42,16 @@ struct FwdParams {
   // number of pidx values.  launch_fwd_combine merges them into out and lse.
   int n_splits;
   float* part;
+  // Pruned key tiles (seq mode, head_dim 128 bf16 only): with kmask set,
+  // query tile i of chunk c of head bh visits only key tile j of its window
+  // (keys kbeg + 64 j ..) where kmask[((bh * n_qchunks + c) * tiles_per_chunk
+  // + i) * nkt + j] != 0.
+  const unsigned char* kmask;
+  int nkt;
 };
+
+// Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).
+constexpr int kSparseMaxKeyTiles = 2048;
 
 // Per-chunk state contribution phi(K_c)^T V_c, sum_t phi(k_t) for a list of
 // chunks, written to (or, with accumulate, added into) float32 state slots.

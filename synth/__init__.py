@@ -5,6 +5,6 @@ HIP side (tests, bench) and by nothing else.  It holds no arithmetic of the
 attention method: it only draws Gaussian tensors and rounds them to the
 storage dtype the kernels read, so that both sides see bit-identical inputs.
 """
-from .workloads import CONFIGS, Workload, gen_head, gen_qkv, to_storage
+from .workloads import CONFIGS, Workload, gen_block_mask, gen_head, gen_qkv, to_storage
 
-__all__ = ["CONFIGS", "Workload", "gen_head", "gen_qkv", "to_storage"]
+__all__ = ["CONFIGS", "Workload", "gen_block_mask", "gen_head", "gen_qkv", "to_storage"]

@@ -101,3 +101,11 @@ def gen_qkv(wl: Workload, L: Optional[int] = None):
         heads = [gen_head(wl, name, b, h, L) for b in range(wl.B) for h in range(wl.H)]
         out.append(torch.stack(heads).reshape(wl.B, wl.H, L, wl.d))
     return tuple(out)
+
+
+def gen_block_mask(shape, density: float, seed: int) -> torch.Tensor:
+    """Seeded 0/1 uint8 mask (CPU) of the given shape: each entry kept with
+    probability ``density`` -- a stand-in for a block-importance criterion,
+    which the pages do not give."""
+    rng = np.random.default_rng(np.random.SeedSequence([9000, seed]))
+    return torch.from_numpy((rng.random(tuple(shape)) < density).astype(np.uint8))

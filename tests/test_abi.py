@@ -184,3 +184,24 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_rha, "_lib", None)
     with pytest.raises(_rha.LibraryNotBuilt):
         _rha.lib()
+
+
+def _sparse(L, prob, mask=P, q=P, k=P, v=P, S=P, z=P, out=P, lse=None):
+    return L.rha_hybrid_fwd_sparse(ctypes.byref(prob), q, k, v, S, z, mask, out, lse, None)
+
+
+def test_sparse_window_checks(L):
+    # pruned windows: bf16 with head_dim 128 only, a mask, and at most 2048 key blocks per window
+    assert _sparse(L, _prob(dtype=_rha.RHA_F32, stride_t=128)) == 2
+    assert _sparse(L, _prob(head_dim=64, stride_t=64)) == 2
+    assert "RHA_BF16" in L.rha_last_error().decode()
+    assert _sparse(L, _prob(), mask=None) == 1
+    assert "block_mask" in L.rha_last_error().decode()
+    assert _sparse(L, _prob(chunk_len=4096 * 16, n_chunks=4, window=3, stride_b=0, stride_h=0)) == 2
+    assert "key blocks" in L.rha_last_error().decode()
+    assert _sparse(L, _prob(), q=None) == 1
+    assert _sparse(L, _prob(window=-1)) == 1
+    # the binding's mask shape: [B, H, N, ceil(C / 256), ceil(min(w, N) * C / 64)]
+    assert _rha.sparse_mask_shape(1, 12, 1560, 21, 3) == (1, 12, 21, 7, 74)
+    assert _rha.sparse_mask_shape(2, 3, 100, 4, 9) == (2, 3, 4, 1, 7)
+    assert _rha.sparse_mask_shape(1, 1, 64, 4, 0) == (1, 1, 4, 1, 0)

@@ -1,0 +1,41 @@
+"""Host-side checks of bench.py's algorithmic counts (no GPU): the Wan-1.3B
+figures the roofline divides by, and the pruned-window count."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from synth import CONFIGS  # noqa: E402
+
+
+def test_wan13b_counts():
+    wl = CONFIGS["wan13b"]
+    BH = wl.B * wl.H
+    assert bench.fwd_flops(wl.C, wl.N, wl.w, wl.d, BH) == 908_250_071_040
+    assert bench.fwd_bytes(wl.C, wl.N, wl.w, wl.d, BH) == 416_821_248
+    assert abs(bench.scan_bytes(wl.C, wl.N, wl.w, wl.d, BH) / 1e6 - 189.2) < 0.1
+
+
+def test_sparse_count_all_kept_equals_dense_and_scales():
+    C, N, w, d, B, H = 300, 5, 2, 128, 1, 2
+    nqt, nkt = -(-C // 256), -(-(w * C) // 64)
+    ones = np.ones((B, H, N, nqt, nkt), np.uint8)
+    dense = bench.fwd_flops(C, N, w, d, B * H)
+    assert bench.sparse_fwd_flops(C, N, w, d, ones) == dense
+    zeros = np.zeros_like(ones)
+    lin = bench.sparse_fwd_flops(C, N, w, d, zeros)
+    assert lin == sum(C * (2 * d * d + 2 * d) for c in range(N) if c >= w) * B * H
+    # dropping one full key block of one query block removes rows * 64 * 4d
+    m = ones.copy()
+    m[0, 0, 3, 0, 2] = 0
+    assert dense - bench.sparse_fwd_flops(C, N, w, d, m) == 256 * 64 * 4 * d
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
