@@ -23,6 +23,13 @@ from .rha_oracle import (
     hybrid_block_sparse,
     hybrid_block_sparse_rows,
     hybrid_block_sparse_batched,
+    window_range_bidir,
+    brute_bidir,
+    state_scan_bidir,
+    hybrid_bidir,
+    hybrid_bidir_rows,
+    hybrid_bidir_batched,
+    state_scan_bidir_batched,
 )
 
 __all__ = [
@@ -41,4 +48,11 @@ __all__ = [
     "hybrid_block_sparse",
     "hybrid_block_sparse_rows",
     "hybrid_block_sparse_batched",
+    "window_range_bidir",
+    "brute_bidir",
+    "state_scan_bidir",
+    "hybrid_bidir",
+    "hybrid_bidir_rows",
+    "hybrid_bidir_batched",
+    "state_scan_bidir_batched",
 ]

@@ -346,3 +346,133 @@ def hybrid_block_sparse_batched(q, k, v, C: int, w: int, mask, return_den: bool 
             out[b, h], den[b, h] = hybrid_block_sparse(q[b, h], k[b, h], v[b, h], C, w, mask[b, h],
                                                        return_den=True, **tiles)
     return (out, den) if return_den else out
+
+
+# ---------------------------------------------------------------- bidirectional hybrid
+#
+# "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers",
+# abstract: the hybrid replaces the softmax attention of video diffusion
+# transformers, whose attention is bidirectional over the whole clip.  Reading
+# taken for the bidirectional form: the softmax window is symmetric around the
+# query's chunk, and every chunk outside it -- before or after -- is folded
+# into the linear term, so that a window covering every chunk is plain dense
+# (unmasked) softmax attention and window 0 is plain (non-causal) linear
+# attention:
+#
+#     W(i) = { j : |floor(j/C) - c| <= w - 1 }           (empty if w == 0)
+#     H(i) = every other key
+#
+# The linear term splits into a past part and a future part:
+#     S_pre_c = sum_{c' <= c - w} U_c'   (with w = 0: c' <= c, own chunk included)
+#     S_suf_c = sum_{c' >= c + max(w, 1)} U_c'
+# and likewise z.  out_i = (sum_W e^s v + phi(q_i)^T (S_pre_c + S_suf_c)) /
+# (sum_W e^s + phi(q_i) . (z_pre_c + z_suf_c)).
+
+
+def window_range_bidir(c: int, w: int, N: int):
+    """Chunks [lo, hi] of the symmetric softmax window of chunk c (empty if w == 0)."""
+    if w <= 0:
+        return c + 1, c
+    return max(0, c - w + 1), min(N - 1, c + w - 1)
+
+
+def brute_bidir(q, k, v, C: int, w: int, return_den: bool = False):
+    """The bidirectional definition as one L x L weight matrix (tiny inputs only)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L = q.shape[0]
+    cid = np.arange(L) // C
+    dist = np.abs(cid[None, :] - cid[:, None])
+    in_window = dist <= w - 1 if w > 0 else np.zeros((L, L), bool)
+    a = np.where(in_window, np.exp(_scores(q, k)), phi(q) @ phi(k).T)
+    den = a.sum(axis=1)
+    out = (a @ v) / den[:, None]
+    return (out, den) if return_den else out
+
+
+def state_scan_bidir(k, v, C: int, w: int):
+    """Past and future states of every chunk: (S_pre, z_pre, S_suf, z_suf)."""
+    U, u = chunk_states(k, v, C)
+    N = U.shape[0]
+    S_pre, z_pre = state_scan(k, v, C, w)
+    S_suf, z_suf = np.zeros_like(U), np.zeros_like(u)
+    first = max(w, 1)
+    for c in range(N):
+        if c + first <= N - 1:
+            S_suf[c] = U[c + first:].sum(axis=0)
+            z_suf[c] = u[c + first:].sum(axis=0)
+    return S_pre, z_pre, S_suf, z_suf
+
+
+def hybrid_bidir(q, k, v, C: int, w: int, return_den: bool = False):
+    """Chunked evaluation of the bidirectional definition (one head)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L, d = q.shape
+    N = L // C
+    S_pre, z_pre, S_suf, z_suf = state_scan_bidir(k, v, C, w)
+    fq = phi(q)
+    out = np.empty((L, v.shape[1]))
+    den_all = np.empty(L)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        num = fq[rows] @ (S_pre[c] + S_suf[c])
+        den = fq[rows] @ (z_pre[c] + z_suf[c])
+        lo, hi = window_range_bidir(c, w, N)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            e = np.exp(_scores(q[rows], k[keys]))
+            num = num + e @ v[keys]
+            den = den + e.sum(axis=1)
+        out[rows] = num / den[:, None]
+        den_all[rows] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_bidir_rows(q, k, v, C: int, w: int, rows, states=None, return_den: bool = False):
+    """The bidirectional definition for selected rows; states from state_scan_bidir."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    N = q.shape[0] // C
+    S_pre, z_pre, S_suf, z_suf = states if states is not None else state_scan_bidir(k, v, C, w)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]))
+    den_all = np.empty(rows.size)
+    for n, r in enumerate(rows):
+        r = int(r)
+        c = r // C
+        fq = phi(q[r])
+        num = fq @ (S_pre[c] + S_suf[c])
+        den = fq @ (z_pre[c] + z_suf[c])
+        lo, hi = window_range_bidir(c, w, N)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            e = np.exp(_scores(q[r : r + 1], k[keys]))[0]
+            num = num + e @ v[keys]
+            den = den + e.sum()
+        out[n] = num / den
+        den_all[n] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_bidir_batched(q, k, v, C: int, w: int, return_den: bool = False):
+    """``hybrid_bidir`` over [B, H, L, d]."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    den = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], den[b, h] = hybrid_bidir(q[b, h], k[b, h], v[b, h], C, w, return_den=True)
+    return (out, den) if return_den else out
+
+
+def state_scan_bidir_batched(k, v, C: int, w: int):
+    """``state_scan_bidir`` over [B, H, L, d]: four arrays [B, H, N, ...]."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    B, H, L, d = k.shape
+    N = L // C
+    res = [np.empty((B, H, N, d, v.shape[-1])), np.empty((B, H, N, d)),
+           np.empty((B, H, N, d, v.shape[-1])), np.empty((B, H, N, d))]
+    for b in range(B):
+        for h in range(H):
+            for arr, val in zip(res, state_scan_bidir(k[b, h], v[b, h], C, w)):
+                arr[b, h] = val
+    return tuple(res)

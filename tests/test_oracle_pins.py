@@ -412,3 +412,80 @@ def test_block_sparse_drops_exactly_the_block():
         lin = O.phi(k[hist]) @ O.phi(q[r])
         ref = (e @ v[keys] + lin @ v[hist]) / (e.sum() + lin.sum())
         np.testing.assert_allclose(out[r], ref, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- bidirectional hybrid
+# (ReHyAt abstract: the hybrid stands in for the bidirectional attention of
+# video diffusion transformers).  Reading: symmetric window, everything outside
+# it -- past and future -- in the linear term.  Pinned to brute force, to
+# unmasked SDPA when the window covers every chunk, to non-causal linear
+# attention (the token RNN's final state) at w = 0, to the causal hybrid on the
+# last chunk, to time reversal, and by a scan identity.
+
+BIDIR_SWEEP = [(C, N, w, d) for C, N in ((1, 7), (3, 4), (5, 3), (16, 5)) for w in (0, 1, 2, 3, N + 1)
+               for d in (4, 32)]
+
+
+@pytest.mark.parametrize("C,N,w,d", BIDIR_SWEEP)
+def test_bidir_brute_equals_chunked(C, N, w, d):
+    q, k, v = _qkv(C * N, d, 900 + 10 * C + N + w, qs=1.5)
+    a, da = O.brute_bidir(q, k, v, C, w, return_den=True)
+    b, db = O.hybrid_bidir(q, k, v, C, w, return_den=True)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(db, da, rtol=1e-12)
+    rows = np.arange(0, C * N, 3)
+    r, dr = O.hybrid_bidir_rows(q, k, v, C, w, rows, return_den=True)
+    np.testing.assert_allclose(r, a[rows], rtol=1e-12, atol=1e-12)
+
+
+def test_bidir_window_all_is_unmasked_sdpa():
+    C, N = 24, 5
+    q, k, v = _qkv(C * N, 32, 910, qs=2.0)
+    ref = _sdpa(q, k, v)
+    for w in (N, N + 2):
+        np.testing.assert_allclose(O.hybrid_bidir(q, k, v, C, w), ref, atol=1e-12)
+        np.testing.assert_allclose(O.brute_bidir(q, k, v, C, w), ref, atol=1e-12)
+
+
+def test_bidir_window0_is_noncausal_linear_attention():
+    # the token-by-token recurrence with one "chunk" spanning the whole
+    # sequence absorbs every token before any query reads the state: plain
+    # non-causal linear attention
+    for C, N in ((1, 40), (6, 5)):
+        q, k, v = _qkv(C * N, 8, 920 + C)
+        ref = _linear_rnn(q, k, v, C * N)
+        np.testing.assert_allclose(O.hybrid_bidir(q, k, v, C, 0), ref, rtol=1e-12)
+        np.testing.assert_allclose(O.brute_bidir(q, k, v, C, 0), ref, rtol=1e-12)
+
+
+def test_bidir_last_chunk_equals_causal():
+    C, N = 7, 6
+    q, k, v = _qkv(C * N, 16, 930, qs=1.5)
+    last = slice((N - 1) * C, N * C)
+    for w in (0, 1, 2, 4):
+        np.testing.assert_allclose(O.hybrid_bidir(q, k, v, C, w)[last], O.hybrid(q, k, v, C, w)[last], rtol=1e-12)
+
+
+def test_bidir_time_reversal():
+    C, N = 5, 6
+    q, k, v = _qkv(C * N, 8, 940, qs=1.5)
+    for w in (0, 1, 2, 3):
+        fwd = O.hybrid_bidir(q, k, v, C, w)
+        rev = O.hybrid_bidir(q[::-1].copy(), k[::-1].copy(), v[::-1].copy(), C, w)
+        np.testing.assert_allclose(rev[::-1], fwd, rtol=1e-12)
+
+
+def test_bidir_scan_identity():
+    # past + future + window contributions = the whole sequence's phi(K)^T V, for every chunk
+    C, N = 4, 7
+    _, k, v = _qkv(C * N, 6, 950)
+    U, u = O.chunk_states(k, v, C)
+    tot = O.phi(k).T @ v
+    for w in (0, 1, 2, 5, 9):
+        Sp, zp, Ss, zs = O.state_scan_bidir(k, v, C, w)
+        for c in range(N):
+            lo, hi = O.window_range_bidir(c, w, N)
+            win = U[lo:hi + 1].sum(axis=0) if lo <= hi else 0.0
+            np.testing.assert_allclose(Sp[c] + Ss[c] + win, tot, rtol=1e-12, atol=1e-12)
+            if w == 0:
+                np.testing.assert_allclose(Sp[c], U[: c + 1].sum(axis=0), rtol=1e-12)
