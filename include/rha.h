@@ -155,6 +155,33 @@ rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void
                                  float* lse, void* stream);
 
 /*
+ * Bidirectional hybrid -- rha_state_scan_bidir and rha_hybrid_fwd_bidir.
+ *
+ * ReHyAt (abstract): the hybrid takes the place of the softmax attention of
+ * video diffusion transformers, which attend over the whole clip in both
+ * directions.  Here the softmax window of chunk c is symmetric,
+ *   chunks max(0, c-w+1) .. min(N-1, c+w-1)      (none if w == 0),
+ * and every chunk outside it, before or after, is in the linear term with the
+ * shared normaliser: S = S_past[c] + S_future[c], z = z_past[c] + z_future[c],
+ *   S_past[c]   = sum over chunks j <= c - w          (w == 0: j <= c)
+ *   S_future[c] = sum over chunks j >= c + max(w, 1)
+ * of phi(K_j)^T V_j (z: of sum phi(k)).  A window covering every chunk is
+ * dense unmasked softmax attention; w == 0 is non-causal linear attention.
+ *
+ *   S_past, S_future : [B, H, N, d, d] float32 contiguous
+ *   z_past, z_future : [B, H, N, d]    float32 contiguous
+ *   other arguments as for rha_state_scan / rha_hybrid_fwd (the scan writes
+ *   the four state tensors, the forward pass reads them).
+ *
+ * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16 and head_dim is 128.
+ */
+rha_status rha_state_scan_bidir(const rha_problem* p, const void* k, const void* v, float* S_past,
+                                float* z_past, float* S_future, float* z_future, void* stream);
+rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void* k, const void* v,
+                                const float* S_past, const float* z_past, const float* S_future,
+                                const float* z_future, void* out, float* lse, void* stream);
+
+/*
  * Streaming cursor: the number of chunks committed so far, which is the
  * index of the chunk the next call processes.  Start at 0 with S, z zeroed.
  */

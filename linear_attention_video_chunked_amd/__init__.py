@@ -10,6 +10,7 @@ Functions mirror the C ABI in ``include/rha.h``:
 * ``state_scan(k, v, C, w)``                     -> S [B,H,N,d,d], z [B,H,N,d]
 * ``hybrid_fwd(q, k, v, S, z, C, w)``            -> out [B,H,L,d] (and lse)
 * ``hybrid_fwd_sparse(q, k, v, S, z, C, w, m)``  the same with pruned window blocks
+* ``state_scan_bidir`` / ``hybrid_fwd_bidir``     symmetric window, past + future states
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
 """
 from ._rha import (
@@ -17,11 +18,13 @@ from ._rha import (
     RhaError,
     StreamState,
     hybrid_fwd,
+    hybrid_fwd_bidir,
     hybrid_fwd_sparse,
     lib,
     lib_path,
     sparse_mask_shape,
     state_scan,
+    state_scan_bidir,
     stream_step,
     version,
 )
@@ -31,11 +34,13 @@ __all__ = [
     "RhaError",
     "StreamState",
     "hybrid_fwd",
+    "hybrid_fwd_bidir",
     "hybrid_fwd_sparse",
     "lib",
     "lib_path",
     "sparse_mask_shape",
     "state_scan",
+    "state_scan_bidir",
     "stream_step",
     "version",
 ]

@@ -65,11 +65,14 @@ def lib():
     L.rha_state_scan.argtypes = [P, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_fwd_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_state_scan_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_hybrid_fwd_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
     L.rha_stream_workspace_size.restype = ctypes.c_size_t
-    for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_stream_step"):
+    for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
+                 "rha_hybrid_fwd_bidir", "rha_stream_step"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
     L.rha_status_string.restype = ctypes.c_char_p
@@ -165,6 +168,51 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     prob = _problem(q, C, w, N)
     _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
                                 _ptr(lse), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def state_scan_bidir(k: torch.Tensor, v: torch.Tensor, C: int, w: int, stream=None):
+    """rha_state_scan_bidir -> (S_past, z_past, S_future, z_future), float32 [B,H,N,d,d] / [B,H,N,d]."""
+    _same_layout(k, v)
+    B, H, L, d = k.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    st = [torch.empty((B, H, N, d, d), dtype=torch.float32, device=k.device),
+          torch.empty((B, H, N, d), dtype=torch.float32, device=k.device),
+          torch.empty((B, H, N, d, d), dtype=torch.float32, device=k.device),
+          torch.empty((B, H, N, d), dtype=torch.float32, device=k.device)]
+    prob = _problem(k, C, w, N)
+    _check(lib().rha_state_scan_bidir(ctypes.byref(prob), _ptr(k), _ptr(v), *(_ptr(x) for x in st),
+                                      _stream(stream)))
+    return tuple(st)
+
+
+def hybrid_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, states, C: int, w: int,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = False, stream=None):
+    """rha_hybrid_fwd_bidir: symmetric window + past and future linear states
+    (``states`` as returned by state_scan_bidir for the same window)."""
+    if out is None:
+        out = torch.empty_like(q)
+    _same_layout(q, k, v, out)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    Sp, zp, Sf, zf = states
+    for S, z in ((Sp, zp), (Sf, zf)):
+        if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+            raise ValueError("states must be float32 [B,H,N,d,d] and [B,H,N,d]")
+        if not (S.is_contiguous() and z.is_contiguous()):
+            raise ValueError("states must be contiguous")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    prob = _problem(q, C, w, N)
+    _check(lib().rha_hybrid_fwd_bidir(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(Sp), _ptr(zp), _ptr(Sf),
+                                      _ptr(zf), _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -225,6 +225,89 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
   return ok();
 }
 
+rha_status rha_state_scan_bidir(const rha_problem* p, const void* k, const void* v, float* S_past, float* z_past,
+                                float* S_future, float* z_future, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (p->dtype != RHA_BF16 || p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "bidirectional problems need dtype RHA_BF16 and head_dim 128");
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S_past, "S_past"));
+  RHA_TRY(need(z_past, "z_past"));
+  RHA_TRY(need(S_future, "S_future"));
+  RHA_TRY(need(z_future, "z_future"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int N = p->n_chunks, w = p->window, d = p->head_dim;
+  const int lag_f = w > 0 ? w : 1;  // the future part starts at chunk c + max(w, 1)
+  if (w < N) {
+    // every chunk's contribution, into past slot j + w and future slot j - lag_f
+    rha::ChunkStateParams c = state_params(p, k, v, S_past, z_past);
+    c.chunk0 = 0;
+    c.n_chunks = N;
+    c.slot_offset = w;
+    c.accumulate = 0;
+    c.s_bh = (int64_t)N * d * d;
+    c.z_bh = (int64_t)N * d;
+    c.tok_end = (int64_t)N * p->chunk_len;
+    c.S2 = S_future;
+    c.z2 = z_future;
+    c.slot_offset2 = -lag_f;
+    c.n_slots = N;
+    hipError_t e = launch_chunk_state(p, c, s);
+    if (e != hipSuccess) return hip_fail(e, "chunk state launch");
+  }
+  rha::PrefixParams pp{S_past, z_past, p->batch * p->heads, N, w, d, 0};
+  hipError_t e = rha::launch_prefix(pp, s);
+  if (e != hipSuccess) return hip_fail(e, "prefix launch");
+  rha::PrefixParams ps{S_future, z_future, p->batch * p->heads, N, lag_f, d, 1};
+  e = rha::launch_prefix(ps, s);
+  if (e != hipSuccess) return hip_fail(e, "suffix launch");
+  return ok();
+}
+
+rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void* k, const void* v,
+                                const float* S_past, const float* z_past, const float* S_future,
+                                const float* z_future, void* out, float* lse, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (p->dtype != RHA_BF16 || p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "bidirectional problems need dtype RHA_BF16 and head_dim 128");
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(q, "q"));
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S_past, "S_past"));
+  RHA_TRY(need(z_past, "z_past"));
+  RHA_TRY(need(S_future, "S_future"));
+  RHA_TRY(need(z_future, "z_future"));
+  RHA_TRY(need(out, "out"));
+  if (lse != nullptr) RHA_TRY(need(lse, "lse", true, 4));
+  rha::FwdParams f{};
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.out = out;
+  f.lse = lse;
+  f.S = S_past;
+  f.z = z_past;
+  f.q_sb = f.kv_sb = p->stride_b;
+  f.q_sh = f.kv_sh = p->stride_h;
+  f.q_st = f.kv_st = p->stride_t;
+  f.B = p->batch;
+  f.H = p->heads;
+  f.C = p->chunk_len;
+  f.w = p->window;
+  f.n_qchunks = p->n_chunks;
+  f.stream_mode = 0;
+  f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  f.bidir = 1;
+  f.S2 = S_future;
+  f.z2 = z_future;
+  hipError_t e = launch_fwd(p, f, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
 static_assert(RHA_SPARSE_QTILE == rha::kQb2RowsPerTile && RHA_SPARSE_KTILE == 64 &&
                   RHA_SPARSE_MAX_KTILES == rha::kSparseMaxKeyTiles,
               "block sizes of the pruned window are the d = 128 kernel's tiles");

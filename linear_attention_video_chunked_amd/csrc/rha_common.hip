@@ -10,7 +10,9 @@ namespace {
 // chunk.  Slots c >= w hold per-chunk contributions on entry; on exit slot c
 // holds their running sum over slots w..c, i.e. the state of every chunk up to
 // c - w.  Slots c < w see no folded history and are zeroed.  Sequential float32
-// sum in chunk order, the same order the streaming fold uses.
+// sum in chunk order, the same order the streaming fold uses.  With reverse
+// the slots are walked from the last (the future part of a bidirectional
+// state: slot c sums the contributions stored in slots c .. N-1-w).
 // Each thread owns 4 consecutive floats of one head's S (or z) and walks the
 // slots in groups of 8: all loads of a group are issued before the running
 // sum touches them, so the HBM latency is paid once per group, not per slot.
@@ -28,6 +30,10 @@ __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
   } else {
     stride = p.d / 4;
     base = reinterpret_cast<f32x4*>(p.z) + bh * p.N * stride + (e4 - dd4);
+  }
+  if (p.reverse) {  // the same walk over slots N-1, N-2, .. 0 (a suffix)
+    base += (int64_t)(p.N - 1) * stride;
+    stride = -stride;
   }
   const int w = min(p.w, p.N);
   for (int c = 0; c < w; ++c) base[c * stride] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -134,19 +134,27 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh;
 
   int64_t kbeg, kend;
-  bool has_state;
+  bool has_state, has_past = true, has_future = false;
   const float* Sp;
   const float* zp;
+  const float* Sp2 = nullptr;  // future state (bidirectional)
+  const float* zp2 = nullptr;
   if (!p.stream_mode) {
     if (p.w > 0) {
       kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
-      kend = (int64_t)(c + 1) * p.C;
+      kend = (int64_t)(p.bidir ? min(p.n_qchunks, c + p.w) : c + 1) * p.C;
     } else {
       kbeg = kend = 0;
     }
-    has_state = (p.w == 0) || (c >= p.w);
+    has_past = (p.w == 0) || (c >= p.w);
+    has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
+    has_state = has_past || has_future;
     Sp = p.S + ((int64_t)bh * p.n_qchunks + c) * D * D;
     zp = p.z + ((int64_t)bh * p.n_qchunks + c) * D;
+    if (p.bidir) {
+      Sp2 = p.S2 + ((int64_t)bh * p.n_qchunks + c) * D * D;
+      zp2 = p.z2 + ((int64_t)bh * p.n_qchunks + c) * D;
+    }
   } else {
     kbeg = 0;
     kend = p.n_keys;
@@ -264,7 +272,12 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       const int eg = u / (D / 4), ng = u % (D / 4);
       f32x4 rows[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rows[i] = *reinterpret_cast<const f32x4*>(Sp + (int64_t)(eg * 8 + i) * D + ng * 4);
+      for (int i = 0; i < 8; ++i) {
+        rows[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (has_past) rows[i] = *reinterpret_cast<const f32x4*>(Sp + (int64_t)(eg * 8 + i) * D + ng * 4);
+        // bidirectional: the past and future states summed in float32 before rounding
+        if (has_future) rows[i] += *reinterpret_cast<const f32x4*>(Sp2 + (int64_t)(eg * 8 + i) * D + ng * 4);
+      }
       unsigned char* dst = eg < DS ? vb0 + (size_t)eg * D * 16 : vb1 + (size_t)(eg - DS) * D * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -288,8 +301,15 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
           f[2 * i] = phi(bf16_lo(qw[i]));
           f[2 * i + 1] = phi(bf16_hi(qw[i]));
         }
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8 + 4);
+        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+        if (has_past) {
+          z0 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8);
+          z1 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8 + 4);
+        }
+        if (has_future) {
+          z0 += *reinterpret_cast<const f32x4*>(zp2 + s * 16 + hh * 8);
+          z1 += *reinterpret_cast<const f32x4*>(zp2 + s * 16 + hh * 8 + 4);
+        }
         lz += f[0] * z0[0] + f[1] * z0[1] + f[2] * z0[2] + f[3] * z0[3] + f[4] * z1[0] + f[5] * z1[1] +
               f[6] * z1[2] + f[7] * z1[3];
         const u32x4 pw = {pack_bf16(f[0] * sc, f[1] * sc), pack_bf16(f[2] * sc, f[3] * sc),

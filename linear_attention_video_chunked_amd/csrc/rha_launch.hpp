@@ -48,6 +48,13 @@ struct FwdParams {
   // + i) * nkt + j] != 0.
   const unsigned char* kmask;
   int nkt;
+  // Bidirectional (seq mode, head_dim 128 bf16 only): the window of chunk c is
+  // chunks max(0, c-w+1) .. min(N-1, c+w-1), and the linear term adds the
+  // future state S2[bh, c], z2[bh, c] (chunks from c + max(w, 1) on) to the
+  // past state S, z.
+  int bidir;
+  const float* S2;
+  const float* z2;
 };
 
 // Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).
@@ -72,6 +79,13 @@ struct ChunkStateParams {
   int slot_offset;
   int accumulate;
   int64_t tok_end;  // (chunk0 + n_chunks) * C for whole chunks
+  // Optional second destination (S2, z2: same strides as S, z), written at
+  // slot j + slot_offset2.  With n_slots > 0, a destination slot outside
+  // [0, n_slots) is skipped (chunks whose contribution one side does not use).
+  float* S2;
+  float* z2;
+  int slot_offset2;
+  int n_slots;
 };
 
 // S[bh] += sum over g of part[bh][g] (g = 0 .. G-1 in order), likewise z:
@@ -86,10 +100,12 @@ struct StateCombineParams {
 // In-place inclusive prefix over the state slots of every head:
 //   slot c < w        -> 0
 //   slot c >= w       -> sum of the per-chunk contributions stored in slots w..c
+// With reverse, the same with slot c read as slot N-1-c (a suffix sum).
 struct PrefixParams {
   float* S;
   float* z;
   int BH, N, w, d;
+  int reverse;
 };
 
 // Copy one chunk [B,H,C,d] (strided) into cache slot `slot` of [B,H,w,C,d].

@@ -201,18 +201,25 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   if (j + 2 < ntiles) iter(j + 2, S2{});
 
   // U: acc[i] reg 4r+q <-> e = es*64 + eb*32 + 8r + 4hh + q, n = (nb0+i)*32 + l32
-  float* Sdst = p.S + (int64_t)bh * p.s_bh + (int64_t)(jc + p.slot_offset) * D * D;
+  const int slot1 = jc + p.slot_offset, slot2 = jc + p.slot_offset2;
+  const bool put1 = p.n_slots <= 0 || (slot1 >= 0 && slot1 < p.n_slots);
+  const bool put2 = p.S2 != nullptr && slot2 >= 0 && slot2 < p.n_slots;
+  auto store_u = [&](float* Sbase, int slot) {
+    float* Sdst = Sbase + (int64_t)bh * p.s_bh + (int64_t)slot * D * D;
 #pragma unroll
-  for (int i = 0; i < Cfg::NBW; ++i) {
-    const int n = (nb0 + i) * 32 + l32;
+    for (int i = 0; i < Cfg::NBW; ++i) {
+      const int n = (nb0 + i) * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = es * ESLICE + eb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      float* dst = Sdst + (int64_t)e * D + n;
-      const float val = acc[i][r];
-      *dst = p.accumulate ? *dst + val : val;
+      for (int r = 0; r < 16; ++r) {
+        const int e = es * ESLICE + eb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float* dst = Sdst + (int64_t)e * D + n;
+        const float val = acc[i][r];
+        *dst = p.accumulate ? *dst + val : val;
+      }
     }
-  }
+  };
+  if (put1) store_u(p.S, slot1);
+  if (put2) store_u(p.S2, slot2);
 
   // u: fixed-order reduction of the per-thread partial sums
 #pragma unroll
@@ -222,8 +229,14 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < THREADS / (ESLICE / 8); ++r) s += zred[r][tid];
-    float* zd = p.z + (int64_t)bh * p.z_bh + (int64_t)(jc + p.slot_offset) * D + es * ESLICE + tid;
-    *zd = p.accumulate ? *zd + s : s;
+    if (put1) {
+      float* zd = p.z + (int64_t)bh * p.z_bh + (int64_t)slot1 * D + es * ESLICE + tid;
+      *zd = p.accumulate ? *zd + s : s;
+    }
+    if (put2) {
+      float* zd = p.z2 + (int64_t)bh * p.z_bh + (int64_t)slot2 * D + es * ESLICE + tid;
+      *zd = p.accumulate ? *zd + s : s;
+    }
   }
 }
 

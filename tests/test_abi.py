@@ -205,3 +205,20 @@ def test_sparse_window_checks(L):
     assert _rha.sparse_mask_shape(1, 12, 1560, 21, 3) == (1, 12, 21, 7, 74)
     assert _rha.sparse_mask_shape(2, 3, 100, 4, 9) == (2, 3, 4, 1, 7)
     assert _rha.sparse_mask_shape(1, 1, 64, 4, 0) == (1, 1, 4, 1, 0)
+
+
+def test_bidir_checks(L):
+    # bidirectional calls: bf16 with head_dim 128 only; every state pointer required
+    args = [P] * 7
+    f32 = _prob(dtype=_rha.RHA_F32, stride_t=128)
+    assert L.rha_state_scan_bidir(ctypes.byref(f32), *args[:6], None) == 2
+    assert L.rha_hybrid_fwd_bidir(ctypes.byref(f32), *([P] * 9), None, None) == 2
+    assert "RHA_BF16" in L.rha_last_error().decode()
+    d64 = _prob(head_dim=64, stride_t=64)
+    assert L.rha_state_scan_bidir(ctypes.byref(d64), *args[:6], None) == 2
+    ok = _prob()
+    assert L.rha_state_scan_bidir(ctypes.byref(ok), P, P, P, P, None, P, None) == 1
+    assert "S_future" in L.rha_last_error().decode()
+    assert L.rha_hybrid_fwd_bidir(ctypes.byref(ok), P, P, P, P, P, P, None, P, None, None) == 1
+    assert "z_future" in L.rha_last_error().decode()
+    assert L.rha_hybrid_fwd_bidir(ctypes.byref(_prob(window=-2)), *([P] * 9), None, None) == 1
