@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -72,6 +72,20 @@ def sparse_fwd_flops(C, N, w, d, mask, qtile=256, ktile=64):
             if w == 0 or c >= w:
                 f += rows * (2 * d * d + 2 * d) * B * H
     return f
+
+
+def bidir_fwd_flops(C, N, w, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_fwd_bidir call: 4d per (query, key) in
+    the symmetric window, plus 2d^2 + 2d per query with any chunk outside it."""
+    f = 0
+    for c in range(N):
+        if w > 0:
+            lo, hi = max(0, c - w + 1), min(N - 1, c + w - 1)
+            nwin, outside = (hi - lo + 1) * C, lo > 0 or hi < N - 1
+        else:
+            nwin, outside = 0, True
+        f += C * (4 * d * nwin + ((2 * d * d + 2 * d) if outside else 0))
+    return f * BH
 
 
 def stream_step_flops(C, w, d, BH):
@@ -142,7 +156,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse"], default=None)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -217,6 +231,21 @@ def main():
         torch.cuda.synchronize()
         return
 
+    # ---- bidirectional hybrid at the same shape (window of 3 chunks each way)
+    def bidir_scan():
+        return rha.state_scan_bidir(k, v, wl.C, wl.w, stream=stream)
+
+    bstates = bidir_scan()
+
+    def bidir_call():
+        rha.hybrid_fwd_bidir(q, k, v, bstates, wl.C, wl.w, out=out, stream=stream)
+
+    if args.only == "bidir":
+        for _ in range(args.steps):
+            bidir_call()
+        torch.cuda.synchronize()
+        return
+
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
     def stream_run(timed_run):
         sw = CONFIGS["stream"]
@@ -264,6 +293,9 @@ def main():
     t_fwd = timed(lambda: rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream), n_k)
     t_scan = timed(lambda: rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream), n_k)
     t_sparse = timed(sparse_call, n_k)
+    t_bidir = timed(bidir_call, n_k)
+    t_bidir_scan = timed(bidir_scan, n_k)
+    bF = bidir_fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
 
     sw, t_stream = stream_run(True)
@@ -310,6 +342,10 @@ def main():
             "sparse_half_kept_frac": float(mask_cpu.float().mean()),
             "sparse_half_TFLOPs": spF / t_sparse / 1e12,
             "sparse_half_mfma_frac": spF / t_sparse / 1e12 / PEAK_BF16_TFLOPS,
+            "bidir_fwd_us": t_bidir * 1e6,
+            "bidir_TFLOPs": bF / t_bidir / 1e12,
+            "bidir_mfma_frac": bF / t_bidir / 1e12 / PEAK_BF16_TFLOPS,
+            "bidir_scan_us": t_bidir_scan * 1e6,
             "timed_wall_s": wall,
         },
     }

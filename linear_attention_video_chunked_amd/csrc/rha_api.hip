@@ -154,6 +154,8 @@ int fold_groups(const rha_problem* p, int* group_len) {
   return (int)g;
 }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 size_t fold_bytes(const rha_problem* p, int groups) {
   const int64_t d = p->head_dim;
   return (size_t)((int64_t)p->batch * p->heads * groups * (d * d + d) * (int64_t)sizeof(float));
@@ -358,13 +360,12 @@ rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void
 
 size_t rha_stream_workspace_size(const rha_problem* p) {
   if (p == nullptr || check_problem(p, true) != RHA_OK || empty(p, true)) return 0;
-  // the split window's partial results, and later in the step the split
-  // fold's partial states, share the workspace
+  // the split window's partial results, then the split fold's partial states
   const int splits = stream_splits(p, (int64_t)p->window * p->chunk_len);
   int glen = 0;
   const int groups = fold_groups(p, &glen);
-  size_t bytes = splits < 2 ? 0 : rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits);
-  if (groups > 1 && fold_bytes(p, groups) > bytes) bytes = fold_bytes(p, groups);
+  size_t bytes = splits < 2 ? 0 : align256(rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits));
+  if (groups > 1) bytes += align256(fold_bytes(p, groups));
   return bytes;
 }
 
@@ -394,8 +395,29 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   const int64_t t = cursor->t;
   const int w = p->window, C = p->chunk_len, d = p->head_dim;
   const int slot = (int)(t % w);
+  const int64_t BH = (int64_t)p->batch * p->heads;
+  hipError_t e;
 
-  // 1. the new chunk's keys and values into its cache slot
+  // The plan.  The window's key range is split over several workgroups per
+  // query tile when a workspace allows (partial results, then a merge), and
+  // the fold of a committed chunk is split into token groups (partial states,
+  // then added in order).  Workspace: split-window partials first, then the
+  // fold's partial states, each 256-byte aligned.
+  const int64_t in_window = t + 1 < w ? t + 1 : w;
+  const int n_keys = (int)(in_window * C);
+  const bool fold = commit && t >= w - 1;
+  const int splits = workspace != nullptr ? stream_splits(p, n_keys) : 1;
+  int glen = C;
+  const int groups = (workspace != nullptr && fold) ? fold_groups(p, &glen) : 1;
+  const size_t fwd_part = splits > 1 ? align256(rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) : 0;
+  const size_t fold_part = groups > 1 ? align256(fold_bytes(p, groups)) : 0;
+  const bool split_fwd = splits > 1 && workspace_bytes >= fwd_part;
+  const bool split_fold = groups > 1 && workspace_bytes >= (split_fwd ? fwd_part : 0) + fold_part;
+  float* fold_ws = split_fold ? reinterpret_cast<float*>(static_cast<char*>(workspace) + (split_fwd ? fwd_part : 0))
+                              : nullptr;
+
+  // 1. the new chunk's keys and values into its cache slot (t % w); with a
+  // split fold, the same launch computes the leaving chunk's partial states
   rha::CopyParams cp{};
   cp.sb = p->stride_b;
   cp.sh = p->stride_h;
@@ -411,11 +433,47 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   cp.dst = k_cache;
   cp.src2 = v_new;
   cp.dst2 = v_cache;
-  hipError_t e = rha::launch_copy_chunk(cp, s);
-  if (e != hipSuccess) return hip_fail(e, "cache copy launch");
+  if (split_fold) {
+    // the chunk leaving the window (t-w+1) sits in slot (t+1) % w, which the
+    // copy does not touch -- except for w = 1, where it is the new chunk
+    // itself, read from k_new / v_new
+    rha::ChunkStateParams c{};
+    if (w > 1) {
+      const int64_t slot_off = (int64_t)((t + 1) % w) * C * d * elem_bytes(p);
+      c.k = static_cast<const char*>(k_cache) + slot_off;
+      c.v = static_cast<const char*>(v_cache) + slot_off;
+      c.kv_sb = (int64_t)p->heads * w * C * d;
+      c.kv_sh = (int64_t)w * C * d;
+      c.kv_st = d;
+    } else {
+      c.k = k_new;
+      c.v = v_new;
+      c.kv_sb = p->stride_b;
+      c.kv_sh = p->stride_h;
+      c.kv_st = p->stride_t;
+    }
+    c.B = p->batch;
+    c.H = p->heads;
+    c.S = fold_ws;
+    c.z = fold_ws + BH * groups * d * d;
+    c.C = glen;
+    c.chunk0 = 0;
+    c.n_chunks = groups;
+    c.slot_offset = 0;
+    c.accumulate = 0;
+    c.s_bh = (int64_t)groups * d * d;
+    c.z_bh = (int64_t)groups * d;
+    c.tok_end = C;
+    c.copy = cp;
+    c.copy_blocks_per_bh = (int)(((int64_t)C * (d * cp.elem_bytes / 16) + 255) / 256);
+    e = launch_chunk_state(p, c, s);
+    if (e != hipSuccess) return hip_fail(e, "cache copy and fold launch");
+  } else {
+    e = rha::launch_copy_chunk(cp, s);
+    if (e != hipSuccess) return hip_fail(e, "cache copy launch");
+  }
 
   // 2. attention of the new chunk: cached window (chunks max(0,t-w+1)..t) + state
-  const int64_t in_window = t + 1 < w ? t + 1 : w;
   rha::FwdParams f{};
   f.q = q_new;
   f.k = k_cache;
@@ -436,74 +494,47 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.w = w;
   f.n_qchunks = 1;
   f.stream_mode = 1;
-  f.n_keys = (int)(in_window * C);
+  f.n_keys = n_keys;
   f.has_state = t >= w ? 1 : 0;
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-  const int splits = workspace != nullptr ? stream_splits(p, f.n_keys) : 1;
-  if (splits > 1 && workspace_bytes >= rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) {
-    // the key window split over several workgroups per query tile, then merged
-    f.n_splits = splits;
-    f.part = static_cast<float*>(workspace);
-    e = launch_fwd(p, f, s);
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-    e = rha::launch_fwd_combine(f, s);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
-  } else {
-    f.n_splits = 1;
-    e = launch_fwd(p, f, s);
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-  }
+  f.n_splits = split_fwd ? splits : 1;
+  f.part = split_fwd ? static_cast<float*>(workspace) : nullptr;
+  e = launch_fwd(p, f, s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
 
-  // 3. commit: fold the chunk that leaves the window, advance the cursor
+  // 3. merges (after the pass has read S, z), then the unsplit fold
+  rha::StateCombineParams sc{};
+  if (split_fold) sc = rha::StateCombineParams{S, z, fold_ws, (int)BH, groups, d};
+  if (split_fwd) {
+    e = rha::launch_fwd_state_combine(f, sc, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  } else if (split_fold) {
+    e = rha::launch_state_combine(sc, s);
+    if (e != hipSuccess) return hip_fail(e, "fold merge launch");
+  }
   if (commit) {
-    if (t >= w - 1) {
+    if (fold && !split_fold) {
       const int out_slot = (int)((t + 1) % w);
-      int glen = C;
-      const int groups = workspace != nullptr ? fold_groups(p, &glen) : 1;
       rha::ChunkStateParams c{};
+      c.k = k_cache;
+      c.v = v_cache;
+      c.S = S;
+      c.z = z;
       c.kv_sb = f.kv_sb;
       c.kv_sh = f.kv_sh;
       c.kv_st = d;
       c.B = p->batch;
       c.H = p->heads;
-      if (groups > 1 && workspace_bytes >= fold_bytes(p, groups)) {
-        // token groups of the chunk into partial states, then added in order
-        const int64_t slot_off = (int64_t)out_slot * C * d * elem_bytes(p);
-        float* part = static_cast<float*>(workspace);
-        const int64_t bh = (int64_t)p->batch * p->heads;
-        c.k = static_cast<const char*>(k_cache) + slot_off;
-        c.v = static_cast<const char*>(v_cache) + slot_off;
-        c.S = part;
-        c.z = part + bh * groups * d * d;
-        c.C = glen;
-        c.chunk0 = 0;
-        c.n_chunks = groups;
-        c.slot_offset = 0;
-        c.accumulate = 0;
-        c.s_bh = (int64_t)groups * d * d;
-        c.z_bh = (int64_t)groups * d;
-        c.tok_end = C;
-        e = launch_chunk_state(p, c, s);
-        if (e != hipSuccess) return hip_fail(e, "fold launch");
-        rha::StateCombineParams sc{S, z, part, (int)bh, groups, d};
-        e = rha::launch_state_combine(sc, s);
-        if (e != hipSuccess) return hip_fail(e, "fold merge launch");
-      } else {
-        c.k = k_cache;
-        c.v = v_cache;
-        c.S = S;
-        c.z = z;
-        c.C = C;
-        c.chunk0 = out_slot;
-        c.n_chunks = 1;
-        c.slot_offset = 0;
-        c.accumulate = 1;
-        c.s_bh = (int64_t)d * d;
-        c.z_bh = d;
-        c.tok_end = (int64_t)(out_slot + 1) * C;
-        e = launch_chunk_state(p, c, s);
-        if (e != hipSuccess) return hip_fail(e, "fold launch");
-      }
+      c.C = C;
+      c.chunk0 = out_slot;
+      c.n_chunks = 1;
+      c.slot_offset = 0;
+      c.accumulate = 1;
+      c.s_bh = (int64_t)d * d;
+      c.z_bh = d;
+      c.tok_end = (int64_t)(out_slot + 1) * C;
+      e = launch_chunk_state(p, c, s);
+      if (e != hipSuccess) return hip_fail(e, "fold launch");
     }
     cursor->t = t + 1;
   }

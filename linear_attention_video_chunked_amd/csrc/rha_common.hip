@@ -2,6 +2,7 @@
 // copy of a new chunk into the streaming KV cache.
 #include "rha_device.hpp"
 #include "rha_launch.hpp"
+#include "rha_small.hpp"
 
 namespace rha {
 namespace {
@@ -58,55 +59,12 @@ __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
 // (blockIdx.y = 1).  blockIdx.x = bh * blocks_per_bh + block within the head,
 // so every per-thread index is 32-bit.
 __global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p, int blocks_per_bh) {
-  const int row_vecs = p.d * p.elem_bytes / 16;
   const int bh = blockIdx.x / blocks_per_bh;
-  const int i = (blockIdx.x - bh * blocks_per_bh) * 256 + threadIdx.x;
-  if (i >= p.C * row_vecs) return;
-  const void* srcp = blockIdx.y ? p.src2 : p.src;
-  void* dstp = blockIdx.y ? p.dst2 : p.dst;
-  const int t = i / row_vecs, vcol = i - t * row_vecs;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const unsigned char* src = (const unsigned char*)srcp +
-                             ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
-                             vcol * 16;
-  unsigned char* dst = (unsigned char*)dstp +
-                       ((((int64_t)bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
-  st16(dst, ld16(src));
+  copy_unit(p, blockIdx.y, bh, (blockIdx.x - bh * blocks_per_bh) * 256 + threadIdx.x);
 }
 
-// S[bh] += sum_g part_S[bh][g] and z[bh] += sum_g part_z[bh][g], the partial
-// sums added in g order first (a fixed order, so the result is deterministic);
-// one thread per 4 floats.
 __global__ __launch_bounds__(64) void state_combine_kernel(const StateCombineParams p) {
-  const int per = (p.d * p.d + p.d) / 4;  // float4 units per head
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)p.BH * per) return;
-  const int bh = (int)(idx / per), r = (int)(idx - (int64_t)bh * per);
-  const int sq = p.d * p.d / 4;
-  const float* src;
-  int64_t gstride;
-  float* dst;
-  if (r < sq) {
-    src = p.part + ((int64_t)bh * p.G * p.d * p.d) + 4 * r;
-    gstride = (int64_t)p.d * p.d;
-    dst = p.S + (int64_t)bh * p.d * p.d + 4 * r;
-  } else {
-    src = p.part + (int64_t)p.BH * p.G * p.d * p.d + (int64_t)bh * p.G * p.d + 4 * (r - sq);
-    gstride = p.d;
-    dst = p.z + (int64_t)bh * p.d + 4 * (r - sq);
-  }
-  // groups of eight loads in flight, added in g order
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int g = 0;
-  for (; g + 8 <= p.G; g += 8) {
-    f32x4 x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const f32x4*>(src + (g + i) * gstride);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc += x[i];
-  }
-  for (; g < p.G; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * gstride);
-  *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(dst) + acc;
+  state_combine_unit(p, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 }  // namespace

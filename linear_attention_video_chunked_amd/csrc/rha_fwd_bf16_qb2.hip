@@ -34,6 +34,7 @@
 #include "rha_device.hpp"
 #include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
+#include "rha_small.hpp"
 
 namespace rha {
 namespace {
@@ -714,9 +715,16 @@ void fwd_bf16_qb2_kernel(const FwdParams p) {
 // Merge of a split pass: per query row, the partial numerators and
 // denominators are brought to the largest reference and summed in split
 // order; one thread per 4 output columns.
+// Workgroups from fwd_blocks on run the state merge sc instead (the fold of a
+// streaming step, merged in the same launch).
 template <int D>
-__global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p) {
+__global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p, const StateCombineParams sc,
+                                                          int fwd_blocks) {
   constexpr int BM = Q2_NW * 32 * Q2_QB;
+  if ((int)blockIdx.x >= fwd_blocks) {
+    state_combine_unit(sc, (int64_t)(blockIdx.x - fwd_blocks) * blockDim.x + threadIdx.x);
+    return;
+  }
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)p.B * p.H * p.C * (D / 4);
   if (idx >= total) return;
@@ -774,11 +782,18 @@ size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits) {
   return (size_t)(n_part * kQb2RowsPerTile * (d + 2) * sizeof(float));
 }
 
-hipError_t launch_fwd_combine(const FwdParams& p, hipStream_t s) {
+hipError_t launch_fwd_state_combine(const FwdParams& p, const StateCombineParams& sc, hipStream_t s) {
   const int64_t total = (int64_t)p.B * p.H * p.C * (128 / 4);
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  const int64_t fwd_blocks = (total + 255) / 256;
+  const int64_t state_units = sc.G > 0 ? (int64_t)sc.BH * ((int64_t)sc.d * sc.d + sc.d) / 4 : 0;
+  const int64_t blocks = fwd_blocks + (state_units + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, p, sc, (int)fwd_blocks);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const FwdParams& p, hipStream_t s) {
+  return launch_fwd_state_combine(p, StateCombineParams{}, s);
 }
 
 }  // namespace rha

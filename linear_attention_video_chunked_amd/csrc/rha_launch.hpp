@@ -60,6 +60,26 @@ struct FwdParams {
 // Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).
 constexpr int kSparseMaxKeyTiles = 2048;
 
+// Copy one chunk [B,H,C,d] (strided) into cache slot `slot` of [B,H,w,C,d].
+struct CopyParams {
+  const void* src;
+  void* dst;
+  const void* src2;  // optional second chunk (same shape and strides) into dst2
+  void* dst2;
+  int64_t sb, sh, st;
+  int B, H, C, d, w, slot;
+  int elem_bytes;
+};
+
+// S[bh] += sum over g of part[bh][g] (g = 0 .. G-1 in order), likewise z:
+// part holds B*H*G slots of d*d floats, then B*H*G slots of d floats.
+struct StateCombineParams {
+  float* S;
+  float* z;
+  const float* part;
+  int BH, G, d;
+};
+
 // Per-chunk state contribution phi(K_c)^T V_c, sum_t phi(k_t) for a list of
 // chunks, written to (or, with accumulate, added into) float32 state slots.
 //   chunk index j in [0, n_chunks) of head bh reads tokens
@@ -86,15 +106,10 @@ struct ChunkStateParams {
   float* z2;
   int slot_offset2;
   int n_slots;
-};
-
-// S[bh] += sum over g of part[bh][g] (g = 0 .. G-1 in order), likewise z:
-// part holds B*H*G slots of d*d floats, then B*H*G slots of d floats.
-struct StateCombineParams {
-  float* S;
-  float* z;
-  const float* part;
-  int BH, G, d;
+  // Optional cache copy run by extra workgroups of the same launch (copy.src
+  // set): copy_blocks_per_bh workgroups of 256 threads per (tensor, head).
+  CopyParams copy;
+  int copy_blocks_per_bh;
 };
 
 // In-place inclusive prefix over the state slots of every head:
@@ -108,17 +123,6 @@ struct PrefixParams {
   int reverse;
 };
 
-// Copy one chunk [B,H,C,d] (strided) into cache slot `slot` of [B,H,w,C,d].
-struct CopyParams {
-  const void* src;
-  void* dst;
-  const void* src2;  // optional second chunk (same shape and strides) into dst2
-  void* dst2;
-  int64_t sb, sh, st;
-  int B, H, C, d, w, slot;
-  int elem_bytes;
-};
-
 // The forward launchers fill in tiles_per_chunk and total_tiles (they depend
 // on the kernel's tile height) before launching.
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
@@ -130,6 +134,8 @@ constexpr int kQb2RowsPerTile = 256;
 size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits);
 // Merge the partial results of a split pass into out (and lse).
 hipError_t launch_fwd_combine(const FwdParams& p, hipStream_t s);
+// The same merge with a state merge (sc.G > 0) run by extra workgroups.
+hipError_t launch_fwd_state_combine(const FwdParams& p, const StateCombineParams& sc, hipStream_t s);
 hipError_t launch_fwd_f32(FwdParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s);
 hipError_t launch_chunk_state_f32(const ChunkStateParams& p, int d, hipStream_t s);

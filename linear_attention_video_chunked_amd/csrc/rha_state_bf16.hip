@@ -22,6 +22,7 @@
 #include "rha_device.hpp"
 #include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
+#include "rha_small.hpp"
 
 namespace rha {
 namespace {
@@ -86,6 +87,13 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
   // slices of one chunk are adjacent in the logical order, which keeps them
   // on one XCD (one L2) so V is fetched from HBM once
   const int total = p.B * p.H * p.n_chunks * Cfg::ES;
+  if ((int)blockIdx.x >= total) {  // the launch's extra workgroups: the cache copy
+    const int cb = blockIdx.x - total;
+    const int pair = cb / p.copy_blocks_per_bh;  // (tensor, head)
+    const int BH = p.B * p.H;
+    copy_unit(p.copy, pair / BH, pair % BH, (cb - pair * p.copy_blocks_per_bh) * THREADS + tid);
+    return;
+  }
   const int logical = fwd::xcd_remap(blockIdx.x, total);
   const int es = logical % Cfg::ES;
   const int jc = (logical / Cfg::ES) % p.n_chunks;
@@ -244,10 +252,14 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
 
 hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t s) {
   const int64_t heads_chunks = (int64_t)p.B * p.H * p.n_chunks;
+  // extra workgroups for a cache copy in the same launch (2 tensors x B*H heads)
+  const int64_t copy_blocks = p.copy.src != nullptr ? 2 * (int64_t)p.B * p.H * p.copy_blocks_per_bh : 0;
   if (d == 128)
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<128>, dim3((unsigned)(heads_chunks * StateCfg<128>::ES)), dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL(chunk_state_bf16_kernel<128>, dim3((unsigned)(heads_chunks * StateCfg<128>::ES + copy_blocks)),
+                       dim3(THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<64>, dim3((unsigned)(heads_chunks * StateCfg<64>::ES)), dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL(chunk_state_bf16_kernel<64>, dim3((unsigned)(heads_chunks * StateCfg<64>::ES + copy_blocks)),
+                       dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -39,3 +39,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bidir_count_limits():
+    C, N, d, BH = 100, 6, 128, 3
+    # w >= N: every key of every query in the window, no state
+    assert bench.bidir_fwd_flops(C, N, N, d, BH) == (C * N) * (4 * d * C * N) * BH
+    # w = 0: state only
+    assert bench.bidir_fwd_flops(C, N, 0, d, BH) == C * N * (2 * d * d + 2 * d) * BH
+    # the last chunk of a causal w = 2 problem sees what a bidirectional one does
+    w = 2
+    assert bench.bidir_fwd_flops(C, N, w, d, BH) > bench.fwd_flops(C, N, w, d, BH)

@@ -48,6 +48,8 @@ SMALL = {
     # 256-row chunks and a 4-chunk window: enough key tiles for the split path
     "bf16_d128_C256_w4": Workload("s7", 306, B=1, H=2, d=128, C=256, N=8, w=4, dtype="bf16"),
     "bf16_d128_C300_w4_q4": Workload("s8", 307, B=1, H=1, d=128, C=300, N=7, w=4, dtype="bf16", qscale=4.0),
+    # w = 1: the chunk leaving the window is the new chunk itself (the split fold reads it from k_new, v_new)
+    "bf16_d128_C300_w1": Workload("s9", 308, B=1, H=2, d=128, C=300, N=6, w=1, dtype="bf16"),
 }
 
 
@@ -87,7 +89,7 @@ def test_split_window_matches_unsplit(name):
         assert (lses_a[t] - lses_b[t]).abs().max().item() <= 1e-3
 
 
-@pytest.mark.parametrize("name", ["bf16_d128_C100_w3", "bf16_d128_C300_w4_q4"])
+@pytest.mark.parametrize("name", ["bf16_d128_C100_w3", "bf16_d128_C300_w4_q4", "bf16_d128_C300_w1"])
 def test_stream_state_equals_state_scan(name):
     # without a workspace the fold is the scan's own per-chunk kernel added in
     # the scan's order: bitwise equal; with one (token groups summed first)
