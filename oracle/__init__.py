@@ -30,6 +30,13 @@ from .rha_oracle import (
     hybrid_bidir_rows,
     hybrid_bidir_batched,
     state_scan_bidir_batched,
+    brute_anchor,
+    state_scan_anchor,
+    anchor_keys,
+    hybrid_anchor,
+    hybrid_anchor_rows,
+    hybrid_anchor_batched,
+    state_scan_anchor_batched,
 )
 
 __all__ = [
@@ -55,4 +62,11 @@ __all__ = [
     "hybrid_bidir_rows",
     "hybrid_bidir_batched",
     "state_scan_bidir_batched",
+    "brute_anchor",
+    "state_scan_anchor",
+    "anchor_keys",
+    "hybrid_anchor",
+    "hybrid_anchor_rows",
+    "hybrid_anchor_batched",
+    "state_scan_anchor_batched",
 ]

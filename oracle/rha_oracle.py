@@ -476,3 +476,129 @@ def state_scan_bidir_batched(k, v, C: int, w: int):
             for arr, val in zip(res, state_scan_bidir(k[b, h], v[b, h], C, w)):
                 arr[b, h] = val
     return tuple(res)
+
+
+# ---------------------------------------------------------------- anchor (sink) chunks
+#
+# Hybrid Forcing explainer, section 1: the attention-sink workaround keeps the
+# first frame(s) of the video attended by every later frame.  Combined with the
+# hybrid: the first `a` chunks are anchors -- always in the softmax window of
+# every query chunk that they do not lie in the future of, and never folded
+# into the linear state:
+#
+#     W(i) = window(c) + { j : floor(j/C) < a and floor(j/C) <= c }
+#     H(i) = { j : a <= floor(j/C) <= c - w }
+#
+# a = 0 is the plain hybrid.
+
+
+def brute_anchor(q, k, v, C: int, w: int, a: int, return_den: bool = False):
+    """The anchored definition as one L x L weight matrix (tiny inputs only)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L = q.shape[0]
+    cid = np.arange(L) // C
+    cq, ck = cid[:, None], cid[None, :]
+    in_window = ((ck <= cq) & (ck >= cq - w + 1)) if w > 0 else np.zeros((L, L), bool)
+    in_window = in_window | ((ck < a) & (ck <= cq))
+    in_history = (ck >= a) & (ck <= cq - w) & ~in_window
+    s = _scores(q, k)
+    wts = np.zeros((L, L))
+    wts[in_window] = np.exp(s[in_window])
+    lin = phi(q) @ phi(k).T
+    wts[in_history] = lin[in_history]
+    den = wts.sum(axis=1)
+    out = (wts @ v) / den[:, None]
+    return (out, den) if return_den else out
+
+
+def state_scan_anchor(k, v, C: int, w: int, a: int):
+    """S_c = sum_{a <= j <= c-w} U_j (z likewise): the history without anchors."""
+    U, u = chunk_states(k, v, C)
+    N = U.shape[0]
+    S, z = np.zeros_like(U), np.zeros_like(u)
+    for c in range(N):
+        lo, hi = a, c - w
+        if hi >= lo:
+            S[c] = U[lo : hi + 1].sum(axis=0)
+            z[c] = u[lo : hi + 1].sum(axis=0)
+    return S, z
+
+
+def anchor_keys(c: int, C: int, w: int, a: int):
+    """Sorted key indices of the anchored softmax window of chunk c."""
+    lo, hi = window_range(c, w)
+    win = set(range(lo * C, (hi + 1) * C)) if lo <= hi else set()
+    anc = set(range(0, min(a, c + 1) * C))
+    return np.array(sorted(win | anc), dtype=np.int64)
+
+
+def hybrid_anchor(q, k, v, C: int, w: int, a: int, return_den: bool = False):
+    """Chunked evaluation of the anchored definition (one head)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    L, d = q.shape
+    N = L // C
+    S, z = state_scan_anchor(k, v, C, w, a)
+    fq = phi(q)
+    out = np.empty((L, v.shape[1]))
+    den_all = np.empty(L)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        num = fq[rows] @ S[c]
+        den = fq[rows] @ z[c]
+        keys = anchor_keys(c, C, w, a)
+        if keys.size:
+            e = np.exp(_scores(q[rows], k[keys]))
+            num = num + e @ v[keys]
+            den = den + e.sum(axis=1)
+        out[rows] = num / den[:, None]
+        den_all[rows] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_anchor_rows(q, k, v, C: int, w: int, a: int, rows, S=None, z=None, return_den: bool = False):
+    """The anchored definition for selected rows (one head)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    if S is None:
+        S, z = state_scan_anchor(k, v, C, w, a)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, v.shape[1]))
+    den_all = np.empty(rows.size)
+    for n, r in enumerate(rows):
+        r = int(r)
+        c = r // C
+        fq = phi(q[r])
+        num = fq @ S[c]
+        den = fq @ z[c]
+        keys = anchor_keys(c, C, w, a)
+        if keys.size:
+            e = np.exp(_scores(q[r : r + 1], k[keys]))[0]
+            num = num + e @ v[keys]
+            den = den + e.sum()
+        out[n] = num / den
+        den_all[n] = den
+    return (out, den_all) if return_den else out
+
+
+def hybrid_anchor_batched(q, k, v, C: int, w: int, a: int, return_den: bool = False):
+    """``hybrid_anchor`` over [B, H, L, d]."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    den = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], den[b, h] = hybrid_anchor(q[b, h], k[b, h], v[b, h], C, w, a, return_den=True)
+    return (out, den) if return_den else out
+
+
+def state_scan_anchor_batched(k, v, C: int, w: int, a: int):
+    """``state_scan_anchor`` over [B, H, L, d]."""
+    k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+    B, H, L, d = k.shape
+    N = L // C
+    S = np.empty((B, H, N, d, v.shape[-1]))
+    z = np.empty((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            S[b, h], z[b, h] = state_scan_anchor(k[b, h], v[b, h], C, w, a)
+    return S, z

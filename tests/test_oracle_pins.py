@@ -489,3 +489,58 @@ def test_bidir_scan_identity():
             np.testing.assert_allclose(Sp[c] + Ss[c] + win, tot, rtol=1e-12, atol=1e-12)
             if w == 0:
                 np.testing.assert_allclose(Sp[c], U[: c + 1].sum(axis=0), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- anchor (sink) chunks
+# (Hybrid Forcing explainer, section 1: the attention-sink workaround keeps the
+# first frame attended).  The first `a` chunks are always in the softmax window
+# of the queries they do not lie in the future of, and never in the state.
+
+ANCHOR_SWEEP = [(C, N, w, a) for C, N in ((1, 8), (3, 5), (4, 4), (7, 3)) for w in (0, 1, 2, N + 1)
+                for a in (0, 1, 2, N)]
+
+
+@pytest.mark.parametrize("C,N,w,a", ANCHOR_SWEEP)
+def test_anchor_brute_equals_chunked(C, N, w, a):
+    q, k, v = _qkv(C * N, 6, 1000 + 10 * C + N + w + 100 * a, qs=1.5)
+    x, dx = O.brute_anchor(q, k, v, C, w, a, return_den=True)
+    y, dy = O.hybrid_anchor(q, k, v, C, w, a, return_den=True)
+    np.testing.assert_allclose(y, x, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dy, dx, rtol=1e-12)
+    rows = np.arange(1, C * N, 2)
+    r = O.hybrid_anchor_rows(q, k, v, C, w, a, rows)
+    np.testing.assert_allclose(r, x[rows], rtol=1e-12, atol=1e-12)
+
+
+def test_anchor_zero_is_plain_hybrid():
+    C, N = 5, 6
+    q, k, v = _qkv(C * N, 8, 1100, qs=1.5)
+    for w in (0, 1, 2, 3):
+        np.testing.assert_allclose(O.hybrid_anchor(q, k, v, C, w, 0), O.hybrid(q, k, v, C, w), rtol=1e-13)
+        np.testing.assert_allclose(O.brute_anchor(q, k, v, C, w, 0), O.brute_masked(q, k, v, C, w), rtol=1e-13)
+
+
+def test_all_chunks_anchored_is_block_causal_sdpa():
+    # every chunk an anchor (or a window covering all): all of the causal past in the softmax
+    C, N = 16, 4
+    q, k, v = _qkv(C * N, 32, 1110, qs=2.0)
+    ref = _sdpa(q, k, v, _block_causal(C * N, C))
+    for w, a in ((0, N), (1, N), (2, N + 3), (N, 1)):
+        np.testing.assert_allclose(O.hybrid_anchor(q, k, v, C, w, a), ref, atol=1e-12)
+        np.testing.assert_allclose(O.brute_anchor(q, k, v, C, w, a), ref, atol=1e-12)
+
+
+def test_anchor_state_is_plain_state_without_anchor_chunks():
+    C, N = 4, 7
+    _, k, v = _qkv(C * N, 5, 1120)
+    U, u = O.chunk_states(k, v, C)
+    for w in (0, 1, 2):
+        S0, z0 = O.state_scan(k, v, C, w)
+        for a in (1, 2, 3):
+            S, z = O.state_scan_anchor(k, v, C, w, a)
+            for c in range(N):
+                hi = min(a - 1, c - w)  # anchors the plain state would hold
+                dropped = U[: hi + 1].sum(axis=0) if hi >= 0 else 0.0
+                dz = u[: hi + 1].sum(axis=0) if hi >= 0 else 0.0
+                np.testing.assert_allclose(S[c], S0[c] - dropped, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(z[c], z0[c] - dz, rtol=1e-12, atol=1e-12)
