@@ -74,11 +74,23 @@ typedef struct {
   int32_t n_chunks;  /* N >= 0 chunks per sequence, L = N*C (ignored by rha_stream_step) */
   int32_t window;    /* w >= 0 softmax window in chunks, the query's own chunk included */
   int32_t dtype;     /* rha_dtype of q, k, v, out and the KV cache */
-  int32_t reserved;  /* must be 0 */
+  int32_t anchor_chunks; /* a >= 0 anchor (sink) chunks, see below; 0 = none */
   int64_t stride_b;  /* element strides of q, k, v and out (see above) */
   int64_t stride_h;
   int64_t stride_t;  /* >= head_dim */
 } rha_problem;
+
+/*
+ * Anchor (sink) chunks.  Hybrid Forcing explainer section 1 (the attention-
+ * sink workaround keeps the first frame attended).  With anchor_chunks = a
+ * > 0, chunks 0 .. a-1 are in the softmax window of every query chunk c they
+ * do not lie in the future of (chunks 0 .. min(a, c+1)-1), in addition to
+ * chunks max(0, c-w+1) .. c, and the state excludes them: it sums chunks
+ * a .. c-w.  rha_state_scan and rha_hybrid_fwd honour it for RHA_BF16 with
+ * head_dim 128 (RHA_ERR_UNSUPPORTED otherwise, and for the streaming, pruned
+ * and bidirectional calls, which need a = 0); the anchor and window keys of a
+ * chunk may span at most 2048 tiles of 64 keys.
+ */
 
 /*
  * rha_state_scan -- the folded history each query chunk reads.
@@ -86,9 +98,9 @@ typedef struct {
  * ReHyAt abstract (chunk-wise recurrent form); Hybrid Forcing explainer
  * section 2.A (frames leaving the window are accumulated into the state).
  * For every (b, h) and chunk c in [0, N):
- *   S[b,h,c] = sum over chunks j <= c - w of phi(K_j)^T V_j      (d x d)
- *   z[b,h,c] = sum over chunks j <= c - w of sum_t phi(k_t)       (d)
- * and zero where c < w.  Per chunk the contribution is one bf16 (f32 for
+ *   S[b,h,c] = sum over chunks a <= j <= c - w of phi(K_j)^T V_j      (d x d)
+ *   z[b,h,c] = sum over chunks a <= j <= c - w of sum_t phi(k_t)       (d)
+ * and zero where c < w + a (a = anchor_chunks, usually 0).  Per chunk the contribution is one bf16 (f32 for
  * RHA_F32) matrix-core product with float32 accumulation; the prefix over
  * chunks is summed in float32 in chunk order, so results are bitwise
  * reproducible.

@@ -33,7 +33,7 @@ class Problem(ctypes.Structure):
         ("n_chunks", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("anchor_chunks", ctypes.c_int32),
         ("stride_b", ctypes.c_int64),
         ("stride_h", ctypes.c_int64),
         ("stride_t", ctypes.c_int64),
@@ -111,13 +111,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _problem(x: torch.Tensor, C: int, w: int, n_chunks: int) -> Problem:
+def _problem(x: torch.Tensor, C: int, w: int, n_chunks: int, anchors: int = 0) -> Problem:
     if x.dim() != 4:
         raise ValueError("tensors are [B, H, T, d]")
     if x.stride(3) != 1:
         raise ValueError("feature dimension must be contiguous")
     B, H, _, d = x.shape
-    return Problem(B, H, d, C, n_chunks, w, _dtype_code(x), 0, x.stride(0), x.stride(1), x.stride(2))
+    return Problem(B, H, d, C, n_chunks, w, _dtype_code(x), anchors, x.stride(0), x.stride(1), x.stride(2))
 
 
 def _same_layout(ref: torch.Tensor, *others: torch.Tensor):
@@ -130,8 +130,8 @@ def _same_layout(ref: torch.Tensor, *others: torch.Tensor):
 
 def state_scan(k: torch.Tensor, v: torch.Tensor, C: int, w: int,
                S: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """rha_state_scan: S[b,h,c] = sum_{chunks j <= c-w} phi(K_j)^T V_j, z likewise."""
+               stream=None, anchors: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rha_state_scan: S[b,h,c] = sum_{chunks anchors <= j <= c-w} phi(K_j)^T V_j, z likewise."""
     _same_layout(k, v)
     B, H, L, d = k.shape
     if L % C:
@@ -141,14 +141,14 @@ def state_scan(k: torch.Tensor, v: torch.Tensor, C: int, w: int,
         S = torch.empty((B, H, N, d, d), dtype=torch.float32, device=k.device)
     if z is None:
         z = torch.empty((B, H, N, d), dtype=torch.float32, device=k.device)
-    prob = _problem(k, C, w, N)
+    prob = _problem(k, C, w, N, anchors)
     _check(lib().rha_state_scan(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _stream(stream)))
     return S, z
 
 
 def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
                C: int, w: int, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               return_lse: bool = False, stream=None):
+               return_lse: bool = False, stream=None, anchors: int = 0):
     """rha_hybrid_fwd: the fused window + linear-state attention pass."""
     if out is None:
         out = torch.empty_like(q)
@@ -165,7 +165,7 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
         raise ValueError("lse must be float32 contiguous [B,H,L]")
-    prob = _problem(q, C, w, N)
+    prob = _problem(q, C, w, N, anchors)
     _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
                                 _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
@@ -273,7 +273,7 @@ class StreamState:
         self.workspace = None
         if split:
             prob = Problem(batch=B, heads=H, head_dim=d, chunk_len=C, n_chunks=1, window=w,
-                           dtype=RHA_BF16 if dtype == torch.bfloat16 else RHA_F32, reserved=0,
+                           dtype=RHA_BF16 if dtype == torch.bfloat16 else RHA_F32, anchor_chunks=0,
                            stride_b=H * C * d, stride_h=C * d, stride_t=d)
             nbytes = int(lib().rha_stream_workspace_size(ctypes.byref(prob)))
             if nbytes > 0:

@@ -52,7 +52,19 @@ rha_status check_problem(const rha_problem* p, bool stream) {
   if (!stream && p->n_chunks < 0) return fail(RHA_ERR_INVALID_ARG, "n_chunks %d must be >= 0", p->n_chunks);
   if (p->window < 0) return fail(RHA_ERR_INVALID_ARG, "window %d must be >= 0", p->window);
   if (stream && p->window < 1) return fail(RHA_ERR_INVALID_ARG, "streaming needs window >= 1 (got %d)", p->window);
-  if (p->reserved != 0) return fail(RHA_ERR_INVALID_ARG, "reserved field must be 0");
+  if (p->anchor_chunks < 0) return fail(RHA_ERR_INVALID_ARG, "anchor_chunks %d must be >= 0", p->anchor_chunks);
+  if (p->anchor_chunks > 0) {
+    if (stream) return fail(RHA_ERR_UNSUPPORTED, "streaming steps take no anchor chunks");
+    if (p->dtype != RHA_BF16 || p->head_dim != 128)
+      return fail(RHA_ERR_UNSUPPORTED, "anchor chunks need dtype RHA_BF16 and head_dim 128");
+    // the anchor and window tiles of a query chunk are listed in LDS
+    const int64_t a = p->anchor_chunks < p->n_chunks ? p->anchor_chunks : p->n_chunks;
+    const int64_t wl = p->window < p->n_chunks ? p->window : p->n_chunks;
+    const int64_t tiles = (a * p->chunk_len + 63) / 64 + (wl * p->chunk_len + 63) / 64;
+    if (tiles > RHA_SPARSE_MAX_KTILES)
+      return fail(RHA_ERR_UNSUPPORTED, "anchors and window span %lld key tiles (at most %d)", (long long)tiles,
+                  RHA_SPARSE_MAX_KTILES);
+  }
   if (p->stride_t < p->head_dim)
     return fail(RHA_ERR_INVALID_ARG, "stride_t %lld < head_dim %d", (long long)p->stride_t, p->head_dim);
   if (p->stride_h < 0 || p->stride_b < 0) return fail(RHA_ERR_INVALID_ARG, "strides must be >= 0");
@@ -174,20 +186,21 @@ rha_status rha_state_scan(const rha_problem* p, const void* k, const void* v, fl
   RHA_TRY(need(z, "z"));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int N = p->n_chunks, w = p->window, d = p->head_dim;
-  const int nproc = N - w;  // chunks 0 .. N-1-w are folded into some later chunk's state
+  const int a = p->anchor_chunks < N ? p->anchor_chunks : N;  // anchors never enter the state
+  const int nproc = N - w - a;  // chunks a .. N-1-w are folded into some later chunk's state
   if (nproc > 0) {
     rha::ChunkStateParams c = state_params(p, k, v, S, z);
-    c.chunk0 = 0;
+    c.chunk0 = a;
     c.n_chunks = nproc;
-    c.slot_offset = w;
+    c.slot_offset = a + w;  // chunk j -> slot j + w
     c.accumulate = 0;
     c.s_bh = (int64_t)N * d * d;
     c.z_bh = (int64_t)N * d;
-    c.tok_end = (int64_t)nproc * p->chunk_len;
+    c.tok_end = (int64_t)(N - w) * p->chunk_len;
     hipError_t e = launch_chunk_state(p, c, s);
     if (e != hipSuccess) return hip_fail(e, "chunk state launch");
   }
-  rha::PrefixParams pp{S, z, p->batch * p->heads, N, w, d};
+  rha::PrefixParams pp{S, z, p->batch * p->heads, N, a + w, d};
   hipError_t e = rha::launch_prefix(pp, s);
   if (e != hipSuccess) return hip_fail(e, "prefix launch");
   return ok();
@@ -222,6 +235,7 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
   f.n_qchunks = p->n_chunks;
   f.stream_mode = 0;
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  f.anchors = p->anchor_chunks;
   hipError_t e = launch_fwd(p, f, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return ok();
@@ -230,6 +244,7 @@ rha_status rha_hybrid_fwd(const rha_problem* p, const void* q, const void* k, co
 rha_status rha_state_scan_bidir(const rha_problem* p, const void* k, const void* v, float* S_past, float* z_past,
                                 float* S_future, float* z_future, void* stream) {
   RHA_TRY(check_problem(p, false));
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "anchor chunks are not supported by this call");
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "bidirectional problems need dtype RHA_BF16 and head_dim 128");
   if (empty(p, false)) return ok();
@@ -272,6 +287,7 @@ rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void*
                                 const float* S_past, const float* z_past, const float* S_future,
                                 const float* z_future, void* out, float* lse, void* stream) {
   RHA_TRY(check_problem(p, false));
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "anchor chunks are not supported by this call");
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "bidirectional problems need dtype RHA_BF16 and head_dim 128");
   if (empty(p, false)) return ok();
@@ -317,6 +333,7 @@ static_assert(RHA_SPARSE_QTILE == rha::kQb2RowsPerTile && RHA_SPARSE_KTILE == 64
 rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
                                  const float* z, const uint8_t* block_mask, void* out, float* lse, void* stream) {
   RHA_TRY(check_problem(p, false));
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "anchor chunks are not supported by this call");
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "pruned windows need dtype RHA_BF16 and head_dim 128");
   if (p->window == 0) return rha_hybrid_fwd(p, q, k, v, S, z, out, lse, stream);

@@ -86,18 +86,24 @@ __shared__ __attribute__((aligned(1024))) unsigned char q2_kb0[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_kb1[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_vb0[Q2_TILE];
 __shared__ __attribute__((aligned(1024))) unsigned char q2_vb1[Q2_TILE];
-// kept key tiles of a pruned pass, in order, then one past the window
+// key tiles a pass visits, in order, then one past the end: pruned passes
+// list kept window tiles; anchored passes list first keys (q2_act) and key
+// counts (q2_actv) of the anchor and window tiles
 __shared__ int q2_act[kSparseMaxKeyTiles + 1];
+__shared__ int q2_actv[kSparseMaxKeyTiles + 1];
 __shared__ int q2_act_n;
 
 // One pass over a tile, output included.  FIRST: references start at 0 (with
 // linear state) or -inf and blocks are checked against the bound; returns
 // nonzero where a reference moved after accumulation.  Otherwise references
 // start at mio and no block is checked.  mio receives the final references.
-template <int D, int NW, bool FIRST, bool PARTIAL, bool SPARSE>
+// VIS: which key tiles a pass visits -- 0 the window's (dense), 1 the kept
+// ones of a pruned window, 2 the anchor chunks' and the window's.
+template <int D, int NW, bool FIRST, bool PARTIAL, int VIS>
 __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]) {
   static_assert(D == Q2_D, "tile buffers are sized for head dimension 128");
-  static_assert(!(PARTIAL && SPARSE), "pruned passes are not split");
+  constexpr bool SPARSE = VIS == 1, ANCH = VIS == 2;
+  static_assert(!(PARTIAL && VIS != 0), "pruned and anchored passes are not split");
   constexpr int THREADS = NW * 64, QB = Q2_QB, BM = NW * 32 * Q2_QB;
   constexpr int DS = D / 16, DB = D / 32, GR = D / 8;
   constexpr int TILE = BN * D * 2;
@@ -147,7 +153,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     } else {
       kbeg = kend = 0;
     }
-    has_past = (p.w == 0) || (c >= p.w);
+    // history: chunks anchors .. c-w (w = 0: own chunk included)
+    has_past = p.anchors > 0 ? (c - p.w >= p.anchors) : ((p.w == 0) || (c >= p.w));
     has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
     has_state = has_past || has_future;
     Sp = p.S + ((int64_t)bh * p.n_qchunks + c) * D * D;
@@ -197,9 +204,47 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     __syncthreads();
     Tp = q2_act_n;
   }
+  // Anchored pass: the anchor keys [0, a_end) (anchors not in the query's
+  // future) and the window [kbeg, kend), merged when they touch, each cut
+  // into 64-key tiles from its start; visit t loads the tile at key
+  // q2_act[t] holding q2_actv[t] keys.
+  if constexpr (ANCH) {
+    const int64_t a_end = (int64_t)min(p.anchors, c + 1) * p.C;
+    int64_t s0e = a_end, s1b = kbeg, s1e = kend;
+    if (s1e <= s1b) s1b = s1e = 0;                                  // no window (w = 0)
+    if (s1e > s1b && s1b <= s0e) {                                  // contiguous union
+      s0e = max(s0e, s1e);
+      s1b = s1e = 0;
+    }
+    const int TA = (int)((s0e + BN - 1) / BN), TW = (int)((s1e - s1b + BN - 1) / BN);
+    Tp = TA + TW;
+    kend = max(s0e, s1e);  // the descriptor covers every visited key
+    for (int t = tid; t <= Tp; t += THREADS) {
+      int64_t st;
+      int64_t n;
+      if (t < TA) {
+        st = (int64_t)t * BN;
+        n = s0e - st;
+      } else if (t < Tp) {
+        st = s1b + (int64_t)(t - TA) * BN;
+        n = s1e - st;
+      } else {
+        st = kend;  // past the end: loads as zeros
+        n = 0;
+      }
+      q2_act[t] = (int)st;
+      q2_actv[t] = (int)min((int64_t)BN, n);
+    }
+    __syncthreads();
+  }
   auto act = [&](int t) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) return q2_act[t];
     else return t;
+  };
+  // first key of visit t
+  auto act_key = [&](int t) __attribute__((always_inline)) -> int64_t {
+    if constexpr (ANCH) return q2_act[t];
+    else return kbeg + (int64_t)act(t) * BN;
   };
 
   // ---- tile loads: direct HBM -> LDS (buffer loads with the LDS flag).  One
@@ -223,13 +268,13 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
   typedef __attribute__((address_space(3))) void lds_void;
-  auto dma_k = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
-    const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
+  auto dma_k = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
+    const int tile_off = (int)(key * p.kv_st * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
                                              kdma[i % 4] + (i / 4) * 4 * vdma_step + tile_off, 0, 0, 0);
   };
-  auto dma_v = [&](unsigned char* dst, int t, int i) __attribute__((always_inline)) {
-    const int tile_off = (int)((kbeg + (int64_t)t * BN) * p.kv_st * 2);
+  auto dma_v = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
+    const int tile_off = (int)(key * p.kv_st * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
                                              vdma0 + i * vdma_step + tile_off, 0, 0, 0);
   };
@@ -339,8 +384,12 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // keys of block blk inside the window (<= 0 for the second block of a last
   // tile that holds at most 32 keys)
   auto block_valid = [&](int blk) __attribute__((always_inline)) {
-    const int real = 2 * act(blk >> 1) + (blk & 1);  // block of the window
-    return (int)min((int64_t)32, kend - (kbeg + (int64_t)real * 32));
+    if constexpr (ANCH) {
+      return min(32, q2_actv[blk >> 1] - 32 * (blk & 1));
+    } else {
+      const int real = 2 * act(blk >> 1) + (blk & 1);  // block of the window
+      return (int)min((int64_t)32, kend - (kbeg + (int64_t)real * 32));
+    }
   };
   // Tile buffers by tile index t + AHEAD.  PAR is the parity of t when known
   // at compile time (0 or 1; -1 if not); then every LDS address folds into a
@@ -478,8 +527,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   };
   // Tile loads of a period's first step, one per round: K of visit t+1 and
   // V of visit t (their buffers were last read in period t-1); tk, tv are the
-  // window tiles of those visits.
-  auto stage_op = [&](auto j_c, auto par_c, int t, int tk, int tv) __attribute__((always_inline)) {
+  // first keys of those visits.
+  auto stage_op = [&](auto j_c, auto par_c, int t, int64_t tk, int64_t tv) __attribute__((always_inline)) {
     constexpr int j = decltype(j_c)::value;
     if constexpr (j < LPW) dma_k(kbuf(par_c, t, A1{}), tk, j);
     else dma_v(vbuf(par_c, t, A0{}), tv, j - LPW);
@@ -491,7 +540,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   enum : int { kQK = 1, kSM = 2, kPV = 4, kMASK = 8, kSTAGE = 16, kPRE_K = 32, kPRE_V = 64 };
   auto step = [&](auto f_c, auto base_c, auto par_c, auto check_c, int t, const unsigned char* kt, int qh,
                   f32x16 (&acc_next)[QB], f32x16 (&acc_cur)[QB], bf16x2 (&pk_cur)[QB][8], int valid,
-                  const unsigned char* vt, int vh, const bf16x2 (&pk_prev)[QB][8], int tk, int tv)
+                  const unsigned char* vt, int vh, const bf16x2 (&pk_prev)[QB][8], int64_t tk, int64_t tv)
                   __attribute__((always_inline)) {
     constexpr int F = decltype(f_c)::value, base = decltype(base_c)::value;
     constexpr bool QK = F & kQK, SM = F & kSM, PV = F & kPV, CHECK = decltype(check_c)::value;
@@ -564,10 +613,10 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     constexpr int FA = FA0 | ((FB & kQK) ? kPRE_K : 0) | ((FB & kPV) ? kPRE_V : 0);
     const unsigned char* kt = kbuf(par_c, t, A0{});
     const unsigned char* vprev = vbuf(par_c, t, Am1{});
-    int tk = t + 1, tv = t;  // window tiles staged in this period
-    if constexpr (SPARSE && ((FA0 & kSTAGE) != 0)) {
-      tk = act(t + 1);
-      tv = act(t);
+    int64_t tk = 0, tv = 0;  // first keys of the visits staged in this period
+    if constexpr ((FA0 & kSTAGE) != 0) {
+      tk = act_key(t + 1);
+      tv = act_key(t);
     }
     if constexpr ((FA & kQK) != 0) {
       kf[0] = read_k(kt, 0, 0);
@@ -587,6 +636,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   using C1 = std::integral_constant<int, kQK | kSM | kMASK>;
   using CA = std::integral_constant<int, kQK | kSM | kPV | kSTAGE>;
   using CB = std::integral_constant<int, kQK | kSM | kPV>;
+  using CAm = std::integral_constant<int, kQK | kSM | kPV | kSTAGE | kMASK>;
   using CBm = std::integral_constant<int, kQK | kSM | kPV | kMASK>;
   using CTa = std::integral_constant<int, kSM | kPV | kMASK>;
   using CTb = std::integral_constant<int, kPV>;
@@ -598,26 +648,32 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
     // prologue: K tile 0 into LDS
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_k(kb0, act(0), i);
+    for (int i = 0; i < LPW; ++i) dma_k(kb0, act_key(0), i);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
     __syncthreads();
     // steady state: every block of K tile t and V tile t-1 is full; two
     // periods per iteration so the buffer parity is known
+    // (anchored passes: the anchor segment's last tile may be partial too,
+    // so every period tests its blocks)
+    using SA = std::conditional_t<ANCH, CAm, CA>;
+    using SB = std::conditional_t<ANCH, CBm, CB>;
+    auto va = [&](int t) __attribute__((always_inline)) { return ANCH ? block_valid(2 * t - 1) : 32; };
+    auto vb = [&](int t) __attribute__((always_inline)) { return ANCH ? block_valid(2 * t) : 32; };
     int t = 1;
     for (; t + 2 < Tp; t += 2) {
-      period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
+      period(t, A1{}, check_c, SA{}, SB{}, va(t), vb(t));
       __syncthreads();
-      period(t + 1, A0{}, check_c, CA{}, CB{}, 32, 32);
+      period(t + 1, A0{}, check_c, SA{}, SB{}, va(t + 1), vb(t + 1));
       __syncthreads();
     }
     if (t + 1 < Tp) {
-      period(t, A1{}, check_c, CA{}, CB{}, 32, 32);
+      period(t, A1{}, check_c, SA{}, SB{}, va(t), vb(t));
       __syncthreads();
     }
     if (Tp > 1) {  // period Tp-1: the last K tile (may be partial)
-      period(Tp - 1, Am1{}, check_c, CA{}, CBm{}, 32, block_valid(2 * Tp - 2));
+      period(Tp - 1, Am1{}, check_c, SA{}, CBm{}, va(Tp - 1), block_valid(2 * Tp - 2));
       __syncthreads();
     }
     // period Tp: softmax of the last block, P V of the last V tile
@@ -695,21 +751,21 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 
 // The rare second pass, kept out of line so that its registers do not add to
 // the first pass's.
-template <int D, int NW, bool PARTIAL, bool SPARSE>
+template <int D, int NW, bool PARTIAL, int VIS>
 __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float m1) {
   float m[Q2_QB] = {m0, m1};
-  tile_pass<D, NW, false, PARTIAL, SPARSE>(p, m);
+  tile_pass<D, NW, false, PARTIAL, VIS>(p, m);
 }
 
-template <int D, int NW, bool PARTIAL, bool SPARSE>
+template <int D, int NW, bool PARTIAL, int VIS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
   float m[Q2_QB];
-  const int dirty = tile_pass<D, NW, true, PARTIAL, SPARSE>(p, m);
+  const int dirty = tile_pass<D, NW, true, PARTIAL, VIS>(p, m);
   // Every wave reaches this barrier.  Where some query's reference moved after
   // accumulation, the whole tile is computed again with the final references
   // (which no score exceeds by the bound); its output replaces the first.
-  if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL, SPARSE>(p, m[0], m[1]);
+  if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL, VIS>(p, m[0], m[1]);
 }
 
 // Merge of a split pass: per query row, the partial numerators and
@@ -762,11 +818,13 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk * splits;
   if (p.total_tiles == 0) return hipSuccess;
   if (splits > 1)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 0>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   else if (p.kmask != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, true>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 1>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+  else if (p.anchors > 0)
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 2>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, false>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 0>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -55,6 +55,10 @@ struct FwdParams {
   int bidir;
   const float* S2;
   const float* z2;
+  // Anchor chunks (seq mode, head_dim 128 bf16 only): chunks 0 .. anchors-1
+  // are in the softmax window of every later (or the same) query chunk, and
+  // the state slots exclude them.
+  int anchors;
 };
 
 // Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).

@@ -50,7 +50,7 @@ def test_status_strings(L):
 
 def _prob(**kw):
     base = dict(batch=1, heads=2, head_dim=128, chunk_len=64, n_chunks=4, window=2, dtype=_rha.RHA_BF16,
-                reserved=0, stride_b=2 * 256 * 128, stride_h=256 * 128, stride_t=128)
+                anchor_chunks=0, stride_b=2 * 256 * 128, stride_h=256 * 128, stride_t=128)
     base.update(kw)
     return _rha.Problem(**base)
 
@@ -71,7 +71,7 @@ def _fwd(L, prob, q=P, k=P, v=P, S=P, z=P, out=P, lse=None):
 @pytest.mark.parametrize("field,value,code", [
     ("batch", -1, 1), ("heads", -3, 1), ("head_dim", 96, 2), ("head_dim", 256, 2),
     ("chunk_len", 0, 1), ("n_chunks", -1, 1), ("window", -1, 1), ("dtype", 7, 1),
-    ("reserved", 1, 1), ("stride_t", 64, 1), ("stride_t", 132, 1), ("stride_h", -128, 1),
+    ("anchor_chunks", -1, 1), ("stride_t", 64, 1), ("stride_t", 132, 1), ("stride_h", -128, 1),
 ])
 def test_invalid_problem_fields(L, field, value, code):
     prob = _prob(**{field: value})
@@ -222,3 +222,18 @@ def test_bidir_checks(L):
     assert L.rha_hybrid_fwd_bidir(ctypes.byref(ok), P, P, P, P, P, P, None, P, None, None) == 1
     assert "z_future" in L.rha_last_error().decode()
     assert L.rha_hybrid_fwd_bidir(ctypes.byref(_prob(window=-2)), *([P] * 9), None, None) == 1
+
+
+def test_anchor_checks(L):
+    # anchor chunks: bf16 with head_dim 128; not for streaming, pruned or bidirectional calls
+    assert _scan(L, _prob(anchor_chunks=1, dtype=_rha.RHA_F32, stride_t=128)) == 2
+    assert _fwd(L, _prob(anchor_chunks=2, head_dim=64, stride_t=64)) == 2
+    assert "anchor" in L.rha_last_error().decode()
+    assert _sparse(L, _prob(anchor_chunks=1)) == 2
+    assert L.rha_state_scan_bidir(ctypes.byref(_prob(anchor_chunks=1)), P, P, P, P, P, P, None) == 2
+    cur = _rha.Cursor(0)
+    assert _step(L, _prob(anchor_chunks=1, window=2), ctypes.byref(cur)) == 2
+    assert cur.t == 0
+    # anchor and window tiles listed per query chunk: at most 2048 tiles of 64 keys
+    big = _prob(anchor_chunks=20, n_chunks=40, window=20, chunk_len=4000, stride_b=0, stride_h=0)
+    assert _fwd(L, big) == 2 and "key tiles" in L.rha_last_error().decode()
