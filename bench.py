@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir|anchor   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -88,6 +88,18 @@ def bidir_fwd_flops(C, N, w, d, BH):
     return f * BH
 
 
+def anchor_fwd_flops(C, N, w, a, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_fwd call with a anchor chunks: 4d per
+    (query, key) over the window and the anchors, 2d^2 + 2d per query whose
+    history (chunks a .. c-w) is non-empty."""
+    f = 0
+    for c in range(N):
+        lo = max(0, c - w + 1) if w > 0 else c + 1
+        keys = set(range(lo, c + 1)) | set(range(0, min(a, c + 1)))
+        f += C * (4 * d * len(keys) * C + ((2 * d * d + 2 * d) if c - w >= a else 0))
+    return f * BH
+
+
 def stream_step_flops(C, w, d, BH):
     """Algorithmic FLOPs of one rha_stream_step with a full window: the new
     chunk's queries against w cached chunks (4d per pair) and the state (2d^2
@@ -156,7 +168,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir"], default=None)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -246,6 +258,24 @@ def main():
         torch.cuda.synchronize()
         return
 
+    # ---- the first frame as an anchor (sink) chunk, same shape
+    SA = torch.empty_like(S)
+    zA = torch.empty_like(z)
+
+    def anchor_step():
+        rha.state_scan(k, v, wl.C, wl.w, S=SA, z=zA, stream=stream, anchors=1)
+        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out, stream=stream, anchors=1)
+
+    def anchor_call():
+        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out, stream=stream, anchors=1)
+
+    anchor_step()
+    if args.only == "anchor":
+        for _ in range(args.steps):
+            anchor_call()
+        torch.cuda.synchronize()
+        return
+
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
     def stream_run(timed_run):
         sw = CONFIGS["stream"]
@@ -296,6 +326,8 @@ def main():
     t_bidir = timed(bidir_call, n_k)
     t_bidir_scan = timed(bidir_scan, n_k)
     bF = bidir_fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
+    t_anchor = timed(anchor_call, n_k)
+    aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
 
     sw, t_stream = stream_run(True)
@@ -346,6 +378,9 @@ def main():
             "bidir_TFLOPs": bF / t_bidir / 1e12,
             "bidir_mfma_frac": bF / t_bidir / 1e12 / PEAK_BF16_TFLOPS,
             "bidir_scan_us": t_bidir_scan * 1e6,
+            "anchor1_fwd_us": t_anchor * 1e6,
+            "anchor1_TFLOPs": aF / t_anchor / 1e12,
+            "anchor1_mfma_frac": aF / t_anchor / 1e12 / PEAK_BF16_TFLOPS,
             "timed_wall_s": wall,
         },
     }

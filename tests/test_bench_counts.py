@@ -50,3 +50,11 @@ def test_bidir_count_limits():
     # the last chunk of a causal w = 2 problem sees what a bidirectional one does
     w = 2
     assert bench.bidir_fwd_flops(C, N, w, d, BH) > bench.fwd_flops(C, N, w, d, BH)
+
+
+def test_anchor_count_limits():
+    C, N, w, d, BH = 100, 6, 2, 128, 2
+    assert bench.anchor_fwd_flops(C, N, w, 0, d, BH) == bench.fwd_flops(C, N, w, d, BH)
+    # every chunk an anchor: block-causal dense attention, no state
+    dense = sum(C * 4 * d * (c + 1) * C for c in range(N)) * BH
+    assert bench.anchor_fwd_flops(C, N, w, N, d, BH) == dense
