@@ -602,3 +602,80 @@ def state_scan_anchor_batched(k, v, C: int, w: int, a: int):
         for h in range(H):
             S[b, h], z[b, h] = state_scan_anchor(k[b, h], v[b, h], C, w, a)
     return S, z
+
+
+# ---------------------------------------------------------------- backward pass
+#
+# Gradients of L = sum_i dout_i . out_i for the causal hybrid (the definition
+# at the top), written out by the chain rule.  With N_i, D_i the numerator and
+# the shared denominator of row i (D_i = exp(lse_i)):
+#
+#   dN_i = dout_i / D_i,   dD_i = -(dout_i . out_i) / D_i
+#   window key j:  E_ij = exp(s_ij),  dE_ij = dN_i . v_j + dD_i
+#                  dv_j += E_ij dN_i,  ds_ij = E_ij dE_ij,
+#                  dq_i += ds_ij k_j / sqrt(d),  dk_j += ds_ij q_i / sqrt(d)
+#   linear term:   dphi(q_i) = S_c dN_i + z_c dD_i   (S_c^T rows)
+#                  dS_c = sum_{i in c} phi(q_i) dN_i^T,  dz_c = sum_{i in c} phi(q_i) dD_i
+#                  dU_j = sum_{c : j <= c - w} dS_c   (likewise du_j)
+#                  dv_t += dU_j^T phi(k_t),  dphi(k_t) = dU_j v_t + du_j
+#   and phi'(x) = 1 for x > 0, exp(x) otherwise.
+
+
+def dphi(x):
+    """Derivative of phi = elu + 1."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def hybrid_backward(q, k, v, C: int, w: int, dout):
+    """(dq, dk, dv) of sum(dout * hybrid(q, k, v, C, w)) for one head."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    L, d = q.shape
+    N = L // C
+    scale = 1.0 / math.sqrt(d)
+    S, z = state_scan(k, v, C, w)
+    U_shape = S.shape
+    out, den = hybrid(q, k, v, C, w, return_den=True)
+    dN = dout / den[:, None]
+    dD = -(dout * out).sum(axis=1) / den
+    fq, fk = phi(q), phi(k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dS, dz = np.zeros(U_shape), np.zeros(z.shape)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        lo, hi = window_range(c, w)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            E = np.exp(_scores(q[rows], k[keys]))
+            dE = dN[rows] @ v[keys].T + dD[rows][:, None]
+            dv[keys] += E.T @ dN[rows]
+            ds = E * dE
+            dq[rows] += ds @ k[keys] * scale
+            dk[keys] += ds.T @ q[rows] * scale
+        gq = dN[rows] @ S[c].T + dD[rows][:, None] * z[c][None, :]
+        dq[rows] += gq * dphi(q[rows])
+        dS[c] = fq[rows].T @ dN[rows]
+        dz[c] = fq[rows].T @ dD[rows]
+    for j in range(N):
+        first = j + w  # S_c contains U_j for c >= j + w
+        if first > N - 1:
+            continue
+        dU = dS[first:].sum(axis=0)
+        du = dz[first:].sum(axis=0)
+        toks = slice(j * C, (j + 1) * C)
+        dv[toks] += fk[toks] @ dU
+        gk = v[toks] @ dU.T + du[None, :]
+        dk[toks] += gk * dphi(k[toks])
+    return dq, dk, dv
+
+
+def hybrid_backward_batched(q, k, v, C: int, w: int, dout):
+    """``hybrid_backward`` over [B, H, L, d]."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    B, H = q.shape[:2]
+    res = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+    for b in range(B):
+        for h in range(H):
+            for arr, g in zip(res, hybrid_backward(q[b, h], k[b, h], v[b, h], C, w, dout[b, h])):
+                arr[b, h] = g
+    return tuple(res)

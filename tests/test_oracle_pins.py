@@ -544,3 +544,62 @@ def test_anchor_state_is_plain_state_without_anchor_chunks():
                 dz = u[: hi + 1].sum(axis=0) if hi >= 0 else 0.0
                 np.testing.assert_allclose(S[c], S0[c] - dropped, rtol=1e-12, atol=1e-12)
                 np.testing.assert_allclose(z[c], z0[c] - dz, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward pass
+# The chain-rule gradients are pinned to central finite differences of the
+# forward oracle along random directions, and to torch autograd through a
+# separately written dense (L x L) torch form of the definition.
+
+def _loss(q, k, v, C, w, dout):
+    return float((O.hybrid(q, k, v, C, w) * dout).sum())
+
+
+@pytest.mark.parametrize("C,N,w", [(3, 4, 2), (5, 3, 1), (4, 4, 0), (2, 5, 9), (6, 3, 3)])
+def test_backward_matches_finite_differences(C, N, w):
+    d = 5
+    q, k, v = _qkv(C * N, d, 1200 + C * N + w, qs=1.2)
+    dout = _rand((C * N, d), 1300 + w)
+    dq, dk, dv = O.hybrid_backward(q, k, v, C, w, dout)
+    rng = np.random.default_rng(1400 + C)
+    eps = 1e-5
+    for which, g in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(3):
+            dirn = rng.standard_normal(q.shape)
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which] += eps * dirn
+            args_m[which] -= eps * dirn
+            fd = (_loss(*args_p, C, w, dout) - _loss(*args_m, C, w, dout)) / (2 * eps)
+            an = float((g * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+def _torch_dense_hybrid(q, k, v, C, w):
+    """The definition as a dense masked L x L weight matrix, in torch ops."""
+    L, d = q.shape
+    c = torch.arange(L) // C
+    cq, ck = c[:, None], c[None, :]
+    win = ((ck <= cq) & (ck >= cq - w + 1)) if w > 0 else torch.zeros((L, L), dtype=torch.bool)
+    hist = ck <= cq - w
+    s = q @ k.T / math.sqrt(d)
+    lin = (torch.nn.functional.elu(q) + 1) @ (torch.nn.functional.elu(k) + 1).T
+    a = torch.where(win, torch.exp(s), torch.where(hist, lin, torch.zeros_like(s)))
+    return (a @ v) / a.sum(dim=1, keepdim=True)
+
+
+@pytest.mark.parametrize("C,N,w", [(4, 5, 2), (7, 3, 1), (3, 4, 0), (5, 4, 6)])
+def test_backward_matches_torch_autograd(C, N, w):
+    d = 8
+    q, k, v = _qkv(C * N, d, 1500 + C + w, qs=1.5)
+    dout = _rand((C * N, d), 1600 + N)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_hybrid(tq, tk, tv, C, w) * torch.from_numpy(dout)).sum().backward()
+    dq, dk, dv = O.hybrid_backward(q, k, v, C, w, dout)
+    for ours, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_dphi_closed_form():
+    x = np.array([-3.0, -1e-3, 0.0, 1e-3, 2.0])
+    np.testing.assert_allclose(O.dphi(x), [math.exp(-3.0), math.exp(-1e-3), 1.0, 1.0, 1.0], rtol=1e-15)
