@@ -167,6 +167,34 @@ rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void
                                  float* lse, void* stream);
 
 /*
+ * rha_hybrid_bwd -- gradients of rha_hybrid_fwd (the causal hybrid, no
+ * anchors, no pruning) for training or distilling through it.
+ *
+ * ReHyAt (abstract) and the Hybrid Forcing explainer (section 2.B) train
+ * models that use the hybrid, so the gradients of its output with respect to
+ * q, k and v are needed: with L = sum(dout * out), the exact derivatives of
+ * the definition at the top of this header (through the softmax window, the
+ * shared normaliser and the linear state, whose gradient flows back to every
+ * earlier chunk that was folded in).  Matrix products use bf16 operands and
+ * float32 accumulation.
+ *
+ *   q, k, v, S, z : as given to rha_hybrid_fwd (read)
+ *   out, lse      : rha_hybrid_fwd's output and lse for them (read; lse required)
+ *   dout          : [B, H, L, d], the problem's strides and dtype (read)
+ *   dq, dk, dv    : [B, H, L, d] float32 contiguous (written)
+ *   workspace     : device scratch of rha_hybrid_bwd_workspace_size(p) bytes,
+ *                   16-byte aligned, no initialisation needed
+ *
+ * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16, head_dim is 128 and
+ * anchor_chunks is 0; RHA_ERR_INVALID_ARG if the workspace is too small.
+ */
+size_t rha_hybrid_bwd_workspace_size(const rha_problem* p);
+rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v,
+                          const float* S, const float* z, const void* out, const float* lse,
+                          const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Bidirectional hybrid -- rha_state_scan_bidir and rha_hybrid_fwd_bidir.
  *
  * ReHyAt (abstract): the hybrid takes the place of the softmax attention of

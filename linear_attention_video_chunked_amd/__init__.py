@@ -11,12 +11,14 @@ Functions mirror the C ABI in ``include/rha.h``:
 * ``hybrid_fwd(q, k, v, S, z, C, w)``            -> out [B,H,L,d] (and lse)
 * ``hybrid_fwd_sparse(q, k, v, S, z, C, w, m)``  the same with pruned window blocks
 * ``state_scan_bidir`` / ``hybrid_fwd_bidir``     symmetric window, past + future states
+* ``hybrid_bwd(q, k, v, S, z, out, lse, dout, C, w)`` -> dq, dk, dv (float32)
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
 """
 from ._rha import (
     LibraryNotBuilt,
     RhaError,
     StreamState,
+    hybrid_bwd,
     hybrid_fwd,
     hybrid_fwd_bidir,
     hybrid_fwd_sparse,
@@ -33,6 +35,7 @@ __all__ = [
     "LibraryNotBuilt",
     "RhaError",
     "StreamState",
+    "hybrid_bwd",
     "hybrid_fwd",
     "hybrid_fwd_bidir",
     "hybrid_fwd_sparse",

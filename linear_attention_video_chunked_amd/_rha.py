@@ -66,13 +66,16 @@ def lib():
     L.rha_hybrid_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_fwd_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_state_scan_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_hybrid_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.rha_hybrid_bwd_workspace_size.argtypes = [P]
+    L.rha_hybrid_bwd_workspace_size.restype = ctypes.c_size_t
     L.rha_hybrid_fwd_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
     L.rha_stream_workspace_size.restype = ctypes.c_size_t
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
-                 "rha_hybrid_fwd_bidir", "rha_stream_step"):
+                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_stream_step"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
     L.rha_status_string.restype = ctypes.c_char_p
@@ -169,6 +172,30 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
                                 _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def hybrid_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
+               out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, C: int, w: int, stream=None):
+    """rha_hybrid_bwd: (dq, dk, dv) float32 [B,H,L,d] of sum(dout * out) for the
+    causal hybrid (out, lse from hybrid_fwd on the same inputs)."""
+    _same_layout(q, k, v, out, dout)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or not (S.is_contiguous() and z.is_contiguous()):
+        raise ValueError("S, z must be contiguous float32 [B,H,N,d,d] and [B,H,N,d]")
+    if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    prob = _problem(q, C, w, N)
+    nbytes = int(lib().rha_hybrid_bwd_workspace_size(ctypes.byref(prob)))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    _check(lib().rha_hybrid_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out), _ptr(lse),
+                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def state_scan_bidir(k: torch.Tensor, v: torch.Tensor, C: int, w: int, stream=None):

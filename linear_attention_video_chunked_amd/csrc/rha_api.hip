@@ -326,6 +326,70 @@ rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void*
   return ok();
 }
 
+size_t rha_hybrid_bwd_workspace_size(const rha_problem* p) {
+  if (p == nullptr || check_problem(p, false) != RHA_OK) return 0;
+  const int64_t BH = (int64_t)p->batch * p->heads, L = (int64_t)p->n_chunks * p->chunk_len, d = p->head_dim;
+  // delta, 1/D, -delta/D per row; the state gradients per chunk
+  return align256((size_t)(3 * BH * L * 4)) + align256((size_t)(BH * p->n_chunks * (d * d + d) * 4));
+}
+
+rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                          const float* z, const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                          float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (p->dtype != RHA_BF16 || p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "the backward pass needs dtype RHA_BF16 and head_dim 128");
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "the backward pass takes no anchor chunks");
+  if (empty(p, false)) return ok();
+  RHA_TRY(need(q, "q"));
+  RHA_TRY(need(k, "k"));
+  RHA_TRY(need(v, "v"));
+  RHA_TRY(need(S, "S"));
+  RHA_TRY(need(z, "z"));
+  RHA_TRY(need(out, "out"));
+  RHA_TRY(need(lse, "lse", true, 4));
+  RHA_TRY(need(dout, "dout"));
+  RHA_TRY(need(dq, "dq"));
+  RHA_TRY(need(dk, "dk"));
+  RHA_TRY(need(dv, "dv"));
+  RHA_TRY(need(workspace, "workspace"));
+  const size_t need_bytes = rha_hybrid_bwd_workspace_size(p);
+  if (workspace_bytes < need_bytes)
+    return fail(RHA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need_bytes);
+  const int64_t BH = (int64_t)p->batch * p->heads, L = (int64_t)p->n_chunks * p->chunk_len;
+  float* ws = static_cast<float*>(workspace);
+  rha::BwdParams b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.out = out;
+  b.dout = dout;
+  b.lse = lse;
+  b.S = S;
+  b.z = z;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.delta = ws;
+  b.rsc = ws + BH * L;
+  b.zw = ws + 2 * BH * L;
+  b.dS = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)(3 * BH * L * 4)));
+  b.dz = b.dS + BH * p->n_chunks * 128 * 128;
+  b.sb = p->stride_b;
+  b.sh = p->stride_h;
+  b.st = p->stride_t;
+  b.B = p->batch;
+  b.H = p->heads;
+  b.C = p->chunk_len;
+  b.N = p->n_chunks;
+  b.w = p->window;
+  b.scale = (float)(1.0 / std::sqrt((double)p->head_dim));
+  b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
+  hipError_t e = rha::launch_bwd_bf16(b, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
 static_assert(RHA_SPARSE_QTILE == rha::kQb2RowsPerTile && RHA_SPARSE_KTILE == 64 &&
                   RHA_SPARSE_MAX_KTILES == rha::kSparseMaxKeyTiles,
               "block sizes of the pruned window are the d = 128 kernel's tiles");

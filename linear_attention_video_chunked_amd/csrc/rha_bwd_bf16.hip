@@ -1,0 +1,446 @@
+// Backward pass of the causal hybrid attention (head_dim 128, bf16) on gfx950.
+//
+// The forward output is out_i = N_i / D_i with N_i = sum_W e^{s_ij} v_j +
+// phi(q_i)^T S_c and D_i = sum_W e^{s_ij} + phi(q_i).z_c (the shared
+// normaliser of the hybrid: ReHyAt, abstract; Hybrid Forcing explainer,
+// section 2.A; phi and the state from "Transformers are RNNs").  With
+// lse_i = ln D_i, P_ij = e^{s_ij - lse_i}, delta_i = dout_i . out_i:
+//   window:  dv_j += sum_i P_ij dout_i
+//            ds_ij = P_ij (dout_i . v_j - delta_i)
+//            dq_i += sum_j ds_ij k_j / sqrt(d),  dk_j += sum_i ds_ij q_i / sqrt(d)
+//   linear:  dphi(q_i) = (S_c dout_i - z_c delta_i) / D_i
+//            dS_c = sum_i phi(q_i) dout_i^T / D_i,  dz_c = -sum_i phi(q_i) delta_i / D_i
+//            dU_j = sum_{c >= j + w} dS_c  (likewise du_j)
+//            dv_t += dU_j^T phi(k_t),  dphi(k_t) = dU_j v_t + du_j
+// and phi'(x) = 1 (x > 0), e^x (otherwise).
+//
+// Kernels (all products on the bf16 matrix cores, float32 accumulation):
+//   bwd_prep_kernel      delta, 1/D and -delta/D per row
+//   bwd_dkdv_kernel      per 128 keys (32 per wave, rows of K and V held as
+//                        operands): every 32-row query block of the chunks
+//                        that see them -- S = Q K^T and dP = dO V^T with keys
+//                        on the lanes, then dV^T += dO^T P and dK^T += Q^T dS
+//   bwd_dq_kernel        per 128 query rows (32 per wave): every 32-key block
+//                        of the window -- S^T = K Q^T and dP^T = V dO^T with
+//                        queries on the lanes, then dQ^T += K^T dS^T
+//   chunk state (rha_state_bf16.hip, scaled rows) for dS_c, dz_c, then a
+//   running sum from the last slot for dU_j, du_j
+//   bwd_rowstate_kernel  the row-by-state products of the linear term
+// The window kernels write dq, dk, dv; the linear-term kernel adds to them.
+// Operand layouts are those of the forward kernels: a row-major LDS tile
+// (16-byte granules XOR-swizzled) is read by rows (ds_read_b128) or, for a
+// transposed operand, by the transpose read ds_read_b64_tr_b16, which hands
+// out the rows in the order the matrix-core output keeps them.
+#include "rha_device.hpp"
+#include "rha_fwd_common.hpp"
+#include "rha_launch.hpp"
+
+namespace rha {
+namespace {
+
+using fwd::i16x4;
+using fwd::lds_i16x4;
+using fwd::vsw;
+using fwd::xcd_remap;
+
+constexpr int BD = 128;              // head dimension
+constexpr int NWB = 4;               // waves per workgroup
+constexpr int TB = NWB * 64;         // threads per workgroup
+constexpr int RB = 32;               // rows (or keys) per matrix-core block
+constexpr int ROWT = RB * BD * 2;    // one 32-row bf16 tile in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+// granule g (8 bf16) of row r of a row-major BD-wide tile
+__device__ __forceinline__ int gran_off(int r, int g) { return r * BD * 2 + ((g ^ vsw<BD>(r)) * 16); }
+
+__device__ __forceinline__ void put_granule(unsigned char* t, int r, int g, const u32x4& x) {
+  *reinterpret_cast<u32x4*>(t + gran_off(r, g)) = x;
+}
+
+// Operand with m = row (row0 + lane % 32) of the tile, k = features 16 ks + 8 (lane / 32) + 0..7.
+__device__ __forceinline__ bf16x8 row_frag(const unsigned char* t, int row0, int ks, int lane) {
+  const int r = row0 + (lane & 31), g = 2 * ks + (lane >> 5);
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t + gran_off(r, g)));
+}
+
+// Operand of the transposed tile: m = feature 32 nb + .., k = 16 rows from
+// 16 ks, in the order in which a 32x32 matrix-core output holds its rows
+// (the order the packed probabilities below follow).
+__device__ __forceinline__ bf16x8 col_frag(const unsigned char* t, int ks, int nb, int lane) {
+  const int hh = lane >> 5, vj = lane & 15;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (vj & 3);
+  const int vrow0 = 4 * hh + (vj >> 2);
+  const int col = nb * 32 + vcol;
+  const unsigned char* pa = t + (vrow0 + 16 * ks) * BD * 2 + (((col >> 3) ^ vsw<BD>(vrow0)) * 16) + (col & 7) * 2;
+  const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * BD * 2));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
+  return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+}
+
+// Packed bf16 pairs of an output block as the second operand of the next
+// product (elements 8 ks .. 8 ks + 7).
+__device__ __forceinline__ bf16x8 pack_b(const uint32_t (&pk)[8], int ks) {
+  return __builtin_bit_cast(bf16x8, u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]});
+}
+
+// element i of a 32x32 output block sits in row 8 (i / 4) + 4 (lane / 32) + i % 4
+__device__ __forceinline__ int out_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
+
+// ---- delta_i = dout_i . out_i, 1 / D_i = exp(-lse_i), -delta_i / D_i
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
+  const int64_t L = (int64_t)p.N * p.C;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)p.B * p.H * L) return;
+  const int64_t bh = idx / L, t = idx - bh * L;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const int64_t off = b * p.sb + h * p.sh + t * p.st;
+  const bf16_t* o = (const bf16_t*)p.out + off;
+  const bf16_t* g = (const bf16_t*)p.dout + off;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int gr = 0; gr < BD / 8; ++gr) {
+    const u32x4 a = ld16(o + gr * 8), c = ld16(g + gr * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(c[i]) + bf16_hi(a[i]) * bf16_hi(c[i]);
+  }
+  const float r = __expf(-p.lse[idx]);
+  p.delta[idx] = acc;
+  p.rsc[idx] = r;
+  p.zw[idx] = -acc * r;
+}
+
+// ---- window gradients of keys and values
+__global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char qs[ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char gs[ROWT];  // dout rows
+  __shared__ float lse_s[RB], del_s[RB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int ktiles = (p.C + 127) / 128;
+  const int total = p.B * p.H * p.N * ktiles;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int tile = logical % ktiles, rest = logical / ktiles;
+  const int j = p.N - 1 - rest % p.N, bh = rest / p.N;
+  const int b = bh / p.H, h = bh % p.H;
+  const int64_t L = (int64_t)p.N * p.C;
+  const int64_t head = b * p.sb + h * p.sh;
+  const bf16_t* qb = (const bf16_t*)p.q + head;
+  const bf16_t* kb = (const bf16_t*)p.k + head;
+  const bf16_t* vb = (const bf16_t*)p.v + head;
+  const bf16_t* gb = (const bf16_t*)p.dout + head;
+
+  const int64_t key0 = (int64_t)j * p.C + 128 * tile + 32 * wave;  // this wave's first key
+  const int nk = (int)max((int64_t)0, min((int64_t)32, (int64_t)(j + 1) * p.C - key0));
+  bf16x8 kr[8], vr[8];  // rows of K and V for this lane's key
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (l32 < nk) {
+      a = ld16(kb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
+      c = ld16(vb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
+    }
+    kr[ks] = __builtin_bit_cast(bf16x8, a);
+    vr[ks] = __builtin_bit_cast(bf16x8, c);
+  }
+  f32x16 dv[4], dk[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) dv[nb] = dk[nb] = f32x16{};
+
+  // query chunks whose window holds chunk j: j .. j + w - 1
+  const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
+  const int nqb = (p.C + RB - 1) / RB;
+  for (int c = j; c <= c_hi; ++c) {
+    for (int qblk = 0; qblk < nqb; ++qblk) {
+      const int64_t row0 = (int64_t)c * p.C + RB * qblk;
+      const int nq = min(RB, p.C - RB * qblk);
+      __syncthreads();  // the previous block's tiles are no longer read
+      for (int u = tid; u < 2 * RB * 16; u += TB) {
+        const int which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (r < nq) x = ld16((which ? gb : qb) + (row0 + r) * p.st + g * 8);
+        put_granule(which ? gs : qs, r, g, x);
+      }
+      if (tid < RB) {
+        const bool ok = tid < nq;
+        lse_s[tid] = ok ? p.lse[bh * L + row0 + tid] * kLog2e : INFINITY;  // rows past the chunk: P = 0
+        del_s[tid] = ok ? p.delta[bh * L + row0 + tid] : 0.f;
+      }
+      __syncthreads();
+      f32x16 sa = {}, pa = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        sa = mfma32(row_frag(qs, 0, ks, lane), kr[ks], sa);  // S = Q K^T, keys on the lanes
+        pa = mfma32(row_frag(gs, 0, ks, lane), vr[ks], pa);  // dP = dO V^T
+      }
+      uint32_t pp[8], dd[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
+        const float p0 = exp2f(fmaf(sa[i], p.scale_log2, -lse_s[m0]));
+        const float p1 = exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[m1]));
+        pp[i >> 1] = pack_bf16(p0, p1);
+        dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[m0]), p1 * (pa[i + 1] - del_s[m1]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          dv[nb] = mfma32(col_frag(gs, ks, nb, lane), pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
+          dk[nb] = mfma32(col_frag(qs, ks, nb, lane), pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
+        }
+    }
+  }
+  // lane = key; element i of block nb = feature 32 nb + out_row(i)
+  if (l32 < nk) {
+    float* dvr = p.dv + (bh * L + key0 + l32) * BD;
+    float* dkr = p.dk + (bh * L + key0 + l32) * BD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int f = 32 * nb + 8 * rr + 4 * hh;
+        *reinterpret_cast<f32x4*>(dvr + f) = f32x4{dv[nb][4 * rr], dv[nb][4 * rr + 1], dv[nb][4 * rr + 2], dv[nb][4 * rr + 3]};
+        *reinterpret_cast<f32x4*>(dkr + f) = f32x4{dk[nb][4 * rr] * p.scale, dk[nb][4 * rr + 1] * p.scale,
+                                                   dk[nb][4 * rr + 2] * p.scale, dk[nb][4 * rr + 3] * p.scale};
+      }
+  }
+}
+
+// ---- window gradient of the queries
+__global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ks_t[ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs_t[ROWT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int qtiles = (p.C + 127) / 128;
+  const int total = p.B * p.H * p.N * qtiles;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int tile = logical % qtiles, rest = logical / qtiles;
+  const int c = p.N - 1 - rest % p.N, bh = rest / p.N;
+  const int b = bh / p.H, h = bh % p.H;
+  const int64_t L = (int64_t)p.N * p.C;
+  const int64_t head = b * p.sb + h * p.sh;
+  const bf16_t* qb = (const bf16_t*)p.q + head;
+  const bf16_t* kb = (const bf16_t*)p.k + head;
+  const bf16_t* vb = (const bf16_t*)p.v + head;
+  const bf16_t* gb = (const bf16_t*)p.dout + head;
+
+  const int64_t row0 = (int64_t)c * p.C + 128 * tile + 32 * wave;  // this wave's first query
+  const int nq = (int)max((int64_t)0, min((int64_t)32, (int64_t)(c + 1) * p.C - row0));
+  const bool qok = l32 < nq;
+  bf16x8 qr[8], gr[8];  // this lane's rows of Q and dO
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 a = {0u, 0u, 0u, 0u}, g = {0u, 0u, 0u, 0u};
+    if (qok) {
+      a = ld16(qb + (row0 + l32) * p.st + 16 * ks + 8 * hh);
+      g = ld16(gb + (row0 + l32) * p.st + 16 * ks + 8 * hh);
+    }
+    qr[ks] = __builtin_bit_cast(bf16x8, a);
+    gr[ks] = __builtin_bit_cast(bf16x8, g);
+  }
+  const float lse2 = qok ? p.lse[bh * L + row0 + l32] * kLog2e : INFINITY;
+  const float del = qok ? p.delta[bh * L + row0 + l32] : 0.f;
+  f32x16 dq[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) dq[nb] = f32x16{};
+
+  const int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
+  const int64_t kend = p.w > 0 ? (int64_t)(c + 1) * p.C : 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += RB) {
+    const int nk = (int)min((int64_t)RB, kend - k0);
+    __syncthreads();
+    for (int u = tid; u < 2 * RB * 16; u += TB) {
+      const int which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < nk) x = ld16((which ? vb : kb) + (k0 + r) * p.st + g * 8);
+      put_granule(which ? vs_t : ks_t, r, g, x);
+    }
+    __syncthreads();
+    f32x16 sa = {}, pa = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sa = mfma32(row_frag(ks_t, 0, ks, lane), qr[ks], sa);  // S^T = K Q^T, queries on the lanes
+      pa = mfma32(row_frag(vs_t, 0, ks, lane), gr[ks], pa);  // dP^T = V dO^T
+    }
+    uint32_t dd[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
+      const float p0 = m0 < nk ? exp2f(fmaf(sa[i], p.scale_log2, -lse2)) : 0.f;
+      const float p1 = m1 < nk ? exp2f(fmaf(sa[i + 1], p.scale_log2, -lse2)) : 0.f;
+      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del), p1 * (pa[i + 1] - del));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) dq[nb] = mfma32(col_frag(ks_t, ks, nb, lane), pack_b(dd, ks), dq[nb]);  // dQ^T += K^T dS^T
+  }
+  if (qok) {
+    float* dqr = p.dq + (bh * L + row0 + l32) * BD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int f = 32 * nb + 8 * rr + 4 * hh;
+        *reinterpret_cast<f32x4*>(dqr + f) = f32x4{dq[nb][4 * rr] * p.scale, dq[nb][4 * rr + 1] * p.scale,
+                                                   dq[nb][4 * rr + 2] * p.scale, dq[nb][4 * rr + 3] * p.scale};
+      }
+  }
+}
+
+// ---- the linear term: rows times a d x d state.
+//   MODE 0 (query chunks c >= w):  dq_i += ((dout_i / D_i) S_c^T - z_c delta_i / D_i) * phi'(q_i)
+//   MODE 1 (key chunks j <= N-1-w): dv_t += phi(k_t) dU_j,  dk_t += (v_t dU_j^T + du_j) * phi'(k_t)
+// One workgroup per 128 rows of a chunk; the state is staged in LDS as bf16
+// rows (output feature m, input feature k), transposed where needed.
+template <int MODE>
+__global__ __launch_bounds__(TB) void bwd_rowstate_kernel(const BwdParams p, int chunk_lo, int n_chunks) {
+  __shared__ __attribute__((aligned(1024))) unsigned char m1[BD * BD * 2];
+  __shared__ __attribute__((aligned(1024))) unsigned char m2[MODE == 1 ? BD * BD * 2 : 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int rtiles = (p.C + 127) / 128;
+  const int tile = blockIdx.x % rtiles, rest = blockIdx.x / rtiles;
+  const int c = chunk_lo + rest % n_chunks, bh = rest / n_chunks;
+  const int b = bh / p.H, h = bh % p.H;
+  const int64_t L = (int64_t)p.N * p.C;
+  const int64_t head = b * p.sb + h * p.sh;
+  const float* Mst = MODE == 0 ? p.S + ((int64_t)bh * p.N + c) * BD * BD : p.dS + ((int64_t)bh * p.N + c) * BD * BD;
+  const float* zst = MODE == 0 ? p.z + ((int64_t)bh * p.N + c) * BD : p.dz + ((int64_t)bh * p.N + c) * BD;
+
+  // stage: m1 rows e = M[e][:] (MODE 0: S_c; MODE 1: dU for dk), m2 rows n = M[:][n] (MODE 1: dU^T for dv)
+  for (int u = tid; u < BD * BD / 8; u += TB) {
+    const int e = u / (BD / 8), g = u % (BD / 8);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(Mst + (int64_t)e * BD + g * 8);
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(Mst + (int64_t)e * BD + g * 8 + 4);
+    put_granule(m1, e, g, u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c4[0], c4[1]), pack_bf16(c4[2], c4[3])});
+    if constexpr (MODE == 1) {
+      const float vals[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = g * 8 + i;  // row n of the transpose, column e
+        *reinterpret_cast<uint16_t*>(m2 + gran_off(n, e >> 3) + (e & 7) * 2) = (uint16_t)(pack_bf16(vals[i], 0.f) & 0xffffu);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t row0 = (int64_t)c * p.C + 128 * tile + 32 * wave;
+  const int nr = (int)max((int64_t)0, min((int64_t)32, (int64_t)(c + 1) * p.C - row0));
+  const bool ok = l32 < nr;
+  const int64_t t = row0 + l32;  // this lane's token
+  const bf16_t* xq = (const bf16_t*)(MODE == 0 ? p.dout : p.k) + head + t * p.st;
+  const bf16_t* xv = (const bf16_t*)p.v + head + t * p.st;
+  const float rs = (MODE == 0 && ok) ? p.rsc[bh * L + t] : 0.f;
+
+  f32x16 o1[4], o2[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) o1[mb] = o2[mb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (ok) {
+      x = ld16(xq + 16 * ks + 8 * hh);
+      if constexpr (MODE == 1) y = ld16(xv + 16 * ks + 8 * hh);
+    }
+    bf16x8 bx;
+    if constexpr (MODE == 0) {  // dout_i / D_i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * rs, bf16_hi(x[i]) * rs);
+      bx = __builtin_bit_cast(bf16x8, x);
+    } else {  // phi(k_t) for dv; v_t for dk
+      bx = ok ? fwd::phi8(__builtin_bit_cast(bf16x8, x)) : __builtin_bit_cast(bf16x8, x);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if constexpr (MODE == 0) {
+        o1[mb] = mfma32(row_frag(m1, 32 * mb, ks, lane), bx, o1[mb]);  // (S_c dN^T): m = e
+      } else {
+        o1[mb] = mfma32(row_frag(m2, 32 * mb, ks, lane), bx, o1[mb]);  // dU^T phi(k)^T: m = n
+        o2[mb] = mfma32(row_frag(m1, 32 * mb, ks, lane), __builtin_bit_cast(bf16x8, y), o2[mb]);  // dU v^T: m = e
+      }
+    }
+  }
+  if (!ok) return;
+  // lane = token; element i of block mb = feature 32 mb + out_row(i)
+  const bf16_t* xr = (const bf16_t*)(MODE == 0 ? p.q : p.k) + head + t * p.st;  // phi' argument
+  float* g1 = (MODE == 0 ? p.dq : p.dv) + (bh * L + t) * BD;
+  float* g2 = p.dk + (bh * L + t) * BD;
+  const float dD = MODE == 0 ? p.zw[bh * L + t] : 0.f;  // -delta_i / D_i
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int f = 32 * mb + 8 * rr + 4 * hh;
+      const f32x4 zz = *reinterpret_cast<const f32x4*>(zst + f);
+      const u32x2 xw = *reinterpret_cast<const u32x2*>(xr + f);
+      const float xs[4] = {bf16_lo(xw[0]), bf16_hi(xw[0]), bf16_lo(xw[1]), bf16_hi(xw[1])};
+      float dphi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dphi[i] = xs[i] > 0.f ? 1.f : __expf(xs[i]);
+      if constexpr (MODE == 0) {
+        f32x4 a = *reinterpret_cast<f32x4*>(g1 + f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] += (o1[mb][4 * rr + i] + zz[i] * dD) * dphi[i];
+        *reinterpret_cast<f32x4*>(g1 + f) = a;
+      } else {
+        f32x4 a = *reinterpret_cast<f32x4*>(g1 + f);
+        f32x4 k4 = *reinterpret_cast<f32x4*>(g2 + f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] += o1[mb][4 * rr + i];
+          k4[i] += (o2[mb][4 * rr + i] + zz[i]) * dphi[i];
+        }
+        *reinterpret_cast<f32x4*>(g1 + f) = a;
+        *reinterpret_cast<f32x4*>(g2 + f) = k4;
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
+  const int64_t BH = (int64_t)p.B * p.H;
+  const int64_t L = (int64_t)p.N * p.C;
+  if (BH == 0 || L == 0) return hipSuccess;
+  const int tiles128 = (p.C + 127) / 128;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((BH * L + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.w >= p.N) return hipSuccess;  // no chunk has a state: no linear term
+  // dS_c, dz_c of chunks c >= w into slot c - w, then slot j <- sum over slots j .. N-1-w = dU_j
+  ChunkStateParams c{};
+  c.k = p.q;
+  c.v = p.dout;
+  c.S = p.dS;
+  c.z = p.dz;
+  c.kv_sb = p.sb;
+  c.kv_sh = p.sh;
+  c.kv_st = p.st;
+  c.s_bh = (int64_t)p.N * BD * BD;
+  c.z_bh = (int64_t)p.N * BD;
+  c.B = p.B;
+  c.H = p.H;
+  c.C = p.C;
+  c.chunk0 = 0;
+  c.n_chunks = p.N;
+  c.slot_offset = -p.w;
+  c.n_slots = p.N;
+  c.accumulate = 0;
+  c.tok_end = L;
+  c.vscale = p.rsc;
+  c.zweight = p.zw;
+  c.scale_bh = L;
+  e = launch_chunk_state_bf16(c, BD, s);
+  if (e != hipSuccess) return e;
+  PrefixParams pr{p.dS, p.dz, (int)BH, p.N, p.w, BD, 1};
+  e = launch_prefix(pr, s);
+  if (e != hipSuccess) return e;
+  const int nq = p.N - p.w;  // query chunks with a state: w .. N-1 (all for w = 0)
+  hipLaunchKernelGGL(bwd_rowstate_kernel<0>, dim3((unsigned)(BH * nq * tiles128)), dim3(TB), 0, s, p, p.w, nq);
+  hipLaunchKernelGGL(bwd_rowstate_kernel<1>, dim3((unsigned)(BH * nq * tiles128)), dim3(TB), 0, s, p, 0, nq);
+  return hipGetLastError();
+}
+
+}  // namespace rha

@@ -114,6 +114,12 @@ struct ChunkStateParams {
   // set): copy_blocks_per_bh workgroups of 256 threads per (tensor, head).
   CopyParams copy;
   int copy_blocks_per_bh;
+  // Optional per-token factors (the backward pass's state gradient): v rows
+  // are multiplied by vscale[bh * scale_bh + token] before rounding, and z
+  // sums phi(k_t) * zweight[bh * scale_bh + token] (token: index in the head).
+  const float* vscale;
+  const float* zweight;
+  int64_t scale_bh;
 };
 
 // In-place inclusive prefix over the state slots of every head:
@@ -126,6 +132,35 @@ struct PrefixParams {
   int BH, N, w, d;
   int reverse;
 };
+
+// Backward pass of the causal hybrid (head_dim 128, bf16 inputs): gradients
+// of sum(dout * out) with respect to q, k, v, in float32 [B,H,L,d]
+// (contiguous).  delta, rsc, zw: float32 [B,H,L] scratch (dout . out,
+// exp(-lse), -delta * exp(-lse)); dS, dz: float32 [B,H,N,d,d] / [B,H,N,d]
+// scratch for the state gradients.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  const float* S;
+  const float* z;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;
+  float* rsc;
+  float* zw;
+  float* dS;
+  float* dz;
+  int64_t sb, sh, st;  // element strides of q, k, v, out, dout
+  int B, H, C, N, w;
+  float scale_log2;  // log2(e) / sqrt(d)
+  float scale;       // 1 / sqrt(d)
+};
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
 
 // The forward launchers fill in tiles_per_chunk and total_tiles (they depend
 // on the kernel's tile height) before launching.

@@ -73,7 +73,9 @@ __device__ __forceinline__ bf16x8 read_frag_t(const unsigned char* tile, int ks,
   return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 }
 
-template <int D>
+// SCALED: the per-token factors vscale / zweight are applied (a separate
+// instantiation, so the plain one keeps its registers).
+template <int D, bool SCALED>
 __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkStateParams p) {
   using Cfg = StateCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char kt_s[2][Cfg::KBYTES];  // phi(K) slice, 2 buffers
@@ -144,26 +146,43 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
       vw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
     }
   };
+  const int64_t sbase = (int64_t)bh * p.scale_bh + t0;  // per-token factors of this chunk
   auto lstore = [&](int j, int buf, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int r = 0; r < Cfg::KG; ++r) {
       const int row = krow0 + r * Cfg::KROWSTEP;
       const bool ok = j * BT + row < len;  // rows past the chunk: phi(0) would be 1
+      float zw = 1.f;
+      if constexpr (SCALED) zw = ok ? p.zweight[sbase + j * BT + row] : 0.f;
       u32x4 fw;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float a = ok ? phi(bf16_lo(kw[sl][r][i])) : 0.f;
         const float c = ok ? phi(bf16_hi(kw[sl][r][i])) : 0.f;
-        zacc[2 * i] += a;
-        zacc[2 * i + 1] += c;
+        if constexpr (SCALED) {
+          zacc[2 * i] += a * zw;
+          zacc[2 * i + 1] += c * zw;
+        } else {
+          zacc[2 * i] += a;
+          zacc[2 * i + 1] += c;
+        }
         fw[i] = pack_bf16(a, c);
       }
       store_granule<ESLICE>(kt_s[buf], row, kfo, fw);
     }
     if (vact) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store_granule<D>(vt_s[buf], vtq * 4 + r, vfo, vw[sl][r]);
+      for (int r = 0; r < 4; ++r) {
+        u32x4 x = vw[sl][r];
+        if constexpr (SCALED) {
+          const int tok = j * BT + vtq * 4 + r;
+          const float sc = tok < len ? p.vscale[sbase + tok] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * sc, bf16_hi(x[i]) * sc);
+        }
+        store_granule<D>(vt_s[buf], vtq * 4 + r, vfo, x);
+      }
     }
   };
   auto mma = [&](int buf) {
@@ -254,12 +273,17 @@ hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t
   const int64_t heads_chunks = (int64_t)p.B * p.H * p.n_chunks;
   // extra workgroups for a cache copy in the same launch (2 tensors x B*H heads)
   const int64_t copy_blocks = p.copy.src != nullptr ? 2 * (int64_t)p.B * p.H * p.copy_blocks_per_bh : 0;
-  if (d == 128)
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<128>, dim3((unsigned)(heads_chunks * StateCfg<128>::ES + copy_blocks)),
-                       dim3(THREADS), 0, s, p);
+  const bool scaled = p.vscale != nullptr;
+  const dim3 g128((unsigned)(heads_chunks * StateCfg<128>::ES + copy_blocks));
+  const dim3 g64((unsigned)(heads_chunks * StateCfg<64>::ES + copy_blocks));
+  if (d == 128 && scaled)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<128, true>), g128, dim3(THREADS), 0, s, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<128, false>), g128, dim3(THREADS), 0, s, p);
+  else if (scaled)
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<64, true>), g64, dim3(THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(chunk_state_bf16_kernel<64>, dim3((unsigned)(heads_chunks * StateCfg<64>::ES + copy_blocks)),
-                       dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL((chunk_state_bf16_kernel<64, false>), g64, dim3(THREADS), 0, s, p);
   return hipGetLastError();
 }
 

@@ -237,3 +237,16 @@ def test_anchor_checks(L):
     # anchor and window tiles listed per query chunk: at most 2048 tiles of 64 keys
     big = _prob(anchor_chunks=20, n_chunks=40, window=20, chunk_len=4000, stride_b=0, stride_h=0)
     assert _fwd(L, big) == 2 and "key tiles" in L.rha_last_error().decode()
+
+
+def test_backward_checks(L):
+    args = [P] * 11
+    assert L.rha_hybrid_bwd(ctypes.byref(_prob(dtype=_rha.RHA_F32, stride_t=128)), *args, 1 << 30, None) == 2
+    assert L.rha_hybrid_bwd(ctypes.byref(_prob(anchor_chunks=1)), *args, 1 << 30, None) == 2
+    ok = _prob()
+    need = L.rha_hybrid_bwd_workspace_size(ctypes.byref(ok))
+    assert need > 0
+    assert L.rha_hybrid_bwd(ctypes.byref(ok), *args, need - 1, None) == 1
+    assert "workspace" in L.rha_last_error().decode()
+    assert L.rha_hybrid_bwd(ctypes.byref(ok), *args[:6], None, *args[7:], need, None) == 1  # lse required
+    assert "lse" in L.rha_last_error().decode()
