@@ -240,7 +240,7 @@ def test_anchor_checks(L):
 
 
 def test_backward_checks(L):
-    args = [P] * 11
+    args = [P] * 12
     assert L.rha_hybrid_bwd(ctypes.byref(_prob(dtype=_rha.RHA_F32, stride_t=128)), *args, 1 << 30, None) == 2
     assert L.rha_hybrid_bwd(ctypes.byref(_prob(anchor_chunks=1)), *args, 1 << 30, None) == 2
     ok = _prob()
