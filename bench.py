@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir|anchor   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir|anchor|bwd   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -100,6 +100,22 @@ def anchor_fwd_flops(C, N, w, a, d, BH):
     return f * BH
 
 
+def bwd_flops(C, N, w, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_bwd call: 10d per (query, window key)
+    pair (scores recomputed once, dP, dV, dQ, dK: the usual five products), 4d^2
+    per query with a state (dS and the query gradient of the linear term) and
+    4d^2 per token folded into some state (its value and key gradients)."""
+    f = 0
+    for c in range(N):
+        nwin = min(c + 1, w) * C if w > 0 else 0
+        f += C * 10 * d * nwin
+        if w == 0 or c >= w:
+            f += C * 4 * d * d
+        if c <= N - 1 - w:
+            f += C * 4 * d * d
+    return f * BH
+
+
 def stream_step_flops(C, w, d, BH):
     """Algorithmic FLOPs of one rha_stream_step with a full window: the new
     chunk's queries against w cached chunks (4d per pair) and the state (2d^2
@@ -168,7 +184,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor"], default=None)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -276,6 +292,23 @@ def main():
         torch.cuda.synchronize()
         return
 
+    # ---- backward pass at the same shape (seeded dout)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    dout = torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(dev)
+    lse_f = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+    out_f = torch.empty_like(q)
+    rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+    rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out_f, lse=lse_f, stream=stream)
+
+    def bwd_call():
+        rha.hybrid_bwd(q, k, v, S, z, out_f, lse_f, dout, wl.C, wl.w, stream=stream)
+
+    if args.only == "bwd":
+        for _ in range(args.steps):
+            bwd_call()
+        torch.cuda.synchronize()
+        return
+
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
     def stream_run(timed_run):
         sw = CONFIGS["stream"]
@@ -327,6 +360,8 @@ def main():
     t_bidir_scan = timed(bidir_scan, n_k)
     bF = bidir_fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     t_anchor = timed(anchor_call, n_k)
+    t_bwd = timed(bwd_call, max(args.steps // 5, 5))
+    gF = bwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
 
@@ -381,6 +416,9 @@ def main():
             "anchor1_fwd_us": t_anchor * 1e6,
             "anchor1_TFLOPs": aF / t_anchor / 1e12,
             "anchor1_mfma_frac": aF / t_anchor / 1e12 / PEAK_BF16_TFLOPS,
+            "bwd_us": t_bwd * 1e6,
+            "bwd_TFLOPs": gF / t_bwd / 1e12,
+            "bwd_mfma_frac": gF / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
             "timed_wall_s": wall,
         },
     }

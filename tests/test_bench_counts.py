@@ -58,3 +58,11 @@ def test_anchor_count_limits():
     # every chunk an anchor: block-causal dense attention, no state
     dense = sum(C * 4 * d * (c + 1) * C for c in range(N)) * BH
     assert bench.anchor_fwd_flops(C, N, w, N, d, BH) == dense
+
+
+def test_bwd_count_is_two_and_a_half_forward_products_plus_state_terms():
+    C, N, w, d, BH = 100, 5, 2, 128, 2
+    pairs = sum(C * min(c + 1, w) * C for c in range(N)) * BH
+    state_rows = sum(C for c in range(N) if c >= w) * BH
+    folded = sum(C for c in range(N) if c <= N - 1 - w) * BH
+    assert bench.bwd_flops(C, N, w, d, BH) == pairs * 10 * d + (state_rows + folded) * 4 * d * d
