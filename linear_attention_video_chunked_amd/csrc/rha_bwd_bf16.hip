@@ -112,9 +112,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 
 // ---- window gradients of keys and values
 __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char qs[ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char gs[ROWT];  // dout rows
-  __shared__ float lse_s[RB], del_s[RB];
+  // two buffers of (Q rows, dout rows, lse, delta) for one 32-row query block
+  __shared__ __attribute__((aligned(1024))) unsigned char qs[2][ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char gs[2][ROWT];
+  __shared__ float lse_s[2][RB], del_s[2][RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int ktiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * ktiles;
@@ -146,49 +147,77 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) dv[nb] = dk[nb] = f32x16{};
 
-  // query chunks whose window holds chunk j: j .. j + w - 1
+  // query blocks of the chunks whose window holds chunk j (j .. j + w - 1),
+  // 32 rows each, numbered qi = (c - j) * nqb + block
   const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
-  for (int c = j; c <= c_hi; ++c) {
-    for (int qblk = 0; qblk < nqb; ++qblk) {
-      const int64_t row0 = (int64_t)c * p.C + RB * qblk;
-      const int nq = min(RB, p.C - RB * qblk);
-      __syncthreads();  // the previous block's tiles are no longer read
-      for (int u = tid; u < 2 * RB * 16; u += TB) {
-        const int which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (r < nq) x = ld16((which ? gb : qb) + (row0 + r) * p.st + g * 8);
-        put_granule(which ? gs : qs, r, g, x);
-      }
-      if (tid < RB) {
-        const bool ok = tid < nq;
-        lse_s[tid] = ok ? p.lse[bh * L + row0 + tid] * kLog2e : INFINITY;  // rows past the chunk: P = 0
-        del_s[tid] = ok ? p.delta[bh * L + row0 + tid] : 0.f;
-      }
-      __syncthreads();
-      f32x16 sa = {}, pa = {};
+  const int nblk = (c_hi - j + 1) * nqb;
+  // staging: thread tid moves granules u = tid + 256 i (i < 4) of the block's
+  // 32 Q rows (u < 512) and 32 dout rows (u >= 512); threads < 32 the lse, delta
+  u32x4 stg[4];
+  float lse_r = 0.f, del_r = 0.f;
+  auto fetch = [&](int qi) {
+    const int c = j + qi / nqb, blk = qi % nqb;
+    const int64_t row0 = (int64_t)c * p.C + RB * blk;
+    const int nq = min(RB, p.C - RB * blk);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        sa = mfma32(row_frag(qs, 0, ks, lane), kr[ks], sa);  // S = Q K^T, keys on the lanes
-        pa = mfma32(row_frag(gs, 0, ks, lane), vr[ks], pa);  // dP = dO V^T
-      }
-      uint32_t pp[8], dd[8];
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-        const float p0 = exp2f(fmaf(sa[i], p.scale_log2, -lse_s[m0]));
-        const float p1 = exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[m1]));
-        pp[i >> 1] = pack_bf16(p0, p1);
-        dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[m0]), p1 * (pa[i + 1] - del_s[m1]));
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          dv[nb] = mfma32(col_frag(gs, ks, nb, lane), pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
-          dk[nb] = mfma32(col_frag(qs, ks, nb, lane), pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+      stg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (r < nq) stg[i] = ld16((which ? gb : qb) + (row0 + r) * p.st + g * 8);
     }
+    if (tid < RB) {
+      const bool ok = tid < nq;
+      lse_r = ok ? p.lse[bh * L + row0 + tid] * kLog2e : INFINITY;  // rows past the chunk: P = 0
+      del_r = ok ? p.delta[bh * L + row0 + tid] : 0.f;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+      put_granule(which ? gs[buf] : qs[buf], r, g, stg[i]);
+    }
+    if (tid < RB) {
+      lse_s[buf][tid] = lse_r;
+      del_s[buf][tid] = del_r;
+    }
+  };
+  if (nblk > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int qi = 0; qi < nblk; ++qi) {
+    const int buf = qi & 1;
+    if (qi + 1 < nblk) fetch(qi + 1);  // in flight while this block is multiplied
+    const unsigned char* qt = qs[buf];
+    const unsigned char* gt = gs[buf];
+    f32x16 sa = {}, pa = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sa = mfma32(row_frag(qt, 0, ks, lane), kr[ks], sa);  // S = Q K^T, keys on the lanes
+      pa = mfma32(row_frag(gt, 0, ks, lane), vr[ks], pa);  // dP = dO V^T
+    }
+    uint32_t pp[8], dd[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
+      const float p0 = exp2f(fmaf(sa[i], p.scale_log2, -lse_s[buf][m0]));
+      const float p1 = exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[buf][m1]));
+      pp[i >> 1] = pack_bf16(p0, p1);
+      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[buf][m0]), p1 * (pa[i + 1] - del_s[buf][m1]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        dv[nb] = mfma32(col_frag(gt, ks, nb, lane), pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
+        dk[nb] = mfma32(col_frag(qt, ks, nb, lane), pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
+      }
+    // the other buffer was last read in the previous block, before the barrier that ended it
+    if (qi + 1 < nblk) stash(buf ^ 1);
+    __syncthreads();
   }
   // lane = key; element i of block nb = feature 32 nb + out_row(i)
   if (l32 < nk) {
@@ -208,8 +237,8 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
 
 // ---- window gradient of the queries
 __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ks_t[ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs_t[ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char ks_t[2][ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char vs_t[2][ROWT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int qtiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * qtiles;
@@ -246,21 +275,43 @@ __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
 
   const int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
   const int64_t kend = p.w > 0 ? (int64_t)(c + 1) * p.C : 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += RB) {
+  const int nblk = (int)((kend - kbeg + RB - 1) / RB);
+  // staging of 32-key blocks: thread tid moves granules u = tid + 256 i of
+  // the block's 32 K rows (u < 512) and 32 V rows (u >= 512)
+  u32x4 stg[4];
+  auto fetch = [&](int bi) {
+    const int64_t k0 = kbeg + (int64_t)RB * bi;
     const int nk = (int)min((int64_t)RB, kend - k0);
-    __syncthreads();
-    for (int u = tid; u < 2 * RB * 16; u += TB) {
-      const int which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < nk) x = ld16((which ? vb : kb) + (k0 + r) * p.st + g * 8);
-      put_granule(which ? vs_t : ks_t, r, g, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+      stg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (r < nk) stg[i] = ld16((which ? vb : kb) + (k0 + r) * p.st + g * 8);
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
+      put_granule(which ? vs_t[buf] : ks_t[buf], r, g, stg[i]);
+    }
+  };
+  if (nblk > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int buf = bi & 1;
+    const int nk = (int)min((int64_t)RB, kend - (kbeg + (int64_t)RB * bi));
+    if (bi + 1 < nblk) fetch(bi + 1);  // in flight while this block is multiplied
+    const unsigned char* kt = ks_t[buf];
+    const unsigned char* vt = vs_t[buf];
     f32x16 sa = {}, pa = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      sa = mfma32(row_frag(ks_t, 0, ks, lane), qr[ks], sa);  // S^T = K Q^T, queries on the lanes
-      pa = mfma32(row_frag(vs_t, 0, ks, lane), gr[ks], pa);  // dP^T = V dO^T
+      sa = mfma32(row_frag(kt, 0, ks, lane), qr[ks], sa);  // S^T = K Q^T, queries on the lanes
+      pa = mfma32(row_frag(vt, 0, ks, lane), gr[ks], pa);  // dP^T = V dO^T
     }
     uint32_t dd[8];
 #pragma unroll
@@ -273,7 +324,9 @@ __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) dq[nb] = mfma32(col_frag(ks_t, ks, nb, lane), pack_b(dd, ks), dq[nb]);  // dQ^T += K^T dS^T
+      for (int nb = 0; nb < 4; ++nb) dq[nb] = mfma32(col_frag(kt, ks, nb, lane), pack_b(dd, ks), dq[nb]);  // dQ^T += K^T dS^T
+    if (bi + 1 < nblk) stash(buf ^ 1);
+    __syncthreads();
   }
   if (qok) {
     float* dqr = p.dq + (bh * L + row0 + l32) * BD;
