@@ -603,3 +603,80 @@ def test_backward_matches_torch_autograd(C, N, w):
 def test_dphi_closed_form():
     x = np.array([-3.0, -1e-3, 0.0, 1e-3, 2.0])
     np.testing.assert_allclose(O.dphi(x), [math.exp(-3.0), math.exp(-1e-3), 1.0, 1.0, 1.0], rtol=1e-15)
+
+
+@pytest.mark.parametrize("C,N,w", [(6, 4, 4), (5, 3, 7), (1, 23, 23)])
+def test_backward_window_all_equals_sdpa_gradient(C, N, w):
+    """A window covering every chunk is block-causal softmax attention: the
+    oracle's gradients equal torch autograd through fp64 SDPA with that mask."""
+    d = 16
+    q, k, v = _qkv(C * N, d, 1700 + C + N, qs=1.5)
+    dout = _rand((C * N, d), 1800 + C)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True)[None, None] for x in (q, k, v))
+    for t in (tq, tk, tv):
+        t.retain_grad()
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=_block_causal(C * N, C))
+    (o[0, 0] * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_backward(q, k, v, C, w, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N", [(1, 30), (4, 6)])
+def test_backward_window0_equals_linear_attention_gradient(C, N):
+    """w = 0 is causal linear attention (the state includes the own chunk):
+    the oracle's gradients equal torch autograd through a cumulative-sum form."""
+    d = 6
+    q, k, v = _qkv(C * N, d, 1900 + C, qs=1.2)
+    dout = _rand((C * N, d), 2000 + C)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    fq = torch.nn.functional.elu(tq) + 1
+    fk = torch.nn.functional.elu(tk) + 1
+    kv = torch.cumsum(fk[:, :, None] * tv[:, None, :], dim=0)  # [L, d, d]: running sum of phi(k) v^T
+    ks = torch.cumsum(fk, dim=0)
+    last = (torch.arange(C * N) // C) * C + C - 1  # each row reads the state after its chunk's last token
+    o = torch.einsum("ld,lde->le", fq, kv[last]) / (fq * ks[last]).sum(dim=1, keepdim=True)
+    (o * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_backward(q, k, v, C, 0, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _backward_pin_errs():
+    """Largest deviation of the oracle's gradients from (a) finite differences
+    of its own forward and (b) torch autograd through the dense form."""
+    C, N, w, d = 3, 4, 2, 5
+    q, k, v = _qkv(C * N, d, 2100, qs=1.2)
+    dout = _rand((C * N, d), 2101)
+    grads = O.hybrid_backward(q, k, v, C, w, dout)
+    rng = np.random.default_rng(2102)
+    fd_err = 0.0
+    for which, g in enumerate(grads):
+        dirn = rng.standard_normal(q.shape)
+        ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+        ap[which] += 1e-5 * dirn
+        am[which] -= 1e-5 * dirn
+        fd = (_loss(*ap, C, w, dout) - _loss(*am, C, w, dout)) / 2e-5
+        fd_err = max(fd_err, abs(fd - float((g * dirn).sum())))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_hybrid(tq, tk, tv, C, w) * torch.from_numpy(dout)).sum().backward()
+    ag_err = max(float(np.max(np.abs(g - t.grad.numpy()))) for g, t in zip(grads, (tq, tk, tv)))
+    return fd_err, ag_err
+
+
+BACKWARD_MUTANTS = {
+    "dphi_constant_one": ("dphi", lambda orig: (lambda x: np.ones_like(np.asarray(x, np.float64)))),
+    "dphi_of_phi": ("dphi", lambda orig: (lambda x: orig(x) + 0.5 * (np.asarray(x) < 0))),
+    "window_one_chunk_short": ("window_range",
+                               lambda orig: (lambda c, w: (max(0, c - w + 2), c) if w > 0 else (c + 1, c))),
+    "score_sign_flip": ("_scores", lambda orig: (lambda q, k: -orig(q, k))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    assert max(_backward_pin_errs()) > 1e-6
+
+
+def test_backward_unmutated_pins_pass():
+    assert max(_backward_pin_errs()) < 1e-8
