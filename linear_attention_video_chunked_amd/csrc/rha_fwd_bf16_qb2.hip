@@ -29,9 +29,13 @@
 //   buffer loads (zero past the window end) into XOR-swizzled LDS; V is read
 //   transposed with ds_read_b64_tr_b16; tiles are visited in an XCD-aware
 //   order, longest windows first.
+// * A short tail of a chunk (C mod 256 rows, at most 32) would leave three of
+//   its tile's four waves without rows; its workgroup instead splits the
+//   tail's key window four ways between its waves (tail_pass).
 #include <type_traits>
 
 #include "rha_device.hpp"
+#include "rha_frag.hpp"
 #include "rha_fwd_common.hpp"
 #include "rha_launch.hpp"
 #include "rha_small.hpp"
@@ -186,7 +190,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // act(t) is the window tile that visit t loads.
   int Tp = T;
   if constexpr (SPARSE) {
-    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.tiles_per_chunk + tile) * p.nkt;
+    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + tile) * p.nkt;
     if (wave == 0) {
       int base = 0;
       for (int j0 = 0; j0 < T; j0 += 64) {
@@ -749,6 +753,319 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   return dirty;
 }
 
+// ---- Short chunk tails (causal or bidirectional window, seq mode).
+// Rows C - tail_rows .. C - 1 of chunk c (at most 32), the chunk's last tile
+// in the launch order (so it runs next to the chunk's other tiles, on the same
+// XCD, while their keys are in L2).
+// Wave i takes the i-th quarter of the window's 32-key blocks with its own
+// running maximum m_i and sum l_i (plain online softmax, rescaled when the
+// maximum grows); the linear term enters every wave at reference 0, wave i
+// taking output features 32i .. 32i+31 of phi(Q) S and wave 0 the
+// denominator term phi(q).z.  The four partial results meet in LDS:
+//   out = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// Products as in the tiles: S^T = K Q^T (one query per lane), O^T += V^T P^T
+// with V read transposed; each wave stages its 32-key blocks of K and V in
+// its own LDS buffer, the next block's rows in flight in registers.
+// A pruned pass (SPARSE) visits only the 32-key blocks of kept 64-key tiles
+// (mask row: query tile C / 256 of the chunk).
+constexpr int kTailMaxRows = 32;
+
+template <bool SPARSE>
+__device__ __noinline__ void tail_pass(const FwdParams pin) {
+  using namespace frag;
+  // The parameters are the same in every lane; copies through readfirstlane
+  // let the compiler keep them (and the block loops) scalar in this
+  // out-of-line function.
+  auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto rfl64 = [](int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  auto uni = [&](const void* ptr) { return (void*)rfl64((int64_t)ptr); };
+  struct {
+    const void *q, *k, *v;
+    void* out;
+    float* lse;
+    const float *S, *z, *S2, *z2;
+    const unsigned char* kmask;
+    int64_t q_sb, q_sh, q_st, kv_sb, kv_sh, kv_st;
+    int H, C, w, n_qchunks, tiles_per_chunk, total_tiles, bidir, tail_rows, mask_qtiles, nkt;
+    float scale_log2;
+  } p;
+  p.q = uni(pin.q);
+  p.k = uni(pin.k);
+  p.v = uni(pin.v);
+  p.out = uni(pin.out);
+  p.lse = (float*)uni(pin.lse);
+  p.S = (const float*)uni(pin.S);
+  p.z = (const float*)uni(pin.z);
+  p.S2 = (const float*)uni(pin.S2);
+  p.z2 = (const float*)uni(pin.z2);
+  p.kmask = (const unsigned char*)uni(pin.kmask);
+  p.q_sb = rfl64(pin.q_sb);
+  p.q_sh = rfl64(pin.q_sh);
+  p.q_st = rfl64(pin.q_st);
+  p.kv_sb = rfl64(pin.kv_sb);
+  p.kv_sh = rfl64(pin.kv_sh);
+  p.kv_st = rfl64(pin.kv_st);
+  p.H = rfl(pin.H);
+  p.C = rfl(pin.C);
+  p.w = rfl(pin.w);
+  p.n_qchunks = rfl(pin.n_qchunks);
+  p.tiles_per_chunk = rfl(pin.tiles_per_chunk);
+  p.total_tiles = rfl(pin.total_tiles);
+  p.bidir = rfl(pin.bidir);
+  p.tail_rows = rfl(pin.tail_rows);
+  p.mask_qtiles = rfl(pin.mask_qtiles);
+  p.nkt = rfl(pin.nkt);
+  p.scale_log2 = __int_as_float(rfl(__float_as_int(pin.scale_log2)));
+  static_assert(Q2_NW == 4 && Q2_TILE == 2 * ROWT, "four waves, each with a buffer for a 32-key block of K and V");
+  static_assert(Q2_TILE == BD * 32 * 4, "one wave's partial output (128 features x 32 rows, float32) fits its buffer");
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block loops stay scalar
+  const int rest = xcd_remap(blockIdx.x, p.total_tiles) / p.tiles_per_chunk;  // as in tile_pass
+  const int c = p.n_qchunks - 1 - rest % p.n_qchunks;
+  const int bh = rest / p.n_qchunks;
+  const int b = bh / p.H, h = bh % p.H;
+  const int nr = p.tail_rows;  // 1 .. kTailMaxRows (checked by the launcher)
+  const int r0 = p.C - nr;
+  const int64_t qtok0 = (int64_t)c * p.C + r0;
+  const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh;
+  const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh;
+
+  int64_t kbeg = 0, kend = 0;
+  if (p.w > 0) {
+    kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
+    kend = (int64_t)(p.bidir ? min(p.n_qchunks, c + p.w) : c + 1) * p.C;
+  }
+  const bool has_past = (p.w == 0) || (c >= p.w);
+  const bool has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
+
+  // Q rows of the tail, second operand, one query per lane (lanes past the
+  // tail repeat its last row; their results are not written)
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = (const bf16_t*)p.q + b * p.q_sb + h * p.q_sh + (qtok0 + min(l32, nr - 1)) * p.q_st;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * ks + 8 * hh));
+  }
+  unsigned char* const vbuf = wave == 0 ? q2_kb0 : wave == 1 ? q2_kb1 : wave == 2 ? q2_vb0 : q2_vb1;
+  f32x16 o[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) o[nb] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  if (has_past || has_future) {
+    // Wave i: output features v = 32 i + lane % 32 of phi(Q) S at reference 0.
+    // The first operand holds S[16 ks + 8 (lane / 32) + 0..7][v], read straight
+    // from memory (32 lanes read 32 consecutive floats of a row of S).
+    const int64_t slot = (int64_t)bh * p.n_qchunks + c;
+    const float* Sp = p.S + slot * BD * BD + 32 * wave + l32;
+    const float* Sp2 = p.bidir ? p.S2 + slot * BD * BD + 32 * wave + l32 : nullptr;
+    float col[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int f = 16 * ks + 8 * hh + e;
+        col[ks][e] = has_past ? Sp[f * BD] : 0.f;
+        if (has_future) col[ks][e] += Sp2[f * BD];
+      }
+    f32x16 t = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 a = {pack_bf16(col[ks][0], col[ks][1]), pack_bf16(col[ks][2], col[ks][3]),
+                       pack_bf16(col[ks][4], col[ks][5]), pack_bf16(col[ks][6], col[ks][7])};
+      t = mfma32(__builtin_bit_cast(bf16x8, a), phi8(qf[ks]), t);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      if (nb == wave) o[nb] = t;
+    if (wave == 0) {  // phi(q).z, summed over both halves of the features
+      const float* zp = p.z + slot * BD;
+      const float* zp2 = p.bidir ? p.z2 + slot * BD : nullptr;
+      float acc = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 x = __builtin_bit_cast(u32x4, qf[ks]);
+        const int f0 = 16 * ks + 8 * hh;
+        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+        if (has_past) {
+          z0 = *reinterpret_cast<const f32x4*>(zp + f0);
+          z1 = *reinterpret_cast<const f32x4*>(zp + f0 + 4);
+        }
+        if (has_future) {
+          z0 += *reinterpret_cast<const f32x4*>(zp2 + f0);
+          z1 += *reinterpret_cast<const f32x4*>(zp2 + f0 + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qv = (e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1]);
+          acc = fmaf(phi(qv), e < 4 ? z0[e] : z1[e - 4], acc);
+        }
+      }
+      const float tot = half_sum(acc);  // the lane swap needs every lane active
+      l = hh == 0 ? tot : 0.f;
+    }
+    m = 0.f;
+  }
+
+  // this wave's quarter of the window's 32-key blocks
+  const int nblk = (int)((kend - kbeg + RB - 1) / RB);
+  const int j0 = wave * nblk / Q2_NW, j1 = (wave + 1) * nblk / Q2_NW;
+  const unsigned char* mrow =
+      SPARSE ? p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + p.mask_qtiles - 1) * p.nkt : nullptr;
+  auto next_kept = [&](int j) {  // first visited block at or after j (j1 if none)
+    if constexpr (SPARSE)
+      while (j < j1 && mrow[j >> 1] == 0) ++j;
+    return j;
+  };
+  // Blocks are taken in pairs (an odd count ends with a padding block past
+  // the window, fully masked).  Per pair: V rows go to the wave's LDS buffer
+  // (8 KB per block) and the next pair's V is loaded; S^T = K Q^T for both
+  // blocks as two interleaved product chains (K rows straight from memory
+  // as the first operand); the next pair's K is loaded; one online-softmax
+  // step over both blocks; then O^T += V^T P^T for both.  Buffer loads whose
+  // descriptors end at the window end read zeros past it (and for padding).
+  const int row_bytes = (int)p.kv_st * 2;
+  const int win_bytes = (int)(kend * p.kv_st * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
+  auto blk_off = [&](int j) { return j < j1 ? (int)((kbeg + (int64_t)RB * j) * p.kv_st * 2) : win_bytes; };
+  const int vofs = (lane >> 4) * row_bytes + (lane & 15) * 16;  // V: 16 lanes per 256-byte row
+  const int kofs = l32 * row_bytes + hh * 16;                   // K: row lane % 32, features 8 (lane / 32) + 16 ks
+  u32x4 kr[2][8], vr[2][8];
+  auto load_k = [&](int ja_, int jb_) __attribute__((always_inline)) {
+    const int oa = blk_off(ja_) + kofs, ob = blk_off(jb_) + kofs;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kr[0][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, oa + 32 * ks, 0, 0));
+      kr[1][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ob + 32 * ks, 0, 0));
+    }
+  };
+  auto load_v = [&](int ja_, int jb_) __attribute__((always_inline)) {
+    const int oa = blk_off(ja_) + vofs, ob = blk_off(jb_) + vofs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vr[0][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, oa + 4 * i * row_bytes, 0, 0));
+      vr[1][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ob + 4 * i * row_bytes, 0, 0));
+    }
+  };
+  auto nk_of = [&](int j) { return j < j1 ? (int)min((int64_t)RB, kend - (kbeg + (int64_t)RB * j)) : 0; };
+  unsigned char* const vt[2] = {vbuf, vbuf + ROWT};
+  int ja = next_kept(j0);
+  int jb = ja < j1 ? next_kept(ja + 1) : j1;
+  load_v(ja, jb);
+  load_k(ja, jb);
+  while (ja < j1) {
+    const int na = jb < j1 ? next_kept(jb + 1) : j1;
+    const int nb_ = na < j1 ? next_kept(na + 1) : j1;
+    // the wave's LDS operations run in order: these writes land after the
+    // previous pair's reads
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) put_granule(vt[sl], (lane >> 4) + 4 * i, lane & 15, vr[sl][i]);
+    load_v(na, nb_);
+    f32x16 sa[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) sa[sl] = mfma32(__builtin_bit_cast(bf16x8, kr[sl][ks]), qf[ks], sa[sl]);
+    load_k(na, nb_);
+    const int nk[2] = {nk_of(ja), nk_of(jb)};
+    float bm = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (nk[sl] == RB) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sa[sl][i] *= p.scale_log2;
+          bm = fmaxf(bm, sa[sl][i]);
+        }
+      } else {  // the window's last, partial block, or padding
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sa[sl][i] = out_row(i, hh) < nk[sl] ? sa[sl][i] * p.scale_log2 : -INFINITY;
+          bm = fmaxf(bm, sa[sl][i]);
+        }
+      }
+    }
+    const float mn = fmaxf(m, half_max(bm));
+    if (__any(mn > m)) {
+      const float sc = exp2f(m - mn);
+      l *= sc;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) o[nb] *= sc;
+      m = mn;
+    }
+    uint32_t pp[2][8];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(sa[sl][i] - m), p1 = __builtin_amdgcn_exp2f(sa[sl][i + 1] - m);
+        l += p0 + p1;
+        pp[sl][i >> 1] = pack_bf16(p0, p1);
+      }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) o[nb] = mfma32(col_frag(vt[sl], ks, nb, lane), pack_b(pp[sl], ks), o[nb]);  // O^T += V^T P^T
+    ja = na;
+    jb = nb_;
+  }
+
+  // ---- merge: partial O^T [feature][row] in the wave's buffer, m and l per row
+  float* const ow = reinterpret_cast<float*>(vbuf);
+  float* const sm = reinterpret_cast<float*>(q2_act);   // [wave][32]
+  float* const sl = reinterpret_cast<float*>(q2_actv);  // [wave][half][32]
+  __syncthreads();  // every wave is done with its V blocks
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ow[(32 * nb + out_row(i, hh)) * 32 + l32] = o[nb][i];
+  if (hh == 0) sm[wave * 32 + l32] = m;
+  sl[(wave * 2 + hh) * 32 + l32] = l;
+  __syncthreads();
+  const int q = tid & 31, f0 = (tid >> 5) * 16;
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < Q2_NW; ++i) M = fmaxf(M, sm[i * 32 + q]);
+  float sc[Q2_NW], den = 0.f;
+#pragma unroll
+  for (int i = 0; i < Q2_NW; ++i) {
+    const float mi = sm[i * 32 + q];
+    sc[i] = mi == -INFINITY ? 0.f : exp2f(mi - M);
+    den = fmaf(sc[i], sl[(i * 2) * 32 + q] + sl[(i * 2 + 1) * 32 + q], den);
+  }
+  if (q < nr) {
+    const float inv = den > 0.f ? 1.0f / den : 0.f;  // no weight at all (everything pruned, no state): 0
+    const float* o0 = reinterpret_cast<const float*>(q2_kb0);
+    const float* o1 = reinterpret_cast<const float*>(q2_kb1);
+    const float* o2 = reinterpret_cast<const float*>(q2_vb0);
+    const float* o3 = reinterpret_cast<const float*>(q2_vb1);
+    uint32_t pk[8];
+#pragma unroll
+    for (int f = 0; f < 16; f += 2) {
+      float v2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = (f0 + f + e) * 32 + q;
+        v2[e] = (sc[0] * o0[idx] + sc[1] * o1[idx] + sc[2] * o2[idx] + sc[3] * o3[idx]) * inv;
+      }
+      pk[f >> 1] = pack_bf16(v2[0], v2[1]);
+    }
+    bf16_t* dst = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + (qtok0 + q) * p.q_st + f0;
+    st16(dst, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    st16(dst + 8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+    if (p.lse != nullptr && f0 == 0)
+      p.lse[(int64_t)bh * p.n_qchunks * p.C + qtok0 + q] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+  }
+}
+
 // The rare second pass, kept out of line so that its registers do not add to
 // the first pass's.
 template <int D, int NW, bool PARTIAL, int VIS>
@@ -760,6 +1077,12 @@ __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float
 template <int D, int NW, bool PARTIAL, int VIS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
+  if constexpr (VIS != 2 && !PARTIAL) {
+    if (p.tail_rows > 0 && xcd_remap(blockIdx.x, p.total_tiles) % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
+      tail_pass<VIS == 1>(p);  // a chunk's short tail
+      return;
+    }
+  }
   float m[Q2_QB];
   const int dirty = tile_pass<D, NW, true, PARTIAL, VIS>(p, m);
   // Every wave reaches this barrier.  Where some query's reference moved after
@@ -813,18 +1136,25 @@ template <int NW>
 hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   constexpr int BM = NW * 32 * Q2_QB;
   static_assert(BM == kQb2RowsPerTile, "partial-result tile size");
-  p.tiles_per_chunk = (p.C + BM - 1) / BM;
   const int splits = p.n_splits > 1 ? p.n_splits : 1;
+  // short tails: dense seq-mode passes whose chunks end in 1 .. 32 rows past
+  // the last full tile (also chunks of at most 32 rows: no tile at all)
+  const int rem = p.C % BM;
+  const bool tails = splits == 1 && p.anchors == 0 && !p.stream_mode && rem > 0 && rem <= kTailMaxRows;
+  p.tail_rows = tails ? rem : 0;
+  p.mask_qtiles = (p.C + BM - 1) / BM;
+  p.tiles_per_chunk = p.mask_qtiles;
   p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk * splits;
-  if (p.total_tiles == 0) return hipSuccess;
+  const int64_t grid = p.total_tiles;
+  if (grid == 0) return hipSuccess;
   if (splits > 1)
     hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 0>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   else if (p.kmask != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 1>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 1>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
   else if (p.anchors > 0)
     hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 2>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 0>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 0>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -44,10 +44,15 @@ struct FwdParams {
   float* part;
   // Pruned key tiles (seq mode, head_dim 128 bf16 only): with kmask set,
   // query tile i of chunk c of head bh visits only key tile j of its window
-  // (keys kbeg + 64 j ..) where kmask[((bh * n_qchunks + c) * tiles_per_chunk
-  // + i) * nkt + j] != 0.
+  // (keys kbeg + 64 j ..) where kmask[((bh * n_qchunks + c) * mask_qtiles
+  // + i) * nkt + j] != 0, mask_qtiles = ceil(C / 256) (set by the launcher).
   const unsigned char* kmask;
   int nkt;
+  int mask_qtiles;
+  // Rows of a short chunk tail (set by the launcher): with tail_rows > 0 the
+  // last tile of every chunk (tile tiles_per_chunk - 1, rows C - tail_rows ..
+  // C - 1) runs the tail pass instead of a full tile.
+  int tail_rows;
   // Bidirectional (seq mode, head_dim 128 bf16 only): the window of chunk c is
   // chunks max(0, c-w+1) .. min(N-1, c+w-1), and the linear term adds the
   // future state S2[bh, c], z2[bh, c] (chunks from c + max(w, 1) on) to the

@@ -35,6 +35,8 @@ CASES = {
     "C130_N5_w0": (1, 2, 130, 5, 0, 1.0, 1.0),
     "C100_N4_w9": (1, 2, 100, 4, 9, 2.0, 1.0),
     "C64_N7_w4": (1, 1, 64, 7, 4, 1.0, 1.0),
+    "C280_N5_w2": (1, 2, 280, 5, 2, 1.0, 0.5),  # 24-row tails
+    "C16_N9_w3": (1, 2, 16, 9, 3, 2.0, 1.0),    # tails only
 }
 
 

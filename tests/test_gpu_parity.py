@@ -54,6 +54,14 @@ MID = {
     "bf16_d128_C130_N4_w9": (1, 2, 128, 130, 4, 9, "bf16", 2.0, 1.0),
     "bf16_d128_C1_N300_w3": (1, 2, 128, 1, 300, 3, "bf16", 1.0, 1.0),
     "bf16_d128_C64_N3_w2": (1, 1, 128, 64, 3, 2, "bf16", 1.0, 1.0),
+    # chunks ending 1..32 rows past a 256-row tile (the short-tail workgroups),
+    # and chunks of at most 32 rows (tails only)
+    "bf16_d128_C280_N6_w3": (1, 2, 128, 280, 6, 3, "bf16", 1.0, 0.5),
+    "bf16_d128_C280_N5_w2_q4": (1, 2, 128, 280, 5, 2, "bf16", 4.0, 0.5),
+    "bf16_d128_C513_N4_w2": (2, 1, 128, 513, 4, 2, "bf16", 1.0, 1.0),
+    "bf16_d128_C288_N4_w0": (1, 2, 128, 288, 4, 0, "bf16", 1.0, 1.0),
+    "bf16_d128_C24_N9_w2": (1, 3, 128, 24, 9, 2, "bf16", 1.0, 1.0),
+    "bf16_d128_C32_N6_w1_q4": (1, 2, 128, 32, 6, 1, "bf16", 4.0, 1.0),
     "bf16_d64_C100_N5_w2": (1, 3, 64, 100, 5, 2, "bf16", 1.0, 1.0),
     "bf16_d64_C100_N5_w2_q4": (1, 3, 64, 100, 5, 2, "bf16", 4.0, 0.5),
     "f32_d64_C70_N5_w2": (1, 2, 64, 70, 5, 2, "f32", 1.0, 1.0),
@@ -164,7 +172,7 @@ def test_empty_problems():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("C", [100, 300])
+@pytest.mark.parametrize("C", [100, 300, 280])
 @pytest.mark.parametrize("alpha", [40.0, 170.0, -170.0])
 def test_score_growth_within_window(alpha, C):
     # Every query shares a component along feature 0; the last key of every
@@ -174,7 +182,8 @@ def test_score_growth_within_window(alpha, C):
     # reference maximum; alpha = 170 (a ~60-nat jump, 2^86) forces reference
     # moves after accumulation, both where the linear state seeds the
     # accumulators and where it does not; -170 makes those keys vanish.
-    # C = 300: query tiles that span two chunks.
+    # C = 300: query tiles that span two chunks; C = 280: a 24-row tail per
+    # chunk (the short-tail workgroups, plain online maximum).
     wl = Workload("growth", 950, B=1, H=2, d=128, C=C, N=4, w=2, dtype="bf16", qscale=1.0, kscale=0.5)
     q, k, v = gen_qkv(wl)
     q = q.clone()

@@ -48,6 +48,7 @@ CASES = {
     "C300_N4_w3_q4": (1, 2, 300, 4, 3, 4.0, 0.5),
     "C520_N3_w9": (1, 1, 520, 3, 9, 2.0, 1.0),
     "C64_N6_w4": (1, 2, 64, 6, 4, 1.0, 1.0),
+    "C280_N5_w2": (1, 2, 280, 5, 2, 1.0, 0.5),  # 24-row chunk tails
 }
 
 
