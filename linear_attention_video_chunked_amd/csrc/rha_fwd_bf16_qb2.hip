@@ -767,10 +767,13 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 // with V read transposed; each wave stages its 32-key blocks of K and V in
 // its own LDS buffer, the next block's rows in flight in registers.
 // A pruned pass (SPARSE) visits only the 32-key blocks of kept 64-key tiles
-// (mask row: query tile C / 256 of the chunk).
+// (mask row: query tile C / 256 of the chunk).  In stream mode the keys are
+// the cache rows and the state is the head's; a split pass (PARTIAL) covers
+// its split's share of the key tiles and writes the unnormalised partial
+// result in the split layout, as the tiles do.
 constexpr int kTailMaxRows = 32;
 
-template <bool SPARSE>
+template <bool SPARSE, bool PARTIAL>
 __device__ __noinline__ void tail_pass(const FwdParams pin) {
   using namespace frag;
   // The parameters are the same in every lane; copies through readfirstlane
@@ -788,8 +791,10 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     float* lse;
     const float *S, *z, *S2, *z2;
     const unsigned char* kmask;
+    float* part;
     int64_t q_sb, q_sh, q_st, kv_sb, kv_sh, kv_st;
-    int H, C, w, n_qchunks, tiles_per_chunk, total_tiles, bidir, tail_rows, mask_qtiles, nkt;
+    int B, H, C, w, n_qchunks, tiles_per_chunk, total_tiles, bidir, tail_rows, mask_qtiles, nkt;
+    int stream_mode, n_keys, has_state, n_splits;
     float scale_log2;
   } p;
   p.q = uni(pin.q);
@@ -802,6 +807,12 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   p.S2 = (const float*)uni(pin.S2);
   p.z2 = (const float*)uni(pin.z2);
   p.kmask = (const unsigned char*)uni(pin.kmask);
+  p.part = (float*)uni(pin.part);
+  p.B = rfl(pin.B);
+  p.stream_mode = rfl(pin.stream_mode);
+  p.n_keys = rfl(pin.n_keys);
+  p.has_state = rfl(pin.has_state);
+  p.n_splits = rfl(pin.n_splits);
   p.q_sb = rfl64(pin.q_sb);
   p.q_sh = rfl64(pin.q_sh);
   p.q_st = rfl64(pin.q_st);
@@ -823,7 +834,10 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   static_assert(Q2_TILE == BD * 32 * 4, "one wave's partial output (128 features x 32 rows, float32) fits its buffer");
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: block loops stay scalar
-  const int rest = xcd_remap(blockIdx.x, p.total_tiles) / p.tiles_per_chunk;  // as in tile_pass
+  // which tail, as in tile_pass
+  const int logical0 = xcd_remap(blockIdx.x, p.total_tiles);
+  const int split = PARTIAL ? logical0 % p.n_splits : 0;
+  const int rest = (PARTIAL ? logical0 / p.n_splits : logical0) / p.tiles_per_chunk;
   const int c = p.n_qchunks - 1 - rest % p.n_qchunks;
   const int bh = rest / p.n_qchunks;
   const int b = bh / p.H, h = bh % p.H;
@@ -834,12 +848,29 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh;
 
   int64_t kbeg = 0, kend = 0;
-  if (p.w > 0) {
-    kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
-    kend = (int64_t)(p.bidir ? min(p.n_qchunks, c + p.w) : c + 1) * p.C;
+  bool has_past, has_future = false;
+  int64_t slot;  // state slot
+  if (!p.stream_mode) {
+    if (p.w > 0) {
+      kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
+      kend = (int64_t)(p.bidir ? min(p.n_qchunks, c + p.w) : c + 1) * p.C;
+    }
+    has_past = (p.w == 0) || (c >= p.w);
+    has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
+    slot = (int64_t)bh * p.n_qchunks + c;
+  } else {
+    kend = p.n_keys;
+    has_past = p.has_state != 0;
+    if (PARTIAL) {  // this split's share of the 64-key tiles; the first split takes the state
+      const int tiles_all = (p.n_keys + BN - 1) / BN;
+      const int t_lo = (int)((int64_t)split * tiles_all / p.n_splits);
+      const int t_hi = (int)((int64_t)(split + 1) * tiles_all / p.n_splits);
+      kbeg = (int64_t)t_lo * BN;
+      kend = min((int64_t)t_hi * BN, (int64_t)p.n_keys);
+      has_past = has_past && split == 0;
+    }
+    slot = bh;
   }
-  const bool has_past = (p.w == 0) || (c >= p.w);
-  const bool has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
 
   // Q rows of the tail, second operand, one query per lane (lanes past the
   // tail repeat its last row; their results are not written)
@@ -859,7 +890,6 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     // Wave i: output features v = 32 i + lane % 32 of phi(Q) S at reference 0.
     // The first operand holds S[16 ks + 8 (lane / 32) + 0..7][v], read straight
     // from memory (32 lanes read 32 consecutive floats of a row of S).
-    const int64_t slot = (int64_t)bh * p.n_qchunks + c;
     const float* Sp = p.S + slot * BD * BD + 32 * wave + l32;
     const float* Sp2 = p.bidir ? p.S2 + slot * BD * BD + 32 * wave + l32 : nullptr;
     float col[8][8];
@@ -1041,12 +1071,35 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     sc[i] = mi == -INFINITY ? 0.f : exp2f(mi - M);
     den = fmaf(sc[i], sl[(i * 2) * 32 + q] + sl[(i * 2 + 1) * 32 + q], den);
   }
-  if (q < nr) {
+  const float* o0 = reinterpret_cast<const float*>(q2_kb0);
+  const float* o1 = reinterpret_cast<const float*>(q2_kb1);
+  const float* o2 = reinterpret_cast<const float*>(q2_vb0);
+  const float* o3 = reinterpret_cast<const float*>(q2_vb1);
+  if (PARTIAL && q < nr) {
+    // split layout: numerator rows at reference M, then {denominator, M};
+    // the tail is the chunk's last tile, rows 0 .. nr-1 of it
+    constexpr int BM = Q2_NW * 32 * Q2_QB;
+    const int64_t pidx = ((int64_t)bh * p.tiles_per_chunk + p.tiles_per_chunk - 1) * p.n_splits + split;
+    const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
+    float* po = p.part + (pidx * BM + q) * BD + f0;
+#pragma unroll
+    for (int f = 0; f < 16; f += 4) {
+      f32x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = (f0 + f + e) * 32 + q;
+        v4[e] = sc[0] * o0[idx] + sc[1] * o1[idx] + sc[2] * o2[idx] + sc[3] * o3[idx];
+      }
+      *reinterpret_cast<f32x4*>(po + f) = v4;
+    }
+    if (f0 == 0) {
+      float* plm = p.part + n_part * BM * BD + (pidx * BM + q) * 2;
+      plm[0] = den;
+      plm[1] = M;
+    }
+  }
+  if (!PARTIAL && q < nr) {
     const float inv = den > 0.f ? 1.0f / den : 0.f;  // no weight at all (everything pruned, no state): 0
-    const float* o0 = reinterpret_cast<const float*>(q2_kb0);
-    const float* o1 = reinterpret_cast<const float*>(q2_kb1);
-    const float* o2 = reinterpret_cast<const float*>(q2_vb0);
-    const float* o3 = reinterpret_cast<const float*>(q2_vb1);
     uint32_t pk[8];
 #pragma unroll
     for (int f = 0; f < 16; f += 2) {
@@ -1077,9 +1130,10 @@ __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float
 template <int D, int NW, bool PARTIAL, int VIS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
-  if constexpr (VIS != 2 && !PARTIAL) {
-    if (p.tail_rows > 0 && xcd_remap(blockIdx.x, p.total_tiles) % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
-      tail_pass<VIS == 1>(p);  // a chunk's short tail
+  if constexpr (VIS != 2) {
+    const int logical = xcd_remap(blockIdx.x, p.total_tiles) / (PARTIAL ? p.n_splits : 1);
+    if (p.tail_rows > 0 && logical % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
+      tail_pass<VIS == 1, PARTIAL>(p);  // a chunk's short tail
       return;
     }
   }
@@ -1140,7 +1194,7 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   // short tails: dense seq-mode passes whose chunks end in 1 .. 32 rows past
   // the last full tile (also chunks of at most 32 rows: no tile at all)
   const int rem = p.C % BM;
-  const bool tails = splits == 1 && p.anchors == 0 && !p.stream_mode && rem > 0 && rem <= kTailMaxRows;
+  const bool tails = p.anchors == 0 && rem > 0 && rem <= kTailMaxRows;
   p.tail_rows = tails ? rem : 0;
   p.mask_qtiles = (p.C + BM - 1) / BM;
   p.tiles_per_chunk = p.mask_qtiles;
