@@ -162,8 +162,8 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-      const float p0 = exp2f(fmaf(sa[i], p.scale_log2, -lse_s[buf][m0]));
-      const float p1 = exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[buf][m1]));
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse_s[buf][m0]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[buf][m1]));
       pp[i >> 1] = pack_bf16(p0, p1);
       dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[buf][m0]), p1 * (pa[i + 1] - del_s[buf][m1]));
     }
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-      const float p0 = m0 < nk ? exp2f(fmaf(sa[i], p.scale_log2, -lse2)) : 0.f;
-      const float p1 = m1 < nk ? exp2f(fmaf(sa[i + 1], p.scale_log2, -lse2)) : 0.f;
+      const float p0 = m0 < nk ? __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse2)) : 0.f;
+      const float p1 = m1 < nk ? __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse2)) : 0.f;
       dd[i >> 1] = pack_bf16(p0 * (pa[i] - del), p1 * (pa[i + 1] - del));
     }
 #pragma unroll

@@ -19,14 +19,19 @@ namespace frag {
 
 using fwd::i16x4;
 using fwd::lds_i16x4;
-using fwd::vsw;
 
 constexpr int BD = 128;            // head dimension
 constexpr int RB = 32;             // rows (or keys) per matrix-core block
 constexpr int ROWT = RB * BD * 2;  // one 32-row bf16 tile in LDS
 
+// Granule swizzle serving both reads: 16 consecutive rows read at one
+// granule (ds_read_b128, one row per lane) hit 16 distinct 16-byte slots, and
+// 4 consecutive rows read by the transpose read (64 bytes each) hit 4
+// distinct 64-byte bank groups.
+__device__ __forceinline__ int fsw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
 // byte offset of granule g (8 bf16) of row r
-__device__ __forceinline__ int gran_off(int r, int g) { return r * BD * 2 + ((g ^ vsw<BD>(r)) * 16); }
+__device__ __forceinline__ int gran_off(int r, int g) { return r * BD * 2 + ((g ^ fsw(r)) * 16); }
 
 __device__ __forceinline__ void put_granule(unsigned char* t, int r, int g, const u32x4& x) {
   *reinterpret_cast<u32x4*>(t + gran_off(r, g)) = x;
@@ -46,9 +51,11 @@ __device__ __forceinline__ bf16x8 col_frag(const unsigned char* t, int ks, int n
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (vj & 3);
   const int vrow0 = 4 * hh + (vj >> 2);
   const int col = nb * 32 + vcol;
-  const unsigned char* pa = t + (vrow0 + 16 * ks) * BD * 2 + (((col >> 3) ^ vsw<BD>(vrow0)) * 16) + (col & 7) * 2;
+  const int r0 = vrow0 + 16 * ks, r1 = r0 + 8;
+  const unsigned char* pa = t + gran_off(r0, col >> 3) + (col & 7) * 2;
+  const unsigned char* pb = t + gran_off(r1, col >> 3) + (col & 7) * 2;
   const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pa);
-  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * BD * 2));
+  const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pb);
   const u32x2 w0 = __builtin_bit_cast(u32x2, x0), w1 = __builtin_bit_cast(u32x2, x1);
   return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 }
