@@ -1137,7 +1137,7 @@ void fwd_bf16_qb2_kernel(const FwdParams p) {
       // a chunk's short tail; the parameter block is passed as its address
       // in the kernel-argument segment (taking &p would copy it to the stack
       // of every workgroup)
-      tail_pass<VIS == 1, PARTIAL>(reinterpret_cast<const FwdParams*>(__builtin_amdgcn_kernarg_segment_ptr()));
+      tail_pass<VIS == 1, PARTIAL>((const FwdParams*)__builtin_amdgcn_kernarg_segment_ptr());
       return;
     }
   }
