@@ -774,8 +774,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 constexpr int kTailMaxRows = 32;
 
 template <bool SPARSE, bool PARTIAL>
-__device__ __noinline__ void tail_pass(const FwdParams* __restrict__ pp) {
-  const FwdParams& pin = *pp;  // the launch's parameter block (read in place)
+__device__ __noinline__ void tail_pass(const FwdParams pin) {
   using namespace frag;
   // The parameters are the same in every lane; copies through readfirstlane
   // let the compiler keep them (and the block loops) scalar in this
@@ -1134,10 +1133,9 @@ void fwd_bf16_qb2_kernel(const FwdParams p) {
   if constexpr (VIS != 2) {
     const int logical = xcd_remap(blockIdx.x, p.total_tiles) / (PARTIAL ? p.n_splits : 1);
     if (p.tail_rows > 0 && logical % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
-      // a chunk's short tail; the parameter block is passed as its address
-      // in the kernel-argument segment (taking &p would copy it to the stack
-      // of every workgroup)
-      tail_pass<VIS == 1, PARTIAL>((const FwdParams*)__builtin_amdgcn_kernarg_segment_ptr());
+      // a chunk's short tail (the parameter block by value: a pointer to it
+      // measured slower, the callee then saves most of its registers)
+      tail_pass<VIS == 1, PARTIAL>(p);
       return;
     }
   }
