@@ -767,13 +767,14 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 // with V read transposed; each wave stages its 32-key blocks of K and V in
 // its own LDS buffer, the next block's rows in flight in registers.
 // A pruned pass (SPARSE) visits only the 32-key blocks of kept 64-key tiles
-// (mask row: query tile C / 256 of the chunk).  In stream mode the keys are
+// (mask row: query tile C / 256 of the chunk); an anchored pass (ANCH) also
+// visits the anchor chunks' keys.  In stream mode the keys are
 // the cache rows and the state is the head's; a split pass (PARTIAL) covers
 // its split's share of the key tiles and writes the unnormalised partial
 // result in the split layout, as the tiles do.
 constexpr int kTailMaxRows = 32;
 
-template <bool SPARSE, bool PARTIAL>
+template <bool SPARSE, bool PARTIAL, bool ANCH>
 __device__ __noinline__ void tail_pass(const FwdParams pin) {
   using namespace frag;
   // The parameters are the same in every lane; copies through readfirstlane
@@ -793,7 +794,7 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     const unsigned char* kmask;
     float* part;
     int64_t q_sb, q_sh, q_st, kv_sb, kv_sh, kv_st;
-    int B, H, C, w, n_qchunks, tiles_per_chunk, total_tiles, bidir, tail_rows, mask_qtiles, nkt;
+    int B, H, C, w, n_qchunks, tiles_per_chunk, total_tiles, bidir, tail_rows, mask_qtiles, nkt, anchors;
     int stream_mode, n_keys, has_state, n_splits;
     float scale_log2;
   } p;
@@ -829,6 +830,7 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   p.tail_rows = rfl(pin.tail_rows);
   p.mask_qtiles = rfl(pin.mask_qtiles);
   p.nkt = rfl(pin.nkt);
+  p.anchors = rfl(pin.anchors);
   p.scale_log2 = __int_as_float(rfl(__float_as_int(pin.scale_log2)));
   static_assert(Q2_NW == 4 && Q2_TILE == 2 * ROWT, "four waves, each with a buffer for a 32-key block of K and V");
   static_assert(Q2_TILE == BD * 32 * 4, "one wave's partial output (128 features x 32 rows, float32) fits its buffer");
@@ -855,7 +857,7 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
       kbeg = (int64_t)max(0, c - p.w + 1) * p.C;
       kend = (int64_t)(p.bidir ? min(p.n_qchunks, c + p.w) : c + 1) * p.C;
     }
-    has_past = (p.w == 0) || (c >= p.w);
+    has_past = ANCH ? (c - p.w >= p.anchors) : ((p.w == 0) || (c >= p.w));
     has_future = p.bidir && c + max(p.w, 1) <= p.n_qchunks - 1;
     slot = (int64_t)bh * p.n_qchunks + c;
   } else {
@@ -941,13 +943,34 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   }
 
   // this wave's quarter of the window's 32-key blocks
-  const int nblk = (int)((kend - kbeg + RB - 1) / RB);
+  // Visited keys: [0, r0e) (anchored passes: the anchor chunks not in the
+  // query's future, merged with the window when they touch) and the window
+  // [r1b, r1e), each cut into 32-key blocks from its start; block j < nA
+  // lies in the first range.
+  int64_t r0e = 0, r1b = kbeg, r1e = kend;
+  if constexpr (ANCH) {
+    r0e = (int64_t)min(p.anchors, c + 1) * p.C;
+    if (r1e <= r1b) r1b = r1e = 0;  // no window (w = 0)
+    if (r1e > r1b && r1b <= r0e) {  // contiguous union
+      r0e = max(r0e, r1e);
+      r1b = r1e = 0;
+    }
+    kend = max(r0e, r1e);  // the descriptors cover every visited key
+  }
+  const int nA = (int)((r0e + RB - 1) / RB);
+  const int nblk = nA + (int)((r1e - r1b + RB - 1) / RB);
   const int j0 = wave * nblk / Q2_NW, j1 = (wave + 1) * nblk / Q2_NW;
+  auto blk_start = [&](int j) { return j < nA ? (int64_t)RB * j : r1b + (int64_t)RB * (j - nA); };
+  auto blk_end = [&](int j) { return j < nA ? r0e : r1e; };
   const unsigned char* mrow =
       SPARSE ? p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + p.mask_qtiles - 1) * p.nkt : nullptr;
-  auto next_kept = [&](int j) {  // first visited block at or after j (j1 if none)
+  // first visited block at or after j (j1 if none); the mask byte is the same
+  // in every lane, and readfirstlane keeps the search (and the block loop
+  // after it) in scalar control flow: the transposed reads and lane swaps of
+  // the loop body need every lane of the wave active
+  auto next_kept = [&](int j) {
     if constexpr (SPARSE)
-      while (j < j1 && mrow[j >> 1] == 0) ++j;
+      while (j < j1 && __builtin_amdgcn_readfirstlane((int)mrow[j >> 1]) == 0) ++j;
     return j;
   };
   // Blocks are taken in pairs (an odd count ends with a padding block past
@@ -961,7 +984,7 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   const int win_bytes = (int)(kend * p.kv_st * 2);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
-  auto blk_off = [&](int j) { return j < j1 ? (int)((kbeg + (int64_t)RB * j) * p.kv_st * 2) : win_bytes; };
+  auto blk_off = [&](int j) { return j < j1 ? (int)(blk_start(j) * p.kv_st * 2) : win_bytes; };
   const int vofs = (lane >> 4) * row_bytes + (lane & 15) * 16;  // V: 16 lanes per 256-byte row
   const int kofs = l32 * row_bytes + hh * 16;                   // K: row lane % 32, features 8 (lane / 32) + 16 ks
   u32x4 kr[2][8], vr[2][8];
@@ -981,7 +1004,7 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
       vr[1][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ob + 4 * i * row_bytes, 0, 0));
     }
   };
-  auto nk_of = [&](int j) { return j < j1 ? (int)min((int64_t)RB, kend - (kbeg + (int64_t)RB * j)) : 0; };
+  auto nk_of = [&](int j) { return j < j1 ? (int)min((int64_t)RB, blk_end(j) - blk_start(j)) : 0; };
   unsigned char* const vt[2] = {vbuf, vbuf + ROWT};
   int ja = next_kept(j0);
   int jb = ja < j1 ? next_kept(ja + 1) : j1;
@@ -1130,12 +1153,12 @@ __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float
 template <int D, int NW, bool PARTIAL, int VIS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_bf16_qb2_kernel(const FwdParams p) {
-  if constexpr (VIS != 2) {
+  {
     const int logical = xcd_remap(blockIdx.x, p.total_tiles) / (PARTIAL ? p.n_splits : 1);
     if (p.tail_rows > 0 && logical % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
       // a chunk's short tail (the parameter block by value: a pointer to it
       // measured slower, the callee then saves most of its registers)
-      tail_pass<VIS == 1, PARTIAL>(p);
+      tail_pass<VIS == 1, PARTIAL, VIS == 2>(p);
       return;
     }
   }
@@ -1196,7 +1219,7 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   // short tails: dense seq-mode passes whose chunks end in 1 .. 32 rows past
   // the last full tile (also chunks of at most 32 rows: no tile at all)
   const int rem = p.C % BM;
-  const bool tails = p.anchors == 0 && rem > 0 && rem <= kTailMaxRows;
+  const bool tails = rem > 0 && rem <= kTailMaxRows;
   p.tail_rows = tails ? rem : 0;
   p.mask_qtiles = (p.C + BM - 1) / BM;
   p.tiles_per_chunk = p.mask_qtiles;

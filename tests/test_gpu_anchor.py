@@ -37,6 +37,12 @@ CASES = {
     "C64_N6_w2_a3": (1, 2, 64, 6, 2, 3, 1.0, 1.0),
     "C150_N4_w2_a4": (1, 1, 150, 4, 2, 4, 2.0, 1.0),
     "C256_N5_w2_a1": (1, 2, 256, 5, 2, 1, 1.0, 1.0),
+    # chunks ending 24 rows past a 256-row tile, and chunks of 24 rows (the
+    # short-tail pass with the anchor range)
+    "C280_N6_w2_a1": (1, 2, 280, 6, 2, 1, 1.0, 0.5),
+    "C280_N5_w1_a2_q4": (1, 2, 280, 5, 1, 2, 4.0, 0.5),
+    "C280_N4_w0_a1": (1, 2, 280, 4, 0, 1, 1.0, 1.0),
+    "C24_N8_w2_a3": (1, 2, 24, 8, 2, 3, 1.0, 1.0),
 }
 
 
