@@ -189,8 +189,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the hot path is "
-              f"single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library computes "
+              f"on one GPU; heads (and chunk ranges, with a halo and a scan of state sums) "
+              f"would be the units to shard across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
