@@ -50,14 +50,18 @@ SMALL = {
     "bf16_d128_C300_w4_q4": Workload("s8", 307, B=1, H=1, d=128, C=300, N=7, w=4, dtype="bf16", qscale=4.0),
     # w = 1: the chunk leaving the window is the new chunk itself (the split fold reads it from k_new, v_new)
     "bf16_d128_C300_w1": Workload("s9", 308, B=1, H=2, d=128, C=300, N=6, w=1, dtype="bf16"),
+    # chunks ending 24 rows past a 256-row tile, and 24-row chunks (the short-tail pass)
+    "bf16_d128_C280_w3": Workload("s10", 309, B=1, H=2, d=128, C=280, N=8, w=3, dtype="bf16"),
+    "bf16_d128_C24_w4_q4": Workload("s11", 310, B=1, H=2, d=128, C=24, N=9, w=4, dtype="bf16", qscale=4.0),
 }
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_stream_matches_oracle_on_concatenation(name):
+def test_stream_matches_oracle_on_concatenation(name, split):
     wl = SMALL[name]
     q, k, v = gen_qkv(wl)
-    st, outs, lses = run_stream(wl, q, k, v, wl.N, lse=True)
+    st, outs, lses = run_stream(wl, q, k, v, wl.N, lse=True, split=split)
     q64, k64, v64 = to64(q), to64(k), to64(v)
     ref, den = oracle.hybrid_batched(q64, k64, v64, wl.C, wl.w, return_den=True)
     tol = TOL[wl.dtype]
@@ -74,7 +78,7 @@ def test_stream_matches_oracle_on_concatenation(name):
     assert st.t == wl.N
 
 
-@pytest.mark.parametrize("name", ["bf16_d128_C256_w4", "bf16_d128_C300_w4_q4"])
+@pytest.mark.parametrize("name", ["bf16_d128_C256_w4", "bf16_d128_C300_w4_q4", "bf16_d128_C280_w3"])
 def test_split_window_matches_unsplit(name):
     # the key window spread over several workgroups per query tile (with the
     # merge kernel) against one workgroup per tile: the same up to rounding
