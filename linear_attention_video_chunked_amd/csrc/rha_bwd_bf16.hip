@@ -80,7 +80,7 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const int total = p.B * p.H * p.N * ktiles;
   const int logical = xcd_remap(blockIdx.x, total);
   const int tile = logical % ktiles, rest = logical / ktiles;
-  const int j = p.N - 1 - rest % p.N, bh = rest / p.N;
+  const int j = rest % p.N, bh = rest / p.N;  // earlier key chunks (more query chunks see them) first
   const int b = bh / p.H, h = bh % p.H;
   const int64_t L = (int64_t)p.N * p.C;
   const int64_t head = b * p.sb + h * p.sh;
