@@ -783,9 +783,10 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
 // taking output features 32i .. 32i+31 of phi(Q) S and wave 0 the
 // denominator term phi(q).z.  The four partial results meet in LDS:
 //   out = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
-// Products as in the tiles: S^T = K Q^T (one query per lane), O^T += V^T P^T
-// with V read transposed; each wave stages its 32-key blocks of K and V in
-// its own LDS buffer, the next block's rows in flight in registers.
+// Products as in the tiles: S^T = K Q^T (one query per lane; K rows straight
+// from memory as the first operand), O^T += V^T P^T with V staged in the
+// wave's own LDS buffer for the transposed read; blocks go in pairs, the next
+// pair's rows in flight in registers.
 // A pruned pass (SPARSE) visits only the 32-key blocks of kept 64-key tiles
 // (mask row: query tile C / 256 of the chunk); an anchored pass (ANCH) also
 // visits the anchor chunks' keys.  In stream mode the keys are
