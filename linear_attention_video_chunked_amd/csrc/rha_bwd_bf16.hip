@@ -16,17 +16,18 @@
 //
 // Kernels (all products on the bf16 matrix cores, float32 accumulation):
 //   bwd_prep_kernel      delta, 1/D and -delta/D per row
+//   chunk state (rha_state_bf16.hip, scaled rows) for dS_c, dz_c, then a
+//   running sum from the last slot for dU_j, du_j
 //   bwd_dkdv_kernel      per 128 keys (32 per wave, rows of K and V held as
 //                        operands): every 32-row query block of the chunks
 //                        that see them -- S = Q K^T and dP = dO V^T with keys
-//                        on the lanes, then dV^T += dO^T P and dK^T += Q^T dS
+//                        on the lanes, then dV^T += dO^T P and dK^T += Q^T dS;
+//                        then the linear term of those keys (dU_j, du_j)
 //   bwd_dq_kernel        per 128 query rows (32 per wave): every 32-key block
 //                        of the window -- S^T = K Q^T and dP^T = V dO^T with
-//                        queries on the lanes, then dQ^T += K^T dS^T
-//   chunk state (rha_state_bf16.hip, scaled rows) for dS_c, dz_c, then a
-//   running sum from the last slot for dU_j, du_j
-//   bwd_rowstate_kernel  the row-by-state products of the linear term
-// The window kernels write dq, dk, dv; the linear-term kernel adds to them.
+//                        queries on the lanes, then dQ^T += K^T dS^T; then the
+//                        linear term of those queries (S_c, z_c)
+// Each of dq, dk, dv is written once, window and linear term together.
 // Operand layouts are those of the forward kernels: a row-major LDS tile
 // (16-byte granules XOR-swizzled) is read by rows (ds_read_b128) or, for a
 // transposed operand, by the transpose read ds_read_b64_tr_b16, which hands
@@ -69,12 +70,45 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   p.zw[idx] = -acc * r;
 }
 
-// ---- window gradients of keys and values
+// ---- the linear term: rows times a d x d state M (float32, row-major),
+// staged in LDS as bf16 rows e = M[e][:] (mr) and, if TRANS, rows n = M[:][n]
+// (mt); every thread of the workgroup takes part.
+template <bool TRANS>
+__device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt, const float* M, int tid) {
+  for (int u = tid; u < BD * BD / 8; u += TB) {
+    const int e = u / (BD / 8), g = u % (BD / 8);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    put_granule(mr, e, g, u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c4[0], c4[1]), pack_bf16(c4[2], c4[3])});
+    if constexpr (TRANS) {
+      const float vals[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = g * 8 + i;  // row n of the transpose, column e
+        *reinterpret_cast<uint16_t*>(mt + gran_off(n, e >> 3) + (e & 7) * 2) = (uint16_t)(pack_bf16(vals[i], 0.f) & 0xffffu);
+      }
+    }
+  }
+}
+
+// phi'(x) of the four features f .. f+3 of a bf16 row
+__device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
+  const u32x2 xw = *reinterpret_cast<const u32x2*>(row + f);
+  const float xs[4] = {bf16_lo(xw[0]), bf16_hi(xw[0]), bf16_lo(xw[1]), bf16_hi(xw[1])};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = xs[i] > 0.f ? 1.f : __expf(xs[i]);
+}
+
+// ---- window gradients of keys and values, then their linear term
+//   (key chunks j <= N-1-w): dv_t += dU_j^T phi(k_t),  dk_t += (dU_j v_t + du_j) * phi'(k_t)
 __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   // two buffers of (Q rows, dout rows, lse, delta) for one 32-row query block
   __shared__ __attribute__((aligned(1024))) unsigned char qs[2][ROWT];
   __shared__ __attribute__((aligned(1024))) unsigned char gs[2][ROWT];
   __shared__ float lse_s[2][RB], del_s[2][RB];
+  // dU_j as bf16 rows, and its transpose
+  __shared__ __attribute__((aligned(1024))) unsigned char um[BD * BD * 2];
+  __shared__ __attribute__((aligned(1024))) unsigned char ut[BD * BD * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int ktiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * ktiles;
@@ -179,9 +213,47 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     __syncthreads();
   }
   // lane = key; element i of block nb = feature 32 nb + out_row(i)
-  if (l32 < nk) {
-    float* dvr = p.dv + (bh * L + key0 + l32) * BD;
-    float* dkr = p.dk + (bh * L + key0 + l32) * BD;
+  float* dvr = p.dv + (bh * L + key0 + l32) * BD;
+  float* dkr = p.dk + (bh * L + key0 + l32) * BD;
+  if (j < p.N - p.w) {  // the chunk is in the state of chunks j + w .. N-1
+    stage_state<true>(um, ut, p.dS + ((int64_t)bh * p.N + j) * BD * BD, tid);
+    __syncthreads();
+    f32x16 o1[4], o2[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) o1[mb] = o2[mb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 pk = l32 < nk ? fwd::phi8(kr[ks]) : kr[ks];  // phi(k_t) (0 past the chunk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        o1[mb] = mfma32(row_frag(ut, 32 * mb, ks, lane), pk, o1[mb]);      // dU^T phi(k)^T: m = n
+        o2[mb] = mfma32(row_frag(um, 32 * mb, ks, lane), vr[ks], o2[mb]);  // dU v^T: m = e
+      }
+    }
+    if (l32 < nk) {
+      const bf16_t* kt = kb + (key0 + l32) * p.st;  // phi' argument
+      const float* dz = p.dz + ((int64_t)bh * p.N + j) * BD;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int f = 32 * nb + 8 * rr + 4 * hh;
+          const f32x4 zz = *reinterpret_cast<const f32x4*>(dz + f);
+          float dphi[4];
+          dphi4(kt, f, dphi);
+          f32x4 a, k4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] = dv[nb][4 * rr + i];
+            k4[i] = dk[nb][4 * rr + i] * p.scale;
+            a[i] += o1[nb][4 * rr + i];
+            k4[i] += (o2[nb][4 * rr + i] + zz[i]) * dphi[i];
+          }
+          *reinterpret_cast<f32x4*>(dvr + f) = a;
+          *reinterpret_cast<f32x4*>(dkr + f) = k4;
+        }
+    }
+  } else if (l32 < nk) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -194,10 +266,12 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   }
 }
 
-// ---- window gradient of the queries
-__global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
+// ---- window gradient of the queries, then their linear term
+//   (query chunks c >= w): dq_i += ((dout_i / D_i) S_c^T - z_c delta_i / D_i) * phi'(q_i)
+__global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ks_t[2][ROWT];
   __shared__ __attribute__((aligned(1024))) unsigned char vs_t[2][ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[BD * BD * 2];  // S_c as bf16 rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int qtiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * qtiles;
@@ -287,8 +361,44 @@ __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
     if (bi + 1 < nblk) stash(buf ^ 1);
     __syncthreads();
   }
-  if (qok) {
-    float* dqr = p.dq + (bh * L + row0 + l32) * BD;
+  float* dqr = p.dq + (bh * L + row0 + l32) * BD;
+  if (c >= p.w) {  // the chunk has a state (every chunk for w = 0)
+    stage_state<false>(sm, nullptr, p.S + ((int64_t)bh * p.N + c) * BD * BD, tid);
+    __syncthreads();
+    const float rs = qok ? p.rsc[bh * L + row0 + l32] : 0.f;  // 1 / D_i
+    const bf16_t* qt = qb + (row0 + l32) * p.st;                // phi' argument
+    const float* zc = p.z + ((int64_t)bh * p.N + c) * BD;
+    const float dD = qok ? p.zw[bh * L + row0 + l32] : 0.f;     // -delta_i / D_i
+    // one 32-feature block at a time (16 more accumulators, not 64: the
+    // kernel keeps two waves per SIMD)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x16 o1 = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4 x = __builtin_bit_cast(u32x4, gr[ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * rs, bf16_hi(x[i]) * rs);  // dout_i / D_i
+        o1 = mfma32(row_frag(sm, 32 * nb, ks, lane), __builtin_bit_cast(bf16x8, x), o1);
+      }
+      if (qok) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int f = 32 * nb + 8 * rr + 4 * hh;
+          const f32x4 zz = *reinterpret_cast<const f32x4*>(zc + f);
+          float dphi[4];
+          dphi4(qt, f, dphi);
+          f32x4 a;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] = dq[nb][4 * rr + i] * p.scale;
+            a[i] += (o1[4 * rr + i] + zz[i] * dD) * dphi[i];
+          }
+          *reinterpret_cast<f32x4*>(dqr + f) = a;
+        }
+      }
+    }
+  } else if (qok) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -300,114 +410,6 @@ __global__ __launch_bounds__(TB) void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-// ---- the linear term: rows times a d x d state.
-//   MODE 0 (query chunks c >= w):  dq_i += ((dout_i / D_i) S_c^T - z_c delta_i / D_i) * phi'(q_i)
-//   MODE 1 (key chunks j <= N-1-w): dv_t += phi(k_t) dU_j,  dk_t += (v_t dU_j^T + du_j) * phi'(k_t)
-// One workgroup per 128 rows of a chunk; the state is staged in LDS as bf16
-// rows (output feature m, input feature k), transposed where needed.
-template <int MODE>
-__global__ __launch_bounds__(TB) void bwd_rowstate_kernel(const BwdParams p, int chunk_lo, int n_chunks) {
-  __shared__ __attribute__((aligned(1024))) unsigned char m1[BD * BD * 2];
-  __shared__ __attribute__((aligned(1024))) unsigned char m2[MODE == 1 ? BD * BD * 2 : 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
-  const int rtiles = (p.C + 127) / 128;
-  const int tile = blockIdx.x % rtiles, rest = blockIdx.x / rtiles;
-  const int c = chunk_lo + rest % n_chunks, bh = rest / n_chunks;
-  const int b = bh / p.H, h = bh % p.H;
-  const int64_t L = (int64_t)p.N * p.C;
-  const int64_t head = b * p.sb + h * p.sh;
-  const float* Mst = MODE == 0 ? p.S + ((int64_t)bh * p.N + c) * BD * BD : p.dS + ((int64_t)bh * p.N + c) * BD * BD;
-  const float* zst = MODE == 0 ? p.z + ((int64_t)bh * p.N + c) * BD : p.dz + ((int64_t)bh * p.N + c) * BD;
-
-  // stage: m1 rows e = M[e][:] (MODE 0: S_c; MODE 1: dU for dk), m2 rows n = M[:][n] (MODE 1: dU^T for dv)
-  for (int u = tid; u < BD * BD / 8; u += TB) {
-    const int e = u / (BD / 8), g = u % (BD / 8);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(Mst + (int64_t)e * BD + g * 8);
-    const f32x4 c4 = *reinterpret_cast<const f32x4*>(Mst + (int64_t)e * BD + g * 8 + 4);
-    put_granule(m1, e, g, u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c4[0], c4[1]), pack_bf16(c4[2], c4[3])});
-    if constexpr (MODE == 1) {
-      const float vals[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = g * 8 + i;  // row n of the transpose, column e
-        *reinterpret_cast<uint16_t*>(m2 + gran_off(n, e >> 3) + (e & 7) * 2) = (uint16_t)(pack_bf16(vals[i], 0.f) & 0xffffu);
-      }
-    }
-  }
-  __syncthreads();
-
-  const int64_t row0 = (int64_t)c * p.C + 128 * tile + 32 * wave;
-  const int nr = (int)max((int64_t)0, min((int64_t)32, (int64_t)(c + 1) * p.C - row0));
-  const bool ok = l32 < nr;
-  const int64_t t = row0 + l32;  // this lane's token
-  const bf16_t* xq = (const bf16_t*)(MODE == 0 ? p.dout : p.k) + head + t * p.st;
-  const bf16_t* xv = (const bf16_t*)p.v + head + t * p.st;
-  const float rs = (MODE == 0 && ok) ? p.rsc[bh * L + t] : 0.f;
-
-  f32x16 o1[4], o2[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) o1[mb] = o2[mb] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (ok) {
-      x = ld16(xq + 16 * ks + 8 * hh);
-      if constexpr (MODE == 1) y = ld16(xv + 16 * ks + 8 * hh);
-    }
-    bf16x8 bx;
-    if constexpr (MODE == 0) {  // dout_i / D_i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * rs, bf16_hi(x[i]) * rs);
-      bx = __builtin_bit_cast(bf16x8, x);
-    } else {  // phi(k_t) for dv; v_t for dk
-      bx = ok ? fwd::phi8(__builtin_bit_cast(bf16x8, x)) : __builtin_bit_cast(bf16x8, x);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if constexpr (MODE == 0) {
-        o1[mb] = mfma32(row_frag(m1, 32 * mb, ks, lane), bx, o1[mb]);  // (S_c dN^T): m = e
-      } else {
-        o1[mb] = mfma32(row_frag(m2, 32 * mb, ks, lane), bx, o1[mb]);  // dU^T phi(k)^T: m = n
-        o2[mb] = mfma32(row_frag(m1, 32 * mb, ks, lane), __builtin_bit_cast(bf16x8, y), o2[mb]);  // dU v^T: m = e
-      }
-    }
-  }
-  if (!ok) return;
-  // lane = token; element i of block mb = feature 32 mb + out_row(i)
-  const bf16_t* xr = (const bf16_t*)(MODE == 0 ? p.q : p.k) + head + t * p.st;  // phi' argument
-  float* g1 = (MODE == 0 ? p.dq : p.dv) + (bh * L + t) * BD;
-  float* g2 = p.dk + (bh * L + t) * BD;
-  const float dD = MODE == 0 ? p.zw[bh * L + t] : 0.f;  // -delta_i / D_i
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int f = 32 * mb + 8 * rr + 4 * hh;
-      const f32x4 zz = *reinterpret_cast<const f32x4*>(zst + f);
-      const u32x2 xw = *reinterpret_cast<const u32x2*>(xr + f);
-      const float xs[4] = {bf16_lo(xw[0]), bf16_hi(xw[0]), bf16_lo(xw[1]), bf16_hi(xw[1])};
-      float dphi[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dphi[i] = xs[i] > 0.f ? 1.f : __expf(xs[i]);
-      if constexpr (MODE == 0) {
-        f32x4 a = *reinterpret_cast<f32x4*>(g1 + f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] += (o1[mb][4 * rr + i] + zz[i] * dD) * dphi[i];
-        *reinterpret_cast<f32x4*>(g1 + f) = a;
-      } else {
-        f32x4 a = *reinterpret_cast<f32x4*>(g1 + f);
-        f32x4 k4 = *reinterpret_cast<f32x4*>(g2 + f);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] += o1[mb][4 * rr + i];
-          k4[i] += (o2[mb][4 * rr + i] + zz[i]) * dphi[i];
-        }
-        *reinterpret_cast<f32x4*>(g1 + f) = a;
-        *reinterpret_cast<f32x4*>(g2 + f) = k4;
-      }
-    }
-}
-
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
@@ -416,42 +418,40 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   if (BH == 0 || L == 0) return hipSuccess;
   const int tiles128 = (p.C + 127) / 128;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((BH * L + 255) / 256)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.w >= p.N) return hipSuccess;  // no chunk has a state: no linear term
-  // dS_c, dz_c of chunks c >= w into slot c - w, then slot j <- sum over slots j .. N-1-w = dU_j
-  ChunkStateParams c{};
-  c.k = p.q;
-  c.v = p.dout;
-  c.S = p.dS;
-  c.z = p.dz;
-  c.kv_sb = p.sb;
-  c.kv_sh = p.sh;
-  c.kv_st = p.st;
-  c.s_bh = (int64_t)p.N * BD * BD;
-  c.z_bh = (int64_t)p.N * BD;
-  c.B = p.B;
-  c.H = p.H;
-  c.C = p.C;
-  c.chunk0 = 0;
-  c.n_chunks = p.N;
-  c.slot_offset = -p.w;
-  c.n_slots = p.N;
-  c.accumulate = 0;
-  c.tok_end = L;
-  c.vscale = p.rsc;
-  c.zweight = p.zw;
-  c.scale_bh = L;
-  e = launch_chunk_state_bf16(c, BD, s);
-  if (e != hipSuccess) return e;
-  PrefixParams pr{p.dS, p.dz, (int)BH, p.N, p.w, BD, 1};
-  e = launch_prefix(pr, s);
-  if (e != hipSuccess) return e;
-  const int nq = p.N - p.w;  // query chunks with a state: w .. N-1 (all for w = 0)
-  hipLaunchKernelGGL(bwd_rowstate_kernel<0>, dim3((unsigned)(BH * nq * tiles128)), dim3(TB), 0, s, p, p.w, nq);
-  hipLaunchKernelGGL(bwd_rowstate_kernel<1>, dim3((unsigned)(BH * nq * tiles128)), dim3(TB), 0, s, p, 0, nq);
+  if (p.w < p.N) {  // some chunk has a state: the linear term
+    // dS_c, dz_c of chunks c >= w into slot c - w, then slot j <- sum over slots j .. N-1-w = dU_j
+    ChunkStateParams c{};
+    c.k = p.q;
+    c.v = p.dout;
+    c.S = p.dS;
+    c.z = p.dz;
+    c.kv_sb = p.sb;
+    c.kv_sh = p.sh;
+    c.kv_st = p.st;
+    c.s_bh = (int64_t)p.N * BD * BD;
+    c.z_bh = (int64_t)p.N * BD;
+    c.B = p.B;
+    c.H = p.H;
+    c.C = p.C;
+    c.chunk0 = 0;
+    c.n_chunks = p.N;
+    c.slot_offset = -p.w;
+    c.n_slots = p.N;
+    c.accumulate = 0;
+    c.tok_end = L;
+    c.vscale = p.rsc;
+    c.zweight = p.zw;
+    c.scale_bh = L;
+    e = launch_chunk_state_bf16(c, BD, s);
+    if (e != hipSuccess) return e;
+    PrefixParams pr{p.dS, p.dz, (int)BH, p.N, p.w, BD, 1};
+    e = launch_prefix(pr, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
   return hipGetLastError();
 }
 
