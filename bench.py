@@ -385,13 +385,38 @@ def main():
         oF = fwd_flops(ow.C, ow.N, ow.w, ow.d, obh)
         dense_causal = obh * sum(ow.C * 4 * ow.d * (c + 1) * ow.C for c in range(ow.N))
         dense_full = obh * ow.L * 4 * ow.d * ow.L
+        res = {f"{name}_fwd_us": t_f * 1e6, f"{name}_query_tokens_per_s": ow.B * ow.L / t_f,
+               f"{name}_TFLOPs": oF / t_f / 1e12, f"{name}_mfma_frac": oF / t_f / 1e12 / PEAK_BF16_TFLOPS,
+               f"{name}_scan_us": t_s * 1e6,
+               f"{name}_flop_reduction_vs_dense_block_causal": dense_causal / oF,
+               f"{name}_flop_reduction_vs_dense_full": dense_full / oF}
+        if name == "long":
+            # the two limits on the first 21 chunks: w = all (block-causal
+            # softmax attention, MFMA-bound) and w = 0 (linear attention only:
+            # q, the state slots and out stream through, HBM-bound)
+            n21 = 21
+            sl = [t[:, :, : n21 * ow.C].contiguous() for t in (oq, ok, ov)]
+            so = torch.empty_like(sl[0])
+            for wlim, tag in ((n21, "wall"), (0, "w0")):
+                sS, sz = rha.state_scan(sl[1], sl[2], ow.C, wlim, stream=stream)
+                fn = lambda: rha.hybrid_fwd(sl[0], sl[1], sl[2], sS, sz, ow.C, wlim, out=so, stream=stream)
+                fn()
+                t_l = timed(fn, n_calls)
+                lF = fwd_flops(ow.C, n21, wlim, ow.d, obh)
+                res[f"{name}_slice21_{tag}_fwd_us"] = t_l * 1e6
+                res[f"{name}_slice21_{tag}_TFLOPs"] = lF / t_l / 1e12
+                if wlim > 0:
+                    res[f"{name}_slice21_{tag}_mfma_frac"] = lF / t_l / 1e12 / PEAK_BF16_TFLOPS
+                else:
+                    # q read, out written (bf16), one state slot per chunk read
+                    lB = obh * (2 * n21 * ow.C * ow.d * 2 + n21 * (ow.d * ow.d + ow.d) * 4)
+                    res[f"{name}_slice21_{tag}_GBps"] = lB / t_l / 1e9
+                    res[f"{name}_slice21_{tag}_hbm_frac"] = lB / t_l / 1e9 / PEAK_HBM_GBS
+                del sS, sz
+            del sl, so
         del oq, ok, ov, oS, oz, oo
         torch.cuda.empty_cache()
-        return {f"{name}_fwd_us": t_f * 1e6, f"{name}_query_tokens_per_s": ow.B * ow.L / t_f,
-                f"{name}_TFLOPs": oF / t_f / 1e12, f"{name}_mfma_frac": oF / t_f / 1e12 / PEAK_BF16_TFLOPS,
-                f"{name}_scan_us": t_s * 1e6,
-                f"{name}_flop_reduction_vs_dense_block_causal": dense_causal / oF,
-                f"{name}_flop_reduction_vs_dense_full": dense_full / oF}
+        return res
 
     more = {}
     for name in ("wan14b", "long"):
