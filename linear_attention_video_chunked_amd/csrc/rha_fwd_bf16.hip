@@ -443,6 +443,9 @@ hipError_t launch(FwdParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s) {
+  // no softmax window (w = 0, causal, unpruned, no anchors): the linear term alone
+  if (d == 128 && p.w == 0 && !p.stream_mode && !p.bidir && p.anchors == 0 && p.kmask == nullptr && p.n_splits <= 1)
+    return launch_fwd_linear_bf16(p, s);
   if (d == 128) return launch_fwd_bf16_qb2(p, s);
   return launch<64, 4>(p, s);
 }

@@ -172,6 +172,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
 // head_dim 128 with 64 query rows per wave (the default for d = 128)
 hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s);
+// head_dim 128, window of 0 chunks (sequence mode, causal, no mask or anchors)
+hipError_t launch_fwd_linear_bf16(const FwdParams& p, hipStream_t s);
 // Query rows per workgroup of the d = 128 bf16 kernel (the partial-result tile).
 constexpr int kQb2RowsPerTile = 256;
 // Bytes of partial results for a split stream pass (see FwdParams::part).
