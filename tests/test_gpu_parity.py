@@ -117,11 +117,20 @@ def test_tiny_config_against_oracle_and_brute_force():
             assert rel_l2(to64(out)[b, h], ref) <= TOL["f32"]
 
 
-def test_strided_sequence_major_layout_matches_contiguous():
+# layout cases: a windowed one and one with no window (w = 0 has its own kernel)
+LAYOUT = {
+    "w2": lambda: mid_workload("bf16_d128_C200_N5_w2"),
+    "w0_B2": lambda: Workload("layout_w0_B2", 190, B=2, H=3, d=128, C=200, N=5, w=0, dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT))
+def test_strided_sequence_major_layout_matches_contiguous(name):
     # [B, L, H, d] storage viewed as [B, H, L, d]
-    wl = mid_workload("bf16_d128_C200_N5_w2")
+    wl = LAYOUT[name]()
     q, k, v = gen_qkv(wl)
     a_out, a_lse, a_S, a_z = run_lib(q, k, v, wl.C, wl.w)
+    check_full(wl, a_out, a_lse, a_S, a_z, to64(q), to64(k), to64(v))
     qs, ks, vs = (t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3) for t in (q, k, v))
     S, z = rha.state_scan(ks, vs, wl.C, wl.w)
     out = torch.empty_like(qs)
@@ -131,8 +140,9 @@ def test_strided_sequence_major_layout_matches_contiguous():
     assert torch.equal(out.contiguous(), a_out)
 
 
-def test_output_guard_bands_untouched():
-    wl = mid_workload("bf16_d128_C300_N4_w1")
+@pytest.mark.parametrize("name", ["bf16_d128_C300_N4_w1", "bf16_d128_C300_N4_w0"])
+def test_output_guard_bands_untouched(name):
+    wl = mid_workload(name)
     q0, k0, v0 = gen_qkv(wl)
     ref_out, _, ref_S, ref_z = run_lib(q0, k0, v0, wl.C, wl.w)
 
