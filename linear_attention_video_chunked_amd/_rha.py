@@ -123,12 +123,32 @@ def _problem(x: torch.Tensor, C: int, w: int, n_chunks: int, anchors: int = 0) -
     return Problem(B, H, d, C, n_chunks, w, _dtype_code(x), anchors, x.stride(0), x.stride(1), x.stride(2))
 
 
+def _on_gpu(ref: torch.Tensor, name: str = "q"):
+    """The library computes on the GPU only: host tensors would hand host
+    pointers to the kernels.  Raised before any library call."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got device {ref.device})")
+
+
 def _same_layout(ref: torch.Tensor, *others: torch.Tensor):
+    _on_gpu(ref)
     for o in others:
         if o.shape != ref.shape or o.stride() != ref.stride() or o.dtype != ref.dtype:
             raise ValueError("q, k, v and out must share shape, strides and dtype")
         if o.device != ref.device:
             raise ValueError("all tensors must be on the same device")
+
+
+def _check_f32(ref: torch.Tensor, t: torch.Tensor, name: str, shape):
+    """t: float32, contiguous, of the given shape, on ref's device."""
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device} (got {t.device})")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def state_scan(k: torch.Tensor, v: torch.Tensor, C: int, w: int,
@@ -144,6 +164,8 @@ def state_scan(k: torch.Tensor, v: torch.Tensor, C: int, w: int,
         S = torch.empty((B, H, N, d, d), dtype=torch.float32, device=k.device)
     if z is None:
         z = torch.empty((B, H, N, d), dtype=torch.float32, device=k.device)
+    _check_f32(k, S, "S", (B, H, N, d, d))
+    _check_f32(k, z, "z", (B, H, N, d))
     prob = _problem(k, C, w, N, anchors)
     _check(lib().rha_state_scan(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _stream(stream)))
     return S, z
@@ -160,14 +182,12 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     if L % C:
         raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
     N = L // C
-    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise ValueError("S, z must be float32 [B,H,N,d,d] and [B,H,N,d]")
-    if not (S.is_contiguous() and z.is_contiguous()):
-        raise ValueError("S and z must be contiguous")
+    _check_f32(q, S, "S", (B, H, N, d, d))
+    _check_f32(q, z, "z", (B, H, N, d))
     if return_lse and lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
-        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    if lse is not None:
+        _check_f32(q, lse, "lse", (B, H, L))
     prob = _problem(q, C, w, N, anchors)
     _check(lib().rha_hybrid_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(out),
                                 _ptr(lse), _stream(stream)))
@@ -183,10 +203,9 @@ def hybrid_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     if L % C:
         raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
     N = L // C
-    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or not (S.is_contiguous() and z.is_contiguous()):
-        raise ValueError("S, z must be contiguous float32 [B,H,N,d,d] and [B,H,N,d]")
-    if lse.shape != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    _check_f32(q, S, "S", (B, H, N, d, d))
+    _check_f32(q, z, "z", (B, H, N, d))
+    _check_f32(q, lse, "lse", (B, H, L))
     prob = _problem(q, C, w, N)
     nbytes = int(lib().rha_hybrid_bwd_workspace_size(ctypes.byref(prob)))
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
@@ -228,15 +247,13 @@ def hybrid_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, states, 
         raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
     N = L // C
     Sp, zp, Sf, zf = states
-    for S, z in ((Sp, zp), (Sf, zf)):
-        if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
-            raise ValueError("states must be float32 [B,H,N,d,d] and [B,H,N,d]")
-        if not (S.is_contiguous() and z.is_contiguous()):
-            raise ValueError("states must be contiguous")
+    for name, S, z in (("past", Sp, zp), ("future", Sf, zf)):
+        _check_f32(q, S, f"S_{name}", (B, H, N, d, d))
+        _check_f32(q, z, f"z_{name}", (B, H, N, d))
     if return_lse and lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
-        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    if lse is not None:
+        _check_f32(q, lse, "lse", (B, H, L))
     prob = _problem(q, C, w, N)
     _check(lib().rha_hybrid_fwd_bidir(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(Sp), _ptr(zp), _ptr(Sf),
                                       _ptr(zf), _ptr(out), _ptr(lse), _stream(stream)))
@@ -267,17 +284,15 @@ def hybrid_fwd_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torc
     if L % C:
         raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
     N = L // C
-    if S.shape != (B, H, N, d, d) or z.shape != (B, H, N, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise ValueError("S, z must be float32 [B,H,N,d,d] and [B,H,N,d]")
-    if not (S.is_contiguous() and z.is_contiguous()):
-        raise ValueError("S and z must be contiguous")
+    _check_f32(q, S, "S", (B, H, N, d, d))
+    _check_f32(q, z, "z", (B, H, N, d))
     if (tuple(block_mask.shape) != sparse_mask_shape(B, H, C, N, w) or block_mask.dtype != torch.uint8
             or not block_mask.is_contiguous() or block_mask.device != q.device):
         raise ValueError(f"block_mask must be contiguous uint8 {sparse_mask_shape(B, H, C, N, w)} on q's device")
     if return_lse and lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, L) or not lse.is_contiguous() or lse.dtype != torch.float32):
-        raise ValueError("lse must be float32 contiguous [B,H,L]")
+    if lse is not None:
+        _check_f32(q, lse, "lse", (B, H, L))
     prob = _problem(q, C, w, N)
     _check(lib().rha_hybrid_fwd_sparse(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                        _ptr(block_mask), _ptr(out), _ptr(lse), _stream(stream)))
@@ -333,8 +348,13 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
         raise ValueError("chunk shape does not match the stream state")
     if q_new.dtype != st.k_cache.dtype:
         raise ValueError("chunk dtype does not match the cache")
-    if lse is not None and (lse.shape != (B, H, C) or not lse.is_contiguous() or lse.dtype != torch.float32):
-        raise ValueError("lse must be float32 contiguous [B,H,C]")
+    for name, t in (("k_cache", st.k_cache), ("v_cache", st.v_cache), ("S", st.S), ("z", st.z)):
+        if t.device != q_new.device:
+            raise ValueError(f"stream state {name} is on {t.device}, the chunk on {q_new.device}")
+    if st.workspace is not None and st.workspace.device != q_new.device:
+        raise ValueError(f"stream workspace is on {st.workspace.device}, the chunk on {q_new.device}")
+    if lse is not None:
+        _check_f32(q_new, lse, "lse", (B, H, C))
     prob = _problem(q_new, C, st.w, 1)
     _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
                                  _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
