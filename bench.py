@@ -19,6 +19,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -26,7 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "hybrid-attn query tokens/s + % MFMA bf16 peak, Wan-1.3B shape (H12 d128 32760 tok)"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (vendor figure)
+# MI355X dense bf16 matrix-core peak: 256 CUs x 2.4 GHz x 4096 flop per clock per CU
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 2516.58
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_wan13b_traffic.md")
 # the dominant kernel at this shape (head_dim 128, bf16)
@@ -124,13 +126,20 @@ def stream_step_flops(C, w, d, BH):
 
 
 def stream_step_bytes(C, w, d, BH, elem=2):
-    """Algorithmic HBM bytes of one rha_stream_step with a full window: new
-    q, k, v read and out written; k, v copied into the cache (read + write);
-    the w cached chunks' k, v read; S, z read; the evicted chunk's k, v read
-    and S, z read and written back by the fold."""
+    """Algorithmic HBM bytes of one rha_stream_step with a full window, the
+    method's own traffic: new q, k, v read and out written; the new k, v
+    written into their cache slot; the w - 1 cached chunks' k, v read; S, z
+    read; the evicted chunk's k, v read and S, z written back by the fold."""
     chunk = C * d * elem
     state = (d * d + d) * 4
-    return BH * (3 * chunk + chunk + 2 * chunk + 2 * w * chunk + state + 2 * chunk + 2 * state)
+    return BH * (3 * chunk + chunk + 2 * chunk + 2 * (w - 1) * chunk + state + 2 * chunk + state)
+
+
+def stream_step_impl_extra_bytes(C, w, d, BH, elem=2):
+    """Traffic of the implementation beyond the method's: the attention reads
+    the new chunk's k, v back from its cache slot (the whole window comes from
+    one buffer), and S, z are read once more by the fold's merge."""
+    return BH * (2 * C * d * elem + (d * d + d) * 4)
 
 
 def read_traffic():
@@ -149,22 +158,43 @@ def read_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle on the host: whole heads of the same workload, run until
-    the time budget is spent (at least one head)."""
-    import numpy as np
+def cpu_model() -> str:
+    """The host's CPU model (lscpu's "Model name", else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s=12.0, per_config=True):
+    """The fp64 oracle on the host: whole heads of the headline workload, run
+    until the time budget is spent (at least one head); then one head of each
+    other full-size configuration (one step of the streaming one), so the
+    oracle's rate is stated per configuration too."""
     import oracle
-    from synth import gen_head
+    from synth import CONFIGS, gen_head
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+
+    def head(w, h, L=None, t0=0):
+        return [gen_head(w, t, 0, h, L=L, t0=t0).double().numpy() for t in ("q", "k", "v")]
+
     heads, elapsed = 0, 0.0
     while True:
-        q = gen_head(wl, "q", 0, heads).double().numpy()
-        k = gen_head(wl, "k", 0, heads).double().numpy()
-        v = gen_head(wl, "v", 0, heads).double().numpy()
+        q, k, v = head(wl, heads)
         ts = time.perf_counter()
         oracle.hybrid(q, k, v, wl.C, wl.w)
         elapsed += time.perf_counter() - ts  # input generation stays off the clock
@@ -173,9 +203,31 @@ def cpu_baseline(wl, budget_s=12.0):
             break
     # query tokens/s in the metric's unit: one query token = one row across all H heads
     value = wl.B * wl.L * heads / wl.H / elapsed
-    return {"value": value, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 chunked oracle on {heads} of {wl.H} heads (b=0) of the full "
-                      f"{wl.N}x{wl.C}-token sequence, {elapsed:.1f} s"}
+    res = {"value": value, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"fp64 chunked oracle on {heads} of {wl.H} heads (b=0) of the full "
+                     f"{wl.N}x{wl.C}-token sequence, {elapsed:.1f} s"}
+    if per_config:
+        pc = {wl.name: {"heads": heads, "oracle_s": elapsed, "query_tokens_per_s": value}}
+        for name in ("wan14b", "long"):
+            ow = CONFIGS[name]
+            q, k, v = head(ow, 0)
+            ts = time.perf_counter()
+            oracle.hybrid(q, k, v, ow.C, ow.w)
+            t = time.perf_counter() - ts
+            pc[name] = {"heads": 1, "oracle_s": t, "query_tokens_per_s": ow.B * ow.L / ow.H / t}
+        # streaming: the step after the prefill, one head, as the oracle states
+        # it (its window's rows over the concatenated sequence up to that step)
+        sw = CONFIGS["stream"]
+        T = sw.prefill + 1
+        q, k, v = head(sw, 0, L=T * sw.C)
+        rows = list(range((T - 1) * sw.C, T * sw.C))
+        ts = time.perf_counter()
+        oracle.hybrid_rows(q, k, v, sw.C, sw.w, rows)
+        t = time.perf_counter() - ts
+        pc["stream"] = {"heads": 1, "steps": 1, "oracle_s": t, "chunks_per_s": 1.0 / (t * sw.H)}
+        res["per_config"] = pc
+    return res
 
 
 def main():
@@ -194,6 +246,7 @@ def main():
               f"would be the units to shard across GPUs.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import linear_attention_video_chunked_amd as rha
     from synth import CONFIGS, gen_block_mask, gen_qkv
@@ -212,106 +265,37 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
         return
 
-    wl = CONFIGS["wan13b"]
-    BH = wl.B * wl.H
-    q, k, v = (t.to(dev) for t in gen_qkv(wl))
-    S = torch.empty((wl.B, wl.H, wl.N, wl.d, wl.d), dtype=torch.float32, device=dev)
-    z = torch.empty((wl.B, wl.H, wl.N, wl.d), dtype=torch.float32, device=dev)
-    out = torch.empty_like(q)
-
-    def step():
-        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
-        rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
-
     def timed(fn, n):
+        """(mean, median, min) seconds per call on the launch stream: the mean
+        from two events around all n calls, median and min from an event pair
+        around each call."""
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(n):
             fn()
         e1.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            ev[2 * i].record(stream)
+            fn()
+            ev[2 * i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / n  # seconds per call
+        per = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]) / 1e3
+        return e0.elapsed_time(e1) / 1e3 / n, float(np.median(per)), float(per.min())
 
-    if args.only == "fwd":
-        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
-        for _ in range(args.steps):
-            rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
+    def run_only(fn, n):
+        for _ in range(n):
+            fn()
         torch.cuda.synchronize()
-        return
-    if args.only == "scan":
-        for _ in range(args.steps):
-            rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
-        torch.cuda.synchronize()
-        return
 
-    # ---- pruned window: half of the (query block, key block) pairs kept (seeded)
-    mask_cpu = gen_block_mask(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), 0.5, seed=31)
-    mask = mask_cpu.to(dev)
+    wl = CONFIGS["wan13b"]
+    BH = wl.B * wl.H
 
-    def sparse_call():
-        rha.hybrid_fwd_sparse(q, k, v, S, z, wl.C, wl.w, mask, out=out, stream=stream)
-
-    if args.only == "sparse":
-        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
-        for _ in range(args.steps):
-            sparse_call()
-        torch.cuda.synchronize()
-        return
-
-    # ---- bidirectional hybrid at the same shape (window of 3 chunks each way)
-    def bidir_scan():
-        return rha.state_scan_bidir(k, v, wl.C, wl.w, stream=stream)
-
-    bstates = bidir_scan()
-
-    def bidir_call():
-        rha.hybrid_fwd_bidir(q, k, v, bstates, wl.C, wl.w, out=out, stream=stream)
-
-    if args.only == "bidir":
-        for _ in range(args.steps):
-            bidir_call()
-        torch.cuda.synchronize()
-        return
-
-    # ---- the first frame as an anchor (sink) chunk, same shape
-    SA = torch.empty_like(S)
-    zA = torch.empty_like(z)
-
-    def anchor_step():
-        rha.state_scan(k, v, wl.C, wl.w, S=SA, z=zA, stream=stream, anchors=1)
-        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out, stream=stream, anchors=1)
-
-    def anchor_call():
-        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out, stream=stream, anchors=1)
-
-    anchor_step()
-    if args.only == "anchor":
-        for _ in range(args.steps):
-            anchor_call()
-        torch.cuda.synchronize()
-        return
-
-    # ---- backward pass at the same shape (seeded dout)
-    gen = torch.Generator(device="cpu").manual_seed(77)
-    dout = torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(dev)
-    lse_f = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
-    out_f = torch.empty_like(q)
-    rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
-    rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out_f, lse=lse_f, stream=stream)
-
-    def bwd_call():
-        rha.hybrid_bwd(q, k, v, S, z, out_f, lse_f, dout, wl.C, wl.w, stream=stream)
-
-    if args.only == "bwd":
-        for _ in range(args.steps):
-            bwd_call()
-        torch.cuda.synchronize()
-        return
-
-    # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps)
-    def stream_run(timed_run):
+    # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps): it
+    # allocates its own tensors and needs nothing from the other sections
+    def stream_run():
         sw = CONFIGS["stream"]
         sq, sk, sv = (t.to(dev) for t in gen_qkv(sw))
         sout = torch.empty_like(sq)  # step outputs land in place, with the inputs' strides
@@ -324,17 +308,102 @@ def main():
         for t in range(sw.prefill):
             push(t)
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        z1 = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for t in range(sw.prefill, sw.prefill + sw.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(sw.steps + 1)]
+        ev[0].record(stream)
+        for i, t in enumerate(range(sw.prefill, sw.prefill + sw.steps)):
             push(t)
-        z1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return sw, a.elapsed_time(z1) / 1e3 / sw.steps
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(sw.steps)]) / 1e3
+        del sq, sk, sv, sout, st
+        torch.cuda.empty_cache()
+        return sw, float(per.mean()), float(np.median(per)), float(per.min())
 
     if args.only == "stream":
-        stream_run(False)
+        stream_run()
+        torch.cuda.synchronize()
+        return
+
+    q, k, v = (t.to(dev) for t in gen_qkv(wl))
+    S = torch.empty((wl.B, wl.H, wl.N, wl.d, wl.d), dtype=torch.float32, device=dev)
+    z = torch.empty((wl.B, wl.H, wl.N, wl.d), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+
+    def step():
+        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+        rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
+
+    def fwd_call():
+        rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream)
+
+    def scan_call():
+        rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream)
+
+    if args.only == "fwd":
+        scan_call()
+        run_only(fwd_call, args.steps)
+        return
+    if args.only == "scan":
+        run_only(scan_call, args.steps)
+        return
+
+    # ---- pruned window: half of the (query block, key block) pairs kept (seeded)
+    mask_cpu = gen_block_mask(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), 0.5, seed=31)
+    mask = mask_cpu.to(dev)
+
+    def sparse_call():
+        rha.hybrid_fwd_sparse(q, k, v, S, z, wl.C, wl.w, mask, out=out, stream=stream)
+
+    if args.only == "sparse":
+        scan_call()
+        run_only(sparse_call, args.steps)
+        return
+
+    # ---- bidirectional hybrid at the same shape (window of 3 chunks each way)
+    bstates = [None]
+
+    def bidir_scan():
+        bstates[0] = rha.state_scan_bidir(k, v, wl.C, wl.w, stream=stream)
+
+    def bidir_call():
+        rha.hybrid_fwd_bidir(q, k, v, bstates[0], wl.C, wl.w, out=out, stream=stream)
+
+    if args.only == "bidir":
+        bidir_scan()
+        run_only(bidir_call, args.steps)
+        return
+
+    # ---- the first frame as an anchor (sink) chunk, same shape
+    SA = torch.empty_like(S)
+    zA = torch.empty_like(z)
+
+    def anchor_call():
+        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out, stream=stream, anchors=1)
+
+    def anchor_setup():
+        rha.state_scan(k, v, wl.C, wl.w, S=SA, z=zA, stream=stream, anchors=1)
+
+    if args.only == "anchor":
+        anchor_setup()
+        run_only(anchor_call, args.steps)
+        return
+
+    # ---- backward pass at the same shape (seeded dout)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    dout = torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(dev)
+    lse_f = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+    out_f = torch.empty_like(q)
+
+    def bwd_setup():
+        scan_call()
+        rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out_f, lse=lse_f, stream=stream)
+
+    def bwd_call():
+        rha.hybrid_bwd(q, k, v, S, z, out_f, lse_f, dout, wl.C, wl.w, stream=stream)
+
+    if args.only == "bwd":
+        bwd_setup()
+        run_only(bwd_call, args.steps)
         return
 
     # ---- the contract: W warmup steps, then exactly K timed steps
@@ -352,21 +421,26 @@ def main():
     wall = time.perf_counter() - t0
     t_step = e0.elapsed_time(e1) / 1e3 / args.steps
 
-    # ---- per-kernel averages over timed regions (same stream)
+    # ---- per-kernel timings over timed regions (same stream)
     n_k = max(args.steps, 10)
-    t_fwd = timed(lambda: rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, out=out, stream=stream), n_k)
-    t_scan = timed(lambda: rha.state_scan(k, v, wl.C, wl.w, S=S, z=z, stream=stream), n_k)
-    t_sparse = timed(sparse_call, n_k)
-    t_bidir = timed(bidir_call, n_k)
-    t_bidir_scan = timed(bidir_scan, n_k)
+    t_fwd, t_fwd_med, t_fwd_min = timed(fwd_call, n_k)
+    t_scan, t_scan_med, t_scan_min = timed(scan_call, n_k)
+    scan_call()
+    t_sparse = timed(sparse_call, n_k)[0]
+    bidir_scan()
+    t_bidir = timed(bidir_call, n_k)[0]
+    t_bidir_scan = timed(bidir_scan, n_k)[0]
     bF = bidir_fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
-    t_anchor = timed(anchor_call, n_k)
-    t_bwd = timed(bwd_call, max(args.steps // 5, 5))
+    anchor_setup()
+    t_anchor = timed(anchor_call, n_k)[0]
+    bwd_setup()
+    t_bwd, t_bwd_med, t_bwd_min = timed(bwd_call, max(args.steps // 5, 5))
     gF = bwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
+    scan_call()  # S, z of the headline problem again (the backward set-up wrote them too)
 
-    sw, t_stream = stream_run(True)
+    sw, t_stream, t_stream_med, t_stream_min = stream_run()
 
     # ---- the two larger shapes (scan + fwd, each timed on its own); inputs
     # drawn on the GPU from a seeded generator with the same distribution (the
@@ -379,8 +453,8 @@ def main():
         oS, oz = rha.state_scan(ok, ov, ow.C, ow.w, stream=stream)
         oo = torch.empty_like(oq)
         rha.hybrid_fwd(oq, ok, ov, oS, oz, ow.C, ow.w, out=oo, stream=stream)
-        t_f = timed(lambda: rha.hybrid_fwd(oq, ok, ov, oS, oz, ow.C, ow.w, out=oo, stream=stream), n_calls)
-        t_s = timed(lambda: rha.state_scan(ok, ov, ow.C, ow.w, S=oS, z=oz, stream=stream), n_calls)
+        t_f = timed(lambda: rha.hybrid_fwd(oq, ok, ov, oS, oz, ow.C, ow.w, out=oo, stream=stream), n_calls)[0]
+        t_s = timed(lambda: rha.state_scan(ok, ov, ow.C, ow.w, S=oS, z=oz, stream=stream), n_calls)[0]
         obh = ow.B * ow.H
         oF = fwd_flops(ow.C, ow.N, ow.w, ow.d, obh)
         dense_causal = obh * sum(ow.C * 4 * ow.d * (c + 1) * ow.C for c in range(ow.N))
@@ -401,7 +475,7 @@ def main():
                 sS, sz = rha.state_scan(sl[1], sl[2], ow.C, wlim, stream=stream)
                 fn = lambda: rha.hybrid_fwd(sl[0], sl[1], sl[2], sS, sz, ow.C, wlim, out=so, stream=stream)
                 fn()
-                t_l = timed(fn, n_calls)
+                t_l = timed(fn, n_calls)[0]
                 lF = fwd_flops(ow.C, n21, wlim, ow.d, obh)
                 res[f"{name}_slice21_{tag}_fwd_us"] = t_l * 1e6
                 res[f"{name}_slice21_{tag}_TFLOPs"] = lF / t_l / 1e12
@@ -427,6 +501,8 @@ def main():
     tokens = wl.B * wl.L
     sF = stream_step_flops(sw.C, sw.w, sw.d, sw.B * sw.H)
     sB = stream_step_bytes(sw.C, sw.w, sw.d, sw.B * sw.H)
+    sX = stream_step_impl_extra_bytes(sw.C, sw.w, sw.d, sw.B * sw.H)
+    scB = scan_bytes(wl.C, wl.N, wl.w, wl.d, BH)
     result = {
         "metric": METRIC,
         "value": tokens / t_step,
@@ -447,19 +523,29 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "fwd_bf16_qb2_kernel (rha_hybrid_fwd)", "flops_per_launch": F,
                      "algorithmic_bytes_per_launch": fwd_bytes(wl.C, wl.N, wl.w, wl.d, BH),
-                     "avg_launch_us": t_fwd * 1e6},
+                     "avg_launch_us": t_fwd * 1e6, "median_launch_us": t_fwd_med * 1e6,
+                     "min_launch_us": t_fwd_min * 1e6},
         "detail": {
             "fwd_query_tokens_per_s": tokens / t_fwd,
             "fwd_us": t_fwd * 1e6,
+            "fwd_median_us": t_fwd_med * 1e6,
+            "fwd_min_us": t_fwd_min * 1e6,
+            "fwd_mfma_frac_at_min": F / t_fwd_min / 1e12 / PEAK_BF16_TFLOPS,
             "scan_us": t_scan * 1e6,
-            "scan_GBps": scan_bytes(wl.C, wl.N, wl.w, wl.d, BH) / t_scan / 1e9,
-            "scan_hbm_frac": scan_bytes(wl.C, wl.N, wl.w, wl.d, BH) / t_scan / 1e9 / PEAK_HBM_GBS,
+            "scan_median_us": t_scan_med * 1e6,
+            "scan_min_us": t_scan_min * 1e6,
+            "scan_GBps": scB / t_scan / 1e9,
+            "scan_hbm_frac": scB / t_scan / 1e9 / PEAK_HBM_GBS,
             "stream_step_us": t_stream * 1e6,
+            "stream_step_median_us": t_stream_med * 1e6,
+            "stream_step_min_us": t_stream_min * 1e6,
             "stream_chunks_per_s": 1.0 / t_stream,
             "stream_step_TFLOPs": sF / t_stream / 1e12,
             "stream_step_mfma_frac": sF / t_stream / 1e12 / PEAK_BF16_TFLOPS,
+            "stream_step_bytes": sB,
             "stream_step_GBps": sB / t_stream / 1e9,
             "stream_step_hbm_frac": sB / t_stream / 1e9 / PEAK_HBM_GBS,
+            "stream_step_impl_extra_bytes": sX,
             "sparse_half_fwd_us": t_sparse * 1e6,
             "sparse_half_kept_frac": float(mask_cpu.float().mean()),
             "sparse_half_TFLOPs": spF / t_sparse / 1e12,
@@ -472,6 +558,8 @@ def main():
             "anchor1_TFLOPs": aF / t_anchor / 1e12,
             "anchor1_mfma_frac": aF / t_anchor / 1e12 / PEAK_BF16_TFLOPS,
             "bwd_us": t_bwd * 1e6,
+            "bwd_median_us": t_bwd_med * 1e6,
+            "bwd_min_us": t_bwd_min * 1e6,
             "bwd_TFLOPs": gF / t_bwd / 1e12,
             "bwd_mfma_frac": gF / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
             **more,
