@@ -91,6 +91,27 @@ __device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt
   }
 }
 
+// The same staging with S split into two bf16 parts, S = hi + lo (exact to
+// about 2^-16 relative): hi rows into mr, lo rows 0..63 into lo0 and 64..127
+// into lo1 (64 rows each).
+__device__ __forceinline__ void stage_state_split(unsigned char* mr, unsigned char* lo0, unsigned char* lo1,
+                                                  const float* M, int tid) {
+  for (int u = tid; u < BD * BD / 8; u += TB) {
+    const int e = u / (BD / 8), g = u % (BD / 8);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
+    const f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
+    u32x4 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+      lo[i] = pack_bf16(x[2 * i] - bf16_lo(hi[i]), x[2 * i + 1] - bf16_hi(hi[i]));
+    }
+    put_granule(mr, e, g, hi);
+    put_granule(e < 64 ? lo0 : lo1, e & 63, g, lo);
+  }
+}
+
 // phi'(x) of the four features f .. f+3 of a bf16 row
 __device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
   const u32x2 xw = *reinterpret_cast<const u32x2*>(row + f);
@@ -363,7 +384,13 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   }
   float* dqr = p.dq + (bh * L + row0 + l32) * BD;
   if (c >= p.w) {  // the chunk has a state (every chunk for w = 0)
-    stage_state<false>(sm, nullptr, p.S + ((int64_t)bh * p.N + c) * BD * BD, tid);
+    // S_c and the rows dout_i / D_i each as two bf16 parts, the three
+    // products that matter (hi hi, hi lo, lo hi) on the matrix cores: with
+    // one bf16 rounding of each operand the sum over features, which cancels
+    // strongly, loses about 5e-3 relative, the same size as the state chunks'
+    // whole query gradient error budget; split, the term is exact to float32
+    // level.  The low part of S goes into the K/V staging buffers, free now.
+    stage_state_split(sm, ks_t[0], vs_t[0], p.S + ((int64_t)bh * p.N + c) * BD * BD, tid);
     __syncthreads();
     const float rs = qok ? p.rsc[bh * L + row0 + l32] : 0.f;  // 1 / D_i
     const bf16_t* qt = qb + (row0 + l32) * p.st;                // phi' argument
@@ -374,12 +401,21 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       f32x16 o1 = {};
+      const unsigned char* slo = nb < 2 ? ks_t[0] : vs_t[0];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        u32x4 x = __builtin_bit_cast(u32x4, gr[ks]);
+        const u32x4 g = __builtin_bit_cast(u32x4, gr[ks]);
+        u32x4 xh, xl;  // dout_i / D_i = xh + xl
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * rs, bf16_hi(x[i]) * rs);  // dout_i / D_i
-        o1 = mfma32(row_frag(sm, 32 * nb, ks, lane), __builtin_bit_cast(bf16x8, x), o1);
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = bf16_lo(g[i]) * rs, x1 = bf16_hi(g[i]) * rs;
+          xh[i] = pack_bf16(x0, x1);
+          xl[i] = pack_bf16(x0 - bf16_lo(xh[i]), x1 - bf16_hi(xh[i]));
+        }
+        const bf16x8 sh = row_frag(sm, 32 * nb, ks, lane), sl = row_frag(slo, 32 * (nb & 1), ks, lane);
+        o1 = mfma32(sh, __builtin_bit_cast(bf16x8, xh), o1);
+        o1 = mfma32(sh, __builtin_bit_cast(bf16x8, xl), o1);
+        o1 = mfma32(sl, __builtin_bit_cast(bf16x8, xh), o1);
       }
       if (qok) {
 #pragma unroll

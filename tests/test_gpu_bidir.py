@@ -14,7 +14,7 @@ import torch
 import oracle
 from synth import CONFIGS, Workload, gen_qkv
 import linear_attention_video_chunked_amd as rha
-from parity_utils import TOL, per_chunk_rel_l2, rel_l2, to64
+from parity_utils import ALARM, GroupedRows, sample_rows, TOL, per_chunk_rel_l2, rel_l2, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -97,15 +97,12 @@ def test_bidir_wan13b_sampled_rows():
     torch.cuda.synchronize()
     og = out.cpu()
     q64, k64, v64 = to64(q), to64(k), to64(v)
-    rng = np.random.default_rng(11)
-    got, want = [], []
+    grouped = GroupedRows("bidir wan13b")
     for h in range(0, wl.H, 4):
         st = oracle.state_scan_bidir(k64[0, h], v64[0, h], wl.C, wl.w)
-        rows = np.unique(np.concatenate([[0, 1559, 1560, 10 * wl.C, wl.L - 1], rng.integers(0, wl.L, 24)]))
-        want.append(oracle.hybrid_bidir_rows(q64[0, h], k64[0, h], v64[0, h], wl.C, wl.w, rows, states=st))
-        got.append(og[0, h, rows].double().numpy())
+        rows = sample_rows(wl.C, wl.N, 4 * wl.N, seed=11 + h)
+        want = oracle.hybrid_bidir_rows(q64[0, h], k64[0, h], v64[0, h], wl.C, wl.w, rows, states=st)
+        grouped.add_by_chunk((0, h), og[0, h, rows].double().numpy(), want, rows, wl.C)
         for x, r in zip(states, st):
             assert rel_l2(to64(x[0, h]), r) <= TOL["bf16"]
-    g = rel_l2(np.concatenate(got), np.concatenate(want))
-    print(f"[parity] bidir wan13b: sampled rel-L2 {g:.3e}", flush=True)
-    assert g <= TOL["bf16"]
+    grouped.check(TOL["bf16"], ALARM["bf16"])

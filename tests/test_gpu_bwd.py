@@ -13,7 +13,7 @@ import torch
 import oracle
 from synth import CONFIGS, Workload, gen_qkv, to_storage
 import linear_attention_video_chunked_amd as rha
-from parity_utils import TOL, rel_l2, to64
+from parity_utils import GroupedRows, sample_rows, TOL, rel_l2, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -74,15 +74,13 @@ def test_backward_wan13b_sampled_rows():
     dout = _dout(wl, 2)
     dq, dk, dv = _run(wl, q, k, v, dout)
     # the oracle's full backward for a few heads; compare sampled rows
-    rng = np.random.default_rng(17)
-    rows = np.unique(np.concatenate([[0, 1559, 1560, 10 * wl.C, wl.L - 1], rng.integers(0, wl.L, 60)]))
-    got, want = [[], [], []], [[], [], []]
+    # rows at chunk edges, tile edges and the short tails, plus random ones;
+    # each gradient checked per chunk as well as over all sampled rows
+    rows = sample_rows(wl.C, wl.N, 4 * wl.N, seed=17)
+    grouped = [GroupedRows(f"bwd wan13b {nm}") for nm in ("dq", "dk", "dv")]
     for h in (0, 7):
         ref = oracle.hybrid_backward(to64(q)[0, h], to64(k)[0, h], to64(v)[0, h], wl.C, wl.w, to64(dout)[0, h])
         for i, (g, r) in enumerate(zip((dq, dk, dv), ref)):
-            got[i].append(to64(g[0, h])[rows])
-            want[i].append(r[rows])
-    for i, nm in enumerate(("dq", "dk", "dv")):
-        e = rel_l2(np.concatenate(got[i]), np.concatenate(want[i]))
-        print(f"[parity] bwd wan13b {nm}: sampled rel-L2 {e:.3e}", flush=True)
-        assert e <= TOL["bf16"]
+            grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
+    for gr in grouped:
+        gr.check(TOL["bf16"])
