@@ -285,6 +285,39 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
  */
 size_t rha_stream_workspace_size(const rha_problem* p);
 
+/* Bytes of device scratch that rha_stream_step_noalloc holds per GPU. */
+#define RHA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+
+/*
+ * rha_stream_step_noalloc -- rha_stream_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.
+ *
+ * The same step, arguments and results as rha_stream_step with its workspace
+ * (the split key window and the split fold), but the workspace is the
+ * library's own: a file-scope device array of RHA_NOALLOC_SCRATCH_BYTES (48
+ * MiB) that every GPU the library runs on holds until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Its address is looked up once per device, on the first call
+ * with that device current.
+ *
+ * The scratch keeps the last call's contents; nothing in it needs clearing
+ * (every byte a step reads it first writes).  Calls that overlap on one GPU
+ * -- on two streams at once, or from two threads -- share that GPU's scratch
+ * and race: serialise them (one stream, or one call in flight per GPU).
+ *
+ * Errors: as rha_stream_step; RHA_ERR_UNSUPPORTED if the step needs more
+ * scratch than RHA_NOALLOC_SCRATCH_BYTES (rha_stream_workspace_size(p) tells
+ * how much: about 41 MB for 12 heads of 1560-token chunks with a 9-chunk
+ * window; the split gives each compute unit at most one workgroup, which on
+ * a 256-CU MI355X bounds any problem's need near 43 MB), RHA_ERR_HIP if the
+ * scratch's address cannot be obtained.
+ */
+rha_status rha_stream_step_noalloc(const rha_problem* p, const void* q_new, const void* k_new,
+                                   const void* v_new, void* k_cache, void* v_cache, float* S, float* z,
+                                   rha_stream_cursor* cursor, int32_t commit, void* out, float* lse,
+                                   void* stream);
+
 /* Static name of a status code. */
 const char* rha_status_string(rha_status s);
 

@@ -13,6 +13,7 @@ Functions mirror the C ABI in ``include/rha.h``:
 * ``state_scan_bidir`` / ``hybrid_fwd_bidir``     symmetric window, past + future states
 * ``hybrid_bwd(q, k, v, S, z, out, lse, dout, C, w)`` -> dq, dk, dv (float32)
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
+* ``stream_step_noalloc(...)``                    the same step with the library's own scratch
 """
 from ._rha import (
     LibraryNotBuilt,
@@ -28,6 +29,7 @@ from ._rha import (
     state_scan,
     state_scan_bidir,
     stream_step,
+    stream_step_noalloc,
     version,
 )
 
@@ -45,5 +47,6 @@ __all__ = [
     "state_scan",
     "state_scan_bidir",
     "stream_step",
+    "stream_step_noalloc",
     "version",
 ]

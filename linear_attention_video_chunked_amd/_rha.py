@@ -74,8 +74,10 @@ def lib():
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
     L.rha_stream_workspace_size.restype = ctypes.c_size_t
+    L.rha_stream_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
+                                          ctypes.c_int32, _vp, _vp, _vp]
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
-                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_stream_step"):
+                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_stream_step", "rha_stream_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
     L.rha_status_string.restype = ctypes.c_char_p
@@ -361,4 +363,36 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
                                  ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _ptr(st.workspace),
                                  ctypes.c_size_t(0 if st.workspace is None else st.workspace.numel()),
                                  _stream(stream)))
+    return out
+
+
+# Bytes of device scratch the no-allocation step holds per GPU (RHA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def stream_step_noalloc(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        commit: bool = True, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rha_stream_step_noalloc: the streaming step with the library's own
+    per-GPU scratch in place of a workspace (st.workspace is not used); for
+    callers that cannot allocate device memory.  Pass ``out`` (and ``lse``)
+    to keep this call free of allocation on the Python side too."""
+    if out is None:
+        out = torch.empty_like(q_new)
+    _same_layout(q_new, k_new, v_new, out)
+    B, H, C, d = q_new.shape
+    if (B, H, C, d) != (st.B, st.H, st.C, st.d):
+        raise ValueError("chunk shape does not match the stream state")
+    if q_new.dtype != st.k_cache.dtype:
+        raise ValueError("chunk dtype does not match the cache")
+    for name, t in (("k_cache", st.k_cache), ("v_cache", st.v_cache), ("S", st.S), ("z", st.z)):
+        if t.device != q_new.device:
+            raise ValueError(f"stream state {name} is on {t.device}, the chunk on {q_new.device}")
+    if lse is not None:
+        _check_f32(q_new, lse, "lse", (B, H, C))
+    prob = _problem(q_new, C, st.w, 1)
+    _check(lib().rha_stream_step_noalloc(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new),
+                                         _ptr(st.k_cache), _ptr(st.v_cache), _ptr(st.S), _ptr(st.z),
+                                         ctypes.byref(st.cursor), ctypes.c_int32(1 if commit else 0), _ptr(out),
+                                         _ptr(lse), _stream(stream)))
     return out

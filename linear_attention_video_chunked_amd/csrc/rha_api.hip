@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "rha.h"
@@ -620,6 +621,48 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
     cursor->t = t + 1;
   }
   return ok();
+}
+
+// ---- the step without allocation: its workspace in a file-scope device
+// array (one copy per GPU), whose device address is looked up once per device
+// with that device current.  In host code `scratch` only names the symbol;
+// kernels and copies get the looked-up address.
+static __device__ __align__(256) unsigned char scratch[RHA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+rha_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RHA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(RHA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RHA_OK;
+}
+}  // namespace
+
+rha_status rha_stream_step_noalloc(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
+                                   int32_t commit, void* out, float* lse, void* stream) {
+  RHA_TRY(check_problem(p, true));
+  const size_t need = rha_stream_workspace_size(p);
+  if (need > RHA_NOALLOC_SCRATCH_BYTES)
+    return fail(RHA_ERR_UNSUPPORTED, "this step needs %zu bytes of scratch, the no-allocation step holds %zu",
+                need, (size_t)RHA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && !empty(p, true)) RHA_TRY(scratch_address(&ws));
+  return rha_stream_step(p, q_new, k_new, v_new, k_cache, v_cache, S, z, cursor, commit, out, lse, ws, need, stream);
 }
 
 const char* rha_status_string(rha_status st) {
