@@ -61,16 +61,19 @@ template <typename T> __device__ __forceinline__ void pin_acc(T& x) { asm volati
 // S^T += K Q^T block product in the VGPR-accumulator form of the
 // instruction (the softmax VALU reads these accumulators; in AGPRs every read
 // would cost a copy).  Written as asm because the compiler picks the AGPR
-// form for every product of a kernel that keeps accumulators in AGPRs.  The
-// leading s_nop covers the wait states a VALU write of an operand needs before
-// a matrix-core read; the results are first read by VALU code one pipeline
-// step (32 further products) later, far past the result latency, and the
-// accumulation chain has three other products between dependent ones.
+// form for every product of a kernel that keeps accumulators in AGPRs.  No
+// vector-ALU instruction writes these operands shortly before: K fragments
+// come from LDS reads (ordered by the LDS counter waits), Q fragments are
+// loaded once, and the accumulators are written by products (or masked by
+// the softmax) a whole pipeline step earlier; the results are first read by
+// VALU code one step (32 further products) later, far past the result
+// latency, and the accumulation chain has three other products between
+// dependent ones.  So no wait states are inserted.
 __device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 constexpr int Q2_QB = 2;  // 32-row query blocks per wave
@@ -144,7 +147,9 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   unsigned char* const vb1 = q2_vb1;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same in every lane: kept scalar, so the tile loads'
+  // LDS addresses are formed without vector instructions
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- which tile
@@ -276,31 +281,35 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // at byte 16L): 4 rows of a tile.  Wave w issues loads i = 0..LPW-1 of a
   // tile, rows 4(LPW*w+i) .. +3; lane L fills row 4(LPW*w+i) + L/16, slot L%16,
   // with the global granule that the swizzle puts there (g = slot ^ sw(row)).
-  // The descriptor ends at the window end, so rows past it read as zero.
+  // The descriptor of a tile starts at the tile's first key and ends at the
+  // window end (its size is clamped at 0 for tiles past the window), so rows
+  // past the end read as zero; the tile's offset lives in the descriptor's
+  // base (scalar arithmetic), and each lane's offset within the tile is a
+  // fixed register.
   constexpr int LPW = BN / 4 / NW;  // 4-row loads per wave and tile
   static_assert(LPW * 4 * NW == BN && LPW % 4 == 0 && GR == 16, "whole 4-row loads per wave");
   const int lrow = lane >> 4, lslot = lane & 15;
-  int kdma[4];  // the K swizzle repeats every 16 rows: load i uses kdma[i % 4] + (i / 4) 16-row steps
+  int kdma[LPW], vdma[LPW];  // byte offsets within a tile of this lane's granule in load i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < LPW; ++i) {
     const int row = 4 * (LPW * wave + i) + lrow;
     kdma[i] = (row * (int)p.kv_st + (lslot ^ ksw<D>(row)) * 8) * 2;
+    vdma[i] = (row * (int)p.kv_st + (lslot ^ vsw<D>(row)) * 8) * 2;
   }
-  const int vdma0 = ((4 * LPW * wave + lrow) * (int)p.kv_st + (lslot ^ vsw<D>(lrow)) * 8) * 2;  // vsw(row) = vsw(lrow)
-  const int vdma_step = 4 * (int)p.kv_st * 2;
   const int win_bytes = (int)(kend * p.kv_st * 2);
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, win_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, win_bytes, kBufWord3);
   typedef __attribute__((address_space(3))) void lds_void;
-  auto dma_k = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
+  auto tile_rsrc = [&](const bf16_t* base, int64_t key) __attribute__((always_inline)) {
     const int tile_off = (int)(key * p.kv_st * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
-                                             kdma[i % 4] + (i / 4) * 4 * vdma_step + tile_off, 0, 0, 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)base + tile_off), (short)0,
+                                             max(win_bytes - tile_off, 0), kBufWord3);
+  };
+  auto dma_k = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(kbase, key), (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
+                                             kdma[i], 0, 0, 0);
   };
   auto dma_v = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
-    const int tile_off = (int)(key * p.kv_st * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
-                                             vdma0 + i * vdma_step + tile_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(vbase, key), (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
+                                             vdma[i], 0, 0, 0);
   };
 
   // ---- Q fragments of both query blocks (rows past the chunk re-read the last valid row)
