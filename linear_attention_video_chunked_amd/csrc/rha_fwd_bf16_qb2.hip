@@ -312,6 +312,29 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
                                              vdma[i], 0, 0, 0);
   };
 
+  // ---- The pass's first loads, all in flight together (one memory round
+  // trip): the first K tile, the linear state and its normaliser (the state
+  // of chunk c is always addressable, so the past state is loaded
+  // unconditionally and dropped below when the chunk has no history), then Q.
+  if (Tp > 0) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) dma_k(kb0, act_key(0), i);
+  }
+  constexpr int SUNITS = (D / 8) * (D / 4);
+  constexpr int UPT = SUNITS / THREADS;  // 8-row x 4-column units of S per thread
+  static_assert(UPT * THREADS == SUNITS && D / 4 <= THREADS, "state units split evenly over the threads");
+  f32x4 srows[UPT][8];
+  f32x4 zq = {0.f, 0.f, 0.f, 0.f};  // z[4 tid .. 4 tid + 3] (threads below D/4)
+  if (has_state) {
+#pragma unroll
+    for (int uu = 0; uu < UPT; ++uu) {
+      const int u = tid + uu * THREADS, eg = u / (D / 4), ng = u % (D / 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) srows[uu][i] = *reinterpret_cast<const f32x4*>(Sp + (int64_t)(eg * 8 + i) * D + ng * 4);
+    }
+    if (tid < D / 4) zq = *reinterpret_cast<const f32x4*>(zp + tid * 4);
+  }
+
   // ---- Q fragments of both query blocks (rows past the chunk re-read the last valid row)
   bf16x8 qf[QB][DS];
 #pragma unroll
@@ -346,26 +369,39 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
       for (int nb = 0; nb < DB; ++nb) o[qb][nb] = f32x16{};
     }
     if (!has_state) return;
-    constexpr int SUNITS = (D / 8) * (D / 4);
-    for (int u = tid; u < SUNITS; u += THREADS) {
-      const int eg = u / (D / 4), ng = u % (D / 4);
-      f32x4 rows[8];
+    if (!has_past) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        rows[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (has_past) rows[i] = *reinterpret_cast<const f32x4*>(Sp + (int64_t)(eg * 8 + i) * D + ng * 4);
-        // bidirectional: the past and future states summed in float32 before rounding
-        if (has_future) rows[i] += *reinterpret_cast<const f32x4*>(Sp2 + (int64_t)(eg * 8 + i) * D + ng * 4);
+      for (int uu = 0; uu < UPT; ++uu)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) srows[uu][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      zq = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (has_future) {  // bidirectional: the past and future states summed in float32 before rounding
+#pragma unroll
+      for (int uu = 0; uu < UPT; ++uu) {
+        const int u = tid + uu * THREADS, eg = u / (D / 4), ng = u % (D / 4);
+        f32x4 r2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r2[i] = *reinterpret_cast<const f32x4*>(Sp2 + (int64_t)(eg * 8 + i) * D + ng * 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) srows[uu][i] += r2[i];
       }
+      if (tid < D / 4) zq += *reinterpret_cast<const f32x4*>(zp2 + tid * 4);
+    }
+#pragma unroll
+    for (int uu = 0; uu < UPT; ++uu) {
+      const int u = tid + uu * THREADS, eg = u / (D / 4), ng = u % (D / 4);
       unsigned char* dst = eg < DS ? vb0 + (size_t)eg * D * 16 : vb1 + (size_t)(eg - DS) * D * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pack_bf16(rows[2 * i][j], rows[2 * i + 1][j]);
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16(srows[uu][2 * i][j], srows[uu][2 * i + 1][j]);
         *reinterpret_cast<u32x4*>(dst + (size_t)(ng * 4 + j) * 16) = w;
       }
     }
+    // the normaliser in float32 in the second K buffer (free until the pipeline starts)
+    if (tid < D / 4) *reinterpret_cast<f32x4*>(kb1 + tid * 16) = zq;
     __syncthreads();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -380,15 +416,8 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
           f[2 * i] = phi(bf16_lo(qw[i]));
           f[2 * i + 1] = phi(bf16_hi(qw[i]));
         }
-        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-        if (has_past) {
-          z0 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8);
-          z1 = *reinterpret_cast<const f32x4*>(zp + s * 16 + hh * 8 + 4);
-        }
-        if (has_future) {
-          z0 += *reinterpret_cast<const f32x4*>(zp2 + s * 16 + hh * 8);
-          z1 += *reinterpret_cast<const f32x4*>(zp2 + s * 16 + hh * 8 + 4);
-        }
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(kb1 + (s * 16 + hh * 8) * 4);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(kb1 + (s * 16 + hh * 8 + 4) * 4);
         lz += f[0] * z0[0] + f[1] * z0[1] + f[2] * z0[2] + f[3] * z0[3] + f[4] * z1[0] + f[5] * z1[1] +
               f[6] * z1[2] + f[7] * z1[3];
         const u32x4 pw = {pack_bf16(f[0] * sc, f[1] * sc), pack_bf16(f[2] * sc, f[3] * sc),
@@ -679,9 +708,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // V tile t from registers, buffer loads of K tile t+2 and V tile t+1
   // (tiles past the window read as zeros and are never used).
   auto pipeline = [&](auto check_c) __attribute__((always_inline)) {
-    // prologue: K tile 0 into LDS
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_k(kb0, act_key(0), i);
+    // prologue: K tile 0 (its loads issued at the start of the pass) in LDS
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
     period(0, A0{}, check_c, C0{}, C1{}, 32, block_valid(0));
