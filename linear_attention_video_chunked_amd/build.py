@@ -22,7 +22,13 @@ ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are disabled for all device code (the compiler would
 # otherwise form v_pk_* fp32 instructions from ordinary float code).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Private arrays are not promoted to LDS: a promoted array is addressed by the
+# flat thread index, for which every workgroup first reads its dispatch packet;
+# on the MI355X those reads spread the start of a launch's first 256
+# workgroups over 12.5 us (0.3 us without them; measured on the split forward
+# of a streaming step).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-disable-promote-alloca-to-lds"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 

@@ -147,8 +147,9 @@ int stream_splits(const rha_problem* p, int64_t n_keys) {
 
 // Split of the streaming fold (bf16): the folded chunk's tokens in groups of
 // whole 64-token tiles, enough groups for about one workgroup per compute
-// unit.  Returns the number of groups (1: no split) and their length.
-int fold_groups(const rha_problem* p, int* group_len) {
+// unit (per `share` compute units).  Returns the number of groups (1: no
+// split) and their length.
+int fold_groups(const rha_problem* p, int* group_len, int share = 1) {
   *group_len = p->chunk_len;
   if (p->dtype != RHA_BF16) return 1;
   int dev = 0, cus = 0;
@@ -157,7 +158,8 @@ int fold_groups(const rha_problem* p, int* group_len) {
     return 1;
   const int64_t units = (int64_t)p->batch * p->heads * (p->head_dim / 64);  // workgroups per group
   const int64_t ntiles = (p->chunk_len + 63) / 64;
-  int64_t g = (cus + units - 1) / units;
+  const int64_t wgs = (cus + share - 1) / share;
+  int64_t g = (wgs + units - 1) / units;
   if (g > ntiles) g = ntiles;
   if (g < 2) return 1;
   const int64_t per = (ntiles + g - 1) / g;
@@ -489,17 +491,22 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   const int n_keys = (int)(in_window * C);
   const bool fold = commit && t >= w - 1;
   const int splits = workspace != nullptr ? stream_splits(p, n_keys) : 1;
-  int glen = C;
-  const int groups = (workspace != nullptr && fold) ? fold_groups(p, &glen) : 1;
   const size_t fwd_part = splits > 1 ? align256(rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) : 0;
-  const size_t fold_part = groups > 1 ? align256(fold_bytes(p, groups)) : 0;
   const bool split_fwd = splits > 1 && workspace_bytes >= fwd_part;
+  // beside a split attention the fold takes the compute units the attention
+  // leaves idle (about one in four), else about all of them
+  int glen = C;
+  const int groups = (workspace != nullptr && fold) ? fold_groups(p, &glen, split_fwd ? 4 : 1) : 1;
+  const size_t fold_part = groups > 1 ? align256(fold_bytes(p, groups)) : 0;
   const bool split_fold = groups > 1 && workspace_bytes >= (split_fwd ? fwd_part : 0) + fold_part;
   float* fold_ws = split_fold ? reinterpret_cast<float*>(static_cast<char*>(workspace) + (split_fwd ? fwd_part : 0))
                               : nullptr;
 
-  // 1. the new chunk's keys and values into its cache slot (t % w); with a
-  // split fold, the same launch computes the leaving chunk's partial states
+  // 1. the new chunk's keys and values into its cache slot (t % w).  A split
+  // fold's partial states (the chunk leaving the window) are computed by extra
+  // workgroups of the split attention launch (step 2), on the compute units
+  // the attention leaves idle; without a split attention, by this launch.
+  const bool fold_in_fwd = split_fold && split_fwd && p->dtype == RHA_BF16 && d == 128;
   rha::CopyParams cp{};
   cp.sb = p->stride_b;
   cp.sh = p->stride_h;
@@ -515,6 +522,7 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   cp.dst = k_cache;
   cp.src2 = v_new;
   cp.dst2 = v_cache;
+  rha::ChunkStateParams fold_c{};
   if (split_fold) {
     // the chunk leaving the window (t-w+1) sits in slot (t+1) % w, which the
     // copy does not touch -- except for w = 1, where it is the new chunk
@@ -546,11 +554,15 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
     c.s_bh = (int64_t)groups * d * d;
     c.z_bh = (int64_t)groups * d;
     c.tok_end = C;
-    c.copy = cp;
-    c.copy_blocks_per_bh = (int)(((int64_t)C * (d * cp.elem_bytes / 16) + 255) / 256);
-    e = launch_chunk_state(p, c, s);
-    if (e != hipSuccess) return hip_fail(e, "cache copy and fold launch");
-  } else {
+    fold_c = c;
+    if (!fold_in_fwd) {
+      c.copy = cp;
+      c.copy_blocks_per_bh = (int)(((int64_t)C * (d * cp.elem_bytes / 16) + 255) / 256);
+      e = launch_chunk_state(p, c, s);
+      if (e != hipSuccess) return hip_fail(e, "cache copy and fold launch");
+    }
+  }
+  if (!split_fold || fold_in_fwd) {
     e = rha::launch_copy_chunk(cp, s);
     if (e != hipSuccess) return hip_fail(e, "cache copy launch");
   }
@@ -581,7 +593,7 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   f.n_splits = split_fwd ? splits : 1;
   f.part = split_fwd ? static_cast<float*>(workspace) : nullptr;
-  e = launch_fwd(p, f, s);
+  e = fold_in_fwd ? rha::launch_fwd_bf16_qb2_fold(f, fold_c, s) : launch_fwd(p, f, s);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
 
   // 3. merges (after the pass has read S, z), then the unsplit fold

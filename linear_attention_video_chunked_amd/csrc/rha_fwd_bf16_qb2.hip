@@ -37,6 +37,7 @@
 #include "rha_device.hpp"
 #include "rha_frag.hpp"
 #include "rha_fwd_common.hpp"
+#include "rha_state_unit.hpp"
 #include "rha_launch.hpp"
 #include "rha_small.hpp"
 
@@ -1207,16 +1208,48 @@ __device__ __noinline__ void tile_second_pass(const FwdParams p, float m0, float
   tile_pass<D, NW, false, PARTIAL, VIS>(p, m);
 }
 
+// A split pass (PARTIAL) may carry the units of the streaming fold (partial
+// states of the chunk leaving the window, `fold`; fold.k set): they run where
+// the attention leaves compute units idle -- after the short tails (which end
+// long before the full tiles), tail workgroup i taking units i, i + n_tails,
+// ..., or, in a pass without tails, in extra workgroups after its
+// p.total_tiles tiles.
+template <int D, int NW>
+__device__ __forceinline__ void fold_unit(const ChunkStateParams& fold, int u) {
+  static_assert(NW * 64 == state::THREADS && state::StateCfg<D>::KBYTES * 2 <= Q2_TILE &&
+                    state::StateCfg<D>::VBYTES <= Q2_TILE &&
+                    sizeof(float) * (state::THREADS / (state::ESLICE / 8)) * state::ESLICE <= Q2_TILE,
+                "the fold unit's buffers fit the tile buffers");
+  state::chunk_state_unit<D, false>(fold, u, q2_kb0, q2_kb0 + state::StateCfg<D>::KBYTES, q2_vb0, q2_vb1,
+                                    reinterpret_cast<float(*)[state::ESLICE]>(q2_kb1));
+}
+
 template <int D, int NW, bool PARTIAL, int VIS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_bf16_qb2_kernel(const FwdParams p) {
+void fwd_bf16_qb2_kernel(const FwdParams p, const ChunkStateParams fold) {
+  if constexpr (PARTIAL) {
+    if ((int)blockIdx.x >= p.total_tiles) {
+      fold_unit<D, NW>(fold, (int)blockIdx.x - p.total_tiles);
+      return;
+    }
+  }
   {
-    const int logical = launch_order(blockIdx.x, p.total_tiles, p.tiles_per_chunk, !PARTIAL && p.tail_rows > 0) /
-                        (PARTIAL ? p.n_splits : 1);
+    const int logical0 = launch_order(blockIdx.x, p.total_tiles, p.tiles_per_chunk, !PARTIAL && p.tail_rows > 0);
+    const int logical = logical0 / (PARTIAL ? p.n_splits : 1);
     if (p.tail_rows > 0 && logical % p.tiles_per_chunk == p.tiles_per_chunk - 1) {
       // a chunk's short tail (the parameter block by value: a pointer to it
       // measured slower, the callee then saves most of its registers)
       tail_pass<VIS == 1, PARTIAL, VIS == 2>(p);
+      if constexpr (PARTIAL) {
+        if (fold.k != nullptr) {
+          const int n_tails = p.total_tiles / p.tiles_per_chunk;
+          const int units = fold.B * fold.H * fold.n_chunks * state::StateCfg<D>::ES;
+          for (int u = (logical / p.tiles_per_chunk) * p.n_splits + logical0 % p.n_splits; u < units; u += n_tails) {
+            __syncthreads();  // the tile buffers are free
+            fold_unit<D, NW>(fold, u);
+          }
+        }
+      }
       return;
     }
   }
@@ -1270,7 +1303,8 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p, con
 }
 
 template <int NW>
-hipError_t launch_nw(FwdParams& p, hipStream_t s) {
+hipError_t launch_nw(FwdParams& p, hipStream_t s, const ChunkStateParams& fold = ChunkStateParams{},
+                     int fold_blocks = 0) {
   constexpr int BM = NW * 32 * Q2_QB;
   static_assert(BM == kQb2RowsPerTile, "partial-result tile size");
   const int splits = p.n_splits > 1 ? p.n_splits : 1;
@@ -1285,13 +1319,14 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
   const int64_t grid = p.total_tiles;
   if (grid == 0) return hipSuccess;
   if (splits > 1)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 0>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 0>), dim3((unsigned)(grid + fold_blocks)), dim3(NW * 64), 0,
+                       s, p, fold);
   else if (p.kmask != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 1>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 1>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p, fold);
   else if (p.anchors > 0)
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 2>), dim3(p.total_tiles), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 2>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p, fold);
   else
-    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 0>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, false, 0>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p, fold);
   return hipGetLastError();
 }
 
@@ -1299,6 +1334,15 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s) {
 
 hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s) {
   return launch_nw<Q2_NW>(p, s);
+}
+
+hipError_t launch_fwd_bf16_qb2_fold(FwdParams& p, const ChunkStateParams& fold, hipStream_t s) {
+  if (p.n_splits < 2 || fold.k == nullptr) return hipErrorInvalidValue;  // the fold rides on a split pass only
+  // extra workgroups only for passes without short tails (the tails take the units)
+  const int rem = p.C % kQb2RowsPerTile;
+  const bool tails = rem > 0 && rem <= kTailMaxRows;
+  const int fold_blocks = tails ? 0 : fold.B * fold.H * fold.n_chunks * state::StateCfg<128>::ES;
+  return launch_nw<Q2_NW>(p, s, fold, fold_blocks);
 }
 
 size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits) {

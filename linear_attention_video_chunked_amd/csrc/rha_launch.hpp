@@ -172,6 +172,11 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(FwdParams& p, int d, hipStream_t s);
 // head_dim 128 with 64 query rows per wave (the default for d = 128)
 hipError_t launch_fwd_bf16_qb2(FwdParams& p, hipStream_t s);
+// The same as a split pass (p.n_splits > 1, stream mode) whose extra
+// workgroups compute the state contributions `fold` (bf16, head_dim 128,
+// accumulate == 0, no cache copy, no per-token factors): the streaming fold,
+// beside the attention on the compute units it leaves idle.
+hipError_t launch_fwd_bf16_qb2_fold(FwdParams& p, const ChunkStateParams& fold, hipStream_t s);
 // head_dim 128, window of 0 chunks (sequence mode, causal, no mask or anchors)
 hipError_t launch_fwd_linear_bf16(const FwdParams& p, hipStream_t s);
 // Query rows per workgroup of the d = 128 bf16 kernel (the partial-result tile).
