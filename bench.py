@@ -307,10 +307,15 @@ def main():
 
         for t in range(sw.prefill):
             push(t)
+        # untimed steps with a full window first (the inputs of the timed
+        # steps, later cursor positions), so the timed steps do not start from
+        # an idle GPU: measured, the first steps after an idle gap run slower
+        for t in range(sw.prefill, sw.prefill + sw.steps):
+            push(t)
         torch.cuda.synchronize()
         # the mean from two events around the timed steps; median and min from
         # an event after each of the same steps run again (later cursor
-        # positions, the same inputs: the window is full in both passes)
+        # positions, the same inputs: the window is full in every pass)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)

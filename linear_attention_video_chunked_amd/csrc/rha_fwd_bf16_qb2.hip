@@ -952,15 +952,30 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     // from memory (32 lanes read 32 consecutive floats of a row of S).
     const float* Sp = p.S + slot * BD * BD + 32 * wave + l32;
     const float* Sp2 = p.bidir ? p.S2 + slot * BD * BD + 32 * wave + l32 : nullptr;
+    // every load in flight at once: the state slot is always addressable, so
+    // the past state is loaded unconditionally and dropped when absent
     float col[8][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int f = 16 * ks + 8 * hh + e;
-        col[ks][e] = has_past ? Sp[f * BD] : 0.f;
-        if (has_future) col[ks][e] += Sp2[f * BD];
-      }
+      for (int e = 0; e < 8; ++e) col[ks][e] = Sp[(16 * ks + 8 * hh + e) * BD];
+    if (!has_past) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[ks][e] = 0.f;
+    }
+    if (has_future) {
+      float c2[8][8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c2[ks][e] = Sp2[(16 * ks + 8 * hh + e) * BD];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[ks][e] += c2[ks][e];
+    }
     f32x16 t = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -974,24 +989,37 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
     if (wave == 0) {  // phi(q).z, summed over both halves of the features
       const float* zp = p.z + slot * BD;
       const float* zp2 = p.bidir ? p.z2 + slot * BD : nullptr;
+      f32x4 zz[8][2];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        zz[ks][0] = *reinterpret_cast<const f32x4*>(zp + 16 * ks + 8 * hh);
+        zz[ks][1] = *reinterpret_cast<const f32x4*>(zp + 16 * ks + 8 * hh + 4);
+      }
+      if (!has_past) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) zz[ks][0] = zz[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if (has_future) {
+        f32x4 z2[8][2];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          z2[ks][0] = *reinterpret_cast<const f32x4*>(zp2 + 16 * ks + 8 * hh);
+          z2[ks][1] = *reinterpret_cast<const f32x4*>(zp2 + 16 * ks + 8 * hh + 4);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          zz[ks][0] += z2[ks][0];
+          zz[ks][1] += z2[ks][1];
+        }
+      }
       float acc = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const u32x4 x = __builtin_bit_cast(u32x4, qf[ks]);
-        const int f0 = 16 * ks + 8 * hh;
-        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-        if (has_past) {
-          z0 = *reinterpret_cast<const f32x4*>(zp + f0);
-          z1 = *reinterpret_cast<const f32x4*>(zp + f0 + 4);
-        }
-        if (has_future) {
-          z0 += *reinterpret_cast<const f32x4*>(zp2 + f0);
-          z1 += *reinterpret_cast<const f32x4*>(zp2 + f0 + 4);
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float qv = (e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1]);
-          acc = fmaf(phi(qv), e < 4 ? z0[e] : z1[e - 4], acc);
+          acc = fmaf(phi(qv), e < 4 ? zz[ks][0][e] : zz[ks][1][e - 4], acc);
         }
       }
       const float tot = half_sum(acc);  // the lane swap needs every lane active
