@@ -84,6 +84,10 @@ constexpr int Q2_NW = 4;
 // Probabilities up to 2^kQ2Slack are accepted against a stale reference
 // (far inside the bf16 and f32 ranges).
 constexpr float kQ2Slack = 64.0f;
+// Key tiles the state-seeded split of a split pass gives up to the others:
+// seeding (the linear term, 64 products per wave plus the state loads)
+// measured about 3 us, two 64-key tiles of the pipeline.
+constexpr int kQ2SeedTiles = 2;
 
 // LDS tile buffers (head dimension 128): K and V, double buffered.  At
 // namespace scope so that the rare second pass, a separate function, shares
@@ -198,9 +202,13 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     kend = p.n_keys;
     has_state = p.has_state != 0;
     if (PARTIAL) {  // this split's share of the key tiles; the first split takes the state
+      // (and kQ2SeedTiles fewer key tiles: seeding the accumulators with the
+      // linear term costs about that much, so the splits end together)
       const int tiles_all = (p.n_keys + BN - 1) / BN;
-      const int t_lo = (int)((int64_t)split * tiles_all / p.n_splits);
-      const int t_hi = (int)((int64_t)(split + 1) * tiles_all / p.n_splits);
+      const int n = p.n_splits;
+      const int e0 = max(1, tiles_all / n - (has_state && tiles_all >= 4 * n ? kQ2SeedTiles : 0));
+      const int t_lo = split == 0 ? 0 : e0 + (int)((int64_t)(split - 1) * (tiles_all - e0) / (n - 1));
+      const int t_hi = split == 0 ? e0 : e0 + (int)((int64_t)split * (tiles_all - e0) / (n - 1));
       kbeg = (int64_t)t_lo * BN;
       kend = min((int64_t)t_hi * BN, (int64_t)p.n_keys);
       has_state = has_state && split == 0;
@@ -744,66 +752,59 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   init_acc();
   if (Tp > 0) pipeline(std::integral_constant<bool, FIRST>{});
 
+  // ---- epilogue: normalise, stage bf16 rows in LDS (per wave), write
+  // coalesced.  A split pass writes its rows, normalised by its own
+  // denominator, to its partial-result slot (row stride D), and beside them
+  // per row {denominator, reference}; the merge weighs the slots.
+  __syncthreads();
+  unsigned char* stage = wave == 0 ? kb0 : wave == 1 ? kb1 : wave == 2 ? vb0 : vb1;
+  bf16_t* obase;
+  int64_t ostride;
+  float* plm = nullptr;
   if constexpr (PARTIAL) {
-    // ---- partial results: unnormalised numerator rows, denominator, reference
     const int64_t pidx = ((int64_t)bh * p.tiles_per_chunk + tile) * p.n_splits + split;
     const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
-    float* po = p.part + pidx * BM * D;
-    float* plm = p.part + n_part * BM * D + pidx * BM * 2;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float ltot = half_sum(lsum[qb]);
-      const int row = wave * 32 * QB + qb * 32 + l32;
-      if (row < nrows) {
-#pragma unroll
-        for (int nb = 0; nb < DB; ++nb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 v4 = {o[qb][nb][4 * rr], o[qb][nb][4 * rr + 1], o[qb][nb][4 * rr + 2], o[qb][nb][4 * rr + 3]};
-            *reinterpret_cast<f32x4*>(po + (int64_t)row * D + nb * 32 + 8 * rr + 4 * hh) = v4;
-          }
-        if (hh == 0) {
-          plm[row * 2] = ltot;
-          plm[row * 2 + 1] = mrun[qb];
-        }
-      }
-    }
+    obase = reinterpret_cast<bf16_t*>(p.part) + pidx * BM * D;
+    ostride = D;
+    plm = reinterpret_cast<float*>(reinterpret_cast<bf16_t*>(p.part) + n_part * BM * D) + pidx * BM * 2;
   } else {
-    // ---- epilogue: normalise, stage bf16 rows in LDS (per wave), write coalesced
-    __syncthreads();
-    unsigned char* stage = wave == 0 ? kb0 : wave == 1 ? kb1 : wave == 2 ? vb0 : vb1;
+    obase = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
+    ostride = p.q_st;
+  }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float ltot = half_sum(lsum[qb]);
-      // (a pruned pass can leave a row with no weight at all: output 0)
-      const float inv = SPARSE ? (ltot > 0.f ? 1.0f / ltot : 0.f) : 1.0f / ltot;
-      const int r = qb * 32 + l32;  // row within the wave's 64
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = half_sum(lsum[qb]);
+    // (a pruned pass can leave a row with no weight at all: output 0)
+    const float inv = SPARSE || PARTIAL ? (ltot > 0.f ? 1.0f / ltot : 0.f) : 1.0f / ltot;
+    const int r = qb * 32 + l32;  // row within the wave's 64
 #pragma unroll
-      for (int nb = 0; nb < DB; ++nb)
+    for (int nb = 0; nb < DB; ++nb)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int col = nb * 32 + 8 * rr + 4 * hh;
-          const int g = col >> 3;
-          u32x2 pr = {pack_bf16(o[qb][nb][4 * rr] * inv, o[qb][nb][4 * rr + 1] * inv),
-                      pack_bf16(o[qb][nb][4 * rr + 2] * inv, o[qb][nb][4 * rr + 3] * inv)};
-          *reinterpret_cast<u32x2*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16) + (col & 7) * 2) = pr;
-        }
-      const int myrow = wave * 32 * QB + r;
-      if (p.lse != nullptr && hh == 0 && myrow < nrows) {
+      for (int rr = 0; rr < 4; ++rr) {
+        const int col = nb * 32 + 8 * rr + 4 * hh;
+        const int g = col >> 3;
+        u32x2 pr = {pack_bf16(o[qb][nb][4 * rr] * inv, o[qb][nb][4 * rr + 1] * inv),
+                    pack_bf16(o[qb][nb][4 * rr + 2] * inv, o[qb][nb][4 * rr + 3] * inv)};
+        *reinterpret_cast<u32x2*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16) + (col & 7) * 2) = pr;
+      }
+    const int myrow = wave * 32 * QB + r;
+    if (hh == 0 && myrow < nrows) {
+      if constexpr (PARTIAL) {
+        plm[myrow * 2] = ltot;
+        plm[myrow * 2 + 1] = mrun[qb];
+      } else if (p.lse != nullptr) {
         const int64_t L = (int64_t)p.n_qchunks * p.C;
         p.lse[(int64_t)bh * L + qtok0 + myrow] = (mrun[qb] + __log2f(ltot)) * kLn2;
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging writes are complete
-    __builtin_amdgcn_wave_barrier();
-    bf16_t* obase = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + qtok0 * p.q_st;
-    for (int idx = lane; idx < 32 * QB * GR; idx += 64) {
-      const int r = idx / GR, g = idx % GR;
-      const int row = wave * 32 * QB + r;
-      if (row < nrows)
-        st16(obase + (int64_t)row * p.q_st + g * 8,
-             *reinterpret_cast<const u32x4*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16)));
-    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging writes are complete
+  __builtin_amdgcn_wave_barrier();
+  for (int idx = lane; idx < 32 * QB * GR; idx += 64) {
+    const int r = idx / GR, g = idx % GR;
+    const int row = wave * 32 * QB + r;
+    if (row < nrows)
+      st16(obase + (int64_t)row * ostride + g * 8, *reinterpret_cast<const u32x4*>(stage + r * D * 2 + ((g ^ ksw<D>(r)) * 16)));
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mio[qb] = mrun[qb];
@@ -1185,24 +1186,29 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   const float* o2 = reinterpret_cast<const float*>(q2_vb0);
   const float* o3 = reinterpret_cast<const float*>(q2_vb1);
   if (PARTIAL && q < nr) {
-    // split layout: numerator rows at reference M, then {denominator, M};
-    // the tail is the chunk's last tile, rows 0 .. nr-1 of it
+    // split layout: bf16 rows normalised by the split's own denominator,
+    // then {denominator, M}; the tail is the chunk's last tile, rows 0 ..
+    // nr-1 of it
     constexpr int BM = Q2_NW * 32 * Q2_QB;
     const int64_t pidx = ((int64_t)bh * p.tiles_per_chunk + p.tiles_per_chunk - 1) * p.n_splits + split;
     const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
-    float* po = p.part + (pidx * BM + q) * BD + f0;
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    uint32_t pk[8];
 #pragma unroll
-    for (int f = 0; f < 16; f += 4) {
-      f32x4 v4;
+    for (int f = 0; f < 16; f += 2) {
+      float v2[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 2; ++e) {
         const int idx = (f0 + f + e) * 32 + q;
-        v4[e] = sc[0] * o0[idx] + sc[1] * o1[idx] + sc[2] * o2[idx] + sc[3] * o3[idx];
+        v2[e] = (sc[0] * o0[idx] + sc[1] * o1[idx] + sc[2] * o2[idx] + sc[3] * o3[idx]) * inv;
       }
-      *reinterpret_cast<f32x4*>(po + f) = v4;
+      pk[f >> 1] = pack_bf16(v2[0], v2[1]);
     }
+    bf16_t* po = reinterpret_cast<bf16_t*>(p.part) + (pidx * BM + q) * BD + f0;
+    st16(po, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    st16(po + 8, u32x4{pk[4], pk[5], pk[6], pk[7]});
     if (f0 == 0) {
-      float* plm = p.part + n_part * BM * BD + (pidx * BM + q) * 2;
+      float* plm = reinterpret_cast<float*>(reinterpret_cast<bf16_t*>(p.part) + n_part * BM * BD) + (pidx * BM + q) * 2;
       plm[0] = den;
       plm[1] = M;
     }
@@ -1289,9 +1295,9 @@ void fwd_bf16_qb2_kernel(const FwdParams p, const ChunkStateParams fold) {
   if (__syncthreads_or(dirty)) tile_second_pass<D, NW, PARTIAL, VIS>(p, m[0], m[1]);
 }
 
-// Merge of a split pass: per query row, the partial numerators and
-// denominators are brought to the largest reference and summed in split
-// order; one thread per 4 output columns.
+// Merge of a split pass: per query row, the splits' normalised rows are
+// weighted by their denominators brought to the largest reference and summed
+// in split order; one thread per 8 output columns.
 // Workgroups from fwd_blocks on run the state merge sc instead (the fold of a
 // streaming step, merged in the same launch).
 template <int D>
@@ -1303,30 +1309,39 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p, con
     return;
   }
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.H * p.C * (D / 4);
+  const int64_t total = (int64_t)p.B * p.H * p.C * (D / 8);
   if (idx >= total) return;
-  const int col = (int)(idx % (D / 4)) * 4;
-  const int64_t r = idx / (D / 4);
+  const int col = (int)(idx % (D / 8)) * 8;
+  const int64_t r = idx / (D / 8);
   const int row = (int)(r % p.C);
   const int bh = (int)(r / p.C);
   const int b = bh / p.H, h = bh % p.H;
   const int tile = row / BM, trow = row % BM;
   const int64_t n_part = (int64_t)p.B * p.H * p.tiles_per_chunk * p.n_splits;
   const int64_t pidx0 = ((int64_t)bh * p.tiles_per_chunk + tile) * p.n_splits;
-  const float* plm = p.part + n_part * BM * D;
+  const bf16_t* pn = reinterpret_cast<const bf16_t*>(p.part);
+  const float* plm = reinterpret_cast<const float*>(pn + n_part * BM * D);
   float mmax = -INFINITY;
   for (int sp = 0; sp < p.n_splits; ++sp) mmax = fmaxf(mmax, plm[((pidx0 + sp) * BM + trow) * 2 + 1]);
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  // split sp holds its rows normalised by its denominator l_sp at reference
+  // m_sp: its weight is l_sp 2^(m_sp - mmax)
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int sp = 0; sp < p.n_splits; ++sp) {
     const float* lm = plm + ((pidx0 + sp) * BM + trow) * 2;
-    const float sc = lm[1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lm[1] - mmax);
-    den = fmaf(lm[0], sc, den);
-    num += sc * *reinterpret_cast<const f32x4*>(p.part + ((pidx0 + sp) * BM + trow) * D + col);
+    const float wgt = lm[1] == -INFINITY ? 0.f : lm[0] * __builtin_amdgcn_exp2f(lm[1] - mmax);
+    den += wgt;
+    const u32x4 x = ld16(pn + ((pidx0 + sp) * BM + trow) * D + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      num[2 * i] = fmaf(wgt, bf16_lo(x[i]), num[2 * i]);
+      num[2 * i + 1] = fmaf(wgt, bf16_hi(x[i]), num[2 * i + 1]);
+    }
   }
   const float inv = 1.0f / den;
   bf16_t* dst = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + (int64_t)row * p.q_st + col;
-  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv)};
+  st16(dst, u32x4{pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv),
+                  pack_bf16(num[4] * inv, num[5] * inv), pack_bf16(num[6] * inv, num[7] * inv)});
   if (p.lse != nullptr && col == 0) p.lse[(int64_t)bh * p.C + row] = (mmax + __log2f(den)) * kLn2;
 }
 
@@ -1376,11 +1391,12 @@ hipError_t launch_fwd_bf16_qb2_fold(FwdParams& p, const ChunkStateParams& fold, 
 size_t fwd_split_bytes(int B, int H, int C, int d, int n_splits) {
   const int64_t tiles = (C + kQb2RowsPerTile - 1) / kQb2RowsPerTile;
   const int64_t n_part = (int64_t)B * H * tiles * n_splits;
-  return (size_t)(n_part * kQb2RowsPerTile * (d + 2) * sizeof(float));
+  // bf16 rows, then {denominator, reference} in float32 per row
+  return (size_t)(n_part * kQb2RowsPerTile * (2 * (int64_t)d + 2 * (int64_t)sizeof(float)));
 }
 
 hipError_t launch_fwd_state_combine(const FwdParams& p, const StateCombineParams& sc, hipStream_t s) {
-  const int64_t total = (int64_t)p.B * p.H * p.C * (128 / 4);
+  const int64_t total = (int64_t)p.B * p.H * p.C * (128 / 8);
   const int64_t fwd_blocks = (total + 255) / 256;
   const int64_t state_units = sc.G > 0 ? (int64_t)sc.BH * ((int64_t)sc.d * sc.d + sc.d) / 4 : 0;
   const int64_t blocks = fwd_blocks + (state_units + 255) / 256;

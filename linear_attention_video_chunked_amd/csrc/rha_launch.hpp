@@ -34,10 +34,13 @@ struct FwdParams {
   float scale_log2;   // log2(e) / sqrt(d)
   // Split of the key range (stream mode, head_dim 128 bf16 only): with
   // n_splits > 1 every query tile is processed by n_splits workgroups, each
-  // over its share of the key tiles (the first one also takes the state), and
-  // the unnormalised partial results go to `part` instead of out:
-  //   part[(pidx * BM + row) * d + col]            numerator (float32)
-  //   part[n_part * BM * d + (pidx * BM + row) * 2] {denominator, reference}
+  // over its share of the key tiles (the first one also takes the state, and
+  // so a little less of them), and the partial results go to `part` instead
+  // of out:
+  //   ((bf16*)part)[(pidx * BM + row) * d + col]      row normalised by its
+  //                                                 own denominator (bf16)
+  //   then float32 {denominator, reference} at index (pidx * BM + row) * 2
+  //   from byte n_part * BM * d * 2 on
   // with pidx = (bh * tiles_per_chunk + tile) * n_splits + split and n_part the
   // number of pidx values.  launch_fwd_combine merges them into out and lse.
   int n_splits;
