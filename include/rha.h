@@ -235,25 +235,31 @@ typedef struct {
  * Hybrid Forcing explainer section 1 (a sliding-window KV cache of recent
  * frames) and section 2.A (frames evicted from the window are folded online
  * into the linear state; the local window can then shrink, e.g. from 21 to 9
- * frames).  With t = cursor->t and window w >= 1:
- *   1. the new chunk's k, v are copied into cache slot t % w;
+ * frames).  With t = cursor->t, window w >= 1 and a = p->anchor_chunks >= 0
+ * anchor (attention-sink) chunks -- the explainer's section 1 describes
+ * streaming generators that keep the first frames in attention for good:
+ *   1. the new chunk's k, v are copied into cache slot t % w, and for t < a
+ *      also into anchor slot w + t, which it keeps;
  *   2. the new chunk's queries attend, with exact softmax, to the cached
- *      chunks max(0, t-w+1) .. t (all in the cache now) plus the state S, z
- *      (chunks 0 .. t-w), with the shared normaliser;
+ *      chunks max(0, t-w+1) .. t and the anchor chunks 0 .. a-1 that have
+ *      left the window, plus the state S, z (chunks a .. t-w), with the shared
+ *      normaliser (rha_hybrid_fwd's anchored definition, chunk t);
  *   3. if commit != 0 and t >= w-1: chunk t-w+1 (slot (t+1) % w) leaves the
- *      window, so phi(K)^T V and sum phi(k) of that slot are added into S, z;
- *      then cursor->t is incremented.
+ *      window; unless it is an anchor (t-w+1 < a), phi(K)^T V and sum phi(k)
+ *      of that slot are added into S, z; then cursor->t is incremented.
  * With commit == 0 nothing but the cache slot of chunk t changes, so the same
  * chunk can be re-run (e.g. once per denoising step) before committing it.
  * Outputs equal those of rha_hybrid_fwd over the concatenated sequence up to
  * float rounding (the key window is visited in another order).  Without a
  * workspace, S, z after each commit equal rha_state_scan's entry for chunk
  * t+1 bitwise; with one, up to float rounding (the fold sums token groups).
+ * p->anchor_chunks applies to the stream from its first chunk on (a is part
+ * of the stream's configuration, like w).
  * Either way a step is deterministic.
  *
  *   p->n_chunks is ignored; p's strides describe q_new, k_new, v_new, out
  *   q_new, k_new, v_new : [B, H, C, d] (read)
- *   k_cache, v_cache    : [B, H, w, C, d] contiguous, dtype p->dtype (read/written)
+ *   k_cache, v_cache    : [B, H, w + a, C, d] contiguous, dtype p->dtype (read/written)
  *   S : [B, H, d, d] float32, z : [B, H, d] float32 (read; written on commit)
  *   out : [B, H, C, d] (written);  lse : NULL or [B, H, C] float32
  *   cursor : host memory, read and (on commit) updated at enqueue time

@@ -302,22 +302,25 @@ def hybrid_fwd_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torc
 
 
 class StreamState:
-    """Caller-owned streaming state: KV cache ring of w chunks, S, z, cursor,
-    and the step's scratch workspace (rha_stream_workspace_size bytes; none if
-    split=False or the library would not split this problem)."""
+    """Caller-owned streaming state: KV cache of w window slots (a ring) and
+    `anchors` anchor slots, S, z, cursor, and the step's scratch workspace
+    (rha_stream_workspace_size bytes; none if split=False or the library would
+    not split this problem)."""
 
     def __init__(self, B: int, H: int, d: int, C: int, w: int, dtype=torch.bfloat16, device="cuda",
-                 split: bool = True):
-        self.B, self.H, self.d, self.C, self.w = B, H, d, C, w
-        self.k_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
-        self.v_cache = torch.zeros((B, H, w, C, d), dtype=dtype, device=device)
+                 split: bool = True, anchors: int = 0):
+        if anchors < 0:
+            raise ValueError("anchors must be >= 0")
+        self.B, self.H, self.d, self.C, self.w, self.anchors = B, H, d, C, w, anchors
+        self.k_cache = torch.zeros((B, H, w + anchors, C, d), dtype=dtype, device=device)
+        self.v_cache = torch.zeros((B, H, w + anchors, C, d), dtype=dtype, device=device)
         self.S = torch.zeros((B, H, d, d), dtype=torch.float32, device=device)
         self.z = torch.zeros((B, H, d), dtype=torch.float32, device=device)
         self.cursor = Cursor(0)
         self.workspace = None
         if split:
             prob = Problem(batch=B, heads=H, head_dim=d, chunk_len=C, n_chunks=1, window=w,
-                           dtype=RHA_BF16 if dtype == torch.bfloat16 else RHA_F32, anchor_chunks=0,
+                           dtype=RHA_BF16 if dtype == torch.bfloat16 else RHA_F32, anchor_chunks=anchors,
                            stride_b=H * C * d, stride_h=C * d, stride_t=d)
             nbytes = int(lib().rha_stream_workspace_size(ctypes.byref(prob)))
             if nbytes > 0:
@@ -329,7 +332,7 @@ class StreamState:
 
     def clone(self) -> "StreamState":
         n = StreamState.__new__(StreamState)
-        n.B, n.H, n.d, n.C, n.w = self.B, self.H, self.d, self.C, self.w
+        n.B, n.H, n.d, n.C, n.w, n.anchors = self.B, self.H, self.d, self.C, self.w, self.anchors
         n.k_cache, n.v_cache = self.k_cache.clone(), self.v_cache.clone()
         n.S, n.z = self.S.clone(), self.z.clone()
         n.cursor = Cursor(self.cursor.t)
@@ -357,7 +360,7 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
         raise ValueError(f"stream workspace is on {st.workspace.device}, the chunk on {q_new.device}")
     if lse is not None:
         _check_f32(q_new, lse, "lse", (B, H, C))
-    prob = _problem(q_new, C, st.w, 1)
+    prob = _problem(q_new, C, st.w, 1, st.anchors)
     _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
                                  _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
                                  ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _ptr(st.workspace),
@@ -390,7 +393,7 @@ def stream_step_noalloc(st: StreamState, q_new: torch.Tensor, k_new: torch.Tenso
             raise ValueError(f"stream state {name} is on {t.device}, the chunk on {q_new.device}")
     if lse is not None:
         _check_f32(q_new, lse, "lse", (B, H, C))
-    prob = _problem(q_new, C, st.w, 1)
+    prob = _problem(q_new, C, st.w, 1, st.anchors)
     _check(lib().rha_stream_step_noalloc(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new),
                                          _ptr(st.k_cache), _ptr(st.v_cache), _ptr(st.S), _ptr(st.z),
                                          ctypes.byref(st.cursor), ctypes.c_int32(1 if commit else 0), _ptr(out),

@@ -54,8 +54,7 @@ rha_status check_problem(const rha_problem* p, bool stream) {
   if (p->window < 0) return fail(RHA_ERR_INVALID_ARG, "window %d must be >= 0", p->window);
   if (stream && p->window < 1) return fail(RHA_ERR_INVALID_ARG, "streaming needs window >= 1 (got %d)", p->window);
   if (p->anchor_chunks < 0) return fail(RHA_ERR_INVALID_ARG, "anchor_chunks %d must be >= 0", p->anchor_chunks);
-  if (p->anchor_chunks > 0) {
-    if (stream) return fail(RHA_ERR_UNSUPPORTED, "streaming steps take no anchor chunks");
+  if (p->anchor_chunks > 0 && !stream) {
     if (p->dtype != RHA_BF16 || p->head_dim != 128)
       return fail(RHA_ERR_UNSUPPORTED, "anchor chunks need dtype RHA_BF16 and head_dim 128");
     // the anchor and window tiles of a query chunk are listed in LDS
@@ -76,7 +75,8 @@ rha_status check_problem(const rha_problem* p, bool stream) {
   const int64_t nc = stream ? 1 : p->n_chunks;
   const int64_t L = nc * (int64_t)p->chunk_len;
   const int64_t bhn = (int64_t)p->batch * p->heads * nc;
-  const int64_t win_keys = (int64_t)(p->window < 1 ? 1 : p->window) * p->chunk_len;
+  // (streaming: the window slots and the anchor slots of the cache)
+  const int64_t win_keys = ((int64_t)(p->window < 1 ? 1 : p->window) + (stream ? p->anchor_chunks : 0)) * p->chunk_len;
   if (L > INT32_MAX / 2 || bhn * p->chunk_len > INT32_MAX || (int64_t)p->batch * p->heads > INT32_MAX / 2 ||
       (stream && win_keys > INT32_MAX / 2))
     return fail(RHA_ERR_INVALID_ARG, "problem too large for 32-bit tile indexing");
@@ -445,7 +445,7 @@ rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void
 size_t rha_stream_workspace_size(const rha_problem* p) {
   if (p == nullptr || check_problem(p, true) != RHA_OK || empty(p, true)) return 0;
   // the split window's partial results, then the split fold's partial states
-  const int splits = stream_splits(p, (int64_t)p->window * p->chunk_len);
+  const int splits = stream_splits(p, ((int64_t)p->window + p->anchor_chunks) * p->chunk_len);
   int glen = 0;
   const int groups = fold_groups(p, &glen);
   size_t bytes = splits < 2 ? 0 : align256(rha::fwd_split_bytes(p->batch, p->heads, p->chunk_len, p->head_dim, splits));
@@ -478,8 +478,10 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t t = cursor->t;
   const int w = p->window, C = p->chunk_len, d = p->head_dim;
+  const int a = p->anchor_chunks;  // anchor (sink) chunks: cache slots w .. w+a-1
   const int slot = (int)(t % w);
   const int64_t BH = (int64_t)p->batch * p->heads;
+  const int64_t slots = (int64_t)w + a;  // cache slots per head
   hipError_t e;
 
   // The plan.  The window's key range is split over several workgroups per
@@ -487,9 +489,15 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   // the fold of a committed chunk is split into token groups (partial states,
   // then added in order).  Workspace: split-window partials first, then the
   // fold's partial states, each 256-byte aligned.
+  // Keys: the window slots in use, then the anchor slots of the anchors that
+  // have left the window (chunk j < a sits in slot w + j) -- one contiguous
+  // row range of the cache, since anchors leave only once the window is full.
+  // The chunk leaving the window at a commit is folded unless it is an anchor.
   const int64_t in_window = t + 1 < w ? t + 1 : w;
-  const int n_keys = (int)(in_window * C);
-  const bool fold = commit && t >= w - 1;
+  const int64_t left = t - w + 1;  // chunks 0 .. left-1 have left the window
+  const int64_t n_anc = left > 0 ? (left < a ? left : a) : 0;
+  const int n_keys = (int)((in_window + n_anc) * C);
+  const bool fold = commit && left >= 0 && left >= a;
   const int splits = workspace != nullptr ? stream_splits(p, n_keys) : 1;
   const size_t fwd_part = splits > 1 ? align256(rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) : 0;
   const bool split_fwd = splits > 1 && workspace_bytes >= fwd_part;
@@ -515,7 +523,7 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   cp.H = p->heads;
   cp.C = C;
   cp.d = d;
-  cp.w = w;
+  cp.w = (int)slots;
   cp.slot = slot;
   cp.elem_bytes = elem_bytes(p);
   cp.src = k_new;
@@ -532,8 +540,8 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
       const int64_t slot_off = (int64_t)((t + 1) % w) * C * d * elem_bytes(p);
       c.k = static_cast<const char*>(k_cache) + slot_off;
       c.v = static_cast<const char*>(v_cache) + slot_off;
-      c.kv_sb = (int64_t)p->heads * w * C * d;
-      c.kv_sh = (int64_t)w * C * d;
+      c.kv_sb = (int64_t)p->heads * slots * C * d;
+      c.kv_sh = slots * C * d;
       c.kv_st = d;
     } else {
       c.k = k_new;
@@ -566,6 +574,12 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
     e = rha::launch_copy_chunk(cp, s);
     if (e != hipSuccess) return hip_fail(e, "cache copy launch");
   }
+  if (t < a) {  // an anchor chunk: also into its own slot, which it keeps for good
+    rha::CopyParams ca = cp;
+    ca.slot = (int)(w + t);
+    e = rha::launch_copy_chunk(ca, s);
+    if (e != hipSuccess) return hip_fail(e, "anchor copy launch");
+  }
 
   // 2. attention of the new chunk: cached window (chunks max(0,t-w+1)..t) + state
   rha::FwdParams f{};
@@ -579,8 +593,8 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.q_sb = p->stride_b;
   f.q_sh = p->stride_h;
   f.q_st = p->stride_t;
-  f.kv_sb = (int64_t)p->heads * w * C * d;
-  f.kv_sh = (int64_t)w * C * d;
+  f.kv_sb = (int64_t)p->heads * slots * C * d;
+  f.kv_sh = slots * C * d;
   f.kv_st = d;
   f.B = p->batch;
   f.H = p->heads;
@@ -589,7 +603,7 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.n_qchunks = 1;
   f.stream_mode = 1;
   f.n_keys = n_keys;
-  f.has_state = t >= w ? 1 : 0;
+  f.has_state = left > a ? 1 : 0;  // chunks a .. t-w are in the state
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   f.n_splits = split_fwd ? splits : 1;
   f.part = split_fwd ? static_cast<float*>(workspace) : nullptr;

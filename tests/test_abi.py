@@ -225,14 +225,17 @@ def test_bidir_checks(L):
 
 
 def test_anchor_checks(L):
-    # anchor chunks: bf16 with head_dim 128; not for streaming, pruned or bidirectional calls
+    # anchor chunks: bf16 with head_dim 128 for the whole-sequence calls; not for
+    # pruned or bidirectional calls (the streaming step keeps them in cache
+    # slots of their own, any dtype: only a negative count is refused there)
     assert _scan(L, _prob(anchor_chunks=1, dtype=_rha.RHA_F32, stride_t=128)) == 2
     assert _fwd(L, _prob(anchor_chunks=2, head_dim=64, stride_t=64)) == 2
     assert "anchor" in L.rha_last_error().decode()
     assert _sparse(L, _prob(anchor_chunks=1)) == 2
     assert L.rha_state_scan_bidir(ctypes.byref(_prob(anchor_chunks=1)), P, P, P, P, P, P, None) == 2
     cur = _rha.Cursor(0)
-    assert _step(L, _prob(anchor_chunks=1, window=2), ctypes.byref(cur)) == 2
+    assert _step(L, _prob(anchor_chunks=-1, window=2), ctypes.byref(cur)) == 1
+    assert "anchor_chunks" in L.rha_last_error().decode()
     assert cur.t == 0
     # anchor and window tiles listed per query chunk: at most 2048 tiles of 64 keys
     big = _prob(anchor_chunks=20, n_chunks=40, window=20, chunk_len=4000, stride_b=0, stride_h=0)

@@ -180,3 +180,62 @@ def test_stream_workload_full_size(qscale):
             Sf, zf = oracle.state_after(k64[b, h], v64[b, h], wl.C, wl.w, wl.N)
             assert rel_l2(to64(st.S[b, h]), Sf) <= TOL["bf16"]
             assert rel_l2(to64(st.z[b, h]), zf) <= TOL["bf16"]
+
+
+# ---- anchor (attention-sink) chunks: the first `a` chunks stay in every
+# later chunk's softmax window and never enter the state (the anchored
+# definition over the concatenated stream, oracle.hybrid_anchor)
+ANCHORED = {
+    "bf16_d128_C100_w3_a2": (Workload("sa1", 320, B=1, H=2, d=128, C=100, N=10, w=3, dtype="bf16"), 2),
+    # short tails (C % 256 = 24) and peaked scores
+    "bf16_d128_C280_w3_a1_q4": (Workload("sa2", 321, B=1, H=2, d=128, C=280, N=8, w=3, dtype="bf16", qscale=4.0), 1),
+    # more anchors than window chunks, the split path
+    "bf16_d128_C256_w2_a3": (Workload("sa3", 322, B=1, H=2, d=128, C=256, N=9, w=2, dtype="bf16"), 3),
+    # w = 1 (the chunk leaving the window is the new chunk itself)
+    "bf16_d128_C300_w1_a2": (Workload("sa4", 323, B=1, H=1, d=128, C=300, N=6, w=1, dtype="bf16"), 2),
+    "f32_d64_C48_w2_a2": (Workload("sa5", 324, B=1, H=2, d=64, C=48, N=8, w=2, dtype="f32"), 2),
+}
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("name", sorted(ANCHORED))
+def test_stream_anchors_match_oracle(name, split):
+    wl, a = ANCHORED[name]
+    q, k, v = gen_qkv(wl)
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, anchors=a,
+                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, device=DEV, split=split)
+    assert tuple(st.k_cache.shape) == (wl.B, wl.H, wl.w + a, wl.C, wl.d)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    ref, den = oracle.hybrid_anchor_batched(q64, k64, v64, wl.C, wl.w, a, return_den=True)
+    tol = TOL[wl.dtype]
+    for t in range(wl.N):
+        lse = torch.empty((wl.B, wl.H, wl.C), dtype=torch.float32, device=DEV)
+        o = rha.stream_step(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C), lse=lse)
+        torch.cuda.synchronize()
+        sl = slice(t * wl.C, (t + 1) * wl.C)
+        e = rel_l2(to64(o), ref[:, :, sl])
+        assert e <= tol, f"step {t}: rel-L2 {e:.3e}"
+        assert np.abs(to64(lse) - np.log(den[:, :, sl])).max() <= (1e-2 if wl.dtype == "bf16" else 1e-4), f"step {t}"
+    # the state after N commits: chunks a .. N-w (the anchors never folded)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            U, u = oracle.chunk_states(k64[b, h], v64[b, h], wl.C)
+            lo, hi = a, wl.N - wl.w
+            Sref = U[lo:hi + 1].sum(axis=0) if hi >= lo else np.zeros(U.shape[1:])
+            zref = u[lo:hi + 1].sum(axis=0) if hi >= lo else np.zeros(u.shape[1:])
+            assert rel_l2(to64(st.S[b, h]), Sref) <= tol
+            assert rel_l2(to64(st.z[b, h]), zref) <= tol
+    assert st.t == wl.N
+
+
+def test_stream_anchor_slots_keep_the_first_chunks():
+    # the anchor slots hold chunks 0 .. a-1 bitwise after the window has moved on
+    wl, a = ANCHORED["bf16_d128_C100_w3_a2"]
+    q, k, v = gen_qkv(wl)
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, anchors=a, device=DEV)
+    for t in range(wl.N):
+        rha.stream_step(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C))
+    torch.cuda.synchronize()
+    for j in range(a):
+        assert torch.equal(st.k_cache[:, :, wl.w + j], chunk(k, j, wl.C))
+        assert torch.equal(st.v_cache[:, :, wl.w + j], chunk(v, j, wl.C))
