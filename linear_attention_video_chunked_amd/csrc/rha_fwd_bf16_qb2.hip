@@ -46,14 +46,6 @@ namespace {
 
 using namespace fwd;
 
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 // Empty asm that claims to modify x: the value is produced before this point
 // and cannot be moved past it (keeps hand-ordered work in its slot).
 template <typename T> __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
@@ -1254,8 +1246,7 @@ __device__ __forceinline__ void fold_unit(const ChunkStateParams& fold, int u) {
                     state::StateCfg<D>::VBYTES <= Q2_TILE &&
                     sizeof(float) * (state::THREADS / (state::ESLICE / 8)) * state::ESLICE <= Q2_TILE,
                 "the fold unit's buffers fit the tile buffers");
-  state::chunk_state_unit<D, false>(fold, u, q2_kb0, q2_kb0 + state::StateCfg<D>::KBYTES, q2_vb0, q2_vb1,
-                                    reinterpret_cast<float(*)[state::ESLICE]>(q2_kb1));
+  state::chunk_state_unit<D, false>(fold, u, q2_kb0, q2_vb0, q2_vb1, reinterpret_cast<float*>(q2_kb1));
 }
 
 template <int D, int NW, bool PARTIAL, int VIS>

@@ -36,7 +36,22 @@ __global__ __launch_bounds__(THREADS) void chunk_state_bf16_kernel(const ChunkSt
     copy_unit(p.copy, pair / BH, pair % BH, (cb - pair * p.copy_blocks_per_bh) * THREADS + (int)threadIdx.x);
     return;
   }
-  chunk_state_unit<D, SCALED>(p, fwd::xcd_remap(blockIdx.x, total), kt_s[0], kt_s[1], vt_s[0], vt_s[1], zred);
+  chunk_state_unit<D, SCALED>(p, fwd::xcd_remap(blockIdx.x, total), &kt_s[0][0], vt_s[0], vt_s[1], &zred[0][0]);
+}
+
+// Head dimension 128 without a cache copy: one workgroup per (head, chunk)
+// with a thread group per slice of e, so each chunk's V is loaded and staged
+// once (the same bits as the one-slice workgroups).
+template <bool SCALED>
+__global__ __launch_bounds__(2 * THREADS) void chunk_state_bf16_both_kernel(const ChunkStateParams p) {
+  using Cfg = StateCfg<128>;
+  static_assert(Cfg::ES == 2, "two slices of 64 rows");
+  __shared__ __attribute__((aligned(1024))) unsigned char kt_s[2][2][Cfg::KBYTES];  // per slice, 2 buffers
+  __shared__ __attribute__((aligned(1024))) unsigned char vt_s[2][Cfg::VBYTES];
+  __shared__ float zred[2][THREADS / (ESLICE / 8)][ESLICE];
+  const int total = p.B * p.H * p.n_chunks;
+  chunk_state_unit<128, SCALED, 2, 4>(p, fwd::xcd_remap(blockIdx.x, total), &kt_s[0][0][0], vt_s[0], vt_s[1],
+                                      &zred[0][0][0]);
 }
 
 }  // namespace
@@ -48,7 +63,9 @@ hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t
   const bool scaled = p.vscale != nullptr;
   const dim3 g128((unsigned)(heads_chunks * StateCfg<128>::ES + copy_blocks));
   const dim3 g64((unsigned)(heads_chunks * StateCfg<64>::ES + copy_blocks));
-  if (d == 128 && scaled)
+  if (d == 128 && copy_blocks == 0 && !scaled) {
+    hipLaunchKernelGGL((chunk_state_bf16_both_kernel<false>), dim3((unsigned)heads_chunks), dim3(2 * THREADS), 0, s, p);
+  } else if (d == 128 && scaled)
     hipLaunchKernelGGL((chunk_state_bf16_kernel<128, true>), g128, dim3(THREADS), 0, s, p);
   else if (d == 128)
     hipLaunchKernelGGL((chunk_state_bf16_kernel<128, false>), g128, dim3(THREADS), 0, s, p);

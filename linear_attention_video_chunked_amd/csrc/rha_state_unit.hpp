@@ -9,7 +9,8 @@
 // through LDS in tiles of 64, stored as loaded (token-major rows, 16-byte
 // granules XOR-swizzled); both operands are contracted over tokens, so both
 // are read with the LDS transpose read ds_read_b64_tr_b16, which hands each
-// lane 8 tokens of one feature column.  Four tiles are in flight from HBM while
+// lane 8 tokens of one feature column.  R tiles (four; six in the two-slice
+// workgroups) are in flight from HBM while
 // one is multiplied (the unit is bound by HBM, not by the products).  phi is evaluated
 // in float32 and rounded to bf16 for the product; u is summed from the float32
 // phi values in a fixed order.  With `accumulate` the result is added into
@@ -72,35 +73,48 @@ __device__ __forceinline__ bf16x8 read_frag_t(const unsigned char* tile, int ks,
   return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 }
 
-// One workgroup of THREADS threads computes unit `logical` (head, chunk, slice
-// of e; slices of a chunk adjacent) with the given LDS buffers: two phi(K)
-// slice tiles of StateCfg<D>::KBYTES, two V tiles of StateCfg<D>::VBYTES and
-// the reduction rows zred[THREADS / (ESLICE / 8)][ESLICE].
+// One workgroup of SL * THREADS threads computes unit `logical` with the
+// given LDS buffers.  SL = 1: the unit is (head, chunk, slice of e), slices of
+// a chunk adjacent.  SL = StateCfg<D>::ES: the unit is (head, chunk) and the
+// workgroup's thread group g (THREADS threads) takes slice g, every group
+// doing exactly what a one-slice workgroup does (so the results are the same
+// bits) except that V, the same for every slice, is loaded and staged once,
+// by group 0.  Buffers: kt holds SL x 2 phi(K) slice tiles of
+// StateCfg<D>::KBYTES (slice-major), vt0 / vt1 the two V tiles of
+// StateCfg<D>::VBYTES, zred SL blocks of reduction rows
+// [THREADS / (ESLICE / 8)][ESLICE].
 // SCALED: the per-token factors vscale / zweight are applied (a separate
 // instantiation, so the plain one keeps its registers).
-template <int D, bool SCALED>
-__device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int logical, unsigned char* kt0,
-                                                 unsigned char* kt1, unsigned char* vt0, unsigned char* vt1,
-                                                 float (*zred)[ESLICE]) {
+template <int D, bool SCALED, int SL = 1, int R = 4>
+__device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int logical, unsigned char* kt,
+                                                 unsigned char* vt0, unsigned char* vt1, float* zred_all) {
   using Cfg = StateCfg<D>;
-  const int tid = threadIdx.x;
+  static_assert(SL == 1 || SL == Cfg::ES, "one slice or every slice per workgroup");
+  const int tid = threadIdx.x % THREADS;  // thread within the slice's group
+  const int grp = SL == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / THREADS);  // wave-uniform
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  auto kt_s = [&](int buf) __attribute__((always_inline)) { return buf ? kt1 : kt0; };
+  unsigned char* const ktg = kt + (size_t)grp * 2 * Cfg::KBYTES;
+  auto kt_s = [&](int buf) __attribute__((always_inline)) { return ktg + buf * Cfg::KBYTES; };
   auto vt_s = [&](int buf) __attribute__((always_inline)) { return buf ? vt1 : vt0; };
+  float (*zred)[ESLICE] = reinterpret_cast<float (*)[ESLICE]>(zred_all + (size_t)grp * (THREADS / (ESLICE / 8)) * ESLICE);
 
-  const int es = logical % Cfg::ES;
-  const int jc = (logical / Cfg::ES) % p.n_chunks;
-  const int bh = logical / Cfg::ES / p.n_chunks;
+  const int es = SL == 1 ? logical % Cfg::ES : grp;
+  const int jc = (SL == 1 ? logical / Cfg::ES : logical) % p.n_chunks;
+  const int bh = (SL == 1 ? logical / Cfg::ES : logical) / p.n_chunks;
   const int b = bh / p.H, h = bh % p.H;
   const int64_t t0 = (int64_t)(p.chunk0 + jc) * p.C;
   const int len = (int)min((int64_t)p.C, p.tok_end - t0);  // tokens of this chunk
   const bf16_t* kbase = (const bf16_t*)p.k + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st + es * ESLICE;
   const bf16_t* vbase = (const bf16_t*)p.v + b * p.kv_sb + h * p.kv_sh + t0 * p.kv_st;
 
-  const bool vact = tid < Cfg::VUNITS;
+  // V rows per thread: 4 (one-slice workgroups, the first VUNITS threads);
+  // 2 in a two-slice workgroup, where every thread of both groups takes part
+  constexpr int VR = SL == 1 ? 4 : 2;
+  const int vt = SL == 1 ? tid : (int)threadIdx.x;
+  const bool vact = SL == 1 ? tid < Cfg::VUNITS : vt < (BT / VR) * (D / 8);
   const int kfo = tid % (ESLICE / 8), krow0 = tid / (ESLICE / 8);  // phi(K): every thread, KG rows
-  const int vfo = tid % (D / 8), vtq = tid / (D / 8);
+  const int vfo = vt % (D / 8), vtq = vt / (D / 8);
 
   const int eb = wave / (NW * Cfg::NBW / (D / 32));
   const int nb0 = (wave * Cfg::NBW) % (D / 32);
@@ -113,8 +127,8 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
   const int ntiles = (len + BT - 1) / BT;
-  constexpr int R = 4;                // tiles in flight from HBM (register ring)
-  u32x4 kw[R][Cfg::KG], vw[R][4];
+  static_assert(R % 2 == 0, "R tiles in flight from HBM (register ring); LDS buffer = slot parity");
+  u32x4 kw[R][Cfg::KG], vw[R][VR];
 
   // Buffer loads whose descriptors end at the chunk's last token: rows past
   // it (and the lanes without a unit) read zeros, so loads and stores need no
@@ -123,7 +137,7 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, chunk_bytes, fwd::kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, chunk_bytes, fwd::kBufWord3);
   const int kofs0 = (krow0 * (int)p.kv_st + kfo * 8) * 2;
-  const int vofs0 = vact ? (vtq * 4 * (int)p.kv_st + vfo * 8) * 2 : chunk_bytes;
+  const int vofs0 = vact ? (vtq * VR * (int)p.kv_st + vfo * 8) * 2 : chunk_bytes;
   const int row_bytes = (int)p.kv_st * 2;
   auto gload = [&](int j, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
@@ -133,7 +147,7 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
       kw[sl][r] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kofs0 + tile_off + r * Cfg::KROWSTEP * row_bytes, 0, 0));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < VR; ++r) {
       const int vo = vact ? vofs0 + tile_off + r * row_bytes : chunk_bytes;
       vw[sl][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0));
     }
@@ -165,15 +179,15 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
     }
     if (vact) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < VR; ++r) {
         u32x4 x = vw[sl][r];
         if constexpr (SCALED) {
-          const int tok = j * BT + vtq * 4 + r;
+          const int tok = j * BT + vtq * VR + r;
           const float sc = tok < len ? p.vscale[sbase + tok] : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = pack_bf16(bf16_lo(x[i]) * sc, bf16_hi(x[i]) * sc);
         }
-        store_granule<D>(vt_s(buf), vtq * 4 + r, vfo, x);
+        store_granule<D>(vt_s(buf), vtq * VR + r, vfo, x);
       }
     }
   };
@@ -186,18 +200,11 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
     }
   };
   using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  static_assert(R == 4, "the loop below is unrolled for a ring of four");
 
   // tile j lives in register slot j % R and LDS buffer j % 2 (tiles past the
   // chunk load as zeros and store harmlessly: phi is masked by token index,
   // and the buffer they land in is not read again)
-  gload(0, S0{});
-  gload(1, S1{});
-  gload(2, S2{});
-  gload(3, S3{});
+  static_for<0, R>([&](auto s_c) __attribute__((always_inline)) { gload(decltype(s_c)::value, s_c); });
   lstore(0, 0, S0{});
   __syncthreads();
   auto iter = [&](int j, auto slot_c) {  // slot_c = j % R
@@ -209,15 +216,11 @@ __device__ __forceinline__ void chunk_state_unit(const ChunkStateParams& p, int 
     __syncthreads();
   };
   int j = 0;
-  for (; j + R - 1 < ntiles; j += R) {
-    iter(j, S0{});
-    iter(j + 1, S1{});
-    iter(j + 2, S2{});
-    iter(j + 3, S3{});
-  }
-  if (j < ntiles) iter(j, S0{});
-  if (j + 1 < ntiles) iter(j + 1, S1{});
-  if (j + 2 < ntiles) iter(j + 2, S2{});
+  for (; j + R - 1 < ntiles; j += R)
+    static_for<0, R>([&](auto s_c) __attribute__((always_inline)) { iter(j + decltype(s_c)::value, s_c); });
+  static_for<0, R - 1>([&](auto s_c) __attribute__((always_inline)) {
+    if (j + decltype(s_c)::value < ntiles) iter(j + decltype(s_c)::value, s_c);
+  });
 
   // U: acc[i] reg 4r+q <-> e = es*64 + eb*32 + 8r + 4hh + q, n = (nb0+i)*32 + l32
   const int slot1 = jc + p.slot_offset, slot2 = jc + p.slot_offset2;
