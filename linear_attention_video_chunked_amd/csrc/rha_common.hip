@@ -15,9 +15,11 @@ namespace {
 // the slots are walked from the last (the future part of a bidirectional
 // state: slot c sums the contributions stored in slots c .. N-1-w).
 // Each thread owns 4 consecutive floats of one head's S (or z) and walks the
-// slots in groups of 8: all loads of a group are issued before the running
-// sum touches them, so the HBM latency is paid once per group, not per slot.
-__global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
+// slots in groups of 24: all loads of a group are issued before the running
+// sum touches them, so the HBM latency is paid once per group, not per slot
+// (once in all for up to 24 summed slots); 128-thread workgroups spread the
+// few threads over more compute units.
+__global__ __launch_bounds__(128) void prefix_kernel(const PrefixParams p) {
   const int64_t per4 = ((int64_t)p.d * p.d + p.d) / 4;  // float4 units per head (d is a multiple of 4)
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.BH * per4) return;
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void prefix_kernel(const PrefixParams p) {
   const int w = min(p.w, p.N);
   for (int c = 0; c < w; ++c) base[c * stride] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int G = 8;
+  constexpr int G = 24;
   for (int c0 = w; c0 < p.N; c0 += G) {
     f32x4 v[G];
 #pragma unroll
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(64) void state_combine_kernel(const StateCombinePar
 hipError_t launch_prefix(const PrefixParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.BH * ((int64_t)p.d * p.d + p.d) / 4;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefix_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(prefix_kernel, dim3((unsigned)((total + 127) / 128)), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 
