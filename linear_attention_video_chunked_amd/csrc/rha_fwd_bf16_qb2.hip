@@ -267,13 +267,17 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
     }
     __syncthreads();
   }
+  // The listed values are the same for every lane; reading them as wave-uniform
+  // keeps the tile descriptors built from them in scalar registers (a
+  // descriptor the compiler cannot prove uniform becomes a loop over lanes
+  // around every tile load).
   auto act = [&](int t) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE) return q2_act[t];
+    if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(q2_act[t]);
     else return t;
   };
   // first key of visit t
   auto act_key = [&](int t) __attribute__((always_inline)) -> int64_t {
-    if constexpr (ANCH) return q2_act[t];
+    if constexpr (ANCH) return __builtin_amdgcn_readfirstlane(q2_act[t]);
     else return kbeg + (int64_t)act(t) * BN;
   };
 
@@ -448,7 +452,7 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // tile that holds at most 32 keys)
   auto block_valid = [&](int blk) __attribute__((always_inline)) {
     if constexpr (ANCH) {
-      return min(32, q2_actv[blk >> 1] - 32 * (blk & 1));
+      return min(32, __builtin_amdgcn_readfirstlane(q2_actv[blk >> 1]) - 32 * (blk & 1));
     } else {
       const int real = 2 * act(blk >> 1) + (blk & 1);  // block of the window
       return (int)min((int64_t)32, kend - (kbeg + (int64_t)real * 32));
