@@ -84,3 +84,71 @@ def test_backward_wan13b_sampled_rows():
             grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
     for gr in grouped:
         gr.check(TOL["bf16"])
+
+
+# layout cases for the gradients: ragged 130-row chunks (a 2-row tail past one
+# 128-key tile of the key-gradient kernel), with a window and without one
+LAYOUT = {"C130_N4_w2_B2": (2, 2, 130, 4, 2), "C130_N4_w0_B2": (2, 2, 130, 4, 0)}
+
+
+def _layout_wl(name):
+    B, H, C, N, w = LAYOUT[name]
+    return Workload(name, 1600 + sorted(LAYOUT).index(name), B=B, H=H, d=128, C=C, N=N, w=w, dtype="bf16",
+                    qscale=1.0, kscale=0.5)
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT))
+def test_backward_strided_sequence_major_matches_contiguous(name):
+    # q, k, v, out, dout in [B, L, H, d] storage viewed as [B, H, L, d]
+    wl = _layout_wl(name)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 3)
+    ref = _run(wl, q, k, v, dout)
+    oref = oracle.hybrid_backward_batched(to64(q), to64(k), to64(v), wl.C, wl.w, to64(dout))
+    for g, r, nm in zip(ref, oref, ("dq", "dk", "dv")):
+        e = rel_l2(to64(g), r)
+        assert e <= TOL["bf16"], f"{nm}: rel-L2 {e:.3e}"
+    qs, ks, vs, gs = (t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3) for t in (q, k, v, dout))
+    assert qs.stride(2) == wl.H * wl.d
+    S, z = rha.state_scan(ks, vs, wl.C, wl.w)
+    out = torch.empty_like(qs)
+    _, lse = rha.hybrid_fwd(qs, ks, vs, S, z, wl.C, wl.w, out=out, return_lse=True)
+    got = rha.hybrid_bwd(qs, ks, vs, S, z, out, lse, gs, wl.C, wl.w)
+    torch.cuda.synchronize()
+    for g, r, nm in zip(got, ref, ("dq", "dk", "dv")):
+        assert torch.equal(g, r), f"{nm} differs from the contiguous call"
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT))
+def test_backward_guard_bands_through_abi(name):
+    # dq, dk, dv and the workspace inside sentinel-filled buffers, called
+    # through the C ABI directly: nothing outside them changes, and the
+    # gradients equal the binding's call on the same inputs
+    import ctypes
+    from linear_attention_video_chunked_amd import _rha as R
+    wl = _layout_wl(name)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 4)
+    ref = _run(wl, q, k, v, dout)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    S, z = rha.state_scan(kd, vd, wl.C, wl.w)
+    out, lse = rha.hybrid_fwd(qd, kd, vd, S, z, wl.C, wl.w, return_lse=True)
+    n = wl.B * wl.H * wl.L * wl.d
+    pad = 4096  # floats on each side
+    bigs = [torch.full((n + 2 * pad,), 9.0, dtype=torch.float32, device=DEV) for _ in range(3)]
+    views = [b[pad: pad + n] for b in bigs]
+    prob = R._problem(qd, wl.C, wl.w, wl.N)
+    nbytes = int(R.lib().rha_hybrid_bwd_workspace_size(ctypes.byref(prob)))
+    assert nbytes > 0
+    wpad = 4096  # bytes on each side (16-byte aligned)
+    wbig = torch.full((nbytes + 2 * wpad,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = wbig[wpad: wpad + nbytes]
+    R._check(R.lib().rha_hybrid_bwd(ctypes.byref(prob), R._ptr(qd), R._ptr(kd), R._ptr(vd), R._ptr(S), R._ptr(z),
+                                    R._ptr(out), R._ptr(lse), R._ptr(gd), R._ptr(views[0]), R._ptr(views[1]),
+                                    R._ptr(views[2]), R._ptr(ws), nbytes, R._stream(None)))
+    torch.cuda.synchronize()
+    for b, nm in zip(bigs, ("dq", "dk", "dv")):
+        assert (b[:pad] == 9.0).all() and (b[pad + n:] == 9.0).all(), f"{nm}: guard band written"
+    assert (wbig[:wpad] == 0xA5).all() and (wbig[wpad + nbytes:] == 0xA5).all(), "workspace guard band written"
+    for vw, r, nm in zip(views, ref, ("dq", "dk", "dv")):
+        assert torch.equal(vw.view(r.shape), r), f"{nm} differs from the binding's call"
