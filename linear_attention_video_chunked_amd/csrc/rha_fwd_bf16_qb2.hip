@@ -303,10 +303,17 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   }
   const int win_bytes = (int)(kend * p.kv_st * 2);
   typedef __attribute__((address_space(3))) void lds_void;
+  // The descriptor's fields are read as wave-uniform: in the kernel they are
+  // scalar already, and in the out-of-line second pass (whose parameter block
+  // arrives in vector registers) this keeps each tile load a single load
+  // instead of a loop over lanes.
   auto tile_rsrc = [&](const bf16_t* base, int64_t key) __attribute__((always_inline)) {
     const int tile_off = (int)(key * p.kv_st * 2);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)base + tile_off), (short)0,
-                                             max(win_bytes - tile_off, 0), kBufWord3);
+    const uint64_t a = (uint64_t)((const unsigned char*)base + tile_off);
+    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)ua, (short)0,
+                                             __builtin_amdgcn_readfirstlane(max(win_bytes - tile_off, 0)), kBufWord3);
   };
   auto dma_k = [&](unsigned char* dst, int64_t key, int i) __attribute__((always_inline)) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(tile_rsrc(kbase, key), (lds_void*)(dst + (LPW * wave + i) * 1024), 16,
