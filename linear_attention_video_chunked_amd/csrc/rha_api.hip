@@ -332,8 +332,8 @@ rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void*
 size_t rha_hybrid_bwd_workspace_size(const rha_problem* p) {
   if (p == nullptr || check_problem(p, false) != RHA_OK) return 0;
   const int64_t BH = (int64_t)p->batch * p->heads, L = (int64_t)p->n_chunks * p->chunk_len, d = p->head_dim;
-  // delta, 1/D, -delta/D per row; the state gradients per chunk
-  return align256((size_t)(3 * BH * L * 4)) + align256((size_t)(BH * p->n_chunks * (d * d + d) * 4));
+  // delta, 1/D, -delta/D, lse log2(e) per row; the state gradients per chunk
+  return align256((size_t)(4 * BH * L * 4)) + align256((size_t)(BH * p->n_chunks * (d * d + d) * 4));
 }
 
 rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
@@ -376,7 +376,8 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
   b.delta = ws;
   b.rsc = ws + BH * L;
   b.zw = ws + 2 * BH * L;
-  b.dS = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)(3 * BH * L * 4)));
+  b.lse2 = ws + 3 * BH * L;
+  b.dS = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)(4 * BH * L * 4)));
   b.dz = b.dS + BH * p->n_chunks * 128 * 128;
   b.sb = p->stride_b;
   b.sh = p->stride_h;

@@ -47,7 +47,16 @@ constexpr int NWB = 4;               // waves per workgroup
 constexpr int TB = NWB * 64;         // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-// ---- delta_i = dout_i . out_i, 1 / D_i = exp(-lse_i), -delta_i / D_i
+// 32x32x16 bf16 products whose accumulator lives in vector registers (the
+// first of a chain starts from zero)
+__device__ __forceinline__ void mfma_v_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// ---- delta_i = dout_i . out_i, 1 / D_i = exp(-lse_i), -delta_i / D_i, lse_i log2(e)
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   const int64_t L = (int64_t)p.N * p.C;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -65,6 +74,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
     for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(c[i]) + bf16_hi(a[i]) * bf16_hi(c[i]);
   }
   const float r = __expf(-p.lse[idx]);
+  p.lse2[idx] = p.lse[idx] * kLog2e;
   p.delta[idx] = acc;
   p.rsc[idx] = r;
   p.zw[idx] = -acc * r;
@@ -123,10 +133,12 @@ __device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
 // ---- window gradients of keys and values, then their linear term
 //   (key chunks j <= N-1-w): dv_t += dU_j^T phi(k_t),  dk_t += (dU_j v_t + du_j) * phi'(k_t)
 __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
-  // two buffers of (Q rows, dout rows, lse, delta) for one 32-row query block
+  // two buffers of (Q rows, dout rows, lse log2(e), delta) for one 32-row
+  // query block (64 entries of lse and delta: one per lane of the load)
   __shared__ __attribute__((aligned(1024))) unsigned char qs[2][ROWT];
   __shared__ __attribute__((aligned(1024))) unsigned char gs[2][ROWT];
-  __shared__ float lse_s[2][RB], del_s[2][RB];
+  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(256))) float del_s[2][64];
   // dU_j as bf16 rows, and its transpose
   __shared__ __attribute__((aligned(1024))) unsigned char um[BD * BD * 2];
   __shared__ __attribute__((aligned(1024))) unsigned char ut[BD * BD * 2];
@@ -166,73 +178,102 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
   const int nblk = (c_hi - j + 1) * nqb;
-  // staging: thread tid moves granules u = tid + 256 i (i < 4) of the block's
-  // 32 Q rows (u < 512) and 32 dout rows (u >= 512); threads < 32 the lse, delta
-  u32x4 stg[4];
-  float lse_r = 0.f, del_r = 0.f;
-  auto fetch = [&](int qi) {
-    const int c = j + qi / nqb, blk = qi % nqb;
-    const int64_t row0 = (int64_t)c * p.C + RB * blk;
-    const int nq = min(RB, p.C - RB * blk);
+  // Query blocks reach LDS through buffer loads that write LDS directly, one
+  // block ahead (two buffers).  A 32-row tile is 8 loads of 4 rows (64 lanes
+  // x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile and of the dO
+  // tile, each lane fetching the global granule that the swizzle puts at its
+  // LDS slot.  The descriptors end at the chunk's last row, so rows past it
+  // read as zero; such rows (q = dout = 0, lse = delta = 0: P = 1, dP = 0)
+  // add exactly nothing to dV and dK.  Waves 0 and 1 load the block's lse
+  // log2(e) and delta.
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int st2 = (int)p.st * 2;  // bytes between rows
+  int doff[2];                    // this lane's byte offset within a tile, loads 2wv and 2wv+1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-      stg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (r < nq) stg[i] = ld16((which ? gb : qb) + (row0 + r) * p.st + g * 8);
-    }
-    if (tid < RB) {
-      const bool ok = tid < nq;
-      lse_r = ok ? p.lse[bh * L + row0 + tid] * kLog2e : INFINITY;  // rows past the chunk: P = 0
-      del_r = ok ? p.delta[bh * L + row0 + tid] : 0.f;
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-      put_granule(which ? gs[buf] : qs[buf], r, g, stg[i]);
-    }
-    if (tid < RB) {
-      lse_s[buf][tid] = lse_r;
-      del_s[buf][tid] = del_r;
-    }
-  };
-  if (nblk > 0) {
-    fetch(0);
-    stash(0);
+  for (int x = 0; x < 2; ++x) {
+    const int row = 4 * (2 * wv + x) + (lane >> 4);
+    doff[x] = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
   }
-  __syncthreads();
-  for (int qi = 0; qi < nblk; ++qi) {
-    const int buf = qi & 1;
-    if (qi + 1 < nblk) fetch(qi + 1);  // in flight while this block is multiplied
-    const unsigned char* qt = qs[buf];
-    const unsigned char* gt = gs[buf];
-    f32x16 sa = {}, pa = {};
+  auto issue = [&](int qi, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const int cq = j + qi / nqb, blk = qi - (qi / nqb) * nqb;
+    const int64_t row0 = (int64_t)cq * p.C + RB * blk;
+    const int nq = min(RB, p.C - RB * blk);
+    const int nbytes = (nq - 1) * st2 + BD * 2;
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qb + row0 * p.st), (short)0, nbytes, fwd::kBufWord3);
+    const __amdgpu_buffer_rsrc_t grs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(gb + row0 * p.st), (short)0, nbytes, fwd::kBufWord3);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(qs[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)(gs[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+    }
+    if (wv < 2) {
+      const float* src = (wv == 0 ? p.lse2 : p.delta) + bh * L + row0;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nq * 4, fwd::kBufWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(wv == 0 ? lse_s[BUF] : del_s[BUF]), 4, lane * 4, 0, 0, 0);
+    }
+  };
+  // block qi from buffer BUF; its loads were issued one block earlier
+  auto block = [&](int qi, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block qi are in LDS
+    __syncthreads();  // every wave's; and every wave is done with block qi-1 (the other buffer)
+    if (qi + 1 < nblk) issue(qi + 1, std::integral_constant<int, BUF ^ 1>{});
+    const unsigned char* qt = qs[BUF];
+    const unsigned char* gt = gs[BUF];
+    // all of the block's operand fragments are read first, in one batch
+    // (the products then wait on none of them one by one)
+    bf16x8 qf[8], gf[8], qc[2][4], gc[2][4];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      sa = mfma32(row_frag(qt, 0, ks, lane), kr[ks], sa);  // S = Q K^T, keys on the lanes
-      pa = mfma32(row_frag(gt, 0, ks, lane), vr[ks], pa);  // dP = dO V^T
-    }
-    uint32_t pp[8], dd[8];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse_s[buf][m0]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[buf][m1]));
-      pp[i >> 1] = pack_bf16(p0, p1);
-      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[buf][m0]), p1 * (pa[i + 1] - del_s[buf][m1]));
+      qf[ks] = row_frag(qt, 0, ks, lane);
+      gf[ks] = row_frag(gt, 0, ks, lane);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        dv[nb] = mfma32(col_frag(gt, ks, nb, lane), pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
-        dk[nb] = mfma32(col_frag(qt, ks, nb, lane), pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
+        gc[ks][nb] = col_frag(gt, ks, nb, lane);
+        qc[ks][nb] = col_frag(qt, ks, nb, lane);
       }
-    // the other buffer was last read in the previous block, before the barrier that ended it
-    if (qi + 1 < nblk) stash(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sa, pa;  // in vector registers: the softmax work reads them there
+    mfma_v_first(sa, qf[0], kr[0]);  // S = Q K^T, keys on the lanes
+    mfma_v_first(pa, gf[0], vr[0]);  // dP = dO V^T
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) {
+      mfma_v(sa, qf[ks], kr[ks]);
+      mfma_v(pa, gf[ks], vr[ks]);
+    }
+    uint32_t pp[8], dd[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse_s[BUF][m0]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[BUF][m1]));
+      pp[i >> 1] = pack_bf16(p0, p1);
+      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[BUF][m0]), p1 * (pa[i + 1] - del_s[BUF][m1]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        dv[nb] = mfma32(gc[ks][nb], pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
+        dk[nb] = mfma32(qc[ks][nb], pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
+      }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (nblk > 0) issue(0, B0{});
+  int qi = 0;
+  for (; qi + 1 < nblk; qi += 2) {  // two blocks per iteration, so each one's buffer is known
+    block(qi, B0{});
+    block(qi + 1, B1{});
   }
+  if (qi < nblk) block(qi, B0{});
   // lane = key; element i of block nb = feature 32 nb + out_row(i)
   float* dvr = p.dv + (bh * L + key0 + l32) * BD;
   float* dkr = p.dk + (bh * L + key0 + l32) * BD;
@@ -330,37 +371,41 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   const int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
   const int64_t kend = p.w > 0 ? (int64_t)(c + 1) * p.C : 0;
   const int nblk = (int)((kend - kbeg + RB - 1) / RB);
-  // staging of 32-key blocks: thread tid moves granules u = tid + 256 i of
-  // the block's 32 K rows (u < 512) and 32 V rows (u >= 512)
-  u32x4 stg[4];
-  auto fetch = [&](int bi) {
+  // 32-key blocks of K and V reach LDS through buffer loads that write LDS
+  // directly, one block ahead (two buffers), as in bwd_dkdv_kernel; keys
+  // past the window read as zero, and their probabilities are masked.
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int st2 = (int)p.st * 2;  // bytes between rows
+  int doff[2];                    // this lane's byte offset within a tile, loads 2wv and 2wv+1
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int row = 4 * (2 * wv + x) + (lane >> 4);
+    doff[x] = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
+  }
+  auto issue = [&](int bi, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
     const int64_t k0 = kbeg + (int64_t)RB * bi;
     const int nk = (int)min((int64_t)RB, kend - k0);
+    const int nbytes = (nk - 1) * st2 + BD * 2;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-      stg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (r < nk) stg[i] = ld16((which ? vb : kb) + (k0 + r) * p.st + g * 8);
+    for (int x = 0; x < 2; ++x) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(ks_t[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vs_t[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + TB * i, which = u >> 9, rem = u & 511, r = rem >> 4, g = rem & 15;
-      put_granule(which ? vs_t[buf] : ks_t[buf], r, g, stg[i]);
-    }
-  };
-  if (nblk > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int buf = bi & 1;
+  auto block = [&](int bi, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block bi are in LDS
+    __syncthreads();  // every wave's; and every wave is done with block bi-1 (the other buffer)
+    if (bi + 1 < nblk) issue(bi + 1, std::integral_constant<int, BUF ^ 1>{});
     const int nk = (int)min((int64_t)RB, kend - (kbeg + (int64_t)RB * bi));
-    if (bi + 1 < nblk) fetch(bi + 1);  // in flight while this block is multiplied
-    const unsigned char* kt = ks_t[buf];
-    const unsigned char* vt = vs_t[buf];
+    const unsigned char* kt = ks_t[BUF];
+    const unsigned char* vt = vs_t[BUF];
     f32x16 sa = {}, pa = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -368,20 +413,39 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
       pa = mfma32(row_frag(vt, 0, ks, lane), gr[ks], pa);  // dP^T = V dO^T
     }
     uint32_t dd[8];
+    // keys past the window (only in the window's last block) get P = 0
+    auto softmax_grad = [&](auto masked_c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-      const float p0 = m0 < nk ? __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse2)) : 0.f;
-      const float p1 = m1 < nk ? __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse2)) : 0.f;
-      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del), p1 * (pa[i + 1] - del));
-    }
+      for (int i = 0; i < 16; i += 2) {
+        const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse2));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse2));
+        if constexpr (decltype(masked_c)::value) {
+          p0 = m0 < nk ? p0 : 0.f;
+          p1 = m1 < nk ? p1 : 0.f;
+        }
+        dd[i >> 1] = pack_bf16(p0 * (pa[i] - del), p1 * (pa[i + 1] - del));
+      }
+    };
+    if (nk < RB)
+      softmax_grad(std::true_type{});
+    else
+      softmax_grad(std::false_type{});
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) dq[nb] = mfma32(col_frag(kt, ks, nb, lane), pack_b(dd, ks), dq[nb]);  // dQ^T += K^T dS^T
-    if (bi + 1 < nblk) stash(buf ^ 1);
-    __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (nblk > 0) issue(0, B0{});
+  int bi = 0;
+  for (; bi + 1 < nblk; bi += 2) {  // two blocks per iteration, so each one's buffer is known
+    block(bi, B0{});
+    block(bi + 1, B1{});
   }
+  if (bi < nblk) block(bi, B0{});
+  __syncthreads();  // the epilogue reuses the K/V buffers
   float* dqr = p.dq + (bh * L + row0 + l32) * BD;
   if (c >= p.w) {  // the chunk has a state (every chunk for w = 0)
     // S_c and the rows dout_i / D_i each as two bf16 parts, the three

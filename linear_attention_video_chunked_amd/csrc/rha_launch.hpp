@@ -161,6 +161,7 @@ struct BwdParams {
   float* delta;
   float* rsc;
   float* zw;
+  float* lse2;  // lse * log2(e) per row
   float* dS;
   float* dz;
   int64_t sb, sh, st;  // element strides of q, k, v, out, dout
