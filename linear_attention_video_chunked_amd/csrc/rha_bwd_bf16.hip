@@ -133,12 +133,12 @@ __device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
 // ---- window gradients of keys and values, then their linear term
 //   (key chunks j <= N-1-w): dv_t += dU_j^T phi(k_t),  dk_t += (dU_j v_t + du_j) * phi'(k_t)
 __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
-  // two buffers of (Q rows, dout rows, lse log2(e), delta) for one 32-row
+  // four buffers of (Q rows, dout rows, lse log2(e), delta) for one 32-row
   // query block (64 entries of lse and delta: one per lane of the load)
-  __shared__ __attribute__((aligned(1024))) unsigned char qs[2][ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char gs[2][ROWT];
-  __shared__ __attribute__((aligned(256))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(256))) float del_s[2][64];
+  __shared__ __attribute__((aligned(1024))) unsigned char qs[4][ROWT];
+  __shared__ __attribute__((aligned(1024))) unsigned char gs[4][ROWT];
+  __shared__ __attribute__((aligned(256))) float lse_s[4][64];
+  __shared__ __attribute__((aligned(256))) float del_s[4][64];
   // dU_j as bf16 rows, and its transpose
   __shared__ __attribute__((aligned(1024))) unsigned char um[BD * BD * 2];
   __shared__ __attribute__((aligned(1024))) unsigned char ut[BD * BD * 2];
@@ -178,14 +178,14 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
   const int nblk = (c_hi - j + 1) * nqb;
-  // Query blocks reach LDS through buffer loads that write LDS directly, one
-  // block ahead (two buffers).  A 32-row tile is 8 loads of 4 rows (64 lanes
-  // x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile and of the dO
-  // tile, each lane fetching the global granule that the swizzle puts at its
-  // LDS slot.  The descriptors end at the chunk's last row, so rows past it
-  // read as zero; such rows (q = dout = 0, lse = delta = 0: P = 1, dP = 0)
-  // add exactly nothing to dV and dK.  Waves 0 and 1 load the block's lse
-  // log2(e) and delta.
+  // Query blocks reach LDS through buffer loads that write LDS directly, two
+  // blocks ahead (block x in buffer x % 4).  A 32-row tile is 8 loads of 4
+  // rows (64 lanes x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile
+  // and of the dO tile, each lane fetching the global granule that the
+  // swizzle puts at its LDS slot.  The descriptors end at the chunk's last
+  // row, so rows past it read as zero; such rows (q = dout = 0, lse = delta =
+  // 0: P = 1, dP = 0) add exactly nothing to dV and dK.  Waves 0 and 1 load
+  // the block's lse log2(e) and delta.
   typedef __attribute__((address_space(3))) void lds_void;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int st2 = (int)p.st * 2;  // bytes between rows
@@ -195,8 +195,8 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     const int row = 4 * (2 * wv + x) + (lane >> 4);
     doff[x] = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
   }
-  auto issue = [&](int qi, auto buf_c) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(buf_c)::value;
+  auto issue = [&](int qi) __attribute__((always_inline)) {
+    const int bo = qi & 3;
     const int cq = j + qi / nqb, blk = qi - (qi / nqb) * nqb;
     const int64_t row0 = (int64_t)cq * p.C + RB * blk;
     const int nq = min(RB, p.C - RB * blk);
@@ -207,73 +207,161 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(gb + row0 * p.st), (short)0, nbytes, fwd::kBufWord3);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(qs[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)(gs[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(qs[bo] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)(gs[bo] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
     }
     if (wv < 2) {
       const float* src = (wv == 0 ? p.lse2 : p.delta) + bh * L + row0;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nq * 4, fwd::kBufWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(wv == 0 ? lse_s[BUF] : del_s[BUF]), 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(wv == 0 ? lse_s[bo] : del_s[bo]), 4, lane * 4, 0, 0, 0);
     }
   };
-  // block qi from buffer BUF; its loads were issued one block earlier
-  auto block = [&](int qi, auto buf_c) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(buf_c)::value;
-    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block qi are in LDS
-    __syncthreads();  // every wave's; and every wave is done with block qi-1 (the other buffer)
-    if (qi + 1 < nblk) issue(qi + 1, std::integral_constant<int, BUF ^ 1>{});
-    const unsigned char* qt = qs[BUF];
-    const unsigned char* gt = gs[BUF];
-    // all of the block's operand fragments are read first, in one batch
-    // (the products then wait on none of them one by one)
-    bf16x8 qf[8], gf[8], qc[2][4], gc[2][4];
+
+  // Software pipeline over the query blocks.  Iteration i runs eight rounds;
+  // round r issues one product of each of four chains and a slice of vector
+  // work:
+  //   S and dP of block i+1, feature step r            (rounds 0-7)
+  //   dV, dK of block i-1 over its queries 16-31, nb = r   (rounds 0-3)
+  //   dV, dK of block i over its queries 0-15, nb = r - 4  (rounds 4-7)
+  //   P and dS of block i, output elements 2r, 2r+1 (the scores of the
+  //   previous iteration): elements 0-7 feed rounds 4-7, elements 8-15 the
+  //   next iteration's rounds 0-3.
+  // Fragments are read two rounds ahead.  Buffer (i+2) % 4 is loaded
+  // meanwhile; block i-1's is still read in this iteration, block i-2's is not.
+  using fwd::kWaitLgkm0;
+  auto qt_of = [&](int x) __attribute__((always_inline)) { return qs[x & 3]; };
+  auto gt_of = [&](int x) __attribute__((always_inline)) { return gs[x & 3]; };
+  // S and dP of block x, all eight feature steps (the pipeline's prologue)
+  auto scores = [&](int x, f32x16& sx, f32x16& px) __attribute__((always_inline)) {
+    const unsigned char* qt = qt_of(x);
+    const unsigned char* gt = gt_of(x);
+    bf16x8 qf[8], gf[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       qf[ks] = row_frag(qt, 0, ks, lane);
       gf[ks] = row_frag(gt, 0, ks, lane);
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        gc[ks][nb] = col_frag(gt, ks, nb, lane);
-        qc[ks][nb] = col_frag(qt, ks, nb, lane);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 sa, pa;  // in vector registers: the softmax work reads them there
-    mfma_v_first(sa, qf[0], kr[0]);  // S = Q K^T, keys on the lanes
-    mfma_v_first(pa, gf[0], vr[0]);  // dP = dO V^T
+    mfma_v_first(sx, qf[0], kr[0]);
+    mfma_v_first(px, gf[0], vr[0]);
 #pragma unroll
     for (int ks = 1; ks < 8; ++ks) {
-      mfma_v(sa, qf[ks], kr[ks]);
-      mfma_v(pa, gf[ks], vr[ks]);
+      mfma_v(sx, qf[ks], kr[ks]);
+      mfma_v(px, gf[ks], vr[ks]);
     }
-    uint32_t pp[8], dd[8];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const int m0 = out_row(i, hh), m1 = out_row(i + 1, hh);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[i], p.scale_log2, -lse_s[BUF][m0]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[i + 1], p.scale_log2, -lse_s[BUF][m1]));
-      pp[i >> 1] = pack_bf16(p0, p1);
-      dd[i >> 1] = pack_bf16(p0 * (pa[i] - del_s[BUF][m0]), p1 * (pa[i + 1] - del_s[BUF][m1]));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        dv[nb] = mfma32(gc[ks][nb], pack_b(pp, ks), dv[nb]);  // dV^T += dO^T P
-        dk[nb] = mfma32(qc[ks][nb], pack_b(dd, ks), dk[nb]);  // dK^T += Q^T dS
-      }
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  if (nblk > 0) issue(0, B0{});
-  int qi = 0;
-  for (; qi + 1 < nblk; qi += 2) {  // two blocks per iteration, so each one's buffer is known
-    block(qi, B0{});
-    block(qi + 1, B1{});
+  // dV, dK of block x over its queries 16-31 (after the last iteration)
+  auto tail_products = [&](int x, const uint32_t (&ph)[4], const uint32_t (&dh)[4]) __attribute__((always_inline)) {
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]});
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      dv[nb] = mfma32(col_frag(gt_of(x), 1, nb, lane), pb, dv[nb]);
+      dk[nb] = mfma32(col_frag(qt_of(x), 1, nb, lane), db, dk[nb]);
+    }
+  };
+  auto iteration = [&](int i, auto prev_c, auto next_c, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
+                       const uint32_t (&ph)[4], const uint32_t (&dh)[4], uint32_t (&pco)[4], uint32_t (&dco)[4])
+                       __attribute__((always_inline)) {
+    constexpr bool PREV = decltype(prev_c)::value, NEXT = decltype(next_c)::value;
+    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block i+1 are in LDS
+    __syncthreads();  // every wave's; and every wave is done with iteration i-1
+    if (i + 2 < nblk) issue(i + 2);
+    const unsigned char* qtn = qt_of(i + 1);
+    const unsigned char* gtn = gt_of(i + 1);
+    const unsigned char* qtc = qt_of(i);
+    const unsigned char* gtc = gt_of(i);
+    const unsigned char* qtp = qt_of(i + 3);  // block i-1's buffer
+    const unsigned char* gtp = gt_of(i + 3);
+    const float* lsc = lse_s[i & 3];
+    const float* dlc = del_s[i & 3];
+    bf16x8 qf[3], gf[3], gcf[3], qcf[3];
+    uint32_t pl[4], dl[4];  // P, dS of block i, elements 0-7
+    // fragments of round rr (read two rounds ahead)
+    auto read_round = [&](auto rr_c) __attribute__((always_inline)) {
+      constexpr int rr = decltype(rr_c)::value, sl = rr % 3;
+      if constexpr (NEXT) {
+        qf[sl] = row_frag(qtn, 0, rr, lane);
+        gf[sl] = row_frag(gtn, 0, rr, lane);
+      }
+      if constexpr (rr < 4) {
+        if constexpr (PREV) {
+          gcf[sl] = col_frag(gtp, 1, rr, lane);
+          qcf[sl] = col_frag(qtp, 1, rr, lane);
+        }
+      } else {
+        gcf[sl] = col_frag(gtc, 0, rr - 4, lane);
+        qcf[sl] = col_frag(qtc, 0, rr - 4, lane);
+      }
+    };
+    read_round(std::integral_constant<int, 0>{});
+    read_round(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 8>([&](auto r_c) __attribute__((always_inline)) {
+      constexpr int r = decltype(r_c)::value, sl = r % 3;
+      if constexpr (r + 2 < 8) read_round(std::integral_constant<int, r + 2>{});
+      const int m = out_row(2 * r, hh);  // rows m, m+1 of block i
+      const float2 l2 = *reinterpret_cast<const float2*>(lsc + m);
+      const float2 d2 = *reinterpret_cast<const float2*>(dlc + m);
+      if constexpr (NEXT) {
+        if constexpr (r == 0) {
+          mfma_v_first(sn, qf[sl], kr[r]);
+          mfma_v_first(pn, gf[sl], vr[r]);
+        } else {
+          mfma_v(sn, qf[sl], kr[r]);
+          mfma_v(pn, gf[sl], vr[r]);
+        }
+      }
+      if constexpr (r < 4) {
+        if constexpr (PREV) {
+          dv[r] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]}), dv[r]);
+          dk[r] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]}), dk[r]);
+        }
+      } else {
+        dv[r - 4] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]}), dv[r - 4]);
+        dk[r - 4] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dl[0], dl[1], dl[2], dl[3]}), dk[r - 4]);
+      }
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * r], p.scale_log2, -l2.x));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * r + 1], p.scale_log2, -l2.y));
+      const uint32_t pw = pack_bf16(p0, p1);
+      const uint32_t dw = pack_bf16(p0 * (pc[2 * r] - d2.x), p1 * (pc[2 * r + 1] - d2.y));
+      if constexpr (r < 4) {
+        pl[r] = pw;
+        dl[r] = dw;
+      } else {
+        pco[r - 4] = pw;
+        dco[r - 4] = dw;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  using F_ = std::false_type;
+  using T_ = std::true_type;
+  if (nblk > 0) {
+    f32x16 s0, p0, s1, p1;
+    uint32_t ca[4], cd[4], cb[4], ce[4];  // carried halves (P, dS) of alternate iterations
+    issue(0);
+    if (nblk > 1) issue(1);
+    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
+    __syncthreads();
+    scores(0, s0, p0);
+    if (nblk > 1) iteration(0, F_{}, T_{}, s0, p0, s1, p1, ca, cd, ca, cd);
+    else iteration(0, F_{}, F_{}, s0, p0, s1, p1, ca, cd, ca, cd);
+    int i = 1;
+    for (; i + 2 < nblk; i += 2) {  // iterations i and i+1 both have a next block
+      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce);
+      iteration(i + 1, T_{}, T_{}, s0, p0, s1, p1, cb, ce, ca, cd);
+    }
+    if (i + 1 < nblk) {  // two left: i (with a next block) and i+1 (the last)
+      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce);
+      iteration(i + 1, T_{}, F_{}, s0, p0, s1, p1, cb, ce, ca, cd);
+      tail_products(i + 1, ca, cd);
+    } else if (i < nblk) {  // one left: i, the last
+      iteration(i, T_{}, F_{}, s1, p1, s0, p0, ca, cd, cb, ce);
+      tail_products(i, cb, ce);
+    } else {  // a single block
+      tail_products(0, ca, cd);
+    }
   }
-  if (qi < nblk) block(qi, B0{});
   // lane = key; element i of block nb = feature 32 nb + out_row(i)
   float* dvr = p.dv + (bh * L + key0 + l32) * BD;
   float* dkr = p.dk + (bh * L + key0 + l32) * BD;
