@@ -293,37 +293,55 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
         qcf[sl] = col_frag(qtc, 0, rr - 4, lane);
       }
     };
+    // the block's lse log2(e) and delta for this lane's 16 rows, read first
+    // (LDS reads complete in order: later fragment reads do not wait on them)
+    f32x4 lr[4], dr[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      lr[g] = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hh);
+      dr[g] = *reinterpret_cast<const f32x4*>(dlc + 8 * g + 4 * hh);
+    }
     read_round(std::integral_constant<int, 0>{});
     read_round(std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 8>([&](auto r_c) __attribute__((always_inline)) {
       constexpr int r = decltype(r_c)::value, sl = r % 3;
+      // output elements 2r, 2r+1 are rows out_row(2r) and out_row(2r) + 1:
+      // entries (2r) % 4 and (2r) % 4 + 1 of group r / 2
+      constexpr int g = r / 2, e = (2 * r) % 4;
       if constexpr (r + 2 < 8) read_round(std::integral_constant<int, r + 2>{});
-      const int m = out_row(2 * r, hh);  // rows m, m+1 of block i
-      const float2 l2 = *reinterpret_cast<const float2*>(lsc + m);
-      const float2 d2 = *reinterpret_cast<const float2*>(dlc + m);
+      // four groups, each one product and a quarter of the vector work
+      float t0, t1, p0, p1;
       if constexpr (NEXT) {
-        if constexpr (r == 0) {
-          mfma_v_first(sn, qf[sl], kr[r]);
-          mfma_v_first(pn, gf[sl], vr[r]);
-        } else {
-          mfma_v(sn, qf[sl], kr[r]);
-          mfma_v(pn, gf[sl], vr[r]);
-        }
+        if constexpr (r == 0) mfma_v_first(sn, qf[sl], kr[r]);
+        else mfma_v(sn, qf[sl], kr[r]);
       }
+      t0 = fmaf(sc[2 * r], p.scale_log2, -lr[g][e]);
+      t1 = fmaf(sc[2 * r + 1], p.scale_log2, -lr[g][e + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NEXT) {
+        if constexpr (r == 0) mfma_v_first(pn, gf[sl], vr[r]);
+        else mfma_v(pn, gf[sl], vr[r]);
+      }
+      p0 = __builtin_amdgcn_exp2f(t0);
+      p1 = __builtin_amdgcn_exp2f(t1);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (r < 4) {
-        if constexpr (PREV) {
+        if constexpr (PREV)
           dv[r] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]}), dv[r]);
-          dk[r] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]}), dk[r]);
-        }
       } else {
         dv[r - 4] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]}), dv[r - 4]);
+      }
+      const uint32_t pw = pack_bf16(p0, p1);
+      const float u0 = pc[2 * r] - dr[g][e], u1 = pc[2 * r + 1] - dr[g][e + 1];
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (r < 4) {
+        if constexpr (PREV)
+          dk[r] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]}), dk[r]);
+      } else {
         dk[r - 4] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dl[0], dl[1], dl[2], dl[3]}), dk[r - 4]);
       }
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * r], p.scale_log2, -l2.x));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * r + 1], p.scale_log2, -l2.y));
-      const uint32_t pw = pack_bf16(p0, p1);
-      const uint32_t dw = pack_bf16(p0 * (pc[2 * r] - d2.x), p1 * (pc[2 * r + 1] - d2.y));
+      const uint32_t dw = pack_bf16(p0 * u0, p1 * u1);
       if constexpr (r < 4) {
         pl[r] = pw;
         dl[r] = dw;
