@@ -679,3 +679,71 @@ def hybrid_backward_batched(q, k, v, C: int, w: int, dout):
             for arr, g in zip(res, hybrid_backward(q[b, h], k[b, h], v[b, h], C, w, dout[b, h])):
                 arr[b, h] = g
     return tuple(res)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the bidirectional hybrid (the hybrid that stands in for the
+# bidirectional attention of video diffusion transformers: ReHyAt, abstract;
+# the symmetric-window reading of the bidirectional form above).  The same
+# chain rule as ``hybrid_backward``, on ``hybrid_bidir``: the window is
+# symmetric, and chunk c's linear term uses S_pre_c + S_suf_c, so the state
+# gradient dS_c reaches chunk j's keys through the past part when
+# j <= c - w (w = 0: j <= c) and through the future part when
+# j >= c + max(w, 1).
+
+def hybrid_bidir_backward(q, k, v, C: int, w: int, dout):
+    """(dq, dk, dv) of sum(dout * hybrid_bidir(q, k, v, C, w)) for one head."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    L, d = q.shape
+    N = L // C
+    scale = 1.0 / math.sqrt(d)
+    S_pre, z_pre, S_suf, z_suf = state_scan_bidir(k, v, C, w)
+    out, den = hybrid_bidir(q, k, v, C, w, return_den=True)
+    dN = dout / den[:, None]  # d loss / d numerator
+    dD = -(dout * out).sum(axis=1) / den  # d loss / d denominator
+    fq, fk = phi(q), phi(k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dS, dz = np.zeros(S_pre.shape), np.zeros(z_pre.shape)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        lo, hi = window_range_bidir(c, w, N)
+        if lo <= hi:
+            keys = slice(lo * C, (hi + 1) * C)
+            E = np.exp(_scores(q[rows], k[keys]))
+            dE = dN[rows] @ v[keys].T + dD[rows][:, None]
+            dv[keys] += E.T @ dN[rows]
+            ds = E * dE
+            dq[rows] += ds @ k[keys] * scale
+            dk[keys] += ds.T @ q[rows] * scale
+        S = S_pre[c] + S_suf[c]
+        z = z_pre[c] + z_suf[c]
+        gq = dN[rows] @ S.T + dD[rows][:, None] * z[None, :]
+        dq[rows] += gq * dphi(q[rows])
+        dS[c] = fq[rows].T @ dN[rows]
+        dz[c] = fq[rows].T @ dD[rows]
+    first = max(w, 1)
+    for j in range(N):
+        # chunks whose linear term holds chunk j: c >= j + w (past part) and
+        # c <= j - max(w, 1) (future part)
+        users = [c for c in range(N) if c >= j + w or c <= j - first]
+        if not users:
+            continue
+        dU = dS[users].sum(axis=0)
+        du = dz[users].sum(axis=0)
+        toks = slice(j * C, (j + 1) * C)
+        dv[toks] += fk[toks] @ dU
+        gk = v[toks] @ dU.T + du[None, :]
+        dk[toks] += gk * dphi(k[toks])
+    return dq, dk, dv
+
+
+def hybrid_bidir_backward_batched(q, k, v, C: int, w: int, dout):
+    """``hybrid_bidir_backward`` over [B, H, L, d]."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    B, H = q.shape[:2]
+    res = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+    for b in range(B):
+        for h in range(H):
+            for arr, g in zip(res, hybrid_bidir_backward(q[b, h], k[b, h], v[b, h], C, w, dout[b, h])):
+                arr[b, h] = g
+    return tuple(res)

@@ -680,3 +680,138 @@ def test_backward_planted_mistake_is_caught(name, monkeypatch):
 
 def test_backward_unmutated_pins_pass():
     assert max(_backward_pin_errs()) < 1e-8
+
+
+# ------------------------------------------------- backward pass, bidirectional
+# ``hybrid_bidir_backward`` is pinned like the causal one: central finite
+# differences of the bidirectional forward oracle, torch autograd through a
+# separately written dense form, and the two limits with a known gradient
+# (a window covering every chunk is unmasked softmax attention; w = 0 is
+# non-causal linear attention).
+
+def _loss_bidir(q, k, v, C, w, dout):
+    return float((O.hybrid_bidir(q, k, v, C, w) * dout).sum())
+
+
+def _torch_dense_bidir(q, k, v, C, w):
+    """The bidirectional definition as a dense L x L weight matrix, in torch ops."""
+    L, d = q.shape
+    c = torch.arange(L) // C
+    win = ((c[None, :] - c[:, None]).abs() <= w - 1) if w > 0 else torch.zeros((L, L), dtype=torch.bool)
+    s = q @ k.T / math.sqrt(d)
+    lin = (torch.nn.functional.elu(q) + 1) @ (torch.nn.functional.elu(k) + 1).T
+    a = torch.where(win, torch.exp(s), lin)
+    return (a @ v) / a.sum(dim=1, keepdim=True)
+
+
+@pytest.mark.parametrize("C,N,w", [(3, 5, 2), (5, 3, 1), (4, 4, 0), (2, 5, 9), (3, 6, 3)])
+def test_bidir_backward_matches_finite_differences(C, N, w):
+    d = 5
+    q, k, v = _qkv(C * N, d, 2200 + C * N + w, qs=1.2)
+    dout = _rand((C * N, d), 2300 + w)
+    grads = O.hybrid_bidir_backward(q, k, v, C, w, dout)
+    rng = np.random.default_rng(2400 + C)
+    eps = 1e-5
+    for which, g in enumerate(grads):
+        for _ in range(3):
+            dirn = rng.standard_normal(q.shape)
+            ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+            ap[which] += eps * dirn
+            am[which] -= eps * dirn
+            fd = (_loss_bidir(*ap, C, w, dout) - _loss_bidir(*am, C, w, dout)) / (2 * eps)
+            an = float((g * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("C,N,w", [(4, 5, 2), (7, 3, 1), (3, 4, 0), (5, 4, 6), (2, 7, 3)])
+def test_bidir_backward_matches_torch_autograd(C, N, w):
+    d = 8
+    q, k, v = _qkv(C * N, d, 2500 + C + w, qs=1.5)
+    dout = _rand((C * N, d), 2600 + N)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_bidir(tq, tk, tv, C, w) * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_bidir_backward(q, k, v, C, w, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w", [(6, 4, 4), (5, 3, 7)])
+def test_bidir_backward_window_all_equals_unmasked_sdpa_gradient(C, N, w):
+    d = 16
+    q, k, v = _qkv(C * N, d, 2700 + C + N, qs=1.5)
+    dout = _rand((C * N, d), 2800 + C)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True)[None, None] for x in (q, k, v))
+    for t in (tq, tk, tv):
+        t.retain_grad()
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    (o[0, 0] * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_bidir_backward(q, k, v, C, w, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N", [(1, 12), (4, 5)])
+def test_bidir_backward_window0_equals_noncausal_linear_attention_gradient(C, N):
+    d = 6
+    q, k, v = _qkv(C * N, d, 2900 + C, qs=1.2)
+    dout = _rand((C * N, d), 3000 + C)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    fq = torch.nn.functional.elu(tq) + 1
+    fk = torch.nn.functional.elu(tk) + 1
+    o = (fq @ (fk.T @ tv)) / (fq @ fk.sum(dim=0))[:, None]
+    (o * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_bidir_backward(q, k, v, C, 0, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _bidir_backward_pin_errs():
+    C, N, w, d = 3, 5, 2, 5
+    q, k, v = _qkv(C * N, d, 3100, qs=1.2)
+    dout = _rand((C * N, d), 3101)
+    grads = O.hybrid_bidir_backward(q, k, v, C, w, dout)
+    rng = np.random.default_rng(3102)
+    fd_err = 0.0
+    for which, g in enumerate(grads):
+        dirn = rng.standard_normal(q.shape)
+        ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+        ap[which] += 1e-5 * dirn
+        am[which] -= 1e-5 * dirn
+        fd = (_loss_bidir(*ap, C, w, dout) - _loss_bidir(*am, C, w, dout)) / 2e-5
+        fd_err = max(fd_err, abs(fd - float((g * dirn).sum())))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_bidir(tq, tk, tv, C, w) * torch.from_numpy(dout)).sum().backward()
+    ag_err = max(float(np.max(np.abs(g - t.grad.numpy()))) for g, t in zip(grads, (tq, tk, tv)))
+    return fd_err, ag_err
+
+
+def _future_one_chunk_late(orig):
+    def scan(k, v, C, w):
+        S_pre, z_pre, S_suf, z_suf = orig(k, v, C, w)
+        U, u = O.chunk_states(k, v, C)
+        N = U.shape[0]
+        first = max(w, 1)
+        for c in range(N):  # drop the nearest future chunk from every future state
+            if c + first <= N - 1:
+                S_suf[c] = S_suf[c] - U[c + first]
+                z_suf[c] = z_suf[c] - u[c + first]
+        return S_pre, z_pre, S_suf, z_suf
+    return scan
+
+
+BIDIR_BACKWARD_MUTANTS = {
+    "dphi_constant_one": ("dphi", lambda orig: (lambda x: np.ones_like(np.asarray(x, np.float64)))),
+    "window_one_chunk_short": ("window_range_bidir",
+                               lambda orig: (lambda c, w, N: (max(0, c - w + 2), min(N - 1, c + w - 1)) if w > 0
+                                             else (c + 1, c))),
+    "future_state_one_chunk_late": ("state_scan_bidir", _future_one_chunk_late),
+    "score_sign_flip": ("_scores", lambda orig: (lambda q, k: -orig(q, k))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BIDIR_BACKWARD_MUTANTS))
+def test_bidir_backward_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = BIDIR_BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    assert max(_bidir_backward_pin_errs()) > 1e-6
+
+
+def test_bidir_backward_unmutated_pins_pass():
+    assert max(_bidir_backward_pin_errs()) < 1e-8
