@@ -195,6 +195,38 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
                           size_t workspace_bytes, void* stream);
 
 /*
+ * rha_hybrid_bwd_bidir -- gradients of rha_hybrid_fwd_bidir, for training or
+ * distilling the bidirectional models that the hybrid serves (ReHyAt,
+ * abstract: the hybrid replaces the attention of video diffusion
+ * transformers, which attend over the whole clip in both directions).
+ *
+ * With L = sum(dout * out) for out = rha_hybrid_fwd_bidir's output (the
+ * definition below, at rha_state_scan_bidir): the exact derivatives through
+ * the symmetric softmax window, the shared normaliser and both states.  The
+ * state used by chunk c is S_past[c] + S_future[c], so its gradient reaches
+ * the keys of chunk j through the past state when j <= c - w (w == 0:
+ * j <= c) and through the future state when j >= c + max(w, 1).  Matrix
+ * products use bf16 operands and float32 accumulation.
+ *
+ *   q, k, v                       : as given to rha_hybrid_fwd_bidir (read)
+ *   S_past, z_past, S_future, z_future : rha_state_scan_bidir's states (read)
+ *   out, lse                      : rha_hybrid_fwd_bidir's output and lse (read; lse required)
+ *   dout                          : [B, H, L, d], the problem's strides and dtype (read)
+ *   dq, dk, dv                    : [B, H, L, d] float32 contiguous (written)
+ *   workspace                     : device scratch of rha_hybrid_bwd_bidir_workspace_size(p)
+ *                                   bytes, 16-byte aligned, no initialisation needed
+ *
+ * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16, head_dim is 128 and
+ * anchor_chunks is 0; RHA_ERR_INVALID_ARG if the workspace is too small.
+ */
+size_t rha_hybrid_bwd_bidir_workspace_size(const rha_problem* p);
+rha_status rha_hybrid_bwd_bidir(const rha_problem* p, const void* q, const void* k, const void* v,
+                                const float* S_past, const float* z_past, const float* S_future,
+                                const float* z_future, const void* out, const float* lse,
+                                const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * Bidirectional hybrid -- rha_state_scan_bidir and rha_hybrid_fwd_bidir.
  *
  * ReHyAt (abstract): the hybrid takes the place of the softmax attention of

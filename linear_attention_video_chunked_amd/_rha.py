@@ -70,6 +70,10 @@ def lib():
     L.rha_hybrid_bwd_workspace_size.argtypes = [P]
     L.rha_hybrid_bwd_workspace_size.restype = ctypes.c_size_t
     L.rha_hybrid_fwd_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.rha_hybrid_bwd_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    L.rha_hybrid_bwd_bidir_workspace_size.argtypes = [P]
+    L.rha_hybrid_bwd_bidir_workspace_size.restype = ctypes.c_size_t
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
@@ -77,7 +81,8 @@ def lib():
     L.rha_stream_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                           ctypes.c_int32, _vp, _vp, _vp]
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
-                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_stream_step", "rha_stream_step_noalloc"):
+                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_hybrid_bwd_bidir", "rha_stream_step",
+                 "rha_stream_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
     L.rha_status_string.restype = ctypes.c_char_p
@@ -260,6 +265,33 @@ def hybrid_fwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, states, 
     _check(lib().rha_hybrid_fwd_bidir(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(Sp), _ptr(zp), _ptr(Sf),
                                       _ptr(zf), _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def hybrid_bwd_bidir(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, states, out: torch.Tensor,
+                     lse: torch.Tensor, dout: torch.Tensor, C: int, w: int, stream=None):
+    """rha_hybrid_bwd_bidir: (dq, dk, dv) float32 [B,H,L,d] of sum(dout * out)
+    for the bidirectional hybrid (``states`` from state_scan_bidir; out, lse
+    from hybrid_fwd_bidir on the same inputs)."""
+    _same_layout(q, k, v, out, dout)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    Sp, zp, Sf, zf = states
+    for name, S, z in (("past", Sp, zp), ("future", Sf, zf)):
+        _check_f32(q, S, f"S_{name}", (B, H, N, d, d))
+        _check_f32(q, z, f"z_{name}", (B, H, N, d))
+    _check_f32(q, lse, "lse", (B, H, L))
+    prob = _problem(q, C, w, N)
+    nbytes = int(lib().rha_hybrid_bwd_bidir_workspace_size(ctypes.byref(prob)))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    _check(lib().rha_hybrid_bwd_bidir(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(Sp), _ptr(zp), _ptr(Sf),
+                                      _ptr(zf), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
 
 
 # Block sizes of the pruned window (RHA_SPARSE_QTILE / RHA_SPARSE_KTILE).

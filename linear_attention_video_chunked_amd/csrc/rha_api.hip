@@ -329,16 +329,21 @@ rha_status rha_hybrid_fwd_bidir(const rha_problem* p, const void* q, const void*
   return ok();
 }
 
-size_t rha_hybrid_bwd_workspace_size(const rha_problem* p) {
-  if (p == nullptr || check_problem(p, false) != RHA_OK) return 0;
+namespace {
+
+// Bytes of the backward pass's workspace: per row delta, 1/D, -delta/D and
+// lse log2(e); the per-chunk state gradients (twice for the bidirectional
+// hybrid: past and future parts).
+size_t bwd_workspace_bytes(const rha_problem* p, bool bidir) {
   const int64_t BH = (int64_t)p->batch * p->heads, L = (int64_t)p->n_chunks * p->chunk_len, d = p->head_dim;
-  // delta, 1/D, -delta/D, lse log2(e) per row; the state gradients per chunk
-  return align256((size_t)(4 * BH * L * 4)) + align256((size_t)(BH * p->n_chunks * (d * d + d) * 4));
+  const size_t states = align256((size_t)(BH * p->n_chunks * (d * d + d) * 4));
+  return align256((size_t)(4 * BH * L * 4)) + (bidir ? 2 : 1) * states;
 }
 
-rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
-                          const float* z, const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                          float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+rha_status hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                      const float* z, const float* S2, const float* z2, const void* out, const float* lse,
+                      const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                      void* stream, bool bidir) {
   RHA_TRY(check_problem(p, false));
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "the backward pass needs dtype RHA_BF16 and head_dim 128");
@@ -347,8 +352,12 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
   RHA_TRY(need(q, "q"));
   RHA_TRY(need(k, "k"));
   RHA_TRY(need(v, "v"));
-  RHA_TRY(need(S, "S"));
-  RHA_TRY(need(z, "z"));
+  RHA_TRY(need(S, bidir ? "S_past" : "S"));
+  RHA_TRY(need(z, bidir ? "z_past" : "z"));
+  if (bidir) {
+    RHA_TRY(need(S2, "S_future"));
+    RHA_TRY(need(z2, "z_future"));
+  }
   RHA_TRY(need(out, "out"));
   RHA_TRY(need(lse, "lse", true, 4));
   RHA_TRY(need(dout, "dout"));
@@ -356,7 +365,7 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
   RHA_TRY(need(dk, "dk"));
   RHA_TRY(need(dv, "dv"));
   RHA_TRY(need(workspace, "workspace"));
-  const size_t need_bytes = rha_hybrid_bwd_workspace_size(p);
+  const size_t need_bytes = bwd_workspace_bytes(p, bidir);
   if (workspace_bytes < need_bytes)
     return fail(RHA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need_bytes);
   const int64_t BH = (int64_t)p->batch * p->heads, L = (int64_t)p->n_chunks * p->chunk_len;
@@ -377,8 +386,17 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
   b.rsc = ws + BH * L;
   b.zw = ws + 2 * BH * L;
   b.lse2 = ws + 3 * BH * L;
-  b.dS = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)(4 * BH * L * 4)));
+  const size_t states = align256((size_t)(BH * p->n_chunks * (128 * 128 + 128) * 4));
+  char* st = static_cast<char*>(workspace) + align256((size_t)(4 * BH * L * 4));
+  b.dS = reinterpret_cast<float*>(st);
   b.dz = b.dS + BH * p->n_chunks * 128 * 128;
+  if (bidir) {
+    b.bidir = 1;
+    b.S2 = S2;
+    b.z2 = z2;
+    b.dS2 = reinterpret_cast<float*>(st + states);
+    b.dz2 = b.dS2 + BH * p->n_chunks * 128 * 128;
+  }
   b.sb = p->stride_b;
   b.sh = p->stride_h;
   b.st = p->stride_t;
@@ -392,6 +410,33 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
   hipError_t e = rha::launch_bwd_bf16(b, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
+}
+
+}  // namespace
+
+size_t rha_hybrid_bwd_workspace_size(const rha_problem* p) {
+  if (p == nullptr || check_problem(p, false) != RHA_OK) return 0;
+  return bwd_workspace_bytes(p, false);
+}
+
+rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                          const float* z, const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                          float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return hybrid_bwd(p, q, k, v, S, z, nullptr, nullptr, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                    stream, false);
+}
+
+size_t rha_hybrid_bwd_bidir_workspace_size(const rha_problem* p) {
+  if (p == nullptr || check_problem(p, false) != RHA_OK) return 0;
+  return bwd_workspace_bytes(p, true);
+}
+
+rha_status rha_hybrid_bwd_bidir(const rha_problem* p, const void* q, const void* k, const void* v,
+                                const float* S_past, const float* z_past, const float* S_future,
+                                const float* z_future, const void* out, const float* lse, const void* dout, float* dq,
+                                float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return hybrid_bwd(p, q, k, v, S_past, z_past, S_future, z_future, out, lse, dout, dq, dk, dv, workspace,
+                    workspace_bytes, stream, true);
 }
 
 static_assert(RHA_SPARSE_QTILE == rha::kQb2RowsPerTile && RHA_SPARSE_KTILE == 64 &&

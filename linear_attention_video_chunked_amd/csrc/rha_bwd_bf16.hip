@@ -28,6 +28,8 @@
 //                        queries on the lanes, then dQ^T += K^T dS^T; then the
 //                        linear term of those queries (S_c, z_c)
 // Each of dq, dk, dv is written once, window and linear term together.
+// The bidirectional hybrid uses the same kernels with a symmetric window and
+// the past and future states (and their gradients) summed in float32.
 // Operand layouts are those of the forward kernels: a row-major LDS tile
 // (16-byte granules XOR-swizzled) is read by rows (ds_read_b128) or, for a
 // transposed operand, by the transpose read ds_read_b64_tr_b16, which hands
@@ -83,12 +85,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 // ---- the linear term: rows times a d x d state M (float32, row-major),
 // staged in LDS as bf16 rows e = M[e][:] (mr) and, if TRANS, rows n = M[:][n]
 // (mt); every thread of the workgroup takes part.
+// With M2 set, the staged matrix is M + M2, summed in float32 (the
+// bidirectional pass's past and future parts).
 template <bool TRANS>
-__device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt, const float* M, int tid) {
+__device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt, const float* M, const float* M2,
+                                            int tid) {
   for (int u = tid; u < BD * BD / 8; u += TB) {
     const int e = u / (BD / 8), g = u % (BD / 8);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
-    const f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
+    f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    if (M2 != nullptr) {
+      a += *reinterpret_cast<const f32x4*>(M2 + (int64_t)e * BD + g * 8);
+      c4 += *reinterpret_cast<const f32x4*>(M2 + (int64_t)e * BD + g * 8 + 4);
+    }
     put_granule(mr, e, g, u32x4{pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(c4[0], c4[1]), pack_bf16(c4[2], c4[3])});
     if constexpr (TRANS) {
       const float vals[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
@@ -105,11 +114,15 @@ __device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt
 // about 2^-16 relative): hi rows into mr, lo rows 0..63 into lo0 and 64..127
 // into lo1 (64 rows each).
 __device__ __forceinline__ void stage_state_split(unsigned char* mr, unsigned char* lo0, unsigned char* lo1,
-                                                  const float* M, int tid) {
+                                                  const float* M, const float* M2, int tid) {
   for (int u = tid; u < BD * BD / 8; u += TB) {
     const int e = u / (BD / 8), g = u % (BD / 8);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
-    const f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
+    f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
+    if (M2 != nullptr) {
+      a += *reinterpret_cast<const f32x4*>(M2 + (int64_t)e * BD + g * 8);
+      c4 += *reinterpret_cast<const f32x4*>(M2 + (int64_t)e * BD + g * 8 + 4);
+    }
     const float x[8] = {a[0], a[1], a[2], a[3], c4[0], c4[1], c4[2], c4[3]};
     u32x4 hi, lo;
 #pragma unroll
@@ -175,9 +188,11 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
 
   // query blocks of the chunks whose window holds chunk j (j .. j + w - 1),
   // 32 rows each, numbered qi = (c - j) * nqb + block
+  // (bidirectional: chunks j - w + 1 .. j + w - 1)
+  const int c_lo = p.bidir ? max(0, j - p.w + 1) : j;
   const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
-  const int nblk = (c_hi - j + 1) * nqb;
+  const int nblk = max(0, c_hi - c_lo + 1) * nqb;
   // Query blocks reach LDS through buffer loads that write LDS directly, two
   // blocks ahead (block x in buffer x % 4).  A 32-row tile is 8 loads of 4
   // rows (64 lanes x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   }
   auto issue = [&](int qi) __attribute__((always_inline)) {
     const int bo = qi & 3;
-    const int cq = j + qi / nqb, blk = qi - (qi / nqb) * nqb;
+    const int cq = c_lo + qi / nqb, blk = qi - (qi / nqb) * nqb;
     const int64_t row0 = (int64_t)cq * p.C + RB * blk;
     const int nq = min(RB, p.C - RB * blk);
     const int nbytes = (nq - 1) * st2 + BD * 2;
@@ -383,8 +398,12 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   // lane = key; element i of block nb = feature 32 nb + out_row(i)
   float* dvr = p.dv + (bh * L + key0 + l32) * BD;
   float* dkr = p.dk + (bh * L + key0 + l32) * BD;
-  if (j < p.N - p.w) {  // the chunk is in the state of chunks j + w .. N-1
-    stage_state<true>(um, ut, p.dS + ((int64_t)bh * p.N + j) * BD * BD, tid);
+  // the chunk is in the state of chunks j + w .. N-1 (and, bidirectional, in
+  // the future state of chunks 0 .. j - max(w, 1))
+  const bool lin = j < p.N - p.w || (p.bidir && j >= max(p.w, 1));
+  if (lin) {
+    const int64_t slot = (int64_t)bh * p.N + j;
+    stage_state<true>(um, ut, p.dS + slot * BD * BD, p.bidir ? p.dS2 + slot * BD * BD : nullptr, tid);
     __syncthreads();
     f32x16 o1[4], o2[4];
 #pragma unroll
@@ -401,12 +420,14 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     if (l32 < nk) {
       const bf16_t* kt = kb + (key0 + l32) * p.st;  // phi' argument
       const float* dz = p.dz + ((int64_t)bh * p.N + j) * BD;
+      const float* dz2 = p.bidir ? p.dz2 + ((int64_t)bh * p.N + j) * BD : nullptr;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int f = 32 * nb + 8 * rr + 4 * hh;
-          const f32x4 zz = *reinterpret_cast<const f32x4*>(dz + f);
+          f32x4 zz = *reinterpret_cast<const f32x4*>(dz + f);
+          if (dz2 != nullptr) zz += *reinterpret_cast<const f32x4*>(dz2 + f);
           float dphi[4];
           dphi4(kt, f, dphi);
           f32x4 a, k4;
@@ -475,7 +496,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   for (int nb = 0; nb < 4; ++nb) dq[nb] = f32x16{};
 
   const int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
-  const int64_t kend = p.w > 0 ? (int64_t)(c + 1) * p.C : 0;
+  const int64_t kend = p.w > 0 ? (int64_t)(p.bidir ? min(p.N, c + p.w) : c + 1) * p.C : 0;
   const int nblk = (int)((kend - kbeg + RB - 1) / RB);
   // 32-key blocks of K and V reach LDS through buffer loads that write LDS
   // directly, one block ahead (two buffers), as in bwd_dkdv_kernel; keys
@@ -553,18 +574,22 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   if (bi < nblk) block(bi, B0{});
   __syncthreads();  // the epilogue reuses the K/V buffers
   float* dqr = p.dq + (bh * L + row0 + l32) * BD;
-  if (c >= p.w) {  // the chunk has a state (every chunk for w = 0)
+  // the chunk has a state (every chunk for w = 0; bidirectional, also a
+  // future one while chunk c + max(w, 1) exists)
+  if (c >= p.w || (p.bidir && c + max(p.w, 1) <= p.N - 1)) {
     // S_c and the rows dout_i / D_i each as two bf16 parts, the three
     // products that matter (hi hi, hi lo, lo hi) on the matrix cores: with
     // one bf16 rounding of each operand the sum over features, which cancels
     // strongly, loses about 5e-3 relative, the same size as the state chunks'
     // whole query gradient error budget; split, the term is exact to float32
     // level.  The low part of S goes into the K/V staging buffers, free now.
-    stage_state_split(sm, ks_t[0], vs_t[0], p.S + ((int64_t)bh * p.N + c) * BD * BD, tid);
+    const int64_t slot = (int64_t)bh * p.N + c;
+    stage_state_split(sm, ks_t[0], vs_t[0], p.S + slot * BD * BD, p.bidir ? p.S2 + slot * BD * BD : nullptr, tid);
     __syncthreads();
     const float rs = qok ? p.rsc[bh * L + row0 + l32] : 0.f;  // 1 / D_i
     const bf16_t* qt = qb + (row0 + l32) * p.st;                // phi' argument
     const float* zc = p.z + ((int64_t)bh * p.N + c) * BD;
+    const float* zc2 = p.bidir ? p.z2 + ((int64_t)bh * p.N + c) * BD : nullptr;
     const float dD = qok ? p.zw[bh * L + row0 + l32] : 0.f;     // -delta_i / D_i
     // one 32-feature block at a time (16 more accumulators, not 64: the
     // kernel keeps two waves per SIMD)
@@ -591,7 +616,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int f = 32 * nb + 8 * rr + 4 * hh;
-          const f32x4 zz = *reinterpret_cast<const f32x4*>(zc + f);
+          f32x4 zz = *reinterpret_cast<const f32x4*>(zc + f);
+          if (zc2 != nullptr) zz += *reinterpret_cast<const f32x4*>(zc2 + f);
           float dphi[4];
           dphi4(qt, f, dphi);
           f32x4 a;
@@ -650,11 +676,22 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
     c.vscale = p.rsc;
     c.zweight = p.zw;
     c.scale_bh = L;
+    const int lag_f = max(p.w, 1);  // bidirectional: the future part starts at chunk c + max(w, 1)
+    if (p.bidir) {  // and dS_c, dz_c of every chunk into future slot c + max(w, 1)
+      c.S2 = p.dS2;
+      c.z2 = p.dz2;
+      c.slot_offset2 = lag_f;
+    }
     e = launch_chunk_state_bf16(c, BD, s);
     if (e != hipSuccess) return e;
     PrefixParams pr{p.dS, p.dz, (int)BH, p.N, p.w, BD, 1};
     e = launch_prefix(pr, s);
     if (e != hipSuccess) return e;
+    if (p.bidir) {  // future slot j <- sum over slots max(w, 1) .. j
+      PrefixParams pf{p.dS2, p.dz2, (int)BH, p.N, lag_f, BD, 0};
+      e = launch_prefix(pf, s);
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);

@@ -162,6 +162,15 @@ struct BwdParams {
   float* rsc;
   float* zw;
   float* lse2;  // lse * log2(e) per row
+  // bidirectional hybrid (bidir != 0): S, z hold the past states and S2, z2
+  // the future ones; dS, dz receive the past part of the state gradients
+  // (suffix sums with lag w) and dS2, dz2 the future part (prefix sums with
+  // lag max(w, 1)); the window is symmetric
+  const float* S2;
+  const float* z2;
+  float* dS2;
+  float* dz2;
+  int bidir;
   float* dS;
   float* dz;
   int64_t sb, sh, st;  // element strides of q, k, v, out, dout

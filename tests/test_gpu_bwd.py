@@ -152,3 +152,81 @@ def test_backward_guard_bands_through_abi(name):
     assert (wbig[:wpad] == 0xA5).all() and (wbig[wpad + nbytes:] == 0xA5).all(), "workspace guard band written"
     for vw, r, nm in zip(views, ref, ("dq", "dk", "dv")):
         assert torch.equal(vw.view(r.shape), r), f"{nm} differs from the binding's call"
+
+
+# ---------------------------------------------------------------- bidirectional
+# rha_hybrid_bwd_bidir against the oracle's bidirectional chain rule (pinned to
+# finite differences of the bidirectional forward and to torch autograd).
+
+def _run_bidir(wl, q, k, v, dout):
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    states = rha.state_scan_bidir(kd, vd, wl.C, wl.w)
+    out, lse = rha.hybrid_fwd_bidir(qd, kd, vd, states, wl.C, wl.w, return_lse=True)
+    grads = rha.hybrid_bwd_bidir(qd, kd, vd, states, out, lse, gd, wl.C, wl.w)
+    torch.cuda.synchronize()
+    return grads
+
+
+# name: (B, H, C, N, w, qscale, kscale)
+BIDIR_CASES = {
+    "C200_N5_w2": (1, 2, 200, 5, 2, 1.0, 0.5),
+    "C300_N4_w1": (1, 2, 300, 4, 1, 1.0, 1.0),
+    "C100_N6_w3_q4": (1, 1, 100, 6, 3, 4.0, 0.5),
+    "C130_N4_w0": (1, 2, 130, 4, 0, 1.0, 1.0),
+    "C64_N5_w9": (1, 2, 64, 5, 9, 2.0, 1.0),
+    "C280_N5_w2_B2": (2, 1, 280, 5, 2, 1.0, 0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BIDIR_CASES))
+def test_bidir_backward_against_oracle(name):
+    B, H, C, N, w, qs, ks = BIDIR_CASES[name]
+    wl = Workload(name, 1700 + sorted(BIDIR_CASES).index(name), B=B, H=H, d=128, C=C, N=N, w=w, dtype="bf16",
+                  qscale=qs, kscale=ks)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 5)
+    grads = _run_bidir(wl, q, k, v, dout)
+    ref = oracle.hybrid_bidir_backward_batched(to64(q), to64(k), to64(v), wl.C, wl.w, to64(dout))
+    errs = [rel_l2(to64(g), r) for g, r in zip(grads, ref)]
+    print(f"{name}: rel-L2 dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    for e, nm in zip(errs, ("dq", "dk", "dv")):
+        assert e <= TOL["bf16"], f"{nm}: rel-L2 {e:.3e}"
+    # and per chunk
+    for g, r, nm in zip(grads, ref, ("dq", "dk", "dv")):
+        g64 = to64(g)
+        for c in range(N):
+            sl = slice(c * C, (c + 1) * C)
+            e = rel_l2(g64[:, :, sl], r[:, :, sl])
+            assert e <= TOL["bf16"], f"{nm} chunk {c}: rel-L2 {e:.3e}"
+
+
+def test_bidir_backward_window_all_equals_causal_call_when_one_chunk():
+    # with a single chunk the symmetric and the causal window coincide and no
+    # chunk has a state: both backward calls compute the same softmax gradient
+    wl = Workload("bidir_one", 1750, B=1, H=2, d=128, C=300, N=1, w=3, dtype="bf16", qscale=1.0, kscale=0.5)
+    q, k, v, dout = (t.to(DEV) for t in (*gen_qkv(wl), _dout(wl, 6)))
+    S, z = rha.state_scan(k, v, wl.C, wl.w)
+    out, lse = rha.hybrid_fwd(q, k, v, S, z, wl.C, wl.w, return_lse=True)
+    states = rha.state_scan_bidir(k, v, wl.C, wl.w)
+    a = rha.hybrid_bwd_bidir(q, k, v, states, out, lse, dout, wl.C, wl.w)
+    b = rha.hybrid_bwd(q, k, v, S, z, out, lse, dout, wl.C, wl.w)
+    torch.cuda.synchronize()
+    for x, y, nm in zip(a, b, ("dq", "dk", "dv")):
+        assert torch.equal(x, y), nm
+
+
+@pytest.mark.timeout(600)
+def test_bidir_backward_wan13b_sampled_rows():
+    wl = CONFIGS["wan13b"]
+    print(f"[parity] bidir bwd wan13b: H{wl.H} C{wl.C} N{wl.N} w{wl.w}", flush=True)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 7)
+    grads = _run_bidir(wl, q, k, v, dout)
+    rows = sample_rows(wl.C, wl.N, 4 * wl.N, seed=19)
+    grouped = [GroupedRows(f"bidir bwd wan13b {nm}") for nm in ("dq", "dk", "dv")]
+    h = 5
+    ref = oracle.hybrid_bidir_backward(to64(q)[0, h], to64(k)[0, h], to64(v)[0, h], wl.C, wl.w, to64(dout)[0, h])
+    for i, (g, r) in enumerate(zip(grads, ref)):
+        grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
+    for gr in grouped:
+        gr.check(TOL["bf16"])
