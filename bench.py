@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir|anchor|bwd   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -114,6 +114,27 @@ def bwd_flops(C, N, w, d, BH):
         if w == 0 or c >= w:
             f += C * 4 * d * d
         if c <= N - 1 - w:
+            f += C * 4 * d * d
+    return f * BH
+
+
+def bidir_bwd_flops(C, N, w, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_bwd_bidir call: 10d per (query, key)
+    pair of the symmetric window, 4d^2 per query with any chunk outside its
+    window (dS and the query gradient of the linear term) and 4d^2 per token
+    in some other chunk's state (its value and key gradients)."""
+    f = 0
+    first = max(w, 1)
+    for c in range(N):
+        if w > 0:
+            lo, hi = max(0, c - w + 1), min(N - 1, c + w - 1)
+            nwin, outside = (hi - lo + 1) * C, lo > 0 or hi < N - 1
+        else:
+            nwin, outside = 0, True
+        f += C * 10 * d * nwin
+        if outside:
+            f += C * 4 * d * d
+        if c <= N - 1 - w or c >= first:  # key chunk c is in some chunk's past or future state
             f += C * 4 * d * d
     return f * BH
 
@@ -236,7 +257,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd"], default=None)
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd", "bwd_bidir"],
+                    default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -421,6 +443,22 @@ def main():
         run_only(bwd_call, args.steps)
         return
 
+    # ---- backward pass of the bidirectional hybrid at the same shape
+    out_b = torch.empty_like(q)
+    lse_b = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+
+    def bwd_bidir_setup():
+        bidir_scan()
+        rha.hybrid_fwd_bidir(q, k, v, bstates[0], wl.C, wl.w, out=out_b, lse=lse_b, stream=stream)
+
+    def bwd_bidir_call():
+        rha.hybrid_bwd_bidir(q, k, v, bstates[0], out_b, lse_b, dout, wl.C, wl.w, stream=stream)
+
+    if args.only == "bwd_bidir":
+        bwd_bidir_setup()
+        run_only(bwd_bidir_call, args.steps)
+        return
+
     # ---- the contract: W warmup steps, then exactly K timed steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -451,6 +489,9 @@ def main():
     bwd_setup()
     t_bwd, t_bwd_med, t_bwd_min = timed(bwd_call, max(args.steps // 5, 5))
     gF = bwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
+    bwd_bidir_setup()
+    t_bbwd, t_bbwd_med, t_bbwd_min = timed(bwd_bidir_call, max(args.steps // 5, 5))
+    gbF = bidir_bwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
     scan_call()  # S, z of the headline problem again (the backward set-up wrote them too)
@@ -577,6 +618,10 @@ def main():
             "bwd_min_us": t_bwd_min * 1e6,
             "bwd_TFLOPs": gF / t_bwd / 1e12,
             "bwd_mfma_frac": gF / t_bwd / 1e12 / PEAK_BF16_TFLOPS,
+            "bidir_bwd_us": t_bbwd * 1e6,
+            "bidir_bwd_median_us": t_bbwd_med * 1e6,
+            "bidir_bwd_TFLOPs": gbF / t_bbwd / 1e12,
+            "bidir_bwd_mfma_frac": gbF / t_bbwd / 1e12 / PEAK_BF16_TFLOPS,
             **more,
             "timed_wall_s": wall,
         },

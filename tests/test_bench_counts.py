@@ -66,3 +66,16 @@ def test_bwd_count_is_two_and_a_half_forward_products_plus_state_terms():
     state_rows = sum(C for c in range(N) if c >= w) * BH
     folded = sum(C for c in range(N) if c <= N - 1 - w) * BH
     assert bench.bwd_flops(C, N, w, d, BH) == pairs * 10 * d + (state_rows + folded) * 4 * d * d
+
+
+def test_bidir_bwd_count_by_brute_force():
+    # pairs of the symmetric window counted token by token; state terms for
+    # rows with any chunk outside their window and keys in some other chunk's
+    # past (c >= j + w) or future (c <= j - max(w, 1)) state
+    for C, N, w in ((3, 5, 2), (2, 4, 0), (2, 3, 5), (1, 6, 1)):
+        d, BH = 4, 2
+        L = C * N
+        pairs = sum(1 for i in range(L) for j in range(L) if w > 0 and abs(i // C - j // C) <= w - 1)
+        rows = sum(1 for i in range(L) if any(not (w > 0 and abs(i // C - c) <= w - 1) for c in range(N)))
+        keys = sum(1 for j in range(L) if any(c >= j // C + w or c <= j // C - max(w, 1) for c in range(N)))
+        assert bench.bidir_bwd_flops(C, N, w, d, BH) == BH * (pairs * 10 * d + (rows + keys) * 4 * d * d)
