@@ -747,3 +747,61 @@ def hybrid_bidir_backward_batched(q, k, v, C: int, w: int, dout):
             for arr, g in zip(res, hybrid_bidir_backward(q[b, h], k[b, h], v[b, h], C, w, dout[b, h])):
                 arr[b, h] = g
     return tuple(res)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the anchored hybrid (anchor chunks as above): the chain rule
+# of ``hybrid_backward`` on ``hybrid_anchor``.  A query chunk's softmax keys are
+# its window and the anchors not in its future; its state holds chunks
+# a .. c - w, so only non-anchor key chunks receive a state gradient.
+
+def hybrid_anchor_backward(q, k, v, C: int, w: int, a: int, dout):
+    """(dq, dk, dv) of sum(dout * hybrid_anchor(q, k, v, C, w, a)) for one head."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    L, d = q.shape
+    N = L // C
+    scale = 1.0 / math.sqrt(d)
+    S, z = state_scan_anchor(k, v, C, w, a)
+    out, den = hybrid_anchor(q, k, v, C, w, a, return_den=True)
+    dN = dout / den[:, None]
+    dD = -(dout * out).sum(axis=1) / den
+    fq, fk = phi(q), phi(k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dS, dz = np.zeros(S.shape), np.zeros(z.shape)
+    for c in range(N):
+        rows = slice(c * C, (c + 1) * C)
+        keys = anchor_keys(c, C, w, a)
+        if keys.size:
+            E = np.exp(_scores(q[rows], k[keys]))
+            dE = dN[rows] @ v[keys].T + dD[rows][:, None]
+            dv[keys] += E.T @ dN[rows]
+            ds = E * dE
+            dq[rows] += ds @ k[keys] * scale
+            dk[keys] += ds.T @ q[rows] * scale
+        gq = dN[rows] @ S[c].T + dD[rows][:, None] * z[c][None, :]
+        dq[rows] += gq * dphi(q[rows])
+        dS[c] = fq[rows].T @ dN[rows]
+        dz[c] = fq[rows].T @ dD[rows]
+    for j in range(a, N):  # anchors are never in a state
+        first = j + w  # S_c holds U_j for c >= j + w
+        if first > N - 1:
+            continue
+        dU = dS[first:].sum(axis=0)
+        du = dz[first:].sum(axis=0)
+        toks = slice(j * C, (j + 1) * C)
+        dv[toks] += fk[toks] @ dU
+        gk = v[toks] @ dU.T + du[None, :]
+        dk[toks] += gk * dphi(k[toks])
+    return dq, dk, dv
+
+
+def hybrid_anchor_backward_batched(q, k, v, C: int, w: int, a: int, dout):
+    """``hybrid_anchor_backward`` over [B, H, L, d]."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    B, H = q.shape[:2]
+    res = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+    for b in range(B):
+        for h in range(H):
+            for arr, g in zip(res, hybrid_anchor_backward(q[b, h], k[b, h], v[b, h], C, w, a, dout[b, h])):
+                arr[b, h] = g
+    return tuple(res)

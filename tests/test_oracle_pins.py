@@ -815,3 +815,120 @@ def test_bidir_backward_planted_mistake_is_caught(name, monkeypatch):
 
 def test_bidir_backward_unmutated_pins_pass():
     assert max(_bidir_backward_pin_errs()) < 1e-8
+
+
+# ------------------------------------------------------ backward pass, anchored
+# ``hybrid_anchor_backward`` is pinned to finite differences of the anchored
+# forward, torch autograd through a separately written dense anchored form,
+# the plain backward at a = 0, and block-causal SDPA autograd when every chunk
+# is an anchor.
+
+def _loss_anchor(q, k, v, C, w, a, dout):
+    return float((O.hybrid_anchor(q, k, v, C, w, a) * dout).sum())
+
+
+def _torch_dense_anchor(q, k, v, C, w, a):
+    """The anchored definition as a dense masked L x L weight matrix, in torch ops."""
+    L, d = q.shape
+    c = torch.arange(L) // C
+    cq, ck = c[:, None], c[None, :]
+    win = ((ck <= cq) & (ck >= cq - w + 1)) if w > 0 else torch.zeros((L, L), dtype=torch.bool)
+    win = win | ((ck < a) & (ck <= cq))
+    hist = (ck >= a) & (ck <= cq - w) & ~win
+    s = q @ k.T / math.sqrt(d)
+    lin = (torch.nn.functional.elu(q) + 1) @ (torch.nn.functional.elu(k) + 1).T
+    wts = torch.where(win, torch.exp(s), torch.where(hist, lin, torch.zeros_like(s)))
+    return (wts @ v) / wts.sum(dim=1, keepdim=True)
+
+
+@pytest.mark.parametrize("C,N,w,a", [(3, 5, 2, 1), (4, 4, 1, 2), (3, 5, 0, 1), (2, 6, 2, 3), (3, 4, 5, 1)])
+def test_anchor_backward_matches_finite_differences(C, N, w, a):
+    d = 5
+    q, k, v = _qkv(C * N, d, 3200 + C * N + w + a, qs=1.2)
+    dout = _rand((C * N, d), 3300 + w + a)
+    grads = O.hybrid_anchor_backward(q, k, v, C, w, a, dout)
+    rng = np.random.default_rng(3400 + C + a)
+    eps = 1e-5
+    for which, g in enumerate(grads):
+        for _ in range(3):
+            dirn = rng.standard_normal(q.shape)
+            ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+            ap[which] += eps * dirn
+            am[which] -= eps * dirn
+            fd = (_loss_anchor(*ap, C, w, a, dout) - _loss_anchor(*am, C, w, a, dout)) / (2 * eps)
+            an = float((g * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("C,N,w,a", [(4, 5, 2, 1), (3, 6, 1, 2), (3, 4, 0, 2), (2, 7, 3, 3), (5, 3, 2, 5)])
+def test_anchor_backward_matches_torch_autograd(C, N, w, a):
+    d = 8
+    q, k, v = _qkv(C * N, d, 3500 + C + w + a, qs=1.5)
+    dout = _rand((C * N, d), 3600 + N)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_anchor(tq, tk, tv, C, w, a) * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_anchor_backward(q, k, v, C, w, a, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w", [(3, 5, 2), (4, 4, 0), (2, 5, 9)])
+def test_anchor_backward_zero_anchors_is_plain_backward(C, N, w):
+    d = 6
+    q, k, v = _qkv(C * N, d, 3700 + C + w, qs=1.2)
+    dout = _rand((C * N, d), 3800 + w)
+    for ours, ref in zip(O.hybrid_anchor_backward(q, k, v, C, w, 0, dout), O.hybrid_backward(q, k, v, C, w, dout)):
+        np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("C,N,w", [(4, 5, 1), (3, 4, 0)])
+def test_anchor_backward_all_anchored_equals_block_causal_sdpa_gradient(C, N, w):
+    d = 16
+    q, k, v = _qkv(C * N, d, 3900 + C + N, qs=1.5)
+    dout = _rand((C * N, d), 4000 + C)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True)[None, None] for x in (q, k, v))
+    for t in (tq, tk, tv):
+        t.retain_grad()
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=_block_causal(C * N, C))
+    (o[0, 0] * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_anchor_backward(q, k, v, C, w, N, dout), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _anchor_backward_pin_errs():
+    C, N, w, a, d = 3, 5, 2, 1, 5
+    q, k, v = _qkv(C * N, d, 4100, qs=1.2)
+    dout = _rand((C * N, d), 4101)
+    grads = O.hybrid_anchor_backward(q, k, v, C, w, a, dout)
+    rng = np.random.default_rng(4102)
+    fd_err = 0.0
+    for which, g in enumerate(grads):
+        dirn = rng.standard_normal(q.shape)
+        ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+        ap[which] += 1e-5 * dirn
+        am[which] -= 1e-5 * dirn
+        fd = (_loss_anchor(*ap, C, w, a, dout) - _loss_anchor(*am, C, w, a, dout)) / 2e-5
+        fd_err = max(fd_err, abs(fd - float((g * dirn).sum())))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_anchor(tq, tk, tv, C, w, a) * torch.from_numpy(dout)).sum().backward()
+    ag_err = max(float(np.max(np.abs(g - t.grad.numpy()))) for g, t in zip(grads, (tq, tk, tv)))
+    return fd_err, ag_err
+
+
+ANCHOR_BACKWARD_MUTANTS = {
+    "dphi_constant_one": ("dphi", lambda orig: (lambda x: np.ones_like(np.asarray(x, np.float64)))),
+    "anchors_dropped_from_keys": ("anchor_keys",
+                                  lambda orig: (lambda c, C, w, a: orig(c, C, w, 0))),
+    "anchors_folded_into_state": ("state_scan_anchor", lambda orig: (lambda k, v, C, w, a: orig(k, v, C, w, 0))),
+    "score_sign_flip": ("_scores", lambda orig: (lambda q, k: -orig(q, k))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ANCHOR_BACKWARD_MUTANTS))
+def test_anchor_backward_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = ANCHOR_BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    assert max(_anchor_backward_pin_errs()) > 1e-6
+
+
+def test_anchor_backward_unmutated_pins_pass():
+    assert max(_anchor_backward_pin_errs()) < 1e-8
