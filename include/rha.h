@@ -86,10 +86,11 @@ typedef struct {
  * > 0, chunks 0 .. a-1 are in the softmax window of every query chunk c they
  * do not lie in the future of (chunks 0 .. min(a, c+1)-1), in addition to
  * chunks max(0, c-w+1) .. c, and the state excludes them: it sums chunks
- * a .. c-w.  rha_state_scan and rha_hybrid_fwd honour it for RHA_BF16 with
- * head_dim 128 (RHA_ERR_UNSUPPORTED otherwise, and for the streaming, pruned
- * and bidirectional calls, which need a = 0); the anchor and window keys of a
- * chunk may span at most 2048 tiles of 64 keys.
+ * a .. c-w.  rha_state_scan, rha_hybrid_fwd, rha_stream_step and
+ * rha_hybrid_bwd honour it for RHA_BF16 with head_dim 128 (RHA_ERR_UNSUPPORTED
+ * otherwise, and for the pruned and bidirectional calls, which need a = 0);
+ * the anchor and window keys of a chunk may span at most 2048 tiles of 64
+ * keys.
  */
 
 /*
@@ -167,26 +168,29 @@ rha_status rha_hybrid_fwd_sparse(const rha_problem* p, const void* q, const void
                                  float* lse, void* stream);
 
 /*
- * rha_hybrid_bwd -- gradients of rha_hybrid_fwd (the causal hybrid, no
- * anchors, no pruning) for training or distilling through it.
+ * rha_hybrid_bwd -- gradients of rha_hybrid_fwd (the causal hybrid, with or
+ * without anchor chunks; no pruning) for training or distilling through it.
  *
  * ReHyAt (abstract) and the Hybrid Forcing explainer (section 2.B) train
  * models that use the hybrid, so the gradients of its output with respect to
  * q, k and v are needed: with L = sum(dout * out), the exact derivatives of
  * the definition at the top of this header (through the softmax window, the
  * shared normaliser and the linear state, whose gradient flows back to every
- * earlier chunk that was folded in).  Matrix products use bf16 operands and
- * float32 accumulation.
+ * earlier chunk that was folded in).  With p->anchor_chunks = a > 0, the
+ * anchored definition (see rha_problem): anchor chunks are softmax keys of
+ * every chunk not before them, so their gradients gather from all later
+ * chunks, and they receive no state gradient.  Matrix products use bf16
+ * operands and float32 accumulation.
  *
- *   q, k, v, S, z : as given to rha_hybrid_fwd (read)
+ *   q, k, v, S, z : as given to rha_hybrid_fwd, with the same anchor_chunks (read)
  *   out, lse      : rha_hybrid_fwd's output and lse for them (read; lse required)
  *   dout          : [B, H, L, d], the problem's strides and dtype (read)
  *   dq, dk, dv    : [B, H, L, d] float32 contiguous (written)
  *   workspace     : device scratch of rha_hybrid_bwd_workspace_size(p) bytes,
  *                   16-byte aligned, no initialisation needed
  *
- * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16, head_dim is 128 and
- * anchor_chunks is 0; RHA_ERR_INVALID_ARG if the workspace is too small.
+ * Errors: RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16 and head_dim is 128;
+ * RHA_ERR_INVALID_ARG if the workspace is too small.
  */
 size_t rha_hybrid_bwd_workspace_size(const rha_problem* p);
 rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v,

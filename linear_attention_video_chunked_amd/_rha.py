@@ -202,9 +202,10 @@ def hybrid_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
 
 
 def hybrid_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
-               out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, C: int, w: int, stream=None):
+               out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, C: int, w: int, stream=None,
+               anchors: int = 0):
     """rha_hybrid_bwd: (dq, dk, dv) float32 [B,H,L,d] of sum(dout * out) for the
-    causal hybrid (out, lse from hybrid_fwd on the same inputs)."""
+    causal hybrid (out, lse from hybrid_fwd on the same inputs and anchors)."""
     _same_layout(q, k, v, out, dout)
     B, H, L, d = q.shape
     if L % C:
@@ -213,7 +214,7 @@ def hybrid_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tenso
     _check_f32(q, S, "S", (B, H, N, d, d))
     _check_f32(q, z, "z", (B, H, N, d))
     _check_f32(q, lse, "lse", (B, H, L))
-    prob = _problem(q, C, w, N)
+    prob = _problem(q, C, w, N, anchors)
     nbytes = int(lib().rha_hybrid_bwd_workspace_size(ctypes.byref(prob)))
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     dq = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)

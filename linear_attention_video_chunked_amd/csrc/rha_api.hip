@@ -347,7 +347,8 @@ rha_status hybrid_bwd(const rha_problem* p, const void* q, const void* k, const 
   RHA_TRY(check_problem(p, false));
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "the backward pass needs dtype RHA_BF16 and head_dim 128");
-  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "the backward pass takes no anchor chunks");
+  if (bidir && p->anchor_chunks > 0)
+    return fail(RHA_ERR_UNSUPPORTED, "the bidirectional backward pass takes no anchor chunks");
   if (empty(p, false)) return ok();
   RHA_TRY(need(q, "q"));
   RHA_TRY(need(k, "k"));
@@ -405,6 +406,7 @@ rha_status hybrid_bwd(const rha_problem* p, const void* q, const void* k, const 
   b.C = p->chunk_len;
   b.N = p->n_chunks;
   b.w = p->window;
+  b.anchors = p->anchor_chunks;
   b.scale = (float)(1.0 / std::sqrt((double)p->head_dim));
   b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   hipError_t e = rha::launch_bwd_bf16(b, reinterpret_cast<hipStream_t>(stream));

@@ -189,8 +189,9 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   // query blocks of the chunks whose window holds chunk j (j .. j + w - 1),
   // 32 rows each, numbered qi = (c - j) * nqb + block
   // (bidirectional: chunks j - w + 1 .. j + w - 1)
+  // (anchored: an anchor chunk is a softmax key of every chunk from j on)
   const int c_lo = p.bidir ? max(0, j - p.w + 1) : j;
-  const int c_hi = p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
+  const int c_hi = j < p.anchors ? p.N - 1 : p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
   const int nblk = max(0, c_hi - c_lo + 1) * nqb;
   // Query blocks reach LDS through buffer loads that write LDS directly, two
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   float* dkr = p.dk + (bh * L + key0 + l32) * BD;
   // the chunk is in the state of chunks j + w .. N-1 (and, bidirectional, in
   // the future state of chunks 0 .. j - max(w, 1))
-  const bool lin = j < p.N - p.w || (p.bidir && j >= max(p.w, 1));
+  const bool lin = (j >= p.anchors && j < p.N - p.w) || (p.bidir && j >= max(p.w, 1));
   if (lin) {
     const int64_t slot = (int64_t)bh * p.N + j;
     stage_state<true>(um, ut, p.dS + slot * BD * BD, p.bidir ? p.dS2 + slot * BD * BD : nullptr, tid);
@@ -495,9 +496,25 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) dq[nb] = f32x16{};
 
-  const int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
-  const int64_t kend = p.w > 0 ? (int64_t)(p.bidir ? min(p.N, c + p.w) : c + 1) * p.C : 0;
-  const int nblk = (int)((kend - kbeg + RB - 1) / RB);
+  int64_t kbeg = p.w > 0 ? (int64_t)max(0, c - p.w + 1) * p.C : 0;
+  int64_t kend = p.w > 0 ? (int64_t)(p.bidir ? min(p.N, c + p.w) : c + 1) * p.C : 0;
+  // Anchored: the anchor keys not in the query's future, [0, a_end), come
+  // first as a range of their own, or join the window when the two touch.
+  int64_t a_end = p.anchors > 0 ? (int64_t)min(p.anchors, c + 1) * p.C : 0;
+  if (a_end > 0 && (kend <= kbeg || kbeg <= a_end)) {  // one range [0, max(a_end, kend))
+    kend = max(kend, a_end);
+    kbeg = 0;
+    a_end = 0;
+  }
+  const int nba = (int)((a_end + RB - 1) / RB);  // blocks of the separate anchor range
+  const int nblk = nba + (int)((kend - kbeg + RB - 1) / RB);
+  // first key and key count of block bi
+  auto blk_k0 = [&](int bi) __attribute__((always_inline)) {
+    return bi < nba ? (int64_t)RB * bi : kbeg + (int64_t)RB * (bi - nba);
+  };
+  auto blk_nk = [&](int bi) __attribute__((always_inline)) {
+    return (int)min((int64_t)RB, (bi < nba ? a_end : kend) - blk_k0(bi));
+  };
   // 32-key blocks of K and V reach LDS through buffer loads that write LDS
   // directly, one block ahead (two buffers), as in bwd_dkdv_kernel; keys
   // past the window read as zero, and their probabilities are masked.
@@ -512,8 +529,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   }
   auto issue = [&](int bi, auto buf_c) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
-    const int64_t k0 = kbeg + (int64_t)RB * bi;
-    const int nk = (int)min((int64_t)RB, kend - k0);
+    const int64_t k0 = blk_k0(bi);
+    const int nk = blk_nk(bi);
     const int nbytes = (nk - 1) * st2 + BD * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
@@ -530,7 +547,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block bi are in LDS
     __syncthreads();  // every wave's; and every wave is done with block bi-1 (the other buffer)
     if (bi + 1 < nblk) issue(bi + 1, std::integral_constant<int, BUF ^ 1>{});
-    const int nk = (int)min((int64_t)RB, kend - (kbeg + (int64_t)RB * bi));
+    const int nk = blk_nk(bi);
     const unsigned char* kt = ks_t[BUF];
     const unsigned char* vt = vs_t[BUF];
     f32x16 sa = {}, pa = {};
@@ -540,7 +557,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
       pa = mfma32(row_frag(vt, 0, ks, lane), gr[ks], pa);  // dP^T = V dO^T
     }
     uint32_t dd[8];
-    // keys past the window (only in the window's last block) get P = 0
+    // keys past the end of their range (only in a range's last block) get P = 0
     auto softmax_grad = [&](auto masked_c) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
@@ -576,7 +593,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   float* dqr = p.dq + (bh * L + row0 + l32) * BD;
   // the chunk has a state (every chunk for w = 0; bidirectional, also a
   // future one while chunk c + max(w, 1) exists)
-  if (c >= p.w || (p.bidir && c + max(p.w, 1) <= p.N - 1)) {
+  // (anchored: the history is chunks a .. c - w)
+  if (c - p.w >= p.anchors || (p.bidir && c + max(p.w, 1) <= p.N - 1)) {
     // S_c and the rows dout_i / D_i each as two bf16 parts, the three
     // products that matter (hi hi, hi lo, lo hi) on the matrix cores: with
     // one bf16 rounding of each operand the sum over features, which cancels

@@ -171,6 +171,9 @@ struct BwdParams {
   float* dS2;
   float* dz2;
   int bidir;
+  // anchor chunks (causal only): chunks 0 .. anchors-1 are softmax keys of
+  // every chunk not before them and are in no state
+  int anchors;
   float* dS;
   float* dz;
   int64_t sb, sh, st;  // element strides of q, k, v, out, dout

@@ -245,8 +245,17 @@ def test_anchor_checks(L):
 def test_backward_checks(L):
     args = [P] * 12
     assert L.rha_hybrid_bwd(ctypes.byref(_prob(dtype=_rha.RHA_F32, stride_t=128)), *args, 1 << 30, None) == 2
-    assert L.rha_hybrid_bwd(ctypes.byref(_prob(anchor_chunks=1)), *args, 1 << 30, None) == 2
+    # the bidirectional backward takes no anchor chunks (the causal one does)
+    bargs = [P] * 14
+    assert L.rha_hybrid_bwd_bidir(ctypes.byref(_prob(anchor_chunks=1)), *bargs, 1 << 30, None) == 2
+    assert L.rha_hybrid_bwd_bidir(ctypes.byref(_prob(dtype=_rha.RHA_F32, stride_t=128)), *bargs, 1 << 30, None) == 2
     ok = _prob()
+    need_b = L.rha_hybrid_bwd_bidir_workspace_size(ctypes.byref(ok))
+    assert need_b > L.rha_hybrid_bwd_workspace_size(ctypes.byref(ok))  # two sets of state gradients
+    assert L.rha_hybrid_bwd_bidir(ctypes.byref(ok), *bargs, need_b - 1, None) == 1
+    assert "workspace" in L.rha_last_error().decode()
+    assert L.rha_hybrid_bwd_bidir(ctypes.byref(ok), *bargs[:5], None, *bargs[6:], need_b, None) == 1  # S_future
+    assert "S_future" in L.rha_last_error().decode()
     need = L.rha_hybrid_bwd_workspace_size(ctypes.byref(ok))
     assert need > 0
     assert L.rha_hybrid_bwd(ctypes.byref(ok), *args, need - 1, None) == 1

@@ -230,3 +230,73 @@ def test_bidir_backward_wan13b_sampled_rows():
         grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
     for gr in grouped:
         gr.check(TOL["bf16"])
+
+
+# ---------------------------------------------------------------- anchored
+# rha_hybrid_bwd with anchor (sink) chunks against the oracle's anchored chain
+# rule (pinned to finite differences of the anchored forward and torch autograd).
+
+def _run_anchor(wl, a, q, k, v, dout):
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    S, z = rha.state_scan(kd, vd, wl.C, wl.w, anchors=a)
+    out, lse = rha.hybrid_fwd(qd, kd, vd, S, z, wl.C, wl.w, return_lse=True, anchors=a)
+    grads = rha.hybrid_bwd(qd, kd, vd, S, z, out, lse, gd, wl.C, wl.w, anchors=a)
+    torch.cuda.synchronize()
+    return grads
+
+
+# name: (B, H, C, N, w, a, qscale, kscale)
+ANCHOR_CASES = {
+    "C200_N5_w2_a1": (1, 2, 200, 5, 2, 1, 1.0, 0.5),
+    "C130_N5_w1_a2": (1, 2, 130, 5, 1, 2, 1.0, 1.0),
+    "C100_N6_w0_a1": (1, 1, 100, 6, 0, 1, 1.0, 0.5),
+    "C64_N5_w3_a3": (1, 2, 64, 5, 3, 3, 2.0, 1.0),
+    "C280_N4_w2_a1_q4": (2, 1, 280, 4, 2, 1, 4.0, 0.5),
+    "C150_N3_w1_a5": (1, 2, 150, 3, 1, 5, 1.0, 1.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ANCHOR_CASES))
+def test_anchor_backward_against_oracle(name):
+    B, H, C, N, w, a, qs, ks = ANCHOR_CASES[name]
+    wl = Workload(name, 1800 + sorted(ANCHOR_CASES).index(name), B=B, H=H, d=128, C=C, N=N, w=w, dtype="bf16",
+                  qscale=qs, kscale=ks)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 8)
+    grads = _run_anchor(wl, a, q, k, v, dout)
+    ref = oracle.hybrid_anchor_backward_batched(to64(q), to64(k), to64(v), wl.C, wl.w, a, to64(dout))
+    for g, r, nm in zip(grads, ref, ("dq", "dk", "dv")):
+        g64 = to64(g)
+        e = rel_l2(g64, r)
+        print(f"{name} {nm}: rel-L2 {e:.2e}")
+        assert e <= TOL["bf16"], f"{nm}: rel-L2 {e:.3e}"
+        for c in range(N):
+            sl = slice(c * C, (c + 1) * C)
+            ec = rel_l2(g64[:, :, sl], r[:, :, sl])
+            assert ec <= TOL["bf16"], f"{nm} chunk {c}: rel-L2 {ec:.3e}"
+
+
+def test_anchor_backward_zero_anchors_equals_plain_call():
+    wl = Workload("anchor0", 1850, B=1, H=2, d=128, C=200, N=4, w=2, dtype="bf16", qscale=1.0, kscale=0.5)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 9)
+    for x, y, nm in zip(_run_anchor(wl, 0, q, k, v, dout), _run(wl, q, k, v, dout), ("dq", "dk", "dv")):
+        assert torch.equal(x, y), nm
+
+
+@pytest.mark.timeout(600)
+def test_anchor_backward_wan13b_sampled_rows():
+    wl = CONFIGS["wan13b"]
+    a = 1
+    print(f"[parity] anchored bwd wan13b: H{wl.H} C{wl.C} N{wl.N} w{wl.w} a{a}", flush=True)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 10)
+    grads = _run_anchor(wl, a, q, k, v, dout)
+    rows = sample_rows(wl.C, wl.N, 4 * wl.N, seed=23)
+    grouped = [GroupedRows(f"anchored bwd wan13b {nm}") for nm in ("dq", "dk", "dv")]
+    h = 9
+    ref = oracle.hybrid_anchor_backward(to64(q)[0, h], to64(k)[0, h], to64(v)[0, h], wl.C, wl.w, a, to64(dout)[0, h])
+    for i, (g, r) in enumerate(zip(grads, ref)):
+        grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
+    for gr in grouped:
+        gr.check(TOL["bf16"])
