@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir|bwd_anchor   run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -139,6 +139,23 @@ def bidir_bwd_flops(C, N, w, d, BH):
     return f * BH
 
 
+def anchor_bwd_flops(C, N, w, a, d, BH):
+    """Algorithmic FLOPs of one rha_hybrid_bwd call with a anchor chunks: 10d
+    per (query, key) pair over the window and the anchors not in the query's
+    future, 4d^2 per query with a history (chunks a .. c-w) and 4d^2 per token
+    of a non-anchor chunk in some history."""
+    f = 0
+    for c in range(N):
+        lo = max(0, c - w + 1) if w > 0 else c + 1
+        keys = set(range(lo, c + 1)) | set(range(0, min(a, c + 1)))
+        f += C * 10 * d * len(keys) * C
+        if c - w >= a:
+            f += C * 4 * d * d
+        if a <= c <= N - 1 - w:
+            f += C * 4 * d * d
+    return f * BH
+
+
 def stream_step_flops(C, w, d, BH):
     """Algorithmic FLOPs of one rha_stream_step with a full window: the new
     chunk's queries against w cached chunks (4d per pair) and the state (2d^2
@@ -257,7 +274,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd", "bwd_bidir"],
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd", "bwd_bidir",
+                                       "bwd_anchor"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -459,6 +477,22 @@ def main():
         run_only(bwd_bidir_call, args.steps)
         return
 
+    # ---- backward pass with the first frame as an anchor chunk, same shape
+    out_a = torch.empty_like(q)
+    lse_a = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+
+    def bwd_anchor_setup():
+        anchor_setup()
+        rha.hybrid_fwd(q, k, v, SA, zA, wl.C, wl.w, out=out_a, lse=lse_a, stream=stream, anchors=1)
+
+    def bwd_anchor_call():
+        rha.hybrid_bwd(q, k, v, SA, zA, out_a, lse_a, dout, wl.C, wl.w, stream=stream, anchors=1)
+
+    if args.only == "bwd_anchor":
+        bwd_anchor_setup()
+        run_only(bwd_anchor_call, args.steps)
+        return
+
     # ---- the contract: W warmup steps, then exactly K timed steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -492,6 +526,9 @@ def main():
     bwd_bidir_setup()
     t_bbwd, t_bbwd_med, t_bbwd_min = timed(bwd_bidir_call, max(args.steps // 5, 5))
     gbF = bidir_bwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
+    bwd_anchor_setup()
+    t_abwd, t_abwd_med, _ = timed(bwd_anchor_call, max(args.steps // 5, 5))
+    gaF = anchor_bwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
     scan_call()  # S, z of the headline problem again (the backward set-up wrote them too)
@@ -622,6 +659,10 @@ def main():
             "bidir_bwd_median_us": t_bbwd_med * 1e6,
             "bidir_bwd_TFLOPs": gbF / t_bbwd / 1e12,
             "bidir_bwd_mfma_frac": gbF / t_bbwd / 1e12 / PEAK_BF16_TFLOPS,
+            "anchor1_bwd_us": t_abwd * 1e6,
+            "anchor1_bwd_median_us": t_abwd_med * 1e6,
+            "anchor1_bwd_TFLOPs": gaF / t_abwd / 1e12,
+            "anchor1_bwd_mfma_frac": gaF / t_abwd / 1e12 / PEAK_BF16_TFLOPS,
             **more,
             "timed_wall_s": wall,
         },

@@ -79,3 +79,15 @@ def test_bidir_bwd_count_by_brute_force():
         rows = sum(1 for i in range(L) if any(not (w > 0 and abs(i // C - c) <= w - 1) for c in range(N)))
         keys = sum(1 for j in range(L) if any(c >= j // C + w or c <= j // C - max(w, 1) for c in range(N)))
         assert bench.bidir_bwd_flops(C, N, w, d, BH) == BH * (pairs * 10 * d + (rows + keys) * 4 * d * d)
+
+
+def test_anchor_bwd_count_limits_and_brute_force():
+    C, N, w, d, BH = 3, 6, 2, 4, 2
+    assert bench.anchor_bwd_flops(C, N, w, 0, d, BH) == bench.bwd_flops(C, N, w, d, BH)
+    for a in (1, 2, 7):
+        L = C * N
+        keys = lambda i, j: (j // C <= i // C) and (j // C >= i // C - w + 1 or j // C < a)
+        pairs = sum(1 for i in range(L) for j in range(L) if keys(i, j))
+        rows = sum(1 for i in range(L) if i // C - w >= a)
+        folded = sum(1 for j in range(L) if a <= j // C <= N - 1 - w)
+        assert bench.anchor_bwd_flops(C, N, w, a, d, BH) == BH * (pairs * 10 * d + (rows + folded) * 4 * d * d)
