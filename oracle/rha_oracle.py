@@ -805,3 +805,70 @@ def hybrid_anchor_backward_batched(q, k, v, C: int, w: int, a: int, dout):
             for arr, g in zip(res, hybrid_anchor_backward(q[b, h], k[b, h], v[b, h], C, w, a, dout[b, h])):
                 arr[b, h] = g
     return tuple(res)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the pruned window (the block-sparse definition above): the
+# chain rule of ``hybrid_backward`` with the pruned (query block, key block)
+# pairs' weights held at zero.  A row left with no weight at all (every block
+# pruned and no history) has out = 0 whatever the inputs, so its gradients are
+# zero.
+
+def hybrid_block_sparse_backward(q, k, v, C: int, w: int, mask, dout, qtile: int = 256, ktile: int = 64):
+    """(dq, dk, dv) of sum(dout * hybrid_block_sparse(q, k, v, C, w, mask)) for one head."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    mask = np.asarray(mask)
+    L, d = q.shape
+    N = L // C
+    scale = 1.0 / math.sqrt(d)
+    S, z = state_scan(k, v, C, w)
+    out, den = hybrid_block_sparse(q, k, v, C, w, mask, qtile, ktile, return_den=True)
+    live = den > 0
+    safe = np.where(live, den, 1.0)
+    dN = np.where(live[:, None], dout / safe[:, None], 0.0)
+    dD = np.where(live, -(dout * out).sum(axis=1) / safe, 0.0)
+    fq, fk = phi(q), phi(k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dS, dz = np.zeros(S.shape), np.zeros(z.shape)
+    for c in range(N):
+        lo, hi = window_range(c, w)
+        for i in range(-(-C // qtile)):
+            rows = slice(c * C + i * qtile, c * C + min(C, (i + 1) * qtile))
+            if lo <= hi:
+                keys = slice(lo * C, (hi + 1) * C)
+                keep = _window_keep(mask[c, i], (hi + 1 - lo) * C, ktile)
+                E = np.exp(_scores(q[rows], k[keys])) * keep[None, :]
+                dE = dN[rows] @ v[keys].T + dD[rows][:, None]
+                dv[keys] += E.T @ dN[rows]
+                ds = E * dE
+                dq[rows] += ds @ k[keys] * scale
+                dk[keys] += ds.T @ q[rows] * scale
+            gq = dN[rows] @ S[c].T + dD[rows][:, None] * z[c][None, :]
+            dq[rows] += gq * dphi(q[rows])
+            dS[c] += fq[rows].T @ dN[rows]
+            dz[c] += fq[rows].T @ dD[rows]
+    for j in range(N):
+        first = j + w
+        if first > N - 1:
+            continue
+        dU = dS[first:].sum(axis=0)
+        du = dz[first:].sum(axis=0)
+        toks = slice(j * C, (j + 1) * C)
+        dv[toks] += fk[toks] @ dU
+        gk = v[toks] @ dU.T + du[None, :]
+        dk[toks] += gk * dphi(k[toks])
+    return dq, dk, dv
+
+
+def hybrid_block_sparse_backward_batched(q, k, v, C: int, w: int, mask, dout, **tiles):
+    """``hybrid_block_sparse_backward`` over [B, H, L, d] with mask [B, H, N, nqt, nkt]."""
+    q, k, v, dout = (np.asarray(t, dtype=np.float64) for t in (q, k, v, dout))
+    mask = np.asarray(mask)
+    B, H = q.shape[:2]
+    res = [np.empty_like(q), np.empty_like(k), np.empty_like(v)]
+    for b in range(B):
+        for h in range(H):
+            g = hybrid_block_sparse_backward(q[b, h], k[b, h], v[b, h], C, w, mask[b, h], dout[b, h], **tiles)
+            for arr, x in zip(res, g):
+                arr[b, h] = x
+    return tuple(res)

@@ -932,3 +932,126 @@ def test_anchor_backward_planted_mistake_is_caught(name, monkeypatch):
 
 def test_anchor_backward_unmutated_pins_pass():
     assert max(_anchor_backward_pin_errs()) < 1e-8
+
+
+# -------------------------------------------------- backward pass, pruned window
+# ``hybrid_block_sparse_backward`` is pinned to finite differences of the
+# pruned forward, torch autograd through a separately written dense masked
+# form, the plain backward when every block is kept, and zero gradients for
+# rows left with no weight.
+
+def _loss_sparse(q, k, v, C, w, m, qt, kt, dout):
+    return float((O.hybrid_block_sparse(q, k, v, C, w, m, qt, kt) * dout).sum())
+
+
+def _torch_dense_sparse(q, k, v, C, w, m, qt, kt):
+    """The pruned definition as a dense L x L weight matrix, in torch ops."""
+    L, d = q.shape
+    idx = torch.arange(L)
+    c = idx // C
+    cq, ck = c[:, None], c[None, :]
+    lo = torch.clamp(cq - w + 1, min=0)
+    win = ((ck <= cq) & (ck >= lo)) if w > 0 else torch.zeros((L, L), dtype=torch.bool)
+    qblk = ((idx - c * C) // qt)[:, None].expand(L, L)
+    kblk = torch.clamp(idx[None, :] - lo * C, min=0) // kt
+    mt = torch.from_numpy(np.asarray(m)).bool()
+    keep = mt[cq.expand(L, L), qblk, torch.clamp(kblk, max=mt.shape[2] - 1)]
+    hist = ck <= cq - w
+    s = q @ k.T / math.sqrt(d)
+    lin = (torch.nn.functional.elu(q) + 1) @ (torch.nn.functional.elu(k) + 1).T
+    wts = torch.where(win & keep, torch.exp(s), torch.where(hist, lin, torch.zeros_like(s)))
+    den = wts.sum(dim=1, keepdim=True)
+    out = (wts @ v) / torch.where(den > 0, den, torch.ones_like(den))
+    return torch.where(den > 0, out, torch.zeros_like(out))
+
+
+SPARSE_BWD = [(3, 4, 2, 2, 2), (5, 3, 1, 3, 5), (4, 4, 3, 2, 3), (4, 5, 2, 4, 4)]
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", SPARSE_BWD)
+def test_sparse_backward_matches_finite_differences(C, N, w, qt, kt):
+    d = 5
+    q, k, v = _qkv(C * N, d, 4200 + C * N + w, qs=1.2)
+    m = _mask(C, N, w, qt, kt, 4300 + C + w, density=0.6)
+    dout = _rand((C * N, d), 4400 + w)
+    grads = O.hybrid_block_sparse_backward(q, k, v, C, w, m, dout, qt, kt)
+    rng = np.random.default_rng(4500 + C)
+    eps = 1e-5
+    for which, g in enumerate(grads):
+        for _ in range(3):
+            dirn = rng.standard_normal(q.shape)
+            ap, am = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+            ap[which] += eps * dirn
+            am[which] -= eps * dirn
+            fd = (_loss_sparse(*ap, C, w, m, qt, kt, dout) - _loss_sparse(*am, C, w, m, qt, kt, dout)) / (2 * eps)
+            an = float((g * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, fd, an)
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", SPARSE_BWD)
+def test_sparse_backward_matches_torch_autograd(C, N, w, qt, kt):
+    d = 8
+    q, k, v = _qkv(C * N, d, 4600 + C + w, qs=1.5)
+    m = _mask(C, N, w, qt, kt, 4700 + C + w, density=0.5)
+    dout = _rand((C * N, d), 4800 + N)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_sparse(tq, tk, tv, C, w, m, qt, kt) * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip(O.hybrid_block_sparse_backward(q, k, v, C, w, m, dout, qt, kt), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w", [(3, 4, 2), (5, 3, 1), (4, 2, 3)])
+def test_sparse_backward_all_kept_is_plain_backward(C, N, w):
+    d = 6
+    q, k, v = _qkv(C * N, d, 4900 + C, qs=1.2)
+    ones = np.ones(O.sparse_mask_shape(C, N, w, 2, 3), np.uint8)
+    dout = _rand((C * N, d), 5000 + C)
+    for ours, ref in zip(O.hybrid_block_sparse_backward(q, k, v, C, w, ones, dout, 2, 3),
+                         O.hybrid_backward(q, k, v, C, w, dout)):
+        np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_backward_rows_without_weight_have_zero_gradient():
+    # every block pruned: chunks c < w have no weight at all (out = 0), so
+    # their queries get no gradient and nothing reaches keys through them
+    C, N, w, d = 4, 4, 2, 5
+    q, k, v = _qkv(C * N, d, 5100)
+    zeros = np.zeros(O.sparse_mask_shape(C, N, w, 2, 3), np.uint8)
+    dout = _rand((C * N, d), 5101)
+    dq, dk, dv = O.hybrid_block_sparse_backward(q, k, v, C, w, zeros, dout, 2, 3)
+    assert np.all(dq[: w * C] == 0)
+    # the rest is the gradient of the linear-only form, checked by autograd
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_sparse(tq, tk, tv, C, w, zeros, 2, 3) * torch.from_numpy(dout)).sum().backward()
+    for ours, ref in zip((dq, dk, dv), (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(ours, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _sparse_backward_pin_err():
+    C, N, w, qt, kt, d = 4, 4, 2, 2, 3, 5
+    q, k, v = _qkv(C * N, d, 5200, qs=1.2)
+    m = _mask(C, N, w, qt, kt, 5201, density=0.5)
+    dout = _rand((C * N, d), 5202)
+    grads = O.hybrid_block_sparse_backward(q, k, v, C, w, m, dout, qt, kt)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    (_torch_dense_sparse(tq, tk, tv, C, w, m, qt, kt) * torch.from_numpy(dout)).sum().backward()
+    return max(float(np.max(np.abs(g - t.grad.numpy()))) for g, t in zip(grads, (tq, tk, tv)))
+
+
+SPARSE_BACKWARD_MUTANTS = {
+    "mask_ignored": ("_window_keep", lambda orig: (lambda row, n, kt: np.ones(n, dtype=bool))),
+    "mask_one_tile_late": ("_window_keep",
+                           lambda orig: (lambda row, n, kt: np.roll(orig(row, n, kt), kt))),
+    "dphi_constant_one": ("dphi", lambda orig: (lambda x: np.ones_like(np.asarray(x, np.float64)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPARSE_BACKWARD_MUTANTS))
+def test_sparse_backward_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = SPARSE_BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    assert _sparse_backward_pin_err() > 1e-6
+
+
+def test_sparse_backward_unmutated_pin_passes():
+    assert _sparse_backward_pin_err() < 1e-8
