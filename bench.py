@@ -9,7 +9,8 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir|bwd_anchor   run just that call --steps times (for rocprofv3)
+    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir|bwd_anchor|bwd_sparse
+                          run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
 from __future__ import annotations
@@ -156,6 +157,25 @@ def anchor_bwd_flops(C, N, w, a, d, BH):
     return f * BH
 
 
+def sparse_bwd_flops(C, N, w, d, mask, qtile=256, ktile=64):
+    """Algorithmic FLOPs of one rha_hybrid_bwd_sparse call: as bwd_flops, but
+    the 10d per (query, key) pair counts only the pairs of kept blocks.
+    mask: numpy [B,H,N,nqt,nkt]."""
+    B, H = mask.shape[:2]
+    f = 0
+    for c in range(N):
+        wk = min(c + 1, w) * C if w > 0 else 0  # keys in this chunk's window
+        keys = [max(0, min(ktile, wk - ktile * j)) for j in range(mask.shape[4])]
+        for i in range(mask.shape[3]):
+            rows = min(C, qtile * (i + 1)) - qtile * i
+            f += rows * 10 * d * int((mask[:, :, c, i, :].astype(int) * keys).sum())
+        if w == 0 or c >= w:
+            f += C * 4 * d * d * B * H
+        if c <= N - 1 - w:
+            f += C * 4 * d * d * B * H
+    return f
+
+
 def stream_step_flops(C, w, d, BH):
     """Algorithmic FLOPs of one rha_stream_step with a full window: the new
     chunk's queries against w cached chunks (4d per pair) and the state (2d^2
@@ -275,7 +295,7 @@ def main():
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd", "bwd_bidir",
-                                       "bwd_anchor"],
+                                       "bwd_anchor", "bwd_sparse"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -493,6 +513,22 @@ def main():
         run_only(bwd_anchor_call, args.steps)
         return
 
+    # ---- backward pass of the pruned window (the half-kept mask above)
+    out_s = torch.empty_like(q)
+    lse_s = torch.empty((wl.B, wl.H, wl.L), dtype=torch.float32, device=dev)
+
+    def bwd_sparse_setup():
+        scan_call()
+        rha.hybrid_fwd_sparse(q, k, v, S, z, wl.C, wl.w, mask, out=out_s, lse=lse_s, stream=stream)
+
+    def bwd_sparse_call():
+        rha.hybrid_bwd_sparse(q, k, v, S, z, mask, out_s, lse_s, dout, wl.C, wl.w, stream=stream)
+
+    if args.only == "bwd_sparse":
+        bwd_sparse_setup()
+        run_only(bwd_sparse_call, args.steps)
+        return
+
     # ---- the contract: W warmup steps, then exactly K timed steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -529,6 +565,9 @@ def main():
     bwd_anchor_setup()
     t_abwd, t_abwd_med, _ = timed(bwd_anchor_call, max(args.steps // 5, 5))
     gaF = anchor_bwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
+    bwd_sparse_setup()
+    t_sbwd, t_sbwd_med, _ = timed(bwd_sparse_call, max(args.steps // 5, 5))
+    gsF = sparse_bwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
     aF = anchor_fwd_flops(wl.C, wl.N, wl.w, 1, wl.d, BH)
     spF = sparse_fwd_flops(wl.C, wl.N, wl.w, wl.d, mask_cpu.numpy())
     scan_call()  # S, z of the headline problem again (the backward set-up wrote them too)
@@ -663,6 +702,10 @@ def main():
             "anchor1_bwd_median_us": t_abwd_med * 1e6,
             "anchor1_bwd_TFLOPs": gaF / t_abwd / 1e12,
             "anchor1_bwd_mfma_frac": gaF / t_abwd / 1e12 / PEAK_BF16_TFLOPS,
+            "sparse_half_bwd_us": t_sbwd * 1e6,
+            "sparse_half_bwd_median_us": t_sbwd_med * 1e6,
+            "sparse_half_bwd_TFLOPs": gsF / t_sbwd / 1e12,
+            "sparse_half_bwd_mfma_frac": gsF / t_sbwd / 1e12 / PEAK_BF16_TFLOPS,
             **more,
             "timed_wall_s": wall,
         },

@@ -199,6 +199,35 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
                           size_t workspace_bytes, void* stream);
 
 /*
+ * rha_hybrid_bwd_sparse -- gradients of rha_hybrid_fwd_sparse (the causal
+ * hybrid with pruned blocks of the window).
+ *
+ * Hybrid Forcing explainer, sections 2.A (the block-sparse window) and 2.B
+ * (the model is trained through it): with L = sum(dout * out), the exact
+ * derivatives of the pruned definition, in which a pruned (query block, key
+ * block) pair has weight zero; its pairs therefore carry no gradient, and the
+ * linear state is as in rha_hybrid_bwd.  A query row left with no weight at
+ * all (lse = -inf, out = 0) gets dq = 0 and sends no gradient to any key.
+ * With every mask entry nonzero the result equals rha_hybrid_bwd's bitwise.
+ *
+ *   q, k, v, S, z, block_mask : as given to rha_hybrid_fwd_sparse (read)
+ *   out, lse                  : its output and lse (read; lse required)
+ *   dout, dq, dk, dv          : as for rha_hybrid_bwd
+ *   workspace                 : device scratch of rha_hybrid_bwd_workspace_size(p)
+ *                               bytes, 16-byte aligned, no initialisation needed
+ *
+ * Errors: as rha_hybrid_fwd_sparse (RHA_ERR_UNSUPPORTED unless dtype is
+ * RHA_BF16, head_dim is 128, anchor_chunks is 0 and the window spans at most
+ * RHA_SPARSE_MAX_KTILES key blocks); RHA_ERR_INVALID_ARG if the workspace is
+ * too small.  With window 0 the call is rha_hybrid_bwd (block_mask may be NULL).
+ */
+rha_status rha_hybrid_bwd_sparse(const rha_problem* p, const void* q, const void* k, const void* v,
+                                 const float* S, const float* z, const uint8_t* block_mask,
+                                 const void* out, const float* lse, const void* dout, float* dq,
+                                 float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * rha_hybrid_bwd_bidir -- gradients of rha_hybrid_fwd_bidir, for training or
  * distilling the bidirectional models that the hybrid serves (ReHyAt,
  * abstract: the hybrid replaces the attention of video diffusion

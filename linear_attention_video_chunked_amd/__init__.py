@@ -12,6 +12,7 @@ Functions mirror the C ABI in ``include/rha.h``:
 * ``hybrid_fwd_sparse(q, k, v, S, z, C, w, m)``  the same with pruned window blocks
 * ``state_scan_bidir`` / ``hybrid_fwd_bidir``     symmetric window, past + future states
 * ``hybrid_bwd(q, k, v, S, z, out, lse, dout, C, w)`` -> dq, dk, dv (float32)
+* ``hybrid_bwd_sparse(q, k, v, S, z, m, out, lse, dout, C, w)`` the same for pruned window blocks
 * ``hybrid_bwd_bidir(q, k, v, states, out, lse, dout, C, w)`` the same for the bidirectional hybrid
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
 * ``stream_step_noalloc(...)``                    the same step with the library's own scratch
@@ -22,6 +23,7 @@ from ._rha import (
     StreamState,
     hybrid_bwd,
     hybrid_bwd_bidir,
+    hybrid_bwd_sparse,
     hybrid_fwd,
     hybrid_fwd_bidir,
     hybrid_fwd_sparse,
@@ -41,6 +43,7 @@ __all__ = [
     "StreamState",
     "hybrid_bwd",
     "hybrid_bwd_bidir",
+    "hybrid_bwd_sparse",
     "hybrid_fwd",
     "hybrid_fwd_bidir",
     "hybrid_fwd_sparse",

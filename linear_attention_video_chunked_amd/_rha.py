@@ -67,6 +67,8 @@ def lib():
     L.rha_hybrid_fwd_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_state_scan_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.rha_hybrid_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.rha_hybrid_bwd_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
     L.rha_hybrid_bwd_workspace_size.argtypes = [P]
     L.rha_hybrid_bwd_workspace_size.restype = ctypes.c_size_t
     L.rha_hybrid_fwd_bidir.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -81,7 +83,7 @@ def lib():
     L.rha_stream_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                           ctypes.c_int32, _vp, _vp, _vp]
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
-                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_hybrid_bwd_bidir", "rha_stream_step",
+                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_hybrid_bwd_sparse", "rha_hybrid_bwd_bidir", "rha_stream_step",
                  "rha_stream_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
@@ -332,6 +334,34 @@ def hybrid_fwd_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torc
     _check(lib().rha_hybrid_fwd_sparse(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                        _ptr(block_mask), _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def hybrid_bwd_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor, z: torch.Tensor,
+                      block_mask: torch.Tensor, out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                      C: int, w: int, stream=None):
+    """rha_hybrid_bwd_sparse: (dq, dk, dv) float32 [B,H,L,d] of sum(dout * out)
+    for the pruned window (out, lse from hybrid_fwd_sparse with the same mask)."""
+    _same_layout(q, k, v, out, dout)
+    B, H, L, d = q.shape
+    if L % C:
+        raise ValueError(f"sequence length {L} is not a multiple of chunk length {C}")
+    N = L // C
+    _check_f32(q, S, "S", (B, H, N, d, d))
+    _check_f32(q, z, "z", (B, H, N, d))
+    _check_f32(q, lse, "lse", (B, H, L))
+    if (tuple(block_mask.shape) != sparse_mask_shape(B, H, C, N, w) or block_mask.dtype != torch.uint8
+            or not block_mask.is_contiguous() or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be contiguous uint8 {sparse_mask_shape(B, H, C, N, w)} on q's device")
+    prob = _problem(q, C, w, N)
+    nbytes = int(lib().rha_hybrid_bwd_workspace_size(ctypes.byref(prob)))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    _check(lib().rha_hybrid_bwd_sparse(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                                       _ptr(block_mask), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
 
 
 class StreamState:

@@ -343,13 +343,14 @@ size_t bwd_workspace_bytes(const rha_problem* p, bool bidir) {
 rha_status hybrid_bwd(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
                       const float* z, const float* S2, const float* z2, const void* out, const float* lse,
                       const void* dout, float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                      void* stream, bool bidir) {
+                      void* stream, bool bidir, const uint8_t* block_mask = nullptr, int64_t nkt = 0) {
   RHA_TRY(check_problem(p, false));
   if (p->dtype != RHA_BF16 || p->head_dim != 128)
     return fail(RHA_ERR_UNSUPPORTED, "the backward pass needs dtype RHA_BF16 and head_dim 128");
   if (bidir && p->anchor_chunks > 0)
     return fail(RHA_ERR_UNSUPPORTED, "the bidirectional backward pass takes no anchor chunks");
   if (empty(p, false)) return ok();
+  if (nkt > 0) RHA_TRY(need(block_mask, "block_mask", true, 1));
   RHA_TRY(need(q, "q"));
   RHA_TRY(need(k, "k"));
   RHA_TRY(need(v, "v"));
@@ -407,6 +408,11 @@ rha_status hybrid_bwd(const rha_problem* p, const void* q, const void* k, const 
   b.N = p->n_chunks;
   b.w = p->window;
   b.anchors = p->anchor_chunks;
+  if (nkt > 0) {
+    b.kmask = block_mask;
+    b.mask_qtiles = (p->chunk_len + RHA_SPARSE_QTILE - 1) / RHA_SPARSE_QTILE;
+    b.nkt = (int)nkt;
+  }
   b.scale = (float)(1.0 / std::sqrt((double)p->head_dim));
   b.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->head_dim));
   hipError_t e = rha::launch_bwd_bf16(b, reinterpret_cast<hipStream_t>(stream));
@@ -426,6 +432,23 @@ rha_status rha_hybrid_bwd(const rha_problem* p, const void* q, const void* k, co
                           float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   return hybrid_bwd(p, q, k, v, S, z, nullptr, nullptr, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
                     stream, false);
+}
+
+rha_status rha_hybrid_bwd_sparse(const rha_problem* p, const void* q, const void* k, const void* v, const float* S,
+                                 const float* z, const uint8_t* block_mask, const void* out, const float* lse,
+                                 const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  RHA_TRY(check_problem(p, false));
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "anchor chunks are not supported by this call");
+  int64_t nkt = 0;  // window 0: nothing to prune, the plain backward pass
+  if (p->window > 0) {
+    const int64_t wl = p->window < p->n_chunks ? p->window : p->n_chunks;
+    nkt = (wl * p->chunk_len + RHA_SPARSE_KTILE - 1) / RHA_SPARSE_KTILE;
+    if (nkt > RHA_SPARSE_MAX_KTILES)
+      return fail(RHA_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)nkt, RHA_SPARSE_MAX_KTILES);
+  }
+  return hybrid_bwd(p, q, k, v, S, z, nullptr, nullptr, out, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                    stream, false, block_mask, nkt);
 }
 
 size_t rha_hybrid_bwd_bidir_workspace_size(const rha_problem* p) {

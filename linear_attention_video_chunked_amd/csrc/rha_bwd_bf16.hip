@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(c[i]) + bf16_hi(a[i]) * bf16_hi(c[i]);
   }
-  const float r = __expf(-p.lse[idx]);
+  // (a row left with no weight by a pruned window has lse = -inf, out = 0)
+  const float r = p.lse[idx] == -INFINITY ? 0.f : __expf(-p.lse[idx]);
   p.lse2[idx] = p.lse[idx] * kLog2e;
   p.delta[idx] = acc;
   p.rsc[idx] = r;
@@ -145,6 +146,9 @@ __device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
 
 // ---- window gradients of keys and values, then their linear term
 //   (key chunks j <= N-1-w): dv_t += dU_j^T phi(k_t),  dk_t += (dU_j v_t + du_j) * phi'(k_t)
+// SPARSE: pruned (query block, key block) pairs of the window have P = 0
+// (block_mask of the pruned forward pass).
+template <bool SPARSE>
 __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   // four buffers of (Q rows, dout rows, lse log2(e), delta) for one 32-row
   // query block (64 entries of lse and delta: one per lane of the load)
@@ -155,6 +159,9 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   // dU_j as bf16 rows, and its transpose
   __shared__ __attribute__((aligned(1024))) unsigned char um[BD * BD * 2];
   __shared__ __attribute__((aligned(1024))) unsigned char ut[BD * BD * 2];
+  // pruned pass: the query blocks for which some key of the workgroup is kept
+  __shared__ unsigned short qlist[SPARSE ? kMaxListedQBlocks : 1];
+  __shared__ int qlist_n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int ktiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * ktiles;
@@ -193,7 +200,46 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const int c_lo = p.bidir ? max(0, j - p.w + 1) : j;
   const int c_hi = j < p.anchors ? p.N - 1 : p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
-  const int nblk = max(0, c_hi - c_lo + 1) * nqb;
+  int nblk = max(0, c_hi - c_lo + 1) * nqb;
+  // Pruned pass: the pipeline visits only the query blocks (in order) for
+  // which one of the key tiles that the workgroup's 128 keys touch is kept;
+  // the blocks are listed in LDS first (wave 0, 64 at a time), unless there
+  // are more than the list holds (then every block is visited).  Keys of a
+  // pruned tile within a visited block get P = 0 lane by lane (keep_of).
+  bool listed = false;
+  if constexpr (SPARSE) {
+    if (nblk <= kMaxListedQBlocks) {
+      listed = true;
+      if (wave == 0) {
+        const int64_t kw0 = (int64_t)j * p.C + 128 * tile;  // the workgroup's first key
+        const int nkw = min(128, p.C - 128 * tile);
+        int base = 0;
+        for (int x0 = 0; x0 < nblk; x0 += 64) {
+          const int x = x0 + lane;
+          bool keep = false;
+          if (x < nblk) {
+            const int cq = c_lo + x / nqb, blk = x - (x / nqb) * nqb;
+            const int64_t ws = (int64_t)max(0, cq - p.w + 1) * p.C;
+            const int t0 = (int)((kw0 - ws) >> 6), t1 = min((int)((kw0 + nkw - 1 - ws) >> 6), p.nkt - 1);
+            const unsigned char* mrow = p.kmask + (((int64_t)bh * p.N + cq) * p.mask_qtiles + (blk >> 3)) * p.nkt;
+            for (int t = t0; t <= t1; ++t) keep = keep || mrow[t] != 0;
+          }
+          const uint64_t bal = __ballot(keep);
+          if (keep) qlist[base + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)x;
+          base += __popcll(bal);
+        }
+        if (lane == 0) qlist_n = base;
+      }
+      __syncthreads();
+      nblk = __builtin_amdgcn_readfirstlane(qlist_n);
+    }
+  }
+  // the query block that pipeline step i works on
+  auto qidx = [&](int i) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE)
+      if (listed) return __builtin_amdgcn_readfirstlane(qlist[i]);
+    return i;
+  };
   // Query blocks reach LDS through buffer loads that write LDS directly, two
   // blocks ahead (block x in buffer x % 4).  A 32-row tile is 8 loads of 4
   // rows (64 lanes x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile
@@ -211,8 +257,9 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     const int row = 4 * (2 * wv + x) + (lane >> 4);
     doff[x] = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
   }
-  auto issue = [&](int qi) __attribute__((always_inline)) {
-    const int bo = qi & 3;
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int bo = i & 3;
+    const int qi = qidx(i);
     const int cq = c_lo + qi / nqb, blk = qi - (qi / nqb) * nqb;
     const int64_t row0 = (int64_t)cq * p.C + RB * blk;
     const int nq = min(RB, p.C - RB * blk);
@@ -275,12 +322,24 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
       dk[nb] = mfma32(col_frag(qt_of(x), 1, nb, lane), db, dk[nb]);
     }
   };
+  // Pruned pass: whether this lane's key is kept for pipeline step i's query block (one
+  // 256-row query tile per 32-row block; the key's 64-key tile counted from
+  // the query chunk's window start).
+  auto keep_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
+    const int x = qidx(i);
+    const int cq = c_lo + x / nqb, blk = x - (x / nqb) * nqb;
+    const int64_t ws = (int64_t)max(0, cq - p.w + 1) * p.C;
+    const int kt = min((int)((key0 + l32 - ws) >> 6), p.nkt - 1);
+    return p.kmask[(((int64_t)bh * p.N + cq) * p.mask_qtiles + (blk >> 3)) * p.nkt + kt] != 0;
+  };
+  // kc: the lane's keep bit for block i; kn receives block i+1's
   auto iteration = [&](int i, auto prev_c, auto next_c, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
-                       const uint32_t (&ph)[4], const uint32_t (&dh)[4], uint32_t (&pco)[4], uint32_t (&dco)[4])
-                       __attribute__((always_inline)) {
+                       const uint32_t (&ph)[4], const uint32_t (&dh)[4], uint32_t (&pco)[4], uint32_t (&dco)[4],
+                       uint32_t kc, uint32_t& kn) __attribute__((always_inline)) {
     constexpr bool PREV = decltype(prev_c)::value, NEXT = decltype(next_c)::value;
     __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block i+1 are in LDS
     __syncthreads();  // every wave's; and every wave is done with iteration i-1
+    if constexpr (SPARSE && NEXT) kn = keep_of(i + 1);  // used in the next iteration
     if (i + 2 < nblk) issue(i + 2);
     const unsigned char* qtn = qt_of(i + 1);
     const unsigned char* gtn = gt_of(i + 1);
@@ -341,6 +400,10 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
       }
       p0 = __builtin_amdgcn_exp2f(t0);
       p1 = __builtin_amdgcn_exp2f(t1);
+      if constexpr (SPARSE) {
+        p0 = kc ? p0 : 0.f;
+        p1 = kc ? p1 : 0.f;
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (r < 4) {
         if constexpr (PREV)
@@ -373,24 +436,26 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   if (nblk > 0) {
     f32x16 s0, p0, s1, p1;
     uint32_t ca[4], cd[4], cb[4], ce[4];  // carried halves (P, dS) of alternate iterations
+    uint32_t k0 = 1, k1 = 1;              // keep bits of even and odd blocks (pruned pass)
+    if constexpr (SPARSE) k0 = keep_of(0);
     issue(0);
     if (nblk > 1) issue(1);
     __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
     __syncthreads();
     scores(0, s0, p0);
-    if (nblk > 1) iteration(0, F_{}, T_{}, s0, p0, s1, p1, ca, cd, ca, cd);
-    else iteration(0, F_{}, F_{}, s0, p0, s1, p1, ca, cd, ca, cd);
+    if (nblk > 1) iteration(0, F_{}, T_{}, s0, p0, s1, p1, ca, cd, ca, cd, k0, k1);
+    else iteration(0, F_{}, F_{}, s0, p0, s1, p1, ca, cd, ca, cd, k0, k1);
     int i = 1;
     for (; i + 2 < nblk; i += 2) {  // iterations i and i+1 both have a next block
-      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce);
-      iteration(i + 1, T_{}, T_{}, s0, p0, s1, p1, cb, ce, ca, cd);
+      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
+      iteration(i + 1, T_{}, T_{}, s0, p0, s1, p1, cb, ce, ca, cd, k0, k1);
     }
     if (i + 1 < nblk) {  // two left: i (with a next block) and i+1 (the last)
-      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce);
-      iteration(i + 1, T_{}, F_{}, s0, p0, s1, p1, cb, ce, ca, cd);
+      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
+      iteration(i + 1, T_{}, F_{}, s0, p0, s1, p1, cb, ce, ca, cd, k0, k1);
       tail_products(i + 1, ca, cd);
     } else if (i < nblk) {  // one left: i, the last
-      iteration(i, T_{}, F_{}, s1, p1, s0, p0, ca, cd, cb, ce);
+      iteration(i, T_{}, F_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
       tail_products(i, cb, ce);
     } else {  // a single block
       tail_products(0, ca, cd);
@@ -458,7 +523,11 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
 
 // ---- window gradient of the queries, then their linear term
 //   (query chunks c >= w): dq_i += ((dout_i / D_i) S_c^T - z_c delta_i / D_i) * phi'(q_i)
+template <bool SPARSE>
 __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(const BwdParams p) {
+  // pruned pass: the kept 64-key tiles of the workgroup's query tile, in order
+  __shared__ unsigned short kept_s[SPARSE ? kSparseMaxKeyTiles : 1];
+  __shared__ int kept_n;
   __shared__ __attribute__((aligned(1024))) unsigned char ks_t[2][ROWT];
   __shared__ __attribute__((aligned(1024))) unsigned char vs_t[2][ROWT];
   __shared__ __attribute__((aligned(1024))) unsigned char sm[BD * BD * 2];  // S_c as bf16 rows
@@ -507,9 +576,30 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     a_end = 0;
   }
   const int nba = (int)((a_end + RB - 1) / RB);  // blocks of the separate anchor range
-  const int nblk = nba + (int)((kend - kbeg + RB - 1) / RB);
-  // first key and key count of block bi
+  int nblk = nba + (int)((kend - kbeg + RB - 1) / RB);
+  if constexpr (SPARSE) {
+    // the workgroup's 128 rows lie in one 256-row query tile: list its kept
+    // key tiles (ballot + prefix count), then visit both 32-key halves of each
+    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.N + c) * p.mask_qtiles + (tile >> 1)) * p.nkt;
+    const int T = (int)((kend - kbeg + 63) / 64);
+    if (wave == 0) {
+      int base = 0;
+      for (int j0 = 0; j0 < T; j0 += 64) {
+        const int jt = j0 + lane;
+        const bool keep = jt < T && mrow[jt] != 0;
+        const uint64_t bal = __ballot(keep);
+        if (keep) kept_s[base + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)jt;
+        base += __popcll(bal);
+      }
+      if (lane == 0) kept_n = base;
+    }
+    __syncthreads();
+    nblk = 2 * __builtin_amdgcn_readfirstlane(kept_n);
+  }
+  // first key and key count of block bi (a pruned pass's second half of the
+  // window's last tile may hold no key: count <= 0, the block is skipped)
   auto blk_k0 = [&](int bi) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return kbeg + 64 * (int64_t)__builtin_amdgcn_readfirstlane(kept_s[bi >> 1]) + RB * (bi & 1);
     return bi < nba ? (int64_t)RB * bi : kbeg + (int64_t)RB * (bi - nba);
   };
   auto blk_nk = [&](int bi) __attribute__((always_inline)) {
@@ -531,6 +621,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     constexpr int BUF = decltype(buf_c)::value;
     const int64_t k0 = blk_k0(bi);
     const int nk = blk_nk(bi);
+    if constexpr (SPARSE)
+      if (nk <= 0) return;  // nothing to load
     const int nbytes = (nk - 1) * st2 + BD * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
@@ -548,6 +640,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     __syncthreads();  // every wave's; and every wave is done with block bi-1 (the other buffer)
     if (bi + 1 < nblk) issue(bi + 1, std::integral_constant<int, BUF ^ 1>{});
     const int nk = blk_nk(bi);
+    if constexpr (SPARSE)
+      if (nk <= 0) return;  // the same for the whole workgroup: no barrier is skipped by some waves only
     const unsigned char* kt = ks_t[BUF];
     const unsigned char* vt = vs_t[BUF];
     f32x16 sa = {}, pa = {};
@@ -711,8 +805,14 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(BH * p.N * tiles128)), dim3(TB), 0, s, p);
+  const dim3 grid((unsigned)(BH * p.N * tiles128));
+  if (p.kmask != nullptr) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, dim3(TB), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, dim3(TB), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, dim3(TB), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, dim3(TB), 0, s, p);
+  }
   return hipGetLastError();
 }
 

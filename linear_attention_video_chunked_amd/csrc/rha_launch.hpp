@@ -71,6 +71,9 @@ struct FwdParams {
 
 // Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).
 constexpr int kSparseMaxKeyTiles = 2048;
+// the pruned backward pass's key-gradient kernel lists at most this many
+// 32-row query blocks per workgroup (beyond it, it visits every block)
+constexpr int kMaxListedQBlocks = 2048;
 
 // Copy one chunk [B,H,C,d] (strided) into cache slot `slot` of [B,H,w,C,d].
 struct CopyParams {
@@ -174,6 +177,10 @@ struct BwdParams {
   // anchor chunks (causal only): chunks 0 .. anchors-1 are softmax keys of
   // every chunk not before them and are in no state
   int anchors;
+  // pruned window (causal, no anchors): kmask[B, H, N, mask_qtiles, nkt] as
+  // for the pruned forward pass; NULL for none
+  const unsigned char* kmask;
+  int mask_qtiles, nkt;
   float* dS;
   float* dz;
   int64_t sb, sh, st;  // element strides of q, k, v, out, dout

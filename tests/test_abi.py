@@ -262,3 +262,17 @@ def test_backward_checks(L):
     assert "workspace" in L.rha_last_error().decode()
     assert L.rha_hybrid_bwd(ctypes.byref(ok), *args[:6], None, *args[7:], need, None) == 1  # lse required
     assert "lse" in L.rha_last_error().decode()
+    # the pruned backward: the pruned forward's rules, the plain workspace
+    sargs = [P] * 13
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(_prob(anchor_chunks=1)), *sargs, 1 << 30, None) == 2
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(_prob(dtype=_rha.RHA_F32, stride_t=128)), *sargs, 1 << 30,
+                                   None) == 2
+    big = _prob(chunk_len=4096 * 16, n_chunks=4, window=3, stride_b=0, stride_h=0)
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(big), *sargs, 1 << 40, None) == 2
+    assert "key blocks" in L.rha_last_error().decode()
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(ok), *sargs[:5], None, *sargs[6:], need, None) == 1  # mask
+    assert "block_mask" in L.rha_last_error().decode()
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(ok), *sargs, need - 1, None) == 1
+    assert "workspace" in L.rha_last_error().decode()
+    assert L.rha_hybrid_bwd_sparse(ctypes.byref(ok), *sargs[:7], None, *sargs[8:], need, None) == 1  # lse
+    assert "lse" in L.rha_last_error().decode()

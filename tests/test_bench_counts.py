@@ -91,3 +91,24 @@ def test_anchor_bwd_count_limits_and_brute_force():
         rows = sum(1 for i in range(L) if i // C - w >= a)
         folded = sum(1 for j in range(L) if a <= j // C <= N - 1 - w)
         assert bench.anchor_bwd_flops(C, N, w, a, d, BH) == BH * (pairs * 10 * d + (rows + folded) * 4 * d * d)
+
+
+def test_sparse_bwd_count_limits_and_brute_force():
+    C, N, w, d, B, H = 300, 5, 2, 128, 1, 2
+    nqt, nkt = -(-C // 256), -(-(w * C) // 64)
+    ones = np.ones((B, H, N, nqt, nkt), np.uint8)
+    assert bench.sparse_bwd_flops(C, N, w, d, ones) == bench.bwd_flops(C, N, w, d, B * H)
+    # token by token on a tiny problem with 2-row query blocks and 3-key key blocks
+    C, N, w, d, B, H = 5, 4, 2, 4, 1, 2
+    rng = np.random.default_rng(3)
+    m = (rng.random((B, H, N, 3, 4)) < 0.5).astype(np.uint8)
+    pairs = 0
+    for h in range(H):
+        for i in range(N * C):
+            c = i // C
+            lo = max(0, c - w + 1) * C
+            for j in range(lo, (c + 1) * C):
+                pairs += int(m[0, h, c, (i - c * C) // 2, (j - lo) // 3])
+    rows = sum(C for c in range(N) if c >= w) * B * H
+    folded = sum(C for c in range(N) if c <= N - 1 - w) * B * H
+    assert bench.sparse_bwd_flops(C, N, w, d, m, qtile=2, ktile=3) == pairs * 10 * d + (rows + folded) * 4 * d * d

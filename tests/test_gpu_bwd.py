@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, Workload, gen_qkv, to_storage
+from synth import CONFIGS, Workload, gen_block_mask, gen_qkv, to_storage
 import linear_attention_video_chunked_amd as rha
 from parity_utils import GroupedRows, sample_rows, TOL, rel_l2, to64
 
@@ -296,6 +296,116 @@ def test_anchor_backward_wan13b_sampled_rows():
     grouped = [GroupedRows(f"anchored bwd wan13b {nm}") for nm in ("dq", "dk", "dv")]
     h = 9
     ref = oracle.hybrid_anchor_backward(to64(q)[0, h], to64(k)[0, h], to64(v)[0, h], wl.C, wl.w, a, to64(dout)[0, h])
+    for i, (g, r) in enumerate(zip(grads, ref)):
+        grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
+    for gr in grouped:
+        gr.check(TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# rha_hybrid_bwd_sparse (pruned blocks of the window) against the oracle's
+# pruned chain rule (pinned to finite differences of the pruned forward, to
+# torch autograd through a separately written dense masked form, and to the
+# plain backward when every block is kept).
+
+def _run_sparse(wl, mask, q, k, v, dout):
+    qd, kd, vd, gd, md = (t.to(DEV) for t in (q, k, v, dout, mask))
+    S, z = rha.state_scan(kd, vd, wl.C, wl.w)
+    out, lse = rha.hybrid_fwd_sparse(qd, kd, vd, S, z, wl.C, wl.w, md, return_lse=True)
+    grads = rha.hybrid_bwd_sparse(qd, kd, vd, S, z, md, out, lse, gd, wl.C, wl.w)
+    torch.cuda.synchronize()
+    return grads, lse
+
+
+# name: (B, H, C, N, w, qscale, kscale); windows of 400, 900, 1560 and 256
+# keys end 16, 4, 24 and 0 keys into their last 64-key block, and chunks of
+# 300 and 520 rows hold a short second or third 256-row query block
+SPARSE_CASES = {
+    "C200_N5_w2": (1, 2, 200, 5, 2, 1.0, 0.5),
+    "C300_N4_w3_q4": (1, 2, 300, 4, 3, 4.0, 0.5),
+    "C520_N3_w9": (1, 1, 520, 3, 9, 2.0, 1.0),
+    "C64_N6_w4_B2": (2, 1, 64, 6, 4, 1.0, 1.0),
+}
+
+
+def _sparse_wl(name):
+    B, H, C, N, w, qs, ks = SPARSE_CASES[name]
+    return Workload(name, 1900 + sorted(SPARSE_CASES).index(name), B=B, H=H, d=128, C=C, N=N, w=w, dtype="bf16",
+                    qscale=qs, kscale=ks)
+
+
+@pytest.mark.parametrize("density", [0.85, 0.5, 0.15])
+@pytest.mark.parametrize("name", sorted(SPARSE_CASES))
+def test_sparse_backward_against_oracle(name, density):
+    wl = _sparse_wl(name)
+    shape = rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w)
+    mask = gen_block_mask(shape, density, seed=wl.wid * 10 + int(density * 100))
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 11)
+    grads, lse = _run_sparse(wl, mask, q, k, v, dout)
+    ref = oracle.hybrid_block_sparse_backward_batched(to64(q), to64(k), to64(v), wl.C, wl.w, mask.numpy(),
+                                                      to64(dout))
+    # rows left with no weight: dq exactly 0
+    empty = np.isneginf(to64(lse))
+    assert np.all(to64(grads[0])[empty] == 0)
+    for g, r, nm in zip(grads, ref, ("dq", "dk", "dv")):
+        g64 = to64(g)
+        e = rel_l2(g64, r)
+        print(f"{name} density {density} {nm}: rel-L2 {e:.2e} ({empty.sum()} rows without weight)")
+        assert e <= TOL["bf16"], f"{nm}: rel-L2 {e:.3e}"
+        for c in range(wl.N):
+            sl = slice(c * wl.C, (c + 1) * wl.C)
+            if np.linalg.norm(r[:, :, sl]) > 0:
+                ec = rel_l2(g64[:, :, sl], r[:, :, sl])
+                assert ec <= TOL["bf16"], f"{nm} chunk {c}: rel-L2 {ec:.3e}"
+            else:
+                assert np.all(g64[:, :, sl] == 0), f"{nm} chunk {c}: nonzero where the oracle is zero"
+
+
+@pytest.mark.parametrize("name", sorted(SPARSE_CASES))
+def test_sparse_backward_all_kept_is_bitwise_plain(name):
+    wl = _sparse_wl(name)
+    ones = torch.ones(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), dtype=torch.uint8)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 12)
+    grads, _ = _run_sparse(wl, ones, q, k, v, dout)
+    for x, y, nm in zip(grads, _run(wl, q, k, v, dout), ("dq", "dk", "dv")):
+        assert torch.equal(x, y), nm
+
+
+@pytest.mark.parametrize("name", ["C200_N5_w2", "C300_N4_w3_q4"])
+def test_sparse_backward_all_pruned_is_linear_only(name):
+    wl = _sparse_wl(name)
+    zeros = torch.zeros(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), dtype=torch.uint8)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 13)
+    grads, lse = _run_sparse(wl, zeros, q, k, v, dout)
+    assert bool(torch.isneginf(lse[:, :, : wl.w * wl.C]).all())
+    ref = oracle.hybrid_block_sparse_backward_batched(to64(q), to64(k), to64(v), wl.C, wl.w, zeros.numpy(),
+                                                      to64(dout))
+    # no weight before chunk w: dq = 0 there; the keys of the last w chunks
+    # are in no query's state: dk = dv = 0 there
+    assert np.all(to64(grads[0])[:, :, : wl.w * wl.C] == 0)
+    for g in grads[1:]:
+        assert np.all(to64(g)[:, :, (wl.N - wl.w) * wl.C:] == 0)
+    for g, r, nm in zip(grads, ref, ("dq", "dk", "dv")):
+        e = rel_l2(to64(g), r)
+        assert e <= TOL["bf16"], f"{nm}: rel-L2 {e:.3e}"
+
+
+@pytest.mark.timeout(600)
+def test_sparse_backward_wan13b_sampled_rows():
+    wl = CONFIGS["wan13b"]
+    print(f"[parity] pruned bwd wan13b: H{wl.H} C{wl.C} N{wl.N} w{wl.w}, half the blocks kept", flush=True)
+    q, k, v = gen_qkv(wl)
+    dout = _dout(wl, 14)
+    mask = gen_block_mask(rha.sparse_mask_shape(wl.B, wl.H, wl.C, wl.N, wl.w), 0.5, seed=31)
+    grads, _ = _run_sparse(wl, mask, q, k, v, dout)
+    rows = sample_rows(wl.C, wl.N, 4 * wl.N, seed=29)
+    grouped = [GroupedRows(f"pruned bwd wan13b {nm}") for nm in ("dq", "dk", "dv")]
+    h = 4
+    ref = oracle.hybrid_block_sparse_backward(to64(q)[0, h], to64(k)[0, h], to64(v)[0, h], wl.C, wl.w,
+                                              mask[0, h].numpy(), to64(dout)[0, h])
     for i, (g, r) in enumerate(zip(grads, ref)):
         grouped[i].add_by_chunk((0, h), to64(g[0, h])[rows], r[rows], rows, wl.C)
     for gr in grouped:
