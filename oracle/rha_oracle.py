@@ -348,6 +348,74 @@ def hybrid_block_sparse_batched(q, k, v, C: int, w: int, mask, return_den: bool 
     return (out, den) if return_den else out
 
 
+# ---------------------------------------------------------------- pruned streaming step
+#
+# Hybrid Forcing explainer, section 1 (the streaming generator keeps the
+# window's chunks in a KV cache) and section 2.A (its window attention is
+# block-sparse).  Reading taken for a pruned streaming step (the pages fix no
+# block layout for the cache): the step for chunk t attends to the chunks of
+# its window as the cache holds them -- one slot per chunk, chunk c in slot
+# c mod w, the slots in order 0, 1, .. (before the ring is full, slots 0 .. t)
+# -- and the key blocks are ktile keys each, counted from slot 0's first key.
+# Query blocks are qtile rows of the new chunk.  One mask per step,
+# [nqt, nkt]; entries past the keys in use are ignored.  A pruned block adds
+# nothing; the folded history is that of the plain step (chunks <= t - w).
+# Softmax is order-free, so with every block kept this is the plain hybrid.
+
+
+def stream_slot_chunks(t: int, w: int):
+    """The chunks of step t's window in cache-slot order (slot s holds chunk c = s mod w)."""
+    if w < 1:
+        raise ValueError("a streaming window has at least one chunk")
+    if t + 1 <= w:
+        return list(range(t + 1))
+    first = t - w + 1
+    return [first + ((s - first) % w) for s in range(w)]
+
+
+def stream_block_sparse(q, k, v, C: int, w: int, masks, qtile: int = 256, ktile: int = 64,
+                        return_den: bool = False):
+    """Pruned streaming steps over a whole stream (one head): chunk t of q
+    attends to its window in cache-slot order with mask masks[t] ([nqt, nkt])
+    and to the folded history; returns [L, d] (and the denominators)."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    masks = np.asarray(masks)
+    L, d = q.shape
+    N = L // C
+    S, z = state_scan(k, v, C, w)
+    fq = phi(q)
+    out = np.empty((L, v.shape[1]))
+    den_all = np.empty(L)
+    for t in range(N):
+        order = stream_slot_chunks(t, w)
+        kw = np.concatenate([k[c * C:(c + 1) * C] for c in order])
+        vw = np.concatenate([v[c * C:(c + 1) * C] for c in order])
+        for i in range(-(-C // qtile)):
+            rows = slice(t * C + i * qtile, t * C + min(C, (i + 1) * qtile))
+            keep = _window_keep(masks[t, i], kw.shape[0], ktile)
+            e = np.exp(_scores(q[rows], kw)) * keep[None, :]
+            num = fq[rows] @ S[t] + e @ vw
+            den = fq[rows] @ z[t] + e.sum(axis=1)
+            safe = np.where(den > 0, den, 1.0)
+            out[rows] = np.where(den[:, None] > 0, num / safe[:, None], 0.0)
+            den_all[rows] = den
+    return (out, den_all) if return_den else out
+
+
+def stream_block_sparse_batched(q, k, v, C: int, w: int, masks, return_den: bool = False, **tiles):
+    """``stream_block_sparse`` over [B, H, L, d] with masks [B, H, N, nqt, nkt]."""
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    masks = np.asarray(masks)
+    B, H, L, _ = q.shape
+    out = np.empty(q.shape[:3] + (v.shape[-1],))
+    den = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], den[b, h] = stream_block_sparse(q[b, h], k[b, h], v[b, h], C, w, masks[b, h],
+                                                       return_den=True, **tiles)
+    return (out, den) if return_den else out
+
+
 # ---------------------------------------------------------------- bidirectional hybrid
 #
 # "ReHyAt: Recurrent Hybrid Attention for Video Diffusion Transformers",

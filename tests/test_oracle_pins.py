@@ -414,6 +414,137 @@ def test_block_sparse_drops_exactly_the_block():
         np.testing.assert_allclose(out[r], ref, rtol=1e-12)
 
 
+# ---------------------------------------------------------------- pruned streaming step
+# (Hybrid Forcing explainer, sections 1 and 2.A: the streaming generator's KV
+# cache and its block-sparse window).  The step's key blocks are counted over
+# the cache slots in slot order (chunk c in slot c mod w).  Pinned to the plain
+# hybrid (every block kept), to the pruned window of the whole sequence (before
+# the ring turns, and with the mask rolled by the ring's turn when blocks do
+# not straddle chunks), and to a pair-by-pair brute force that places each key
+# by its own slot arithmetic.
+
+def _stream_masks(C, N, w, qt, kt, seed, density=0.5):
+    shape = (N, -(-C // qt), -(-(w * C) // kt))
+    return (np.random.default_rng(seed).random(shape) < density).astype(np.uint8)
+
+
+def _stream_brute(q, k, v, C, w, masks, qt, kt):
+    L, d = q.shape
+    out, den = np.zeros((L, v.shape[1])), np.zeros(L)
+    for i in range(L):
+        t = i // C
+        fq = O.phi(q[i])
+        num, dsum = np.zeros(v.shape[1]), 0.0
+        for j in range(L):
+            c = j // C
+            if max(0, t - w + 1) <= c <= t:
+                slot = c % w                      # the chunk's cache slot
+                pos = slot * C + (j - c * C)      # its key's row in slot order
+                if masks[t, (i - t * C) // qt, pos // kt]:
+                    a = math.exp(q[i] @ k[j] / math.sqrt(d))
+                    num, dsum = num + a * v[j], dsum + a
+            elif c <= t - w:
+                a = fq @ O.phi(k[j])
+                num, dsum = num + a * v[j], dsum + a
+        den[i] = dsum
+        out[i] = num / dsum if dsum > 0 else 0.0
+    return out, den
+
+
+STREAM_SPARSE_SWEEP = [(3, 5, 2, 2, 2), (4, 6, 3, 3, 5), (5, 4, 1, 5, 1), (2, 7, 3, 1, 3), (4, 5, 4, 2, 4)]
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", STREAM_SPARSE_SWEEP)
+def test_stream_sparse_matches_pair_brute_force(C, N, w, qt, kt):
+    q, k, v = _qkv(C * N, 4, 6000 + 10 * C + N, qs=1.5)
+    m = _stream_masks(C, N, w, qt, kt, 6001 + C + w)
+    a, da = _stream_brute(q, k, v, C, w, m, qt, kt)
+    b, db = O.stream_block_sparse(q, k, v, C, w, m, qt, kt, return_den=True)
+    np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(db, da, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", STREAM_SPARSE_SWEEP)
+def test_stream_sparse_all_kept_is_plain_hybrid(C, N, w, qt, kt):
+    q, k, v = _qkv(C * N, 4, 6100 + C, qs=1.5)
+    ones = np.ones((N, -(-C // qt), -(-(w * C) // kt)), np.uint8)
+    np.testing.assert_allclose(O.stream_block_sparse(q, k, v, C, w, ones, qt, kt), O.hybrid(q, k, v, C, w),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w,qt,kt", STREAM_SPARSE_SWEEP)
+def test_stream_sparse_before_the_ring_turns_is_the_pruned_window(C, N, w, qt, kt):
+    # steps t < w: slots 0 .. t hold chunks 0 .. t in order, the whole-sequence
+    # window order
+    q, k, v = _qkv(C * N, 4, 6200 + C, qs=1.5)
+    m = _stream_masks(C, N, w, qt, kt, 6201 + N)
+    nkt_seq = O.sparse_mask_shape(C, N, w, qt, kt)[2]
+    ref = O.hybrid_block_sparse(q, k, v, C, w, m[:, :, :nkt_seq], qt, kt)
+    got = O.stream_block_sparse(q, k, v, C, w, m, qt, kt)
+    n = min(w, N) * C
+    np.testing.assert_allclose(got[:n], ref[:n], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,N,w,kt", [(4, 7, 3, 2), (6, 6, 2, 3), (4, 5, 4, 4), (2, 6, 3, 1)])
+def test_stream_sparse_turned_ring_is_the_pruned_window_with_a_rolled_mask(C, N, w, kt):
+    # with C a multiple of the key block, chronological window block i*m + u
+    # (chunk first + i, block u of m = C/kt) is slot-order block
+    # ((first + i) mod w) * m + u
+    assert C % kt == 0
+    qt, m_ = 2, C // kt
+    q, k, v = _qkv(C * N, 4, 6300 + C + w, qs=1.5)
+    ms = _stream_masks(C, N, w, qt, kt, 6301 + w)
+    nkt_seq = O.sparse_mask_shape(C, N, w, qt, kt)[2]
+    mc = np.zeros((N, ms.shape[1], nkt_seq), np.uint8)
+    for t in range(N):
+        first = max(0, t - w + 1)
+        for i in range(t - first + 1):
+            for u in range(m_):
+                mc[t, :, i * m_ + u] = ms[t, :, ((first + i) % w) * m_ + u]
+    np.testing.assert_allclose(O.stream_block_sparse(q, k, v, C, w, ms, qt, kt),
+                               O.hybrid_block_sparse(q, k, v, C, w, mc, qt, kt), rtol=1e-12, atol=1e-12)
+
+
+def test_stream_sparse_all_pruned_leaves_the_history():
+    C, N, w, qt, kt = 3, 5, 2, 2, 2
+    q, k, v = _qkv(C * N, 3, 6400)
+    zeros = np.zeros((N, 2, 3), np.uint8)
+    out, den = O.stream_block_sparse(q, k, v, C, w, zeros, qt, kt, return_den=True)
+    assert np.all(den[: w * C] == 0) and np.all(out[: w * C] == 0)
+    fq, fk = O.phi(q), O.phi(k)
+    for i in range(w * C, C * N):
+        hist = slice(0, (i // C - w + 1) * C)
+        wts = fk[hist] @ fq[i]
+        np.testing.assert_allclose(out[i], wts @ v[hist] / wts.sum(), rtol=1e-13)
+
+
+def _stream_sparse_pin_err():
+    C, N, w, qt, kt = 3, 6, 3, 2, 2
+    q, k, v = _qkv(C * N, 4, 6500, qs=1.2)
+    m = _stream_masks(C, N, w, qt, kt, 6501)
+    a, _ = _stream_brute(q, k, v, C, w, m, qt, kt)
+    return float(np.max(np.abs(O.stream_block_sparse(q, k, v, C, w, m, qt, kt) - a)))
+
+
+STREAM_SPARSE_MUTANTS = {
+    "chronological_order": ("stream_slot_chunks",
+                            lambda orig: (lambda t, w: list(range(max(0, t - w + 1), t + 1)))),
+    "mask_ignored": ("_window_keep", lambda orig: (lambda row, n, kt: np.ones(n, dtype=bool))),
+    "mask_one_tile_late": ("_window_keep", lambda orig: (lambda row, n, kt: np.roll(orig(row, n, kt), kt))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STREAM_SPARSE_MUTANTS))
+def test_stream_sparse_planted_mistake_is_caught(name, monkeypatch):
+    attr, make = STREAM_SPARSE_MUTANTS[name]
+    monkeypatch.setattr(O, attr, make(getattr(O, attr)))
+    assert _stream_sparse_pin_err() > 1e-6
+
+
+def test_stream_sparse_unmutated_pin_passes():
+    assert _stream_sparse_pin_err() < 1e-10
+
+
 # ---------------------------------------------------------------- bidirectional hybrid
 # (ReHyAt abstract: the hybrid stands in for the bidirectional attention of
 # video diffusion transformers).  Reading: symmetric window, everything outside
