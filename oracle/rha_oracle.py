@@ -402,6 +402,28 @@ def stream_block_sparse(q, k, v, C: int, w: int, masks, qtile: int = 256, ktile:
     return (out, den_all) if return_den else out
 
 
+def stream_block_sparse_rows(q, k, v, C: int, w: int, t: int, mask_t, rows, S=None, z=None, qtile: int = 256,
+                             ktile: int = 64):
+    """``stream_block_sparse`` for selected rows (within chunk t) of step t only
+    (one head; mask_t [nqt, nkt]; S, z: state_scan's slots, computed if absent)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    if S is None:
+        S, z = state_scan(k, v, C, w)
+    order = stream_slot_chunks(t, w)
+    kw = np.concatenate([k[c * C:(c + 1) * C] for c in order])
+    vw = np.concatenate([v[c * C:(c + 1) * C] for c in order])
+    out = np.empty((len(rows), v.shape[1]))
+    for n, r in enumerate(rows):
+        r = int(r)
+        keep = _window_keep(np.asarray(mask_t)[r // qtile], kw.shape[0], ktile)
+        e = np.exp(_scores(q[t * C + r : t * C + r + 1], kw))[0] * keep
+        fq = phi(q[t * C + r])
+        num = e @ vw + fq @ S[t]
+        den = e.sum() + fq @ z[t]
+        out[n] = num / den if den > 0 else 0.0
+    return out
+
+
 def stream_block_sparse_batched(q, k, v, C: int, w: int, masks, return_den: bool = False, **tiles):
     """``stream_block_sparse`` over [B, H, L, d] with masks [B, H, N, nqt, nkt]."""
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))

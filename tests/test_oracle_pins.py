@@ -505,6 +505,17 @@ def test_stream_sparse_turned_ring_is_the_pruned_window_with_a_rolled_mask(C, N,
                                O.hybrid_block_sparse(q, k, v, C, w, mc, qt, kt), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("C,N,w,qt,kt", STREAM_SPARSE_SWEEP)
+def test_stream_sparse_rows_match_whole_stream(C, N, w, qt, kt):
+    q, k, v = _qkv(C * N, 4, 6600 + C, qs=1.5)
+    m = _stream_masks(C, N, w, qt, kt, 6601 + w)
+    full = O.stream_block_sparse(q, k, v, C, w, m, qt, kt)
+    for t in range(N):
+        rows = np.arange(0, C, 2)
+        got = O.stream_block_sparse_rows(q, k, v, C, w, t, m[t], rows, qtile=qt, ktile=kt)
+        np.testing.assert_allclose(got, full[t * C + rows], rtol=1e-13, atol=1e-13)
+
+
 def test_stream_sparse_all_pruned_leaves_the_history():
     C, N, w, qt, kt = 3, 5, 2, 2, 2
     q, k, v = _qkv(C * N, 3, 6400)
