@@ -356,6 +356,42 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
  */
 size_t rha_stream_workspace_size(const rha_problem* p);
 
+/*
+ * rha_stream_step_sparse -- rha_stream_step with pruned blocks of the window.
+ *
+ * Hybrid Forcing explainer, section 1 (the streaming generator's KV cache)
+ * and section 2.A (its window attention is block-sparse: blocks judged
+ * unimportant are pruned; the page gives no criterion, so the kept blocks are
+ * an input, one mask per step).  The blocks follow the cache's own layout,
+ * the order in which the step reads the window:
+ *   query block i : rows RHA_SPARSE_QTILE*i .. of the new chunk (clipped)
+ *   key block j   : keys RHA_SPARSE_KTILE*j .. of the window's chunks taken in
+ *                   cache-slot order (chunk c sits in slot c % w; before the
+ *                   ring is full the slots in use are 0 .. t)
+ * so a key block may span two chunks.  A pruned block adds nothing to the
+ * numerator or the denominator; the fold and the state are those of
+ * rha_stream_step.  A query left with no weight at all (every block pruned
+ * and no state yet) gets out = 0 and lse = -inf.  Until the ring turns
+ * (t < w) slot order is the sequence order, and the step equals
+ * rha_hybrid_fwd_sparse over the concatenated sequence, chunk t, with this
+ * step's mask; with every entry nonzero it equals rha_stream_step.
+ *
+ *   block_mask : uint8 [B, H, ceil(C / RHA_SPARSE_QTILE), ceil(w * C / RHA_SPARSE_KTILE)]
+ *                contiguous device memory (read); nonzero keeps the block;
+ *                entries past the keys in use (t < w-1) are ignored.
+ *   other arguments as for rha_stream_step.  The window's attention runs
+ *   unsplit (the workspace, if any, serves the split fold).
+ *
+ * Errors: as rha_stream_step; RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16,
+ * head_dim is 128 and anchor_chunks is 0, or when the window spans more than
+ * RHA_SPARSE_MAX_KTILES key blocks.
+ */
+rha_status rha_stream_step_sparse(const rha_problem* p, const void* q_new, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache, float* S,
+                                  float* z, rha_stream_cursor* cursor, int32_t commit,
+                                  const uint8_t* block_mask, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Bytes of device scratch that rha_stream_step_noalloc holds per GPU. */
 #define RHA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 

@@ -15,6 +15,7 @@ Functions mirror the C ABI in ``include/rha.h``:
 * ``hybrid_bwd_sparse(q, k, v, S, z, m, out, lse, dout, C, w)`` the same for pruned window blocks
 * ``hybrid_bwd_bidir(q, k, v, states, out, lse, dout, C, w)`` the same for the bidirectional hybrid
 * ``StreamState`` + ``stream_step(...)``         one chunk of streaming decode
+* ``stream_step_sparse(..., block_mask)``          the step with pruned window blocks
 * ``stream_step_noalloc(...)``                    the same step with the library's own scratch
 """
 from ._rha import (
@@ -32,8 +33,10 @@ from ._rha import (
     sparse_mask_shape,
     state_scan,
     state_scan_bidir,
+    stream_mask_shape,
     stream_step,
     stream_step_noalloc,
+    stream_step_sparse,
     version,
 )
 
@@ -52,7 +55,9 @@ __all__ = [
     "sparse_mask_shape",
     "state_scan",
     "state_scan_bidir",
+    "stream_mask_shape",
     "stream_step",
+    "stream_step_sparse",
     "stream_step_noalloc",
     "version",
 ]

@@ -78,12 +78,14 @@ def lib():
     L.rha_hybrid_bwd_bidir_workspace_size.restype = ctypes.c_size_t
     L.rha_stream_step.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                   ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.rha_stream_step_sparse.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
+                                         ctypes.c_int32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.rha_stream_workspace_size.argtypes = [P]
     L.rha_stream_workspace_size.restype = ctypes.c_size_t
     L.rha_stream_step_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Cursor),
                                           ctypes.c_int32, _vp, _vp, _vp]
     for name in ("rha_state_scan", "rha_hybrid_fwd", "rha_hybrid_fwd_sparse", "rha_state_scan_bidir",
-                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_hybrid_bwd_sparse", "rha_hybrid_bwd_bidir", "rha_stream_step",
+                 "rha_hybrid_fwd_bidir", "rha_hybrid_bwd", "rha_hybrid_bwd_sparse", "rha_hybrid_bwd_bidir", "rha_stream_step", "rha_stream_step_sparse",
                  "rha_stream_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.rha_status_string.argtypes = [ctypes.c_int]
@@ -410,6 +412,43 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
     the chunk that leaves the window and advance the cursor."""
     if out is None:
         out = torch.empty_like(q_new)
+    prob = _stream_checks(st, q_new, k_new, v_new, out, lse)
+    _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
+                                 _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
+                                 ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _ptr(st.workspace),
+                                 ctypes.c_size_t(0 if st.workspace is None else st.workspace.numel()),
+                                 _stream(stream)))
+    return out
+
+
+def stream_mask_shape(B: int, H: int, C: int, w: int):
+    """Shape [B, H, nqt, nkt] of one step's block mask for stream_step_sparse."""
+    return (B, H, -(-C // SPARSE_QTILE), -(-(w * C) // SPARSE_KTILE))
+
+
+def stream_step_sparse(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       block_mask: torch.Tensor, commit: bool = True, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rha_stream_step_sparse: stream_step with pruned blocks of the window;
+    block_mask is uint8 [B, H, nqt, nkt] (stream_mask_shape), key blocks over
+    the window's keys in cache-slot order."""
+    if out is None:
+        out = torch.empty_like(q_new)
+    prob = _stream_checks(st, q_new, k_new, v_new, out, lse)
+    shape = stream_mask_shape(st.B, st.H, st.C, st.w)
+    if (tuple(block_mask.shape) != shape or block_mask.dtype != torch.uint8 or not block_mask.is_contiguous()
+            or block_mask.device != q_new.device):
+        raise ValueError(f"block_mask must be contiguous uint8 {shape} on the chunk's device")
+    _check(lib().rha_stream_step_sparse(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new),
+                                        _ptr(st.k_cache), _ptr(st.v_cache), _ptr(st.S), _ptr(st.z),
+                                        ctypes.byref(st.cursor), ctypes.c_int32(1 if commit else 0),
+                                        _ptr(block_mask), _ptr(out), _ptr(lse), _ptr(st.workspace),
+                                        ctypes.c_size_t(0 if st.workspace is None else st.workspace.numel()),
+                                        _stream(stream)))
+    return out
+
+
+def _stream_checks(st: StreamState, q_new, k_new, v_new, out, lse) -> Problem:
     _same_layout(q_new, k_new, v_new, out)
     B, H, C, d = q_new.shape
     if (B, H, C, d) != (st.B, st.H, st.C, st.d):
@@ -423,13 +462,7 @@ def stream_step(st: StreamState, q_new: torch.Tensor, k_new: torch.Tensor, v_new
         raise ValueError(f"stream workspace is on {st.workspace.device}, the chunk on {q_new.device}")
     if lse is not None:
         _check_f32(q_new, lse, "lse", (B, H, C))
-    prob = _problem(q_new, C, st.w, 1, st.anchors)
-    _check(lib().rha_stream_step(ctypes.byref(prob), _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(st.k_cache),
-                                 _ptr(st.v_cache), _ptr(st.S), _ptr(st.z), ctypes.byref(st.cursor),
-                                 ctypes.c_int32(1 if commit else 0), _ptr(out), _ptr(lse), _ptr(st.workspace),
-                                 ctypes.c_size_t(0 if st.workspace is None else st.workspace.numel()),
-                                 _stream(stream)))
-    return out
+    return _problem(q_new, C, st.w, 1, st.anchors)
 
 
 # Bytes of device scratch the no-allocation step holds per GPU (RHA_NOALLOC_SCRATCH_BYTES).

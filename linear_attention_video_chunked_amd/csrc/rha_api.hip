@@ -524,10 +524,14 @@ size_t rha_stream_workspace_size(const rha_problem* p) {
   return bytes;
 }
 
-rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
-                           void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
-                           int32_t commit, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+namespace {
+
+// The streaming step; block_mask (pruned steps, bf16 d = 128 without anchors)
+// is [B, H, ceil(C/256), ceil(w*C/64)] over the window's keys in slot order.
+rha_status stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, float* S, float* z, rha_stream_cursor* cursor, int32_t commit,
+                       const uint8_t* block_mask, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   RHA_TRY(check_problem(p, true));
   if (cursor == nullptr) return fail(RHA_ERR_CURSOR, "cursor is NULL");
   if (cursor->t < 0) return fail(RHA_ERR_CURSOR, "cursor->t = %lld < 0", (long long)cursor->t);
@@ -569,7 +573,8 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   const int64_t n_anc = left > 0 ? (left < a ? left : a) : 0;
   const int n_keys = (int)((in_window + n_anc) * C);
   const bool fold = commit && left >= 0 && left >= a;
-  const int splits = workspace != nullptr ? stream_splits(p, n_keys) : 1;
+  // (a pruned step's attention runs unsplit)
+  const int splits = workspace != nullptr && block_mask == nullptr ? stream_splits(p, n_keys) : 1;
   const size_t fwd_part = splits > 1 ? align256(rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) : 0;
   const bool split_fwd = splits > 1 && workspace_bytes >= fwd_part;
   // beside a split attention the fold takes the compute units the attention
@@ -678,6 +683,10 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
   f.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   f.n_splits = split_fwd ? splits : 1;
   f.part = split_fwd ? static_cast<float*>(workspace) : nullptr;
+  if (block_mask != nullptr) {
+    f.kmask = block_mask;
+    f.nkt = (int)(((int64_t)w * C + RHA_SPARSE_KTILE - 1) / RHA_SPARSE_KTILE);
+  }
   e = fold_in_fwd ? rha::launch_fwd_bf16_qb2_fold(f, fold_c, s) : launch_fwd(p, f, s);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
 
@@ -718,6 +727,32 @@ rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* 
     cursor->t = t + 1;
   }
   return ok();
+}
+
+}  // namespace
+
+rha_status rha_stream_step(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
+                           int32_t commit, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return stream_step(p, q_new, k_new, v_new, k_cache, v_cache, S, z, cursor, commit, nullptr, out, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+rha_status rha_stream_step_sparse(const rha_problem* p, const void* q_new, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, float* S, float* z, rha_stream_cursor* cursor,
+                                  int32_t commit, const uint8_t* block_mask, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  RHA_TRY(check_problem(p, true));
+  if (p->anchor_chunks > 0) return fail(RHA_ERR_UNSUPPORTED, "anchor chunks are not supported by this call");
+  if (p->dtype != RHA_BF16 || p->head_dim != 128)
+    return fail(RHA_ERR_UNSUPPORTED, "pruned windows need dtype RHA_BF16 and head_dim 128");
+  const int64_t nkt = ((int64_t)p->window * p->chunk_len + RHA_SPARSE_KTILE - 1) / RHA_SPARSE_KTILE;
+  if (nkt > RHA_SPARSE_MAX_KTILES)
+    return fail(RHA_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)nkt, RHA_SPARSE_MAX_KTILES);
+  if (!empty(p, true)) RHA_TRY(need(block_mask, "block_mask", true, 1));
+  return stream_step(p, q_new, k_new, v_new, k_cache, v_cache, S, z, cursor, commit, block_mask, out, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 // ---- the step without allocation: its workspace in a file-scope device

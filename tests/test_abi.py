@@ -156,6 +156,34 @@ def test_stream_workspace_checks(L):
     assert L.rha_stream_workspace_size(None) == 0
 
 
+def _sstep(L, prob, cursor, mask=P, commit=1, **ptrs):
+    a = dict(q=P, k=P, v=P, kc=P, vc=P, S=P, z=P, out=P)
+    a.update(ptrs)
+    return L.rha_stream_step_sparse(ctypes.byref(prob), a["q"], a["k"], a["v"], a["kc"], a["vc"], a["S"], a["z"],
+                                    cursor, commit, mask, a["out"], None, None, 0, None)
+
+
+def test_stream_sparse_checks(L):
+    cur = _rha.Cursor(5)
+    # the pruned step: bf16, head_dim 128, no anchors, a mask; the plain step's rules
+    assert _sstep(L, _prob(window=3, dtype=_rha.RHA_F32, stride_t=128), ctypes.byref(cur)) == 2
+    assert _sstep(L, _prob(window=3, head_dim=64, stride_t=64), ctypes.byref(cur)) == 2
+    assert _sstep(L, _prob(window=3, anchor_chunks=1), ctypes.byref(cur)) == 2
+    assert "anchor" in L.rha_last_error().decode()
+    assert _sstep(L, _prob(window=3), ctypes.byref(cur), mask=None) == 1
+    assert "block_mask" in L.rha_last_error().decode()
+    assert _sstep(L, _prob(window=0), ctypes.byref(cur)) == 1
+    assert _sstep(L, _prob(window=3), None) == 3
+    assert _sstep(L, _prob(window=3), ctypes.byref(cur), kc=None) == 1
+    big = _prob(window=3, chunk_len=4096 * 16, stride_b=0, stride_h=0)
+    assert _sstep(L, big, ctypes.byref(cur)) == 2 and "key blocks" in L.rha_last_error().decode()
+    assert cur.t == 5  # nothing happened
+    # an empty problem needs no mask and still advances the cursor
+    assert _sstep(L, _prob(batch=0, window=3), ctypes.byref(cur), mask=None, q=None) == 0
+    assert cur.t == 6
+    assert _rha.stream_mask_shape(1, 12, 1560, 9) == (1, 12, 7, 220)
+
+
 def test_stream_empty_problem_advances_cursor(L):
     prob = _prob(batch=0, window=3)
     cur = _rha.Cursor(4)

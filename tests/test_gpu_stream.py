@@ -239,3 +239,104 @@ def test_stream_anchor_slots_keep_the_first_chunks():
     for j in range(a):
         assert torch.equal(st.k_cache[:, :, wl.w + j], chunk(k, j, wl.C))
         assert torch.equal(st.v_cache[:, :, wl.w + j], chunk(v, j, wl.C))
+
+
+# ---- pruned streaming steps (rha_stream_step_sparse): one block mask per
+# step over the window's keys in cache-slot order, against the oracle's pruned
+# streaming definition (pinned to brute force, to the plain hybrid and to the
+# whole-sequence pruned window)
+SPARSE_STREAM = {
+    # ring turns several times; 100-key chunks, so key blocks span two chunks
+    "bf16_d128_C100_w3": Workload("sp1", 330, B=1, H=2, d=128, C=100, N=9, w=3, dtype="bf16"),
+    # two query blocks per chunk (256 + 44 rows), q x4
+    "bf16_d128_C300_w4_q4": Workload("sp2", 331, B=1, H=1, d=128, C=300, N=7, w=4, dtype="bf16", qscale=4.0),
+    # chunks ending 24 rows past a 256-row tile (the short-tail pass), B = 2
+    "bf16_d128_C280_w3_B2": Workload("sp3", 332, B=2, H=1, d=128, C=280, N=6, w=3, dtype="bf16"),
+    # 24-row chunks (tails only) and w = 1
+    "bf16_d128_C24_w4": Workload("sp4", 333, B=1, H=2, d=128, C=24, N=9, w=4, dtype="bf16"),
+    "bf16_d128_C128_w1": Workload("sp5", 334, B=1, H=2, d=128, C=128, N=5, w=1, dtype="bf16"),
+}
+
+
+def _stream_masks(wl, density, seed):
+    from synth import gen_block_mask
+    shape = rha.stream_mask_shape(wl.B, wl.H, wl.C, wl.w)
+    return gen_block_mask((wl.N,) + shape, density, seed)  # [N, B, H, nqt, nkt]
+
+
+def run_sparse_stream(wl, q, k, v, masks, split):
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV, split=split)
+    outs, lses = [], []
+    for t in range(wl.N):
+        l = torch.empty((wl.B, wl.H, wl.C), dtype=torch.float32, device=DEV)
+        outs.append(rha.stream_step_sparse(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C),
+                                           masks[t].contiguous().to(DEV), lse=l))
+        lses.append(l)
+    torch.cuda.synchronize()
+    return st, outs, lses
+
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("density", [0.85, 0.5, 0.15])
+@pytest.mark.parametrize("name", sorted(SPARSE_STREAM))
+def test_stream_sparse_matches_oracle(name, density, split):
+    wl = SPARSE_STREAM[name]
+    q, k, v = gen_qkv(wl)
+    masks = _stream_masks(wl, density, wl.wid * 10 + int(100 * density))
+    st, outs, lses = run_sparse_stream(wl, q, k, v, masks, split)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    m = masks.numpy().transpose(1, 2, 0, 3, 4)  # [B, H, N, nqt, nkt]
+    ref, den = oracle.stream_block_sparse_batched(q64, k64, v64, wl.C, wl.w, m, return_den=True)
+    for t, (o, l) in enumerate(zip(outs, lses)):
+        sl = slice(t * wl.C, (t + 1) * wl.C)
+        og, lg, dt = to64(o), to64(l), den[:, :, sl]
+        empty = dt == 0
+        assert np.all(og[empty] == 0) and np.all(np.isneginf(lg[empty])), f"step {t}: rows without weight"
+        if (~empty).any():
+            e = rel_l2(np.where(empty[..., None], 0.0, og), ref[:, :, sl])
+            assert e <= TOL["bf16"], f"step {t}: rel-L2 {e:.3e}"
+            assert np.abs(lg[~empty] - np.log(dt[~empty])).max() <= 1e-2
+    for b in range(wl.B):
+        for h in range(wl.H):
+            Sref, zref = oracle.state_after(k64[b, h], v64[b, h], wl.C, wl.w, wl.N)
+            assert rel_l2(to64(st.S[b, h]), Sref) <= TOL["bf16"]
+            assert rel_l2(to64(st.z[b, h]), zref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", sorted(SPARSE_STREAM))
+def test_stream_sparse_all_kept_equals_plain_step(name):
+    wl = SPARSE_STREAM[name]
+    q, k, v = gen_qkv(wl)
+    ones = torch.ones((wl.N,) + rha.stream_mask_shape(wl.B, wl.H, wl.C, wl.w), dtype=torch.uint8)
+    st1, outs1, lses1 = run_sparse_stream(wl, q, k, v, ones, split=False)
+    st0, outs0, lses0 = run_stream(wl, q, k, v, wl.N, lse=True, split=False)
+    for t in range(wl.N):
+        assert torch.equal(outs1[t], outs0[t]) and torch.equal(lses1[t], lses0[t]), f"step {t}"
+    assert torch.equal(st1.S, st0.S) and torch.equal(st1.z, st0.z)
+
+
+@pytest.mark.timeout(900)
+def test_stream_sparse_workload_half_kept_sampled_rows():
+    """The 9-frame streaming workload's first 30 chunks, half the blocks of
+    each step kept: sampled rows of every step against the oracle."""
+    wl = CONFIGS["stream"].replace(N=30)
+    print(f"[parity] pruned stream: H{wl.H} C{wl.C} w{wl.w} chunks {wl.N}", flush=True)
+    q, k, v = gen_qkv(wl)
+    masks = _stream_masks(wl, 0.5, 41)
+    st = rha.StreamState(wl.B, wl.H, wl.d, wl.C, wl.w, device=DEV)
+    rng = np.random.default_rng(11)
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    Sref, zref = oracle.state_scan_batched(k64, v64, wl.C, wl.w)
+    grouped = GroupedRows("pruned stream")
+    heads = (0, 5, 11)
+    for t in range(wl.N):
+        o = rha.stream_step_sparse(st, chunk(q, t, wl.C), chunk(k, t, wl.C), chunk(v, t, wl.C),
+                                   masks[t].contiguous().to(DEV))
+        rows = np.unique(np.concatenate([[0, 255, 256, wl.C - 25, wl.C - 24, wl.C - 1], rng.integers(0, wl.C, 6)]))
+        og = o.cpu()
+        for h in heads:
+            ref = oracle.stream_block_sparse_rows(q64[0, h], k64[0, h], v64[0, h], wl.C, wl.w, t,
+                                                  masks[t, 0, h].numpy(), rows, S=Sref[0, h], z=zref[0, h])
+            grouped.add((0, h, t), og[0, h, rows].double().numpy(), ref)
+    torch.cuda.synchronize()
+    grouped.check(TOL["bf16"])
