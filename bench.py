@@ -9,7 +9,7 @@ Gaussians resident in HBM before timing starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Extra modes used for profiling (not part of the contract):
-    --only fwd|scan|stream|sparse|bidir|anchor|bwd|bwd_bidir|bwd_anchor|bwd_sparse
+    --only fwd|scan|stream|stream_sparse|sparse|bidir|anchor|bwd|bwd_bidir|bwd_anchor|bwd_sparse
                           run just that call --steps times (for rocprofv3)
     --copy-calib             run a plain device copy of a known size (counter calibration)
 """
@@ -183,6 +183,19 @@ def stream_step_flops(C, w, d, BH):
     return BH * C * (4 * d * w * C + 2 * d * d + 2 * d) + BH * C * (2 * d * d + 2 * d)
 
 
+def stream_sparse_step_flops(C, w, d, mask, qtile=256, ktile=64):
+    """Algorithmic FLOPs of one rha_stream_step_sparse with a full window: as
+    stream_step_flops, but the window's 4d per (query, key) pair counts only
+    the pairs of kept blocks.  mask: numpy [B, H, nqt, nkt] of the step."""
+    B, H = mask.shape[:2]
+    keys = [max(0, min(ktile, w * C - ktile * j)) for j in range(mask.shape[3])]
+    f = 0
+    for i in range(mask.shape[2]):
+        rows = min(C, qtile * (i + 1)) - qtile * i
+        f += rows * 4 * d * int((mask[:, :, i, :].astype(int) * keys).sum())
+    return f + B * H * C * (2 * d * d + 2 * d) * 2
+
+
 def stream_step_bytes(C, w, d, BH, elem=2):
     """Algorithmic HBM bytes of one rha_stream_step with a full window, the
     method's own traffic: new q, k, v read and out written; the new k, v
@@ -294,7 +307,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # ~0.2 s of work before the timed region, so the GPU clocks have settled
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["fwd", "scan", "stream", "sparse", "bidir", "anchor", "bwd", "bwd_bidir",
+    ap.add_argument("--only", choices=["fwd", "scan", "stream", "stream_sparse", "sparse", "bidir", "anchor", "bwd", "bwd_bidir",
                                        "bwd_anchor", "bwd_sparse"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
@@ -355,15 +368,23 @@ def main():
 
     # ---- streaming workload (9-frame window, 21-chunk prefill, 60 steps): it
     # allocates its own tensors and needs nothing from the other sections
-    def stream_run():
+    def stream_run(pruned=False):
         sw = CONFIGS["stream"]
         sq, sk, sv = (t.to(dev) for t in gen_qkv(sw))
         sout = torch.empty_like(sq)  # step outputs land in place, with the inputs' strides
         st = rha.StreamState(sw.B, sw.H, sw.d, sw.C, sw.w, device=dev)
+        # pruned steps: half of each step's blocks kept (seeded, one mask per chunk)
+        smask_cpu = (gen_block_mask((sw.N,) + rha.stream_mask_shape(sw.B, sw.H, sw.C, sw.w), 0.5, seed=43)
+                     if pruned else None)
+        smask = smask_cpu.to(dev) if pruned else None
 
         def push(t):
             sl = slice(t * sw.C, (t + 1) * sw.C)
-            rha.stream_step(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], out=sout[:, :, sl], stream=stream)
+            if pruned:
+                rha.stream_step_sparse(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], smask[t], out=sout[:, :, sl],
+                                       stream=stream)
+            else:
+                rha.stream_step(st, sq[:, :, sl], sk[:, :, sl], sv[:, :, sl], out=sout[:, :, sl], stream=stream)
 
         for t in range(sw.prefill):
             push(t)
@@ -392,10 +413,18 @@ def main():
         mean = e0.elapsed_time(e1) / 1e3 / sw.steps
         del sq, sk, sv, sout, st
         torch.cuda.empty_cache()
+        if pruned:  # the timed steps' mean algorithmic FLOPs
+            flops = np.mean([stream_sparse_step_flops(sw.C, sw.w, sw.d, smask_cpu[t].numpy())
+                             for t in range(sw.prefill, sw.prefill + sw.steps)])
+            return sw, float(mean), float(np.median(per)), float(per.min()), float(flops)
         return sw, float(mean), float(np.median(per)), float(per.min())
 
     if args.only == "stream":
         stream_run()
+        torch.cuda.synchronize()
+        return
+    if args.only == "stream_sparse":
+        stream_run(pruned=True)
         torch.cuda.synchronize()
         return
 
@@ -573,6 +602,7 @@ def main():
     scan_call()  # S, z of the headline problem again (the backward set-up wrote them too)
 
     sw, t_stream, t_stream_med, t_stream_min = stream_run()
+    _, t_sstream, t_sstream_med, _, ssF = stream_run(pruned=True)
 
     # ---- the two larger shapes (scan + fwd, each timed on its own); inputs
     # drawn on the GPU from a seeded generator with the same distribution (the
@@ -673,6 +703,10 @@ def main():
             "stream_step_min_us": t_stream_min * 1e6,
             "stream_chunks_per_s": 1.0 / t_stream,
             "stream_step_TFLOPs": sF / t_stream / 1e12,
+            "stream_sparse_half_step_us": t_sstream * 1e6,
+            "stream_sparse_half_step_median_us": t_sstream_med * 1e6,
+            "stream_sparse_half_step_TFLOPs": ssF / t_sstream / 1e12,
+            "stream_sparse_half_step_mfma_frac": ssF / t_sstream / 1e12 / PEAK_BF16_TFLOPS,
             "stream_step_mfma_frac": sF / t_stream / 1e12 / PEAK_BF16_TFLOPS,
             "stream_step_bytes": sB,
             "stream_step_GBps": sB / t_stream / 1e9,

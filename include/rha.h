@@ -379,8 +379,8 @@ size_t rha_stream_workspace_size(const rha_problem* p);
  *   block_mask : uint8 [B, H, ceil(C / RHA_SPARSE_QTILE), ceil(w * C / RHA_SPARSE_KTILE)]
  *                contiguous device memory (read); nonzero keeps the block;
  *                entries past the keys in use (t < w-1) are ignored.
- *   other arguments as for rha_stream_step.  The window's attention runs
- *   unsplit (the workspace, if any, serves the split fold).
+ *   other arguments as for rha_stream_step, the workspace included (each
+ *   split of the key window visits the kept blocks of its share).
  *
  * Errors: as rha_stream_step; RHA_ERR_UNSUPPORTED unless dtype is RHA_BF16,
  * head_dim is 128 and anchor_chunks is 0, or when the window spans more than

@@ -573,8 +573,7 @@ rha_status stream_step(const rha_problem* p, const void* q_new, const void* k_ne
   const int64_t n_anc = left > 0 ? (left < a ? left : a) : 0;
   const int n_keys = (int)((in_window + n_anc) * C);
   const bool fold = commit && left >= 0 && left >= a;
-  // (a pruned step's attention runs unsplit)
-  const int splits = workspace != nullptr && block_mask == nullptr ? stream_splits(p, n_keys) : 1;
+  const int splits = workspace != nullptr ? stream_splits(p, n_keys) : 1;
   const size_t fwd_part = splits > 1 ? align256(rha::fwd_split_bytes(p->batch, p->heads, C, d, splits)) : 0;
   const bool split_fwd = splits > 1 && workspace_bytes >= fwd_part;
   // beside a split attention the fold takes the compute units the attention

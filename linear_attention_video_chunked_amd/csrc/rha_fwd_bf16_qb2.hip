@@ -127,7 +127,7 @@ template <int D, int NW, bool FIRST, bool PARTIAL, int VIS>
 __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]) {
   static_assert(D == Q2_D, "tile buffers are sized for head dimension 128");
   constexpr bool SPARSE = VIS == 1, ANCH = VIS == 2;
-  static_assert(!(PARTIAL && VIS != 0), "pruned and anchored passes are not split");
+  static_assert(!(PARTIAL && ANCH), "anchored passes are not split");
   constexpr int THREADS = NW * 64, QB = Q2_QB, BM = NW * 32 * Q2_QB;
   constexpr int DS = D / 16, DB = D / 32, GR = D / 8;
   constexpr int TILE = BN * D * 2;
@@ -216,7 +216,10 @@ __device__ __forceinline__ int tile_pass(const FwdParams& p, float (&mio)[Q2_QB]
   // act(t) is the window tile that visit t loads.
   int Tp = T;
   if constexpr (SPARSE) {
-    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + tile) * p.nkt;
+    // (a split streaming pass lists the kept tiles of its own share: its
+    // first tile is tile kbeg / BN of the step's window)
+    const unsigned char* mrow = p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + tile) * p.nkt +
+                                (p.stream_mode ? kbeg / BN : 0);
     if (wave == 0) {
       int base = 0;
       for (int j0 = 0; j0 < T; j0 += 64) {
@@ -1053,7 +1056,9 @@ __device__ __noinline__ void tail_pass(const FwdParams pin) {
   auto blk_start = [&](int j) { return j < nA ? (int64_t)RB * j : r1b + (int64_t)RB * (j - nA); };
   auto blk_end = [&](int j) { return j < nA ? r0e : r1e; };
   const unsigned char* mrow =
-      SPARSE ? p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + p.mask_qtiles - 1) * p.nkt : nullptr;
+      SPARSE ? p.kmask + (((int64_t)bh * p.n_qchunks + c) * p.mask_qtiles + p.mask_qtiles - 1) * p.nkt +
+                   (p.stream_mode ? kbeg / 64 : 0)
+             : nullptr;
   // first visited block at or after j (j1 if none); the mask byte is the same
   // in every lane, and readfirstlane keeps the search (and the block loop
   // after it) in scalar control flow: the transposed reads and lane swaps of
@@ -1340,11 +1345,11 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p, con
       num[2 * i + 1] = fmaf(wgt, bf16_hi(x[i]), num[2 * i + 1]);
     }
   }
-  const float inv = 1.0f / den;
+  const float inv = den > 0.f ? 1.0f / den : 0.f;  // (pruned: a row with no weight at all gets 0)
   bf16_t* dst = (bf16_t*)p.out + b * p.q_sb + h * p.q_sh + (int64_t)row * p.q_st + col;
   st16(dst, u32x4{pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv),
                   pack_bf16(num[4] * inv, num[5] * inv), pack_bf16(num[6] * inv, num[7] * inv)});
-  if (p.lse != nullptr && col == 0) p.lse[(int64_t)bh * p.C + row] = (mmax + __log2f(den)) * kLn2;
+  if (p.lse != nullptr && col == 0) p.lse[(int64_t)bh * p.C + row] = den > 0.f ? (mmax + __log2f(den)) * kLn2 : -INFINITY;
 }
 
 template <int NW>
@@ -1363,7 +1368,10 @@ hipError_t launch_nw(FwdParams& p, hipStream_t s, const ChunkStateParams& fold =
   p.total_tiles = p.B * p.H * p.n_qchunks * p.tiles_per_chunk * splits;
   const int64_t grid = p.total_tiles;
   if (grid == 0) return hipSuccess;
-  if (splits > 1)
+  if (splits > 1 && p.kmask != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 1>), dim3((unsigned)(grid + fold_blocks)), dim3(NW * 64), 0,
+                       s, p, fold);
+  else if (splits > 1)
     hipLaunchKernelGGL((fwd_bf16_qb2_kernel<128, NW, true, 0>), dim3((unsigned)(grid + fold_blocks)), dim3(NW * 64), 0,
                        s, p, fold);
   else if (p.kmask != nullptr)

@@ -112,3 +112,14 @@ def test_sparse_bwd_count_limits_and_brute_force():
     rows = sum(C for c in range(N) if c >= w) * B * H
     folded = sum(C for c in range(N) if c <= N - 1 - w) * B * H
     assert bench.sparse_bwd_flops(C, N, w, d, m, qtile=2, ktile=3) == pairs * 10 * d + (rows + folded) * 4 * d * d
+
+
+def test_stream_sparse_count_all_kept_and_one_block():
+    C, w, d, B, H = 1560, 9, 128, 1, 12
+    nqt, nkt = -(-C // 256), -(-(w * C) // 64)
+    ones = np.ones((B, H, nqt, nkt), np.uint8)
+    full = bench.stream_sparse_step_flops(C, w, d, ones)
+    assert full == bench.stream_step_flops(C, w, d, B * H)
+    m = ones.copy()
+    m[0, 3, 6, nkt - 1] = 0  # the last query block (24 rows) x the last key block (24 keys)
+    assert full - bench.stream_sparse_step_flops(C, w, d, m) == 24 * 24 * 4 * d
