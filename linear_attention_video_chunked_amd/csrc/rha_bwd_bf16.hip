@@ -165,9 +165,38 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int ktiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * ktiles;
-  const int logical = xcd_remap(blockIdx.x, total);
-  const int tile = logical % ktiles, rest = logical / ktiles;
-  const int j = rest % p.N, bh = rest / p.N;  // earlier key chunks (more query chunks see them) first
+  int tile, j, bh;
+  if (p.anchors > 0 && p.anchors < p.N) {
+    // Anchored: a workgroup of an anchor chunk walks every later query chunk,
+    // several times the others' work.  The first `heavy` workgroup ids (the
+    // first in every XCD's queue) take those, each XCD a contiguous range of
+    // them; the rest take the other key chunks, each XCD a contiguous range.
+    const int bid = blockIdx.x, x = bid & 7;
+    const int heavy = p.B * p.H * p.anchors * ktiles;
+    if (bid < heavy) {
+      const int hi = xcd_remap(bid, heavy);
+      tile = hi % ktiles;
+      const int rest = hi / ktiles;
+      j = rest % p.anchors;
+      bh = rest / p.anchors;
+    } else {
+      auto per_xcd = [](int n, int xx) { return n > xx ? (n - xx + 7) / 8 : 0; };  // ids < n on XCD xx
+      int start = 0;
+      for (int xx = 0; xx < x; ++xx) start += per_xcd(total, xx) - per_xcd(heavy, xx);
+      const int li = start + (bid >> 3) - per_xcd(heavy, x);
+      const int nl = p.N - p.anchors;
+      tile = li % ktiles;
+      const int rest = li / ktiles;
+      j = p.anchors + rest % nl;
+      bh = rest / nl;
+    }
+  } else {
+    const int logical = xcd_remap(blockIdx.x, total);
+    tile = logical % ktiles;
+    const int rest = logical / ktiles;
+    j = rest % p.N;  // earlier key chunks (more query chunks see them) first
+    bh = rest / p.N;
+  }
   const int b = bh / p.H, h = bh % p.H;
   const int64_t L = (int64_t)p.N * p.C;
   const int64_t head = b * p.sb + h * p.sh;
