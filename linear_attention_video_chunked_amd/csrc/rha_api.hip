@@ -141,7 +141,7 @@ int stream_splits(const rha_problem* p, int64_t n_keys) {
   int64_t splits = cus / (tiles > 0 ? tiles : 1);
   const int64_t key_tiles = (n_keys + 63) / 64;
   if (splits > key_tiles / 4) splits = key_tiles / 4;
-  if (splits > 8) splits = 8;
+  if (splits > rha::kMaxSplits) splits = rha::kMaxSplits;
   return splits < 2 ? 1 : (int)splits;
 }
 

@@ -1328,21 +1328,33 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const FwdParams p, con
   const int64_t pidx0 = ((int64_t)bh * p.tiles_per_chunk + tile) * p.n_splits;
   const bf16_t* pn = reinterpret_cast<const bf16_t*>(p.part);
   const float* plm = reinterpret_cast<const float*>(pn + n_part * BM * D);
+  // every split's {denominator, reference} and row slice requested at once
+  // (at most kMaxSplits splits)
+  f32x2 lmv[kMaxSplits];
+  u32x4 xs[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < p.n_splits) {
+      lmv[sp] = *reinterpret_cast<const f32x2*>(plm + ((pidx0 + sp) * BM + trow) * 2);
+      xs[sp] = ld16(pn + ((pidx0 + sp) * BM + trow) * D + col);
+    }
   float mmax = -INFINITY;
-  for (int sp = 0; sp < p.n_splits; ++sp) mmax = fmaxf(mmax, plm[((pidx0 + sp) * BM + trow) * 2 + 1]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    if (sp < p.n_splits) mmax = fmaxf(mmax, lmv[sp][1]);
   // split sp holds its rows normalised by its denominator l_sp at reference
   // m_sp: its weight is l_sp 2^(m_sp - mmax)
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int sp = 0; sp < p.n_splits; ++sp) {
-    const float* lm = plm + ((pidx0 + sp) * BM + trow) * 2;
-    const float wgt = lm[1] == -INFINITY ? 0.f : lm[0] * __builtin_amdgcn_exp2f(lm[1] - mmax);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    if (sp >= p.n_splits) break;
+    const float wgt = lmv[sp][1] == -INFINITY ? 0.f : lmv[sp][0] * __builtin_amdgcn_exp2f(lmv[sp][1] - mmax);
     den += wgt;
-    const u32x4 x = ld16(pn + ((pidx0 + sp) * BM + trow) * D + col);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      num[2 * i] = fmaf(wgt, bf16_lo(x[i]), num[2 * i]);
-      num[2 * i + 1] = fmaf(wgt, bf16_hi(x[i]), num[2 * i + 1]);
+      num[2 * i] = fmaf(wgt, bf16_lo(xs[sp][i]), num[2 * i]);
+      num[2 * i + 1] = fmaf(wgt, bf16_hi(xs[sp][i]), num[2 * i + 1]);
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;  // (pruned: a row with no weight at all gets 0)

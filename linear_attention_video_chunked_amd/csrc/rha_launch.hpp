@@ -71,6 +71,8 @@ struct FwdParams {
 
 // Most key tiles per window of a pruned pass (the kept-tile list lives in LDS).
 constexpr int kSparseMaxKeyTiles = 2048;
+// most workgroups a streaming step splits one query tile's key window over
+constexpr int kMaxSplits = 8;
 // the pruned backward pass's key-gradient kernel lists at most this many
 // 32-row query blocks per workgroup (beyond it, it visits every block)
 constexpr int kMaxListedQBlocks = 2048;

@@ -10,18 +10,24 @@ namespace rha {
 
 // One 16-byte unit of the cache copy: tensor `which` (0: src -> dst, 1: src2
 // -> dst2), head bh, unit i of that head's C * d * elem_bytes / 16.
-__device__ __forceinline__ void copy_unit(const CopyParams& p, int which, int bh, int i) {
+// Source and destination of that unit.
+__device__ __forceinline__ void copy_addr(const CopyParams& p, int which, int bh, int i, const unsigned char*& src,
+                                          unsigned char*& dst) {
   const int row_vecs = p.d * p.elem_bytes / 16;
-  if (i >= p.C * row_vecs) return;
   const void* srcp = which ? p.src2 : p.src;
   void* dstp = which ? p.dst2 : p.dst;
   const int t = i / row_vecs, vcol = i - t * row_vecs;
   const int b = bh / p.H, h = bh - b * p.H;
-  const unsigned char* src = (const unsigned char*)srcp +
-                             ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
-                             vcol * 16;
-  unsigned char* dst = (unsigned char*)dstp +
-                       ((((int64_t)bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
+  src = (const unsigned char*)srcp + ((int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st) * p.elem_bytes +
+        vcol * 16;
+  dst = (unsigned char*)dstp + ((((int64_t)bh * p.w + p.slot) * p.C + t) * (int64_t)p.d) * p.elem_bytes + vcol * 16;
+}
+
+__device__ __forceinline__ void copy_unit(const CopyParams& p, int which, int bh, int i) {
+  if (i >= p.C * (p.d * p.elem_bytes / 16)) return;
+  const unsigned char* src;
+  unsigned char* dst;
+  copy_addr(p, which, bh, i, src, dst);
   st16(dst, ld16(src));
 }
 
