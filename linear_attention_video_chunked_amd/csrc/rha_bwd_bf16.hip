@@ -557,9 +557,15 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   // pruned pass: the kept 64-key tiles of the workgroup's query tile, in order
   __shared__ unsigned short kept_s[SPARSE ? kSparseMaxKeyTiles : 1];
   __shared__ int kept_n;
-  __shared__ __attribute__((aligned(1024))) unsigned char ks_t[2][ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char vs_t[2][ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char sm[BD * BD * 2];  // S_c as bf16 rows
+  // One 64 KiB arena: during the key loop three buffers of a 32-key block's
+  // K and V rows (8 KiB each); in the epilogue S_c as bf16 rows (32 KiB) and
+  // its low parts (two 16 KiB halves).
+  __shared__ __attribute__((aligned(1024))) unsigned char arena[4 * BD * BD];
+  auto ks_t = [&](int buf) __attribute__((always_inline)) { return arena + buf * (2 * ROWT); };
+  auto vs_t = [&](int buf) __attribute__((always_inline)) { return arena + buf * (2 * ROWT) + ROWT; };
+  unsigned char* const sm = arena;                         // S_c as bf16 rows
+  unsigned char* const slo_k = arena + BD * BD * 2;        // low parts, rows 0..63
+  unsigned char* const slo_v = arena + BD * BD * 2 + BD * BD;  // low parts, rows 64..127
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int qtiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * qtiles;
@@ -635,8 +641,8 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     return (int)min((int64_t)RB, (bi < nba ? a_end : kend) - blk_k0(bi));
   };
   // 32-key blocks of K and V reach LDS through buffer loads that write LDS
-  // directly, one block ahead (two buffers), as in bwd_dkdv_kernel; keys
-  // past the window read as zero, and their probabilities are masked.
+  // directly, two blocks ahead (three buffers); keys past the window read as
+  // zero, and their probabilities are masked.
   typedef __attribute__((address_space(3))) void lds_void;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int st2 = (int)p.st * 2;  // bytes between rows
@@ -650,29 +656,34 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     constexpr int BUF = decltype(buf_c)::value;
     const int64_t k0 = blk_k0(bi);
     const int nk = blk_nk(bi);
-    if constexpr (SPARSE)
-      if (nk <= 0) return;  // nothing to load
-    const int nbytes = (nk - 1) * st2 + BD * 2;
+    // (a block with no key still issues its loads, which read zeros: every
+    // block counts the same loads in the waits below)
+    const int nbytes = nk > 0 ? (nk - 1) * st2 + BD * 2 : 0;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vb + k0 * p.st), (short)0, nbytes, fwd::kBufWord3);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(ks_t[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vs_t[BUF] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(ks_t(BUF) + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vs_t(BUF) + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
     }
   };
   auto block = [&](int bi, auto buf_c) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
-    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block bi are in LDS
-    __syncthreads();  // every wave's; and every wave is done with block bi-1 (the other buffer)
-    if (bi + 1 < nblk) issue(bi + 1, std::integral_constant<int, BUF ^ 1>{});
+    // this wave's loads of block bi are in LDS (those of block bi+1, four,
+    // may still be in flight)
+    if (bi + 1 < nblk)
+      __builtin_amdgcn_s_waitcnt(fwd::wait_vm(4));
+    else
+      __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
+    __syncthreads();  // every wave's; and every wave is done with block bi-1, whose buffer block bi+2 takes
+    if (bi + 2 < nblk) issue(bi + 2, std::integral_constant<int, (BUF + 2) % 3>{});
     const int nk = blk_nk(bi);
     if constexpr (SPARSE)
       if (nk <= 0) return;  // the same for the whole workgroup: no barrier is skipped by some waves only
-    const unsigned char* kt = ks_t[BUF];
-    const unsigned char* vt = vs_t[BUF];
+    const unsigned char* kt = ks_t(BUF);
+    const unsigned char* vt = vs_t(BUF);
     f32x16 sa = {}, pa = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -705,13 +716,17 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   if (nblk > 0) issue(0, B0{});
+  if (nblk > 1) issue(1, B1{});
   int bi = 0;
-  for (; bi + 1 < nblk; bi += 2) {  // two blocks per iteration, so each one's buffer is known
+  for (; bi + 2 < nblk; bi += 3) {  // three blocks per iteration, so each one's buffer is known
     block(bi, B0{});
     block(bi + 1, B1{});
+    block(bi + 2, B2{});
   }
   if (bi < nblk) block(bi, B0{});
+  if (bi + 1 < nblk) block(bi + 1, B1{});
   __syncthreads();  // the epilogue reuses the K/V buffers
   float* dqr = p.dq + (bh * L + row0 + l32) * BD;
   // the chunk has a state (every chunk for w = 0; bidirectional, also a
@@ -725,7 +740,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
     // whole query gradient error budget; split, the term is exact to float32
     // level.  The low part of S goes into the K/V staging buffers, free now.
     const int64_t slot = (int64_t)bh * p.N + c;
-    stage_state_split(sm, ks_t[0], vs_t[0], p.S + slot * BD * BD, p.bidir ? p.S2 + slot * BD * BD : nullptr, tid);
+    stage_state_split(sm, slo_k, slo_v, p.S + slot * BD * BD, p.bidir ? p.S2 + slot * BD * BD : nullptr, tid);
     __syncthreads();
     const float rs = qok ? p.rsc[bh * L + row0 + l32] : 0.f;  // 1 / D_i
     const bf16_t* qt = qb + (row0 + l32) * p.st;                // phi' argument
@@ -737,7 +752,7 @@ __global__ __launch_bounds__(TB) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       f32x16 o1 = {};
-      const unsigned char* slo = nb < 2 ? ks_t[0] : vs_t[0];
+      const unsigned char* slo = nb < 2 ? slo_k : slo_v;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const u32x4 g = __builtin_bit_cast(u32x4, gr[ks]);
