@@ -607,8 +607,8 @@ def main():
     # ---- the two larger shapes (scan + fwd, each timed on its own); inputs
     # drawn on the GPU from a seeded generator with the same distribution (the
     # parity tests check these shapes against the oracle on sampled rows)
-    def other_shape(name, n_calls=5):
-        ow = CONFIGS[name]
+    def other_shape(name, n_calls=5, ow=None):
+        ow = CONFIGS[name] if ow is None else ow
         g = torch.Generator(device=dev).manual_seed(1000 + ow.wid)
         shape = (ow.B, ow.H, ow.L, ow.d)
         oq, ok, ov = (torch.randn(shape, generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
@@ -657,6 +657,9 @@ def main():
     more = {}
     for name in ("wan14b", "long"):
         more.update(other_shape(name))
+    # head_dim 64 at the Wan-1.3B model width (24 heads x 64 = 1536 features):
+    # the d = 64 kernel, measured only (its parity is tested at mid sizes)
+    more.update(other_shape("wan13b_d64", ow=CONFIGS["wan13b"].replace(name="wan13b_d64", wid=90, H=24, d=64)))
     F = fwd_flops(wl.C, wl.N, wl.w, wl.d, BH)
     achieved = F / t_fwd / 1e12
     traffic = read_traffic()
