@@ -60,27 +60,9 @@ __global__ __launch_bounds__(128) void prefix_kernel(const PrefixParams p) {
 // contiguous [B,H,w,C,d] cache; with src2 set, a second chunk into dst2
 // (blockIdx.y = 1).  blockIdx.x = bh * blocks_per_bh + block within the head,
 // so every per-thread index is 32-bit.
-// kCopyUnits 16-byte units per thread, 256 apart (each load instruction of a
-// wave reads 1 KiB in a row), every load issued before the first store.
-constexpr int kCopyUnits = 4;
 __global__ __launch_bounds__(256) void copy_chunk_kernel(const CopyParams p, int blocks_per_bh) {
   const int bh = blockIdx.x / blocks_per_bh;
-  const int i0 = (blockIdx.x - bh * blocks_per_bh) * 256 * kCopyUnits + threadIdx.x;
-  const int n = p.C * (p.d * p.elem_bytes / 16);
-  const unsigned char* src[kCopyUnits];
-  unsigned char* dst[kCopyUnits];
-  u32x4 v[kCopyUnits];
-#pragma unroll
-  for (int u = 0; u < kCopyUnits; ++u) {
-    const int i = i0 + 256 * u;
-    if (i < n) {
-      copy_addr(p, blockIdx.y, bh, i, src[u], dst[u]);
-      v[u] = ld16(src[u]);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyUnits; ++u)
-    if (i0 + 256 * u < n) st16(dst[u], v[u]);
+  copy_unit(p, blockIdx.y, bh, (blockIdx.x - bh * blocks_per_bh) * 256 + threadIdx.x);
 }
 
 __global__ __launch_bounds__(64) void state_combine_kernel(const StateCombineParams p) {
@@ -100,7 +82,7 @@ hipError_t launch_copy_chunk(const CopyParams& p, hipStream_t s) {
   const int64_t per_bh = (int64_t)p.C * (p.d * p.elem_bytes / 16);
   const int64_t BH = (int64_t)p.B * p.H;
   if (per_bh == 0 || BH == 0) return hipSuccess;
-  const int blocks_per_bh = (int)((per_bh + 256 * kCopyUnits - 1) / (256 * kCopyUnits));
+  const int blocks_per_bh = (int)((per_bh + 255) / 256);
   hipLaunchKernelGGL(copy_chunk_kernel, dim3((unsigned)(BH * blocks_per_bh), p.src2 != nullptr ? 2u : 1u), dim3(256), 0, s,
                      p, blocks_per_bh);
   return hipGetLastError();
