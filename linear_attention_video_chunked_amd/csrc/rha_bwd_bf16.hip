@@ -59,28 +59,33 @@ __device__ __forceinline__ void mfma_v(f32x16& acc, const bf16x8& a, const bf16x
 }
 
 // ---- delta_i = dout_i . out_i, 1 / D_i = exp(-lse_i), -delta_i / D_i, lse_i log2(e)
+// 16 lanes per row (one 16-byte granule of out and of dout each), so that a
+// wave's loads cover four whole rows; the partial dot products meet by lane
+// swaps within each group of 16.
+constexpr int kPrepRowsPerBlock = 16;
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
   const int64_t L = (int64_t)p.N * p.C;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)p.B * p.H * L) return;
-  const int64_t bh = idx / L, t = idx - bh * L;
-  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const int64_t off = b * p.sb + h * p.sh + t * p.st;
-  const bf16_t* o = (const bf16_t*)p.out + off;
-  const bf16_t* g = (const bf16_t*)p.dout + off;
+  const int gl = threadIdx.x & 15;
+  const int64_t idx = (int64_t)blockIdx.x * kPrepRowsPerBlock + (threadIdx.x >> 4);
+  const bool ok = idx < (int64_t)p.B * p.H * L;
   float acc = 0.f;
-#pragma unroll 4
-  for (int gr = 0; gr < BD / 8; ++gr) {
-    const u32x4 a = ld16(o + gr * 8), c = ld16(g + gr * 8);
+  if (ok) {
+    const int64_t bh = idx / L, t = idx - bh * L;
+    const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+    const int64_t off = b * p.sb + h * p.sh + t * p.st + gl * 8;
+    const u32x4 a = ld16((const bf16_t*)p.out + off), c = ld16((const bf16_t*)p.dout + off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc += bf16_lo(a[i]) * bf16_lo(c[i]) + bf16_hi(a[i]) * bf16_hi(c[i]);
   }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (!ok || gl >= 4) return;
+  // lanes 0..3 of the group write the row's four values
+  const float lse = p.lse[idx];
   // (a row left with no weight by a pruned window has lse = -inf, out = 0)
-  const float r = p.lse[idx] == -INFINITY ? 0.f : __expf(-p.lse[idx]);
-  p.lse2[idx] = p.lse[idx] * kLog2e;
-  p.delta[idx] = acc;
-  p.rsc[idx] = r;
-  p.zw[idx] = -acc * r;
+  const float r = lse == -INFINITY ? 0.f : __expf(-lse);
+  float* const dst = gl == 0 ? p.lse2 : gl == 1 ? p.delta : gl == 2 ? p.rsc : p.zw;
+  dst[idx] = gl == 0 ? lse * kLog2e : gl == 1 ? acc : gl == 2 ? r : -acc * r;
 }
 
 // ---- the linear term: rows times a d x d state M (float32, row-major),
@@ -805,7 +810,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t L = (int64_t)p.N * p.C;
   if (BH == 0 || L == 0) return hipSuccess;
   const int tiles128 = (p.C + 127) / 128;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((BH * L + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((BH * L + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock)),
+                     dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.w < p.N) {  // some chunk has a state: the linear term
