@@ -65,6 +65,8 @@ hipError_t launch_chunk_state_bf16(const ChunkStateParams& p, int d, hipStream_t
   const dim3 g64((unsigned)(heads_chunks * StateCfg<64>::ES + copy_blocks));
   if (d == 128 && copy_blocks == 0 && !scaled) {
     hipLaunchKernelGGL((chunk_state_bf16_both_kernel<false>), dim3((unsigned)heads_chunks), dim3(2 * THREADS), 0, s, p);
+  } else if (d == 128 && copy_blocks == 0) {  // scaled (the backward pass's state gradients)
+    hipLaunchKernelGGL((chunk_state_bf16_both_kernel<true>), dim3((unsigned)heads_chunks), dim3(2 * THREADS), 0, s, p);
   } else if (d == 128 && scaled)
     hipLaunchKernelGGL((chunk_state_bf16_kernel<128, true>), g128, dim3(THREADS), 0, s, p);
   else if (d == 128)
