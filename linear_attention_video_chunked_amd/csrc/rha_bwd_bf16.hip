@@ -18,11 +18,13 @@
 //   bwd_prep_kernel      delta, 1/D and -delta/D per row
 //   chunk state (rha_state_bf16.hip, scaled rows) for dS_c, dz_c, then a
 //   running sum from the last slot for dU_j, du_j
-//   bwd_dkdv_kernel      per 128 keys (32 per wave, rows of K and V held as
-//                        operands): every 32-row query block of the chunks
-//                        that see them -- S = Q K^T and dP = dO V^T with keys
-//                        on the lanes, then dV^T += dO^T P and dK^T += Q^T dS;
-//                        then the linear term of those keys (dU_j, du_j)
+//   bwd_dkdv_pp_kernel   per 128 keys, two waves per SIMD for each 32 of them:
+//                        a score wave (rows of K and V held as operands)
+//                        computes, per 32-row query block of the chunks that
+//                        see them, S = Q K^T and dP = dO V^T with keys on the
+//                        lanes, then P and dS; a gradient wave accumulates
+//                        dV^T += dO^T P and dK^T += Q^T dS, then adds the
+//                        linear term of those keys (dU_j, du_j)
 //   bwd_dq_kernel        per 128 query rows (32 per wave): every 32-key block
 //                        of the window -- S^T = K Q^T and dP^T = V dO^T with
 //                        queries on the lanes, then dQ^T += K^T dS^T; then the
@@ -93,10 +95,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
 // (mt); every thread of the workgroup takes part.
 // With M2 set, the staged matrix is M + M2, summed in float32 (the
 // bidirectional pass's past and future parts).
-template <bool TRANS>
+template <bool TRANS, int NT = TB>
 __device__ __forceinline__ void stage_state(unsigned char* mr, unsigned char* mt, const float* M, const float* M2,
                                             int tid) {
-  for (int u = tid; u < BD * BD / 8; u += TB) {
+  for (int u = tid; u < BD * BD / 8; u += NT) {
     const int e = u / (BD / 8), g = u % (BD / 8);
     f32x4 a = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8);
     f32x4 c4 = *reinterpret_cast<const f32x4*>(M + (int64_t)e * BD + g * 8 + 4);
@@ -149,33 +151,48 @@ __device__ __forceinline__ void dphi4(const bf16_t* row, int f, float out[4]) {
   for (int i = 0; i < 4; ++i) out[i] = xs[i] > 0.f ? 1.f : __expf(xs[i]);
 }
 
-// ---- window gradients of keys and values, then their linear term
-//   (key chunks j <= N-1-w): dv_t += dU_j^T phi(k_t),  dk_t += (dU_j v_t + du_j) * phi'(k_t)
-// SPARSE: pruned (query block, key block) pairs of the window have P = 0
-// (block_mask of the pruned forward pass).
+// ---- dK, dV with two waves per SIMD (eight per workgroup, 128 keys).
+// Waves 0-3 (score waves) each hold the K and V rows of 32 keys as operands
+// and compute, per 32-row query block, S = Q K^T and dP = dO V^T (keys on the
+// lanes), then P and dS = P (dP - delta); they hand P and dS, packed to bf16
+// pairs in register order, to the gradient wave of the same keys (wave 4 +
+// the same index) through LDS.  The gradient wave accumulates dV^T += dO^T P
+// and dK^T += Q^T dS one block behind, then adds the keys' linear term.  On a
+// SIMD the score wave's vector work (exponentials, dS) runs beside the
+// gradient wave's products: each step has two barriers, the score waves'
+// products before the second and their vector work after it, beside the
+// gradient waves' products.
+// Query blocks of the chunks whose window holds chunk j (j .. j + w - 1;
+// bidirectional j - w + 1 .. j + w - 1; an anchor chunk: every chunk from j
+// on), 32 rows each, reach LDS through buffer loads that write LDS directly,
+// two blocks ahead (four buffers; each wave one 4-row slice of the Q and the
+// dO tile, whose descriptors end at the chunk's last row: rows past it read as
+// zero, and such rows (q = dout = 0, lse = delta = 0: P = 1, dP = 0) add
+// nothing).  A pruned pass visits only the query blocks for which some key
+// tile of the workgroup is kept (listed in LDS) and gives a pruned key P = 0
+// lane by lane.  Anchor chunks' workgroups come first in every XCD's queue.
 template <bool SPARSE>
-__global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
-  // four buffers of (Q rows, dout rows, lse log2(e), delta) for one 32-row
-  // query block (64 entries of lse and delta: one per lane of the load)
-  __shared__ __attribute__((aligned(1024))) unsigned char qs[4][ROWT];
-  __shared__ __attribute__((aligned(1024))) unsigned char gs[4][ROWT];
+__global__ __launch_bounds__(2 * TB) void bwd_dkdv_pp_kernel(const BwdParams p) {
+  constexpr int NW = 2 * NWB;  // waves per workgroup
+  // Q tiles 0..3 and dO tiles 4..7 of the ring; in the epilogue dU as bf16
+  // rows (the first half) and its transpose (the second)
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[8][ROWT];
   __shared__ __attribute__((aligned(256))) float lse_s[4][64];
   __shared__ __attribute__((aligned(256))) float del_s[4][64];
-  // dU_j as bf16 rows, and its transpose
-  __shared__ __attribute__((aligned(1024))) unsigned char um[BD * BD * 2];
-  __shared__ __attribute__((aligned(1024))) unsigned char ut[BD * BD * 2];
-  // pruned pass: the query blocks for which some key of the workgroup is kept
+  // P and dS of a block from score wave k to gradient wave k: [buffer][k][P, dS][half][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][NWB][2][2][64];
   __shared__ unsigned short qlist[SPARSE ? kMaxListedQBlocks : 1];
   __shared__ int qlist_n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grad = wv >= NWB;  // gradient wave
+  const int kw = wv & (NWB - 1);  // the wave's 32 keys within the workgroup's 128
   const int ktiles = (p.C + 127) / 128;
   const int total = p.B * p.H * p.N * ktiles;
   int tile, j, bh;
   if (p.anchors > 0 && p.anchors < p.N) {
-    // Anchored: a workgroup of an anchor chunk walks every later query chunk,
-    // several times the others' work.  The first `heavy` workgroup ids (the
-    // first in every XCD's queue) take those, each XCD a contiguous range of
-    // them; the rest take the other key chunks, each XCD a contiguous range.
+    // anchor chunks' workgroups first in every XCD's queue (each XCD a
+    // contiguous range of them, and of the others)
     const int bid = blockIdx.x, x = bid & 7;
     const int heavy = p.B * p.H * p.anchors * ktiles;
     if (bid < heavy) {
@@ -185,7 +202,7 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
       j = rest % p.anchors;
       bh = rest / p.anchors;
     } else {
-      auto per_xcd = [](int n, int xx) { return n > xx ? (n - xx + 7) / 8 : 0; };  // ids < n on XCD xx
+      auto per_xcd = [](int n, int xx) { return n > xx ? (n - xx + 7) / 8 : 0; };
       int start = 0;
       for (int xx = 0; xx < x; ++xx) start += per_xcd(total, xx) - per_xcd(heavy, xx);
       const int li = start + (bid >> 3) - per_xcd(heavy, x);
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     const int logical = xcd_remap(blockIdx.x, total);
     tile = logical % ktiles;
     const int rest = logical / ktiles;
-    j = rest % p.N;  // earlier key chunks (more query chunks see them) first
+    j = rest % p.N;
     bh = rest / p.N;
   }
   const int b = bh / p.H, h = bh % p.H;
@@ -210,41 +227,18 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
   const bf16_t* vb = (const bf16_t*)p.v + head;
   const bf16_t* gb = (const bf16_t*)p.dout + head;
 
-  const int64_t key0 = (int64_t)j * p.C + 128 * tile + 32 * wave;  // this wave's first key
+  const int64_t key0 = (int64_t)j * p.C + 128 * tile + 32 * kw;  // the wave's first key
   const int nk = (int)max((int64_t)0, min((int64_t)32, (int64_t)(j + 1) * p.C - key0));
-  bf16x8 kr[8], vr[8];  // rows of K and V for this lane's key
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (l32 < nk) {
-      a = ld16(kb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
-      c = ld16(vb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
-    }
-    kr[ks] = __builtin_bit_cast(bf16x8, a);
-    vr[ks] = __builtin_bit_cast(bf16x8, c);
-  }
-  f32x16 dv[4], dk[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) dv[nb] = dk[nb] = f32x16{};
 
-  // query blocks of the chunks whose window holds chunk j (j .. j + w - 1),
-  // 32 rows each, numbered qi = (c - j) * nqb + block
-  // (bidirectional: chunks j - w + 1 .. j + w - 1)
-  // (anchored: an anchor chunk is a softmax key of every chunk from j on)
   const int c_lo = p.bidir ? max(0, j - p.w + 1) : j;
   const int c_hi = j < p.anchors ? p.N - 1 : p.w > 0 ? min(p.N - 1, j + p.w - 1) : j - 1;
   const int nqb = (p.C + RB - 1) / RB;
   int nblk = max(0, c_hi - c_lo + 1) * nqb;
-  // Pruned pass: the pipeline visits only the query blocks (in order) for
-  // which one of the key tiles that the workgroup's 128 keys touch is kept;
-  // the blocks are listed in LDS first (wave 0, 64 at a time), unless there
-  // are more than the list holds (then every block is visited).  Keys of a
-  // pruned tile within a visited block get P = 0 lane by lane (keep_of).
   bool listed = false;
   if constexpr (SPARSE) {
     if (nblk <= kMaxListedQBlocks) {
       listed = true;
-      if (wave == 0) {
+      if (wv == 0) {
         const int64_t kw0 = (int64_t)j * p.C + 128 * tile;  // the workgroup's first key
         const int nkw = min(128, p.C - 128 * tile);
         int base = 0;
@@ -268,28 +262,19 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
       nblk = __builtin_amdgcn_readfirstlane(qlist_n);
     }
   }
-  // the query block that pipeline step i works on
   auto qidx = [&](int i) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE)
       if (listed) return __builtin_amdgcn_readfirstlane(qlist[i]);
     return i;
   };
-  // Query blocks reach LDS through buffer loads that write LDS directly, two
-  // blocks ahead (block x in buffer x % 4).  A 32-row tile is 8 loads of 4
-  // rows (64 lanes x 16 bytes); wave w issues loads 2w and 2w+1 of the Q tile
-  // and of the dO tile, each lane fetching the global granule that the
-  // swizzle puts at its LDS slot.  The descriptors end at the chunk's last
-  // row, so rows past it read as zero; such rows (q = dout = 0, lse = delta =
-  // 0: P = 1, dP = 0) add exactly nothing to dV and dK.  Waves 0 and 1 load
-  // the block's lse log2(e) and delta.
+  // loads: each wave one 4-row load of the Q tile and one of the dO tile;
+  // waves 0 and 1 the block's lse log2(e) and delta
   typedef __attribute__((address_space(3))) void lds_void;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int st2 = (int)p.st * 2;  // bytes between rows
-  int doff[2];                    // this lane's byte offset within a tile, loads 2wv and 2wv+1
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int row = 4 * (2 * wv + x) + (lane >> 4);
-    doff[x] = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
+  const int st2 = (int)p.st * 2;
+  int doff;
+  {
+    const int row = 4 * wv + (lane >> 4);
+    doff = row * st2 + (((lane & 15) ^ fsw(row)) * 16);
   }
   auto issue = [&](int i) __attribute__((always_inline)) {
     const int bo = i & 3;
@@ -302,11 +287,8 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(qb + row0 * p.st), (short)0, nbytes, fwd::kBufWord3);
     const __amdgpu_buffer_rsrc_t grs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(gb + row0 * p.st), (short)0, nbytes, fwd::kBufWord3);
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(qs[bo] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)(gs[bo] + (2 * wv + x) * 1024), 16, doff[x], 0, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(ring[bo] + wv * 1024), 16, doff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)(ring[4 + bo] + wv * 1024), 16, doff, 0, 0, 0);
     if (wv < 2) {
       const float* src = (wv == 0 ? p.lse2 : p.delta) + bh * L + row0;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nq * 4, fwd::kBufWord3);
@@ -314,244 +296,196 @@ __global__ __launch_bounds__(TB) void bwd_dkdv_kernel(const BwdParams p) {
     }
   };
 
-  // Software pipeline over the query blocks.  Iteration i runs eight rounds;
-  // round r issues one product of each of four chains and a slice of vector
-  // work:
-  //   S and dP of block i+1, feature step r            (rounds 0-7)
-  //   dV, dK of block i-1 over its queries 16-31, nb = r   (rounds 0-3)
-  //   dV, dK of block i over its queries 0-15, nb = r - 4  (rounds 4-7)
-  //   P and dS of block i, output elements 2r, 2r+1 (the scores of the
-  //   previous iteration): elements 0-7 feed rounds 4-7, elements 8-15 the
-  //   next iteration's rounds 0-3.
-  // Fragments are read two rounds ahead.  Buffer (i+2) % 4 is loaded
-  // meanwhile; block i-1's is still read in this iteration, block i-2's is not.
-  using fwd::kWaitLgkm0;
-  auto qt_of = [&](int x) __attribute__((always_inline)) { return qs[x & 3]; };
-  auto gt_of = [&](int x) __attribute__((always_inline)) { return gs[x & 3]; };
-  // S and dP of block x, all eight feature steps (the pipeline's prologue)
-  auto scores = [&](int x, f32x16& sx, f32x16& px) __attribute__((always_inline)) {
-    const unsigned char* qt = qt_of(x);
-    const unsigned char* gt = gt_of(x);
-    bf16x8 qf[8], gf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[ks] = row_frag(qt, 0, ks, lane);
-      gf[ks] = row_frag(gt, 0, ks, lane);
-    }
-    mfma_v_first(sx, qf[0], kr[0]);
-    mfma_v_first(px, gf[0], vr[0]);
-#pragma unroll
-    for (int ks = 1; ks < 8; ++ks) {
-      mfma_v(sx, qf[ks], kr[ks]);
-      mfma_v(px, gf[ks], vr[ks]);
-    }
-  };
-  // dV, dK of block x over its queries 16-31 (after the last iteration)
-  auto tail_products = [&](int x, const uint32_t (&ph)[4], const uint32_t (&dh)[4]) __attribute__((always_inline)) {
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8 db = __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]});
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      dv[nb] = mfma32(col_frag(gt_of(x), 1, nb, lane), pb, dv[nb]);
-      dk[nb] = mfma32(col_frag(qt_of(x), 1, nb, lane), db, dk[nb]);
-    }
-  };
-  // Pruned pass: whether this lane's key is kept for pipeline step i's query block (one
-  // 256-row query tile per 32-row block; the key's 64-key tile counted from
-  // the query chunk's window start).
-  auto keep_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
-    const int x = qidx(i);
-    const int cq = c_lo + x / nqb, blk = x - (x / nqb) * nqb;
-    const int64_t ws = (int64_t)max(0, cq - p.w + 1) * p.C;
-    const int kt = min((int)((key0 + l32 - ws) >> 6), p.nkt - 1);
-    return p.kmask[(((int64_t)bh * p.N + cq) * p.mask_qtiles + (blk >> 3)) * p.nkt + kt] != 0;
-  };
-  // kc: the lane's keep bit for block i; kn receives block i+1's
-  auto iteration = [&](int i, auto prev_c, auto next_c, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn,
-                       const uint32_t (&ph)[4], const uint32_t (&dh)[4], uint32_t (&pco)[4], uint32_t (&dco)[4],
-                       uint32_t kc, uint32_t& kn) __attribute__((always_inline)) {
-    constexpr bool PREV = decltype(prev_c)::value, NEXT = decltype(next_c)::value;
-    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));  // this wave's loads of block i+1 are in LDS
-    __syncthreads();  // every wave's; and every wave is done with iteration i-1
-    if constexpr (SPARSE && NEXT) kn = keep_of(i + 1);  // used in the next iteration
-    if (i + 2 < nblk) issue(i + 2);
-    const unsigned char* qtn = qt_of(i + 1);
-    const unsigned char* gtn = gt_of(i + 1);
-    const unsigned char* qtc = qt_of(i);
-    const unsigned char* gtc = gt_of(i);
-    const unsigned char* qtp = qt_of(i + 3);  // block i-1's buffer
-    const unsigned char* gtp = gt_of(i + 3);
-    const float* lsc = lse_s[i & 3];
-    const float* dlc = del_s[i & 3];
-    bf16x8 qf[3], gf[3], gcf[3], qcf[3];
-    uint32_t pl[4], dl[4];  // P, dS of block i, elements 0-7
-    // fragments of round rr (read two rounds ahead)
-    auto read_round = [&](auto rr_c) __attribute__((always_inline)) {
-      constexpr int rr = decltype(rr_c)::value, sl = rr % 3;
-      if constexpr (NEXT) {
-        qf[sl] = row_frag(qtn, 0, rr, lane);
-        gf[sl] = row_frag(gtn, 0, rr, lane);
-      }
-      if constexpr (rr < 4) {
-        if constexpr (PREV) {
-          gcf[sl] = col_frag(gtp, 1, rr, lane);
-          qcf[sl] = col_frag(qtp, 1, rr, lane);
-        }
-      } else {
-        gcf[sl] = col_frag(gtc, 0, rr - 4, lane);
-        qcf[sl] = col_frag(qtc, 0, rr - 4, lane);
-      }
-    };
-    // the block's lse log2(e) and delta for this lane's 16 rows, read first
-    // (LDS reads complete in order: later fragment reads do not wait on them)
-    f32x4 lr[4], dr[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      lr[g] = *reinterpret_cast<const f32x4*>(lsc + 8 * g + 4 * hh);
-      dr[g] = *reinterpret_cast<const f32x4*>(dlc + 8 * g + 4 * hh);
-    }
-    read_round(std::integral_constant<int, 0>{});
-    read_round(std::integral_constant<int, 1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<0, 8>([&](auto r_c) __attribute__((always_inline)) {
-      constexpr int r = decltype(r_c)::value, sl = r % 3;
-      // output elements 2r, 2r+1 are rows out_row(2r) and out_row(2r) + 1:
-      // entries (2r) % 4 and (2r) % 4 + 1 of group r / 2
-      constexpr int g = r / 2, e = (2 * r) % 4;
-      if constexpr (r + 2 < 8) read_round(std::integral_constant<int, r + 2>{});
-      // four groups, each one product and a quarter of the vector work
-      float t0, t1, p0, p1;
-      if constexpr (NEXT) {
-        if constexpr (r == 0) mfma_v_first(sn, qf[sl], kr[r]);
-        else mfma_v(sn, qf[sl], kr[r]);
-      }
-      t0 = fmaf(sc[2 * r], p.scale_log2, -lr[g][e]);
-      t1 = fmaf(sc[2 * r + 1], p.scale_log2, -lr[g][e + 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NEXT) {
-        if constexpr (r == 0) mfma_v_first(pn, gf[sl], vr[r]);
-        else mfma_v(pn, gf[sl], vr[r]);
-      }
-      p0 = __builtin_amdgcn_exp2f(t0);
-      p1 = __builtin_amdgcn_exp2f(t1);
-      if constexpr (SPARSE) {
-        p0 = kc ? p0 : 0.f;
-        p1 = kc ? p1 : 0.f;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (r < 4) {
-        if constexpr (PREV)
-          dv[r] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]}), dv[r]);
-      } else {
-        dv[r - 4] = mfma32(gcf[sl], __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]}), dv[r - 4]);
-      }
-      const uint32_t pw = pack_bf16(p0, p1);
-      const float u0 = pc[2 * r] - dr[g][e], u1 = pc[2 * r + 1] - dr[g][e + 1];
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (r < 4) {
-        if constexpr (PREV)
-          dk[r] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dh[0], dh[1], dh[2], dh[3]}), dk[r]);
-      } else {
-        dk[r - 4] = mfma32(qcf[sl], __builtin_bit_cast(bf16x8, u32x4{dl[0], dl[1], dl[2], dl[3]}), dk[r - 4]);
-      }
-      const uint32_t dw = pack_bf16(p0 * u0, p1 * u1);
-      if constexpr (r < 4) {
-        pl[r] = pw;
-        dl[r] = dw;
-      } else {
-        pco[r - 4] = pw;
-        dco[r - 4] = dw;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  using F_ = std::false_type;
-  using T_ = std::true_type;
+  // every wave issues its slices of the first two blocks
   if (nblk > 0) {
-    f32x16 s0, p0, s1, p1;
-    uint32_t ca[4], cd[4], cb[4], ce[4];  // carried halves (P, dS) of alternate iterations
-    uint32_t k0 = 1, k1 = 1;              // keep bits of even and odd blocks (pruned pass)
-    if constexpr (SPARSE) k0 = keep_of(0);
     issue(0);
     if (nblk > 1) issue(1);
-    __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
-    __syncthreads();
-    scores(0, s0, p0);
-    if (nblk > 1) iteration(0, F_{}, T_{}, s0, p0, s1, p1, ca, cd, ca, cd, k0, k1);
-    else iteration(0, F_{}, F_{}, s0, p0, s1, p1, ca, cd, ca, cd, k0, k1);
-    int i = 1;
-    for (; i + 2 < nblk; i += 2) {  // iterations i and i+1 both have a next block
-      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
-      iteration(i + 1, T_{}, T_{}, s0, p0, s1, p1, cb, ce, ca, cd, k0, k1);
-    }
-    if (i + 1 < nblk) {  // two left: i (with a next block) and i+1 (the last)
-      iteration(i, T_{}, T_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
-      iteration(i + 1, T_{}, F_{}, s0, p0, s1, p1, cb, ce, ca, cd, k0, k1);
-      tail_products(i + 1, ca, cd);
-    } else if (i < nblk) {  // one left: i, the last
-      iteration(i, T_{}, F_{}, s1, p1, s0, p0, ca, cd, cb, ce, k1, k0);
-      tail_products(i, cb, ce);
-    } else {  // a single block
-      tail_products(0, ca, cd);
-    }
   }
-  // lane = key; element i of block nb = feature 32 nb + out_row(i)
-  float* dvr = p.dv + (bh * L + key0 + l32) * BD;
-  float* dkr = p.dk + (bh * L + key0 + l32) * BD;
-  // the chunk is in the state of chunks j + w .. N-1 (and, bidirectional, in
-  // the future state of chunks 0 .. j - max(w, 1))
-  const bool lin = (j >= p.anchors && j < p.N - p.w) || (p.bidir && j >= max(p.w, 1));
-  if (lin) {
-    const int64_t slot = (int64_t)bh * p.N + j;
-    stage_state<true>(um, ut, p.dS + slot * BD * BD, p.bidir ? p.dS2 + slot * BD * BD : nullptr, tid);
-    __syncthreads();
-    f32x16 o1[4], o2[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) o1[mb] = o2[mb] = f32x16{};
+  if (!grad) {
+    // ---- score wave
+    bf16x8 kr[8], vr[8];  // rows of K and V for this lane's key
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 pk = l32 < nk ? fwd::phi8(kr[ks]) : kr[ks];  // phi(k_t) (0 past the chunk)
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (l32 < nk) {
+        a = ld16(kb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
+        c = ld16(vb + (key0 + l32) * p.st + 16 * ks + 8 * hh);
+      }
+      kr[ks] = __builtin_bit_cast(bf16x8, a);
+      vr[ks] = __builtin_bit_cast(bf16x8, c);
+    }
+    for (int s = 0; s <= nblk; ++s) {
+      __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
+      __syncthreads();
+      if (s + 2 < nblk) issue(s + 2);
+      if (s >= nblk) {
+        __syncthreads();  // the step's second barrier
+        continue;
+      }
+      {
+        const int x = s;
+        uint32_t kc = 1;
+        if constexpr (SPARSE) {
+          const int qi = qidx(x);
+          const int cq = c_lo + qi / nqb, blk = qi - (qi / nqb) * nqb;
+          const int64_t ws = (int64_t)max(0, cq - p.w + 1) * p.C;
+          const int kt = min((int)((key0 + l32 - ws) >> 6), p.nkt - 1);
+          kc = p.kmask[(((int64_t)bh * p.N + cq) * p.mask_qtiles + (blk >> 3)) * p.nkt + kt] != 0;
+        }
+        const unsigned char* qt = ring[x & 3];
+        const unsigned char* gt = ring[4 + (x & 3)];
+        f32x4 lr[4], dr[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        o1[mb] = mfma32(row_frag(ut, 32 * mb, ks, lane), pk, o1[mb]);      // dU^T phi(k)^T: m = n
-        o2[mb] = mfma32(row_frag(um, 32 * mb, ks, lane), vr[ks], o2[mb]);  // dU v^T: m = e
+        for (int g = 0; g < 4; ++g) {
+          lr[g] = *reinterpret_cast<const f32x4*>(lse_s[x & 3] + 8 * g + 4 * hh);
+          dr[g] = *reinterpret_cast<const f32x4*>(del_s[x & 3] + 8 * g + 4 * hh);
+        }
+        bf16x8 qf[8], gf[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          qf[ks] = row_frag(qt, 0, ks, lane);
+          gf[ks] = row_frag(gt, 0, ks, lane);
+        }
+        f32x16 sa, pa;
+        mfma_v_first(sa, qf[0], kr[0]);
+        mfma_v_first(pa, gf[0], vr[0]);
+#pragma unroll
+        for (int ks = 1; ks < 8; ++ks) {
+          mfma_v(sa, qf[ks], kr[ks]);
+          mfma_v(pa, gf[ks], vr[ks]);
+        }
+        // the products go first on the SIMD: the gradient wave starts its own
+        // after this barrier, beside this wave's vector work
+        __syncthreads();
+        uint32_t pk[8], dk8[8];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const int g = e >> 2, ee = e & 3;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sa[e], p.scale_log2, -lr[g][ee]));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sa[e + 1], p.scale_log2, -lr[g][ee + 1]));
+          if constexpr (SPARSE) {
+            p0 = kc ? p0 : 0.f;
+            p1 = kc ? p1 : 0.f;
+          }
+          pk[e >> 1] = pack_bf16(p0, p1);
+          dk8[e >> 1] = pack_bf16(p0 * (pa[e] - dr[g][ee]), p1 * (pa[e + 1] - dr[g][ee + 1]));
+        }
+        u32x4* xo = &xch[x & 1][kw][0][0][0];
+        xo[lane] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        xo[64 + lane] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+        xo[128 + lane] = u32x4{dk8[0], dk8[1], dk8[2], dk8[3]};
+        xo[192 + lane] = u32x4{dk8[4], dk8[5], dk8[6], dk8[7]};
       }
     }
-    if (l32 < nk) {
-      const bf16_t* kt = kb + (key0 + l32) * p.st;  // phi' argument
+  } else {
+    // ---- gradient wave
+    f32x16 dv[4], dk[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) dv[nb] = dk[nb] = f32x16{};
+    for (int s = 0; s <= nblk; ++s) {
+      __builtin_amdgcn_s_waitcnt(fwd::wait_vm(0));
+      __syncthreads();
+      if (s + 2 < nblk) issue(s + 2);
+      if (s < 1) {
+        __syncthreads();  // the step's second barrier
+        continue;
+      }
+      {
+        const int x = s - 1;
+        const unsigned char* qt = ring[x & 3];
+        const unsigned char* gt = ring[4 + (x & 3)];
+        const u32x4* xi = &xch[x & 1][kw][0][0][0];
+        const u32x4 ph0 = xi[lane], ph1 = xi[64 + lane], dh0 = xi[128 + lane], dh1 = xi[192 + lane];
+        bf16x8 gc[2][4], qc[2][4];  // the block's transposed fragments, read before the barrier
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            gc[ks][nb] = col_frag(gt, ks, nb, lane);
+            qc[ks][nb] = col_frag(qt, ks, nb, lane);
+          }
+        __syncthreads();  // the score wave's products are done
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          dv[nb] = mfma32(gc[0][nb], __builtin_bit_cast(bf16x8, ph0), dv[nb]);
+          dk[nb] = mfma32(qc[0][nb], __builtin_bit_cast(bf16x8, dh0), dk[nb]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          dv[nb] = mfma32(gc[1][nb], __builtin_bit_cast(bf16x8, ph1), dv[nb]);
+          dk[nb] = mfma32(qc[1][nb], __builtin_bit_cast(bf16x8, dh1), dk[nb]);
+        }
+      }
+    }
+    // the loads issued by this wave are complete (nothing after the last wait)
+    // ---- epilogue below, after the staging shared with the score waves
+    const bool lin = (j >= p.anchors && j < p.N - p.w) || (p.bidir && j >= max(p.w, 1));
+    float* dvr = p.dv + (bh * L + key0 + l32) * BD;
+    float* dkr = p.dk + (bh * L + key0 + l32) * BD;
+    if (lin) {
+      __syncthreads();  // every wave is done with the ring
+      const int64_t slot = (int64_t)bh * p.N + j;
+      unsigned char* um = ring[0];
+      unsigned char* ut = ring[4];
+      stage_state<true, 2 * TB>(um, ut, p.dS + slot * BD * BD, p.bidir ? p.dS2 + slot * BD * BD : nullptr, tid);
+      __syncthreads();
+      // this lane's key row (lanes past the chunk read its last row; their
+      // columns of the products are not written)
+      const int64_t krw = min(key0 + l32, (int64_t)(j + 1) * p.C - 1);
+      const bf16_t* krow = kb + krw * p.st;
+      const bf16_t* vrow = vb + krw * p.st;
       const float* dz = p.dz + ((int64_t)bh * p.N + j) * BD;
       const float* dz2 = p.bidir ? p.dz2 + ((int64_t)bh * p.N + j) * BD : nullptr;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        f32x16 o1 = {}, o2 = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 kk = __builtin_bit_cast(bf16x8, ld16(krow + 16 * ks + 8 * hh));
+          const bf16x8 vv = __builtin_bit_cast(bf16x8, ld16(vrow + 16 * ks + 8 * hh));
+          o1 = mfma32(row_frag(ut, 32 * nb, ks, lane), fwd::phi8(kk), o1);  // dU^T phi(k)^T: m = n
+          o2 = mfma32(row_frag(um, 32 * nb, ks, lane), vv, o2);             // dU v^T: m = e
+        }
+        if (l32 < nk) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int f = 32 * nb + 8 * rr + 4 * hh;
+            f32x4 zz = *reinterpret_cast<const f32x4*>(dz + f);
+            if (dz2 != nullptr) zz += *reinterpret_cast<const f32x4*>(dz2 + f);
+            float dphi[4];
+            dphi4(krow, f, dphi);
+            f32x4 a, k4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              a[i] = dv[nb][4 * rr + i] + o1[4 * rr + i];
+              k4[i] = dk[nb][4 * rr + i] * p.scale + (o2[4 * rr + i] + zz[i]) * dphi[i];
+            }
+            *reinterpret_cast<f32x4*>(dvr + f) = a;
+            *reinterpret_cast<f32x4*>(dkr + f) = k4;
+          }
+        }
+      }
+    } else if (l32 < nk) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int f = 32 * nb + 8 * rr + 4 * hh;
-          f32x4 zz = *reinterpret_cast<const f32x4*>(dz + f);
-          if (dz2 != nullptr) zz += *reinterpret_cast<const f32x4*>(dz2 + f);
-          float dphi[4];
-          dphi4(kt, f, dphi);
-          f32x4 a, k4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[i] = dv[nb][4 * rr + i];
-            k4[i] = dk[nb][4 * rr + i] * p.scale;
-            a[i] += o1[nb][4 * rr + i];
-            k4[i] += (o2[nb][4 * rr + i] + zz[i]) * dphi[i];
-          }
-          *reinterpret_cast<f32x4*>(dvr + f) = a;
-          *reinterpret_cast<f32x4*>(dkr + f) = k4;
+          *reinterpret_cast<f32x4*>(dvr + f) =
+              f32x4{dv[nb][4 * rr], dv[nb][4 * rr + 1], dv[nb][4 * rr + 2], dv[nb][4 * rr + 3]};
+          *reinterpret_cast<f32x4*>(dkr + f) = f32x4{dk[nb][4 * rr] * p.scale, dk[nb][4 * rr + 1] * p.scale,
+                                                     dk[nb][4 * rr + 2] * p.scale, dk[nb][4 * rr + 3] * p.scale};
         }
     }
-  } else if (l32 < nk) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int f = 32 * nb + 8 * rr + 4 * hh;
-        *reinterpret_cast<f32x4*>(dvr + f) = f32x4{dv[nb][4 * rr], dv[nb][4 * rr + 1], dv[nb][4 * rr + 2], dv[nb][4 * rr + 3]};
-        *reinterpret_cast<f32x4*>(dkr + f) = f32x4{dk[nb][4 * rr] * p.scale, dk[nb][4 * rr + 1] * p.scale,
-                                                   dk[nb][4 * rr + 2] * p.scale, dk[nb][4 * rr + 3] * p.scale};
-      }
+    return;
+  }
+  // score waves: take part in the staging of dU, then leave
+  const bool lin = (j >= p.anchors && j < p.N - p.w) || (p.bidir && j >= max(p.w, 1));
+  if (lin) {
+    __syncthreads();
+    const int64_t slot = (int64_t)bh * p.N + j;
+    stage_state<true, 2 * TB>(ring[0], ring[4], p.dS + slot * BD * BD, p.bidir ? p.dS2 + slot * BD * BD : nullptr, tid);
+    __syncthreads();
   }
 }
 
@@ -857,10 +791,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   }
   const dim3 grid((unsigned)(BH * p.N * tiles128));
   if (p.kmask != nullptr) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, grid, dim3(TB), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_pp_kernel<true>, grid, dim3(2 * TB), 0, s, p);
     hipLaunchKernelGGL(bwd_dq_kernel<true>, grid, dim3(TB), 0, s, p);
   } else {
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, grid, dim3(TB), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkdv_pp_kernel<false>, grid, dim3(2 * TB), 0, s, p);
     hipLaunchKernelGGL(bwd_dq_kernel<false>, grid, dim3(TB), 0, s, p);
   }
   return hipGetLastError();
