@@ -310,6 +310,10 @@ def main():
     ap.add_argument("--only", choices=["fwd", "scan", "stream", "stream_sparse", "sparse", "bidir", "anchor", "bwd", "bwd_bidir",
                                        "bwd_anchor", "bwd_sparse"],
                     default=None)
+    # the GPU's clocks ramp up over the first ~0.1-0.2 s of load after an idle
+    # gap: before the W warm-up steps, steps run untimed for this many seconds,
+    # so the timed steps see settled clocks whatever W is
+    ap.add_argument("--settle", type=float, default=0.25)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
@@ -564,6 +568,14 @@ def main():
     # ---- the contract: W warmup steps, then exactly K timed steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    t_settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle0 < args.settle:
+        for _ in range(8):
+            step()
+        n_settle += 8
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle0
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -678,6 +690,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": settle_s, "steps": n_settle},
         "ms_per_step": t_step * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
